@@ -1,0 +1,329 @@
+"""FAST-AR attention step: plain fp64 CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, ``__graft_entry__.smoke()`` and the cpu_baseline leg of
+``bench.py`` may import this module.  It never runs on the product path.
+
+Sources (the FAST-AR pages; cited below by page and section):
+
+* "FAST-AR: NVIDIA Cracks the Video Diffusion Bottleneck" (deltav-cc blog),
+  sections "1. TempCache", "2. AnnCA", "3. AnnSA"  -- cited as *blog, <section>*.
+* "Fast Autoregressive Video Diffusion and World Models with Temporal Cache
+  Compression and Sparse Attention" (gist.science technical summary),
+  "2. Core Components", parts A (TempCache), B (AnnCA), C (AnnSA)
+  -- cited as *summary, Core Components <part>*.
+* the arXiv abstract of the same paper (mlsanity.com index page)
+  -- cited as *abstract*.
+
+Every function works on one attention head; heads are independent (the pages
+never couple them).  Floating point is fp64 throughout; inputs that are stored
+as bf16 or fp32 enter as their exact values.
+
+Readings of points the pages leave open (each repeated where it is used):
+
+R1  ANN = random-hyperplane (sign) LSH: bit p of a token's bucket id is
+    [<x, r_p> >= 0]; plane p is bit p.  Queries, cached keys, current keys
+    and prompt keys are hashed with the same planes of their head ("shared
+    embedding space", summary, Core Components B).
+R2  One hash table, one bucket per token (blog, "3. AnnSA": "same bucket(s)").
+R3  AnnSA key context = [valid cache slots 0..n-1 ; current chunk in token
+    order]; a query attends to every key of its bucket, no causal mask; an
+    empty bucket gives O = 0 and lse = -inf; softmax scale is a parameter
+    (1/sqrt(d) by default).
+R4  AnnCA keeps, per frame, the prompt tokens whose bucket holds at least one
+    query of that frame, and attends densely over the kept tokens in
+    ascending order; no kept token gives O = 0.
+R5  TempCache top-1: cosine between the current query and each cached key of
+    the query's own bucket (ANN instead of a full attention map, summary,
+    Core Components A); candidates are previous-frame keys only (the valid
+    cache slots).  Ties go to the lowest slot.  A zero norm gives cosine 0.
+R6  Merge: matched = has a candidate and cosine >= tau (inclusive).  The
+    current token replaces the matched slot ("only the most recent
+    representative stays", blog, "1. TempCache").  When several current
+    tokens match one slot, the largest token index (the most recent) wins
+    and the others are dropped.
+R7  Unmatched tokens are appended in token order; once the cache is full they
+    replace the slots with the oldest timestamps (ties: lower slot first),
+    never a slot refreshed in this update.  The replaced slots are filled in
+    ascending slot order.
+R8  Inserted and refreshed slots get timestamp ``step``.
+R9  A ``best`` value outside [0, n) counts as "no candidate".
+
+Tie flags (the decision is numerically fragile; a parallel fp32 result may
+legitimately differ there): a hash bit whose |<x, r>| / (|x| |r|) < 1e-5; an
+argmax whose runner-up cosine is within 1e-5; a threshold test with
+|cos - tau| < 1e-5.
+
+Parity pins (tests/test_oracle_*.py): every function is pinned by closed forms,
+library routines or hand-worked fixtures; see the tests' docstrings.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+TIE_EPS = 1e-5
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# ANN hash  (summary, Core Components A and B: "LSH or quantization"; R1, R2)
+# ---------------------------------------------------------------------------
+
+def ann_hash(x, planes) -> Tuple[np.ndarray, np.ndarray]:
+    """Bucket id of every row of ``x`` [N, d] under the hyperplanes ``planes``
+    [P, d]:  id = sum_p [<x, r_p> >= 0] * 2**p.
+
+    Returns ``(ids, tie_bits)``, both uint16 [N]; ``tie_bits`` marks the planes
+    whose normalised projection is within 1e-5 of zero."""
+    X = _f64(x)
+    R = _f64(planes).reshape(-1, X.shape[1]) if np.size(planes) else np.zeros((0, X.shape[1]))
+    N, P = X.shape[0], R.shape[0]
+    ids = np.zeros(N, np.int64)
+    tie = np.zeros(N, np.int64)
+    if P == 0:
+        return ids.astype(np.uint16), tie.astype(np.uint16)
+    proj = X @ R.T
+    denom = np.linalg.norm(X, axis=1)[:, None] * np.linalg.norm(R, axis=1)[None, :]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.where(denom > 0, np.abs(proj) / np.where(denom > 0, denom, 1.0), 0.0)
+    for p in range(P):
+        ids |= (proj[:, p] >= 0).astype(np.int64) << p
+        tie |= (rel[:, p] < TIE_EPS).astype(np.int64) << p
+    return ids.astype(np.uint16), tie.astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Bucket grouping  (summary, Core Components C: block-sparse attention needs
+# the tokens of each bucket gathered together)
+# ---------------------------------------------------------------------------
+
+def bucket_sort(ids, P: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Stable grouping of token indices by bucket.
+
+    ``off[b]`` = number of tokens whose id is below b (``off[B]`` = N);
+    ``perm[off[b]:off[b+1]]`` = the indices with id b, ascending."""
+    ids = np.asarray(ids).astype(np.int64)
+    B = 1 << P
+    off = np.zeros(B + 1, np.int64)
+    parts: List[np.ndarray] = []
+    for b in range(B):
+        members = np.nonzero(ids == b)[0]
+        parts.append(members)
+        off[b + 1] = off[b] + members.size
+    perm = np.concatenate(parts) if parts else np.zeros(0, np.int64)
+    return off.astype(np.int32), perm.astype(np.int32)
+
+
+def key_context(cache_k, cache_v, cache_ids, n: int, k_cur, v_cur, kcur_ids):
+    """AnnSA's key context (R3): valid cache slots 0..n-1, then the current chunk."""
+    return (np.concatenate([_f64(cache_k[:n]), _f64(k_cur)], 0),
+            np.concatenate([_f64(cache_v[:n]), _f64(v_cur)], 0),
+            np.concatenate([np.asarray(cache_ids[:n]), np.asarray(kcur_ids)]).astype(np.int64))
+
+
+# ---------------------------------------------------------------------------
+# AnnSA  (blog, "3. AnnSA"; summary, Core Components C; R2, R3)
+# ---------------------------------------------------------------------------
+
+def annsa(q, q_ids, k, v, k_ids, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Each query attends only to the keys of its own bucket:
+    O_i = sum_{j: idk_j = idq_i} softmax_j(scale * <q_i, k_j>) v_j,
+    lse_i = log sum_{j in bucket} exp(scale * <q_i, k_j>).
+    Queries whose bucket holds no key get O = 0, lse = -inf."""
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    qid = np.asarray(q_ids).astype(np.int64)
+    kid = np.asarray(k_ids).astype(np.int64)
+    O = np.zeros((Q.shape[0], V.shape[1]))
+    lse = np.full(Q.shape[0], -np.inf)
+    for b in np.unique(qid):
+        qi = np.nonzero(qid == b)[0]
+        kj = np.nonzero(kid == b)[0]
+        if kj.size == 0:
+            continue
+        S = (Q[qi] @ K[kj].T) * scale
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        l = E.sum(axis=1, keepdims=True)
+        O[qi] = (E @ V[kj]) / l
+        lse[qi] = m[:, 0] + np.log(l[:, 0])
+    return O, lse
+
+
+# ---------------------------------------------------------------------------
+# AnnCA  (blog, "2. AnnCA"; summary, Core Components B; R4)
+# ---------------------------------------------------------------------------
+
+def annca(q, q_ids, frame_len: int, kp, vp, kp_ids, scale: float):
+    """Per frame f (queries f*frame_len .. (f+1)*frame_len-1): keep the prompt
+    tokens whose bucket holds at least one query of the frame, then dense
+    softmax cross-attention over the kept tokens.
+
+    Returns ``(O [Nq, d], keep [F, L] bool)``."""
+    Q, Kp, Vp = _f64(q), _f64(kp), _f64(vp)
+    Nq, L = Q.shape[0], Kp.shape[0]
+    if frame_len <= 0 or Nq % frame_len:
+        raise ValueError("frame_len must divide the number of queries")
+    F = Nq // frame_len
+    qid = np.asarray(q_ids).astype(np.int64)
+    pid = np.asarray(kp_ids).astype(np.int64)
+    keep = np.zeros((F, L), bool)
+    O = np.zeros((Nq, Vp.shape[1]))
+    for f in range(F):
+        rows = slice(f * frame_len, (f + 1) * frame_len)
+        present = set(int(i) for i in qid[rows])
+        keep[f] = [int(t) in present for t in pid]
+        idx = np.nonzero(keep[f])[0]
+        if idx.size == 0:
+            continue
+        S = (Q[rows] @ Kp[idx].T) * scale
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        O[rows] = (E @ Vp[idx]) / E.sum(axis=1, keepdims=True)
+    return O, keep
+
+
+# ---------------------------------------------------------------------------
+# TempCache  (blog, "1. TempCache"; summary, Core Components A; R5-R9)
+# ---------------------------------------------------------------------------
+
+def tempcache_top1(q, q_ids, cache_k, cache_ids, n: int):
+    """For each current query, its most similar previous-frame key within the
+    query's bucket (R5).
+
+    Returns ``(best [N] int64 (-1: no candidate), cos [N] (-inf: none),
+    argmax_tie [N] bool, near: list of the candidate slots whose cosine is
+    within 1e-5 of the maximum)``."""
+    Q = _f64(q)
+    K = _f64(cache_k[:n])
+    kid = np.asarray(cache_ids[:n]).astype(np.int64)
+    qid = np.asarray(q_ids).astype(np.int64)
+    N = Q.shape[0]
+    best = np.full(N, -1, np.int64)
+    cos = np.full(N, -np.inf)
+    tie = np.zeros(N, bool)
+    near: List[np.ndarray] = [np.zeros(0, np.int64) for _ in range(N)]
+    qn = np.linalg.norm(Q, axis=1)
+    kn = np.linalg.norm(K, axis=1)
+    for b in np.unique(qid):
+        qi = np.nonzero(qid == b)[0]
+        kj = np.nonzero(kid == b)[0]
+        if kj.size == 0:
+            continue
+        den = qn[qi][:, None] * kn[kj][None, :]
+        dots = Q[qi] @ K[kj].T
+        c = np.where(den > 0, dots / np.where(den > 0, den, 1.0), 0.0)
+        a = np.argmax(c, axis=1)            # first maximum = lowest slot
+        s = c[np.arange(qi.size), a]
+        best[qi] = kj[a]
+        cos[qi] = s
+        for r, i in enumerate(qi):
+            close = kj[c[r] >= s[r] - TIE_EPS]
+            near[i] = close
+            tie[i] = close.size > 1
+    return best, cos, tie, near
+
+
+def tempcache_commit(cache: Dict[str, np.ndarray], n: int, k_cur, v_cur, kcur_ids,
+                     best, cos, tau: float, step: int):
+    """Apply one chunk's merge/append/evict to one head's cache (R6-R9).
+
+    ``cache`` holds ``k``, ``v`` [cap, d], ``ids`` [cap], ``ts`` [cap]; it is
+    not modified.  Returns a dict with the new ``cache``, ``n`` (valid slots
+    after the update), ``dest`` [N] (slot each token was written to, -1 if it
+    was merged away), ``evicted`` [N] (-1 padded, ascending slots),
+    ``counts`` = (matched, refreshed, dropped, appended, evicted),
+    ``matched`` [N] and ``thr_tie`` [N] (|cos - tau| < 1e-5)."""
+    K, V = cache["k"], cache["v"]
+    ids, ts = np.asarray(cache["ids"]), np.asarray(cache["ts"])
+    cap = K.shape[0]
+    best = np.asarray(best).astype(np.int64)
+    cos = _f64(cos)
+    N = best.size
+    if N > cap:
+        raise ValueError("a chunk larger than the cache capacity cannot be committed")
+    if not 0 <= n <= cap:
+        raise ValueError("n must lie in [0, cap]")
+    has_cand = (best >= 0) & (best < n)                      # R9
+    matched = has_cand & (cos >= tau)                          # R6, inclusive
+    claim = np.full(cap, -1, np.int64)
+    for i in range(N):
+        if matched[i]:
+            claim[best[i]] = max(claim[best[i]], i)            # most recent wins
+    refreshed = claim >= 0
+    dest = np.full(N, -1, np.int64)
+    for j in np.nonzero(refreshed)[0]:
+        dest[claim[j]] = j
+    unmatched = [i for i in range(N) if not matched[i]]
+    u = len(unmatched)
+    e = max(0, n + u - cap)
+    candidates = [j for j in range(n) if not refreshed[j]]
+    oldest = sorted(candidates, key=lambda j: (int(ts[j]), j))[:e]    # R7
+    evicted_slots = sorted(oldest)
+    n_new = min(cap, n + u)
+    free = list(range(n, n_new)) + evicted_slots
+    for slot, i in zip(free, unmatched):
+        dest[i] = slot
+    new = {"k": np.array(K, copy=True), "v": np.array(V, copy=True),
+           "ids": np.array(ids, copy=True), "ts": np.array(ts, copy=True)}
+    kcur_ids = np.asarray(kcur_ids)
+    for i in range(N):
+        j = dest[i]
+        if j >= 0:
+            new["k"][j] = k_cur[i]
+            new["v"][j] = v_cur[i]
+            new["ids"][j] = kcur_ids[i]
+            new["ts"][j] = step                                # R8
+    evicted = np.full(N, -1, np.int64)
+    evicted[:e] = evicted_slots
+    n_matched = int(matched.sum())
+    n_ref = int(refreshed.sum())
+    counts = np.array([n_matched, n_ref, n_matched - n_ref, n_new - n, e], np.int64)
+    thr_tie = has_cand & (np.abs(cos - tau) < TIE_EPS)
+    return {"cache": new, "n": n_new, "dest": dest, "evicted": evicted, "counts": counts,
+            "matched": matched, "thr_tie": thr_tie}
+
+
+def tempcache_update(cache: Dict[str, np.ndarray], n: int, q, q_ids, k_cur, v_cur, kcur_ids,
+                     tau: float, step: int):
+    """Top-1 search, then commit (blog, "1. TempCache")."""
+    best, cos, tie, near = tempcache_top1(q, q_ids, cache["k"], cache["ids"], n)
+    out = tempcache_commit(cache, n, k_cur, v_cur, kcur_ids, best, cos, tau, step)
+    out.update(best=best, cos=cos, argmax_tie=tie, near=near)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# One attention step, all heads: hash -> AnnSA -> AnnCA -> TempCache commit
+# (attend to [old cache ; current chunk], then commit the chunk)
+# ---------------------------------------------------------------------------
+
+def attention_step(q, k_cur, v_cur, cache_k, cache_v, cache_ids, cache_ts, n_valid,
+                   planes, kp, vp, frame_len: int, tau: float, step: int,
+                   scale: Optional[float] = None, heads=None) -> Dict[str, object]:
+    """Runs the whole step head by head; arrays carry a leading head axis."""
+    H = q.shape[0] if heads is None else len(heads)
+    heads = range(q.shape[0]) if heads is None else heads
+    d = q.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    res: Dict[str, list] = {k: [] for k in ("q_ids", "kcur_ids", "kp_ids", "hash_tie",
+                                            "o_sa", "lse", "o_ca", "keep", "tc")}
+    for h in heads:
+        qi, tq = ann_hash(q[h], planes[h])
+        ki, tk = ann_hash(k_cur[h], planes[h])
+        pi, tp = ann_hash(kp[h], planes[h])
+        n = int(n_valid[h])
+        K, V, kid = key_context(cache_k[h], cache_v[h], cache_ids[h], n, k_cur[h], v_cur[h], ki)
+        o_sa, lse = annsa(q[h], qi, K, V, kid, scale)
+        o_ca, keep = annca(q[h], qi, frame_len, kp[h], vp[h], pi, scale)
+        tc = tempcache_update({"k": cache_k[h], "v": cache_v[h], "ids": cache_ids[h],
+                               "ts": cache_ts[h]}, n, q[h], qi, k_cur[h], v_cur[h], ki, tau, step)
+        for key, val in (("q_ids", qi), ("kcur_ids", ki), ("kp_ids", pi),
+                         ("hash_tie", (tq, tk, tp)), ("o_sa", o_sa), ("lse", lse),
+                         ("o_ca", o_ca), ("keep", keep), ("tc", tc)):
+            res[key].append(val)
+    res["H"] = H
+    return res
