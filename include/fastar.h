@@ -1,0 +1,223 @@
+/*
+ * fastar.h -- C ABI of the FAST-AR attention step for AMD Instinct MI355X (gfx950).
+ *
+ * One autoregressive denoising step's attention over a bounded KV cache, as
+ * described on the FAST-AR pages ("Fast Autoregressive Video Diffusion and
+ * World Models with Temporal Cache Compression and Sparse Attention"; the
+ * gist.science technical summary, "2. Core Components", and the FAST-AR blog
+ * post, sections "1. TempCache", "2. AnnCA", "3. AnnSA").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer unless marked "host".
+ *  - Tensors are dense and row-major: [H][N][d] means d is fastest, then N,
+ *    then the head index H.  Heads are fully independent.
+ *  - Element types: FASTAR_F32 (IEEE binary32) or FASTAR_BF16 (bfloat16 bits
+ *    stored as uint16).  Hyperplanes are always fp32.  d is 64 or 128.
+ *  - ``P`` is the number of hyperplanes; bucket ids are in [0, 2^P).  The
+ *    bucketed calls accept P in [0, FASTAR_MAX_PLANES]; ``fastar_ann_hash``
+ *    accepts P up to FASTAR_MAX_HASH_PLANES.  Id bits at or above P are
+ *    ignored wherever ids are consumed.
+ *  - ``stream`` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and returns without synchronising the host;
+ *    results are valid once the stream has reached that point.
+ *  - The caller owns all memory: inputs, outputs, the cache and the scratch
+ *    workspace.  The library allocates no device memory.  A workspace must be
+ *    at least the size returned by the matching ``*_workspace`` query and is
+ *    clobbered by the call; buffers must stay alive until the stream work has
+ *    completed.  Calls on one stream are ordered; two calls that share a
+ *    workspace or a cache must not run concurrently on different streams.
+ *  - Arguments are validated on the host before anything is launched.  A
+ *    negative status means nothing was enqueued and nothing was modified.
+ *    FASTAR_EHIP reports a HIP launch error after validation; outputs (and,
+ *    for fastar_tempcache_update, the cache) are then undefined.
+ *  - Sizes are int32; every tensor must hold fewer than 2^31 elements.
+ *  - Pointers to d-wide tensors (activations, cache K/V, planes) must be
+ *    16-byte aligned (FASTAR_EINVAL otherwise); a tensor with no elements
+ *    may be passed as NULL.
+ */
+#ifndef FASTAR_H
+#define FASTAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FASTAR_ABI_VERSION 1
+#define FASTAR_MAX_PLANES 10      /* bucketed calls: at most 1024 buckets per head */
+#define FASTAR_MAX_HASH_PLANES 16 /* ids are uint16 */
+
+typedef enum {
+    FASTAR_OK = 0,
+    FASTAR_EINVAL = -1,      /* null pointer, negative size, non-finite scalar */
+    FASTAR_EDTYPE = -2,      /* unknown dtype, or dtypes that must agree do not */
+    FASTAR_ESHAPE = -3,      /* d not 64/128, P out of range, frame_len not dividing Nq, H mismatch */
+    FASTAR_EWORKSPACE = -4,  /* workspace smaller than the query returned (or NULL with size > 0) */
+    FASTAR_ECAPACITY = -5,   /* a chunk larger than the cache capacity */
+    FASTAR_EHIP = -6         /* HIP error while enqueueing */
+} fastar_status;
+
+typedef enum { FASTAR_F32 = 0, FASTAR_BF16 = 1 } fastar_dtype;
+
+/* One attention layer's bounded KV cache, all heads.  The struct itself lives
+ * in host memory; its array members are device pointers.
+ *   k, v     [H][cap][d] of ``dtype``
+ *   ids      [H][cap]  bucket id of the key held in each slot
+ *   ts       [H][cap]  timestamp (step) at which each slot was written
+ *   n_valid  [H]       number of valid slots; slots 0..n_valid[h]-1 are valid.
+ * n_valid stays on the device so that a step never waits on the host; values
+ * outside [0, cap] are clamped when read. */
+typedef struct {
+    int32_t H;
+    int32_t cap;
+    int32_t d;
+    int32_t dtype;            /* fastar_dtype of k and v */
+    void* k;
+    void* v;
+    uint16_t* ids;
+    int32_t* ts;
+    int32_t* n_valid;
+} fastar_cache;
+
+/* Status name, e.g. "FASTAR_ESHAPE" (static storage, never NULL). */
+const char* fastar_status_string(int32_t status);
+int32_t fastar_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * ANN bucket ids (summary, Core Components A and B: queries and keys are
+ * projected into a shared LSH space; read as random-hyperplane sign hashing).
+ *
+ *   ids[h][i] = sum_{p<P} [ <x[h][i], planes[h][p]> >= 0 ] << p
+ *
+ * x       [H][N][d] of ``dtype``      planes  [H][P][d] fp32
+ * ids     [H][N] uint16 (output)
+ * P in [0, 16]; P = 0 puts every token in bucket 0.  The projection is
+ * accumulated in fp32; a projection within fp32 rounding of 0 may take either
+ * sign.
+ * ------------------------------------------------------------------------ */
+fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
+                              const float* planes, int32_t P, uint16_t* ids, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stable grouping of tokens by bucket -- the block-sparse layout AnnSA runs
+ * on (summary, Core Components C).  Exposed for callers that reuse one
+ * grouping across layers.
+ *
+ * ids   [H][N] uint16 (bits >= P ignored)
+ * off   [H][2^P + 1] int32 (output): off[h][b] = #tokens of head h with id < b
+ * perm  [H][N] int32 (output): perm[h][off[h][b] .. off[h][b+1]) = the token
+ *       indices with id b, ascending.  Bit-exact and deterministic.
+ * ------------------------------------------------------------------------ */
+size_t fastar_bucket_sort_workspace(int32_t H, int32_t N, int32_t P);
+fastar_status fastar_bucket_sort(const uint16_t* ids, int32_t H, int32_t N, int32_t P,
+                                 int32_t* off, int32_t* perm, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * AnnSA: bucket-restricted self-attention (blog, "3. AnnSA"; summary, Core
+ * Components C).  Key context of head h = [cache slots 0..n_valid[h]-1 ;
+ * the Ncur current keys in token order].  Query i attends to exactly the
+ * context keys whose id equals q_ids[h][i]:
+ *   out[h][i] = sum_j softmax_j(scale * <q_i, k_j>) v_j,
+ *   lse[h][i] = log sum_j exp(scale * <q_i, k_j>),
+ * with out = 0 and lse = -inf when the bucket holds no key.  No causal mask.
+ *
+ * q         [H][Nq][d] of ``dtype``      q_ids [H][Nq] uint16
+ * cache     host pointer, may be NULL (no cached keys); its H, d and dtype
+ *           must equal the call's
+ * k_cur, v_cur [H][Ncur][d] of ``dtype``, kcur_ids [H][Ncur]; Ncur may be 0
+ * scale     softmax scale (finite); 1/sqrt(d) is the usual value
+ * out       [H][Nq][d] of ``out_dtype`` (FASTAR_F32 or FASTAR_BF16)
+ * lse       [H][Nq] fp32, may be NULL
+ * ws        workspace of fastar_annsa_workspace(H, Nq, cap, Ncur, P) bytes,
+ *           cap = cache ? cache->cap : 0
+ * Products are bf16 x bf16 (or fp32 x fp32) on the matrix cores with fp32
+ * accumulation; softmax is fp32.
+ * ------------------------------------------------------------------------ */
+size_t fastar_annsa_workspace(int32_t H, int32_t Nq, int32_t cap, int32_t Ncur, int32_t P);
+fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                   int32_t d, int32_t dtype, const fastar_cache* cache,
+                                   const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
+                                   int32_t Ncur, int32_t P, float scale, void* out,
+                                   int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * AnnCA: frame-relevant prompt pruning + cross-attention (blog, "2. AnnCA";
+ * summary, Core Components B).  Queries are split into F = Nq / frame_len
+ * frames.  For frame f, prompt token t is kept iff some query of the frame
+ * shares its bucket; each query of the frame attends densely (softmax, scale)
+ * over the kept tokens of its frame.  No kept token gives out = 0.
+ *
+ * q [H][Nq][d], q_ids [H][Nq]; kp, vp [H][L][d]; kp_ids [H][L]
+ * out        [H][Nq][d] of ``out_dtype``
+ * keep       [H][F][L] uint8 (0/1), may be NULL
+ * keep_count [H][F] int32, may be NULL
+ * frame_len must divide Nq.  L may be 0.
+ * ------------------------------------------------------------------------ */
+size_t fastar_annca_workspace(int32_t H, int32_t Nq, int32_t frame_len, int32_t L, int32_t P);
+fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                   int32_t frame_len, int32_t d, int32_t dtype, const void* kp,
+                                   const void* vp, const uint16_t* kp_ids, int32_t L, int32_t P,
+                                   float scale, void* out, int32_t out_dtype, uint8_t* keep,
+                                   int32_t* keep_count, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * TempCache commit of one chunk (blog, "1. TempCache"; summary, Core
+ * Components A).  Per head, with n = n_valid[h] before the call:
+ *  1. top-1: for each current token i, best[i] = the valid slot j < n with
+ *     ids[j] == q_ids[i] maximising cos(q_i, k_j) (ties: lowest j; a zero
+ *     norm gives cosine 0); -1 and cos = -inf if the bucket has no slot.
+ *     Skipped when best_in and cos_in are given (then those are used; a
+ *     best_in value outside [0, n) means "no candidate").
+ *  2. matched[i] = best[i] >= 0 && cos[i] >= tau.  Each matched slot is
+ *     refreshed with the current token of largest index that matched it
+ *     (k, v, id <- the token's k_cur, v_cur, kcur_id; ts <- step); the other
+ *     tokens that matched the same slot are dropped (merged away).
+ *  3. the u unmatched tokens, in token order, fill slots n, n+1, ... up to
+ *     cap, then the e = max(0, n + u - cap) non-refreshed slots with the
+ *     smallest (ts, slot), taken in ascending slot order.
+ *     n_valid[h] <- min(cap, n + u), so it never exceeds cap.
+ * Outputs (each may be NULL):
+ *   best [H][N] int32, best_cos [H][N] fp32 (step 1's result, or the inputs),
+ *   dest [H][N] int32 (slot written by each token, -1 if dropped),
+ *   evicted [H][N] int32 (replaced slots ascending, -1 padded),
+ *   counts [H][5] int32 = {matched, refreshed, dropped, appended, evicted}.
+ * Requires N <= cache->cap (else FASTAR_ECAPACITY) and a non-NaN tau.
+ * q, k_cur, v_cur are [H][N][d] of cache->dtype; q_ids, kcur_ids [H][N].
+ * Slot order, dest, evicted and counts are deterministic.
+ * ------------------------------------------------------------------------ */
+size_t fastar_tempcache_workspace(int32_t H, int32_t N, int32_t cap, int32_t P);
+fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
+                                      const uint16_t* q_ids, const void* k_cur, const void* v_cur,
+                                      const uint16_t* kcur_ids, int32_t N, int32_t P, float tau,
+                                      int32_t step, const int32_t* best_in, const float* cos_in,
+                                      int32_t* best, float* best_cos, int32_t* dest,
+                                      int32_t* evicted, int32_t* counts, void* ws,
+                                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Optional per-kernel timing, for measurement only.  While enabled, every
+ * kernel the library enqueues is bracketed by HIP events on its own stream
+ * (at most FASTAR_TIMER_MAX launches are recorded).  fastar_timer_stop waits
+ * for those events, fills up to ``max`` entries (one per kernel name: the
+ * number of launches and their summed duration in ms), returns the number of
+ * distinct kernels, and disables timing.  Process-wide, not thread-safe.
+ * ------------------------------------------------------------------------ */
+#define FASTAR_TIMER_MAX 8192
+typedef struct {
+    char name[48];
+    int32_t launches;
+    float total_ms;
+} fastar_kernel_time;
+fastar_status fastar_timer_start(void);
+int32_t fastar_timer_stop(fastar_kernel_time* out, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FASTAR_H */

@@ -1,0 +1,220 @@
+"""FAST-AR attention step on AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of ``libfastar.so`` (include/fastar.h): each
+function checks tensor shapes and dtypes, passes raw device pointers and the
+current HIP stream, and returns the output tensors.  Every step of the
+computation runs in the library's HIP kernels; PyTorch only provides device
+memory and the stream.  Names follow the C ABI without its ``fastar_`` prefix.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import FASTAR_BF16, FASTAR_F32, FastarError, check, load
+
+__all__ = ["ann_hash", "bucket_sort", "annsa_forward", "annca_forward", "tempcache_update",
+           "KVCache", "kernel_timer", "load", "FastarError"]
+
+_DT = {torch.float32: FASTAR_F32, torch.bfloat16: FASTAR_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[Optional[int], int]:
+    if nbytes == 0:
+        return None, 0
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws.data_ptr(), ws.numel()
+
+
+@dataclass
+class KVCache:
+    """Device tensors of one layer's bounded cache (all heads)."""
+    k: torch.Tensor          # [H, cap, d]
+    v: torch.Tensor          # [H, cap, d]
+    ids: torch.Tensor        # [H, cap] int16 (uint16 bit pattern)
+    ts: torch.Tensor         # [H, cap] int32
+    n_valid: torch.Tensor    # [H] int32
+
+    @classmethod
+    def empty(cls, H: int, cap: int, d: int, dtype=torch.bfloat16, device="cuda") -> "KVCache":
+        return cls(k=torch.zeros(H, cap, d, dtype=dtype, device=device),
+                   v=torch.zeros(H, cap, d, dtype=dtype, device=device),
+                   ids=torch.zeros(H, cap, dtype=torch.int16, device=device),
+                   ts=torch.zeros(H, cap, dtype=torch.int32, device=device),
+                   n_valid=torch.zeros(H, dtype=torch.int32, device=device))
+
+    @property
+    def H(self) -> int:
+        return self.k.shape[0]
+
+    @property
+    def cap(self) -> int:
+        return self.k.shape[1]
+
+    @property
+    def d(self) -> int:
+        return self.k.shape[2]
+
+    def struct(self) -> _lib.FastarCache:
+        for t in (self.k, self.v, self.ids, self.ts, self.n_valid):
+            if not t.is_contiguous():
+                raise ValueError("cache tensors must be contiguous")
+        if self.ids.dtype != torch.int16 or self.ts.dtype != torch.int32 \
+                or self.n_valid.dtype != torch.int32:
+            raise TypeError("cache ids must be int16, ts and n_valid int32")
+        return _lib.FastarCache(self.H, self.cap, self.d, _dtype_code(self.k), _ptr(self.k),
+                                _ptr(self.v), _ptr(self.ids), _ptr(self.ts), _ptr(self.n_valid))
+
+
+def _ids_check(ids: torch.Tensor, shape) -> None:
+    if ids.dtype != torch.int16 or tuple(ids.shape) != tuple(shape):
+        raise ValueError(f"ids must be int16 of shape {tuple(shape)}, got {ids.dtype} {tuple(ids.shape)}")
+
+
+def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Bucket ids [H, N] (int16 holding uint16 bits) of x [H, N, d] under planes [H, P, d] fp32."""
+    H, N, d = x.shape
+    P = planes.shape[1]
+    if planes.dtype != torch.float32 or tuple(planes.shape) != (H, P, d):
+        raise ValueError("planes must be float32 [H, P, d]")
+    if ids is None:
+        ids = torch.empty(H, N, dtype=torch.int16, device=x.device)
+    _ids_check(ids, (H, N))
+    check("fastar_ann_hash", load().fastar_ann_hash(_ptr(x), _dtype_code(x), H, N, d, _ptr(planes),
+                                                    P, _ptr(ids), _stream(x.device)))
+    return ids
+
+
+def bucket_sort(ids: torch.Tensor, P: int, ws: Optional[torch.Tensor] = None):
+    """Stable grouping by bucket: (off [H, 2^P + 1], perm [H, N]) int32."""
+    H, N = ids.shape
+    _ids_check(ids, (H, N))
+    lib = load()
+    off = torch.empty(H, (1 << P) + 1, dtype=torch.int32, device=ids.device)
+    perm = torch.empty(H, N, dtype=torch.int32, device=ids.device)
+    wsp, wsn = _workspace(lib.fastar_bucket_sort_workspace(H, N, P), ids.device, ws)
+    check("fastar_bucket_sort", lib.fastar_bucket_sort(_ptr(ids), H, N, P, _ptr(off), _ptr(perm),
+                                                       wsp, wsn, _stream(ids.device)))
+    return off, perm
+
+
+def annsa_forward(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor, v_cur: torch.Tensor,
+                  kcur_ids: torch.Tensor, P: int, cache: Optional[KVCache] = None,
+                  scale: Optional[float] = None, out_dtype=torch.float32,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  want_lse: bool = True, ws: Optional[torch.Tensor] = None):
+    """Bucket-restricted self-attention over [cache ; current chunk]: (out, lse)."""
+    H, Nq, d = q.shape
+    Ncur = k_cur.shape[1]
+    _ids_check(q_ids, (H, Nq))
+    _ids_check(kcur_ids, (H, Ncur))
+    if k_cur.shape != (H, Ncur, d) or v_cur.shape != (H, Ncur, d):
+        raise ValueError("k_cur / v_cur must be [H, Ncur, d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    lib = load()
+    if out is None:
+        out = torch.empty(H, Nq, d, dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(H, Nq, dtype=torch.float32, device=q.device)
+    cs = cache.struct() if cache is not None else None
+    cap = cache.cap if cache is not None else 0
+    wsp, wsn = _workspace(lib.fastar_annsa_workspace(H, Nq, cap, Ncur, P), q.device, ws)
+    check("fastar_annsa_forward", lib.fastar_annsa_forward(
+        _ptr(q), _ptr(q_ids), H, Nq, d, _dtype_code(q), ctypes.byref(cs) if cs else None,
+        _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), Ncur, P, scale, _ptr(out), _dtype_code(out),
+        _ptr(lse), wsp, wsn, _stream(q.device)))
+    return out, lse
+
+
+def annca_forward(q: torch.Tensor, q_ids: torch.Tensor, frame_len: int, kp: torch.Tensor,
+                  vp: torch.Tensor, kp_ids: torch.Tensor, P: int, scale: Optional[float] = None,
+                  out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                  want_keep: bool = True, ws: Optional[torch.Tensor] = None):
+    """Frame-pruned cross-attention: (out, keep [H, F, L] uint8, keep_count [H, F])."""
+    H, Nq, d = q.shape
+    L = kp.shape[1]
+    _ids_check(q_ids, (H, Nq))
+    _ids_check(kp_ids, (H, L))
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    F = Nq // frame_len if frame_len > 0 else 0
+    lib = load()
+    if out is None:
+        out = torch.empty(H, Nq, d, dtype=out_dtype, device=q.device)
+    keep = torch.empty(H, F, L, dtype=torch.uint8, device=q.device) if want_keep else None
+    cnt = torch.empty(H, F, dtype=torch.int32, device=q.device) if want_keep else None
+    wsp, wsn = _workspace(lib.fastar_annca_workspace(H, Nq, frame_len, L, P), q.device, ws)
+    check("fastar_annca_forward", lib.fastar_annca_forward(
+        _ptr(q), _ptr(q_ids), H, Nq, frame_len, d, _dtype_code(q), _ptr(kp), _ptr(vp),
+        _ptr(kp_ids), L, P, scale, _ptr(out), _dtype_code(out), _ptr(keep), _ptr(cnt), wsp, wsn,
+        _stream(q.device)))
+    return out, keep, cnt
+
+
+def tempcache_update(cache: KVCache, q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor,
+                     v_cur: torch.Tensor, kcur_ids: torch.Tensor, P: int, tau: float, step: int,
+                     best_in: Optional[torch.Tensor] = None, cos_in: Optional[torch.Tensor] = None,
+                     outputs: bool = True, ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Commits one chunk to ``cache`` in place; returns best, cos, dest, evicted, counts."""
+    H, N, d = q.shape
+    _ids_check(q_ids, (H, N))
+    _ids_check(kcur_ids, (H, N))
+    lib = load()
+    dev = q.device
+    res: Dict[str, torch.Tensor] = {}
+    if outputs:
+        res = {"best": torch.empty(H, N, dtype=torch.int32, device=dev),
+               "cos": torch.empty(H, N, dtype=torch.float32, device=dev),
+               "dest": torch.empty(H, N, dtype=torch.int32, device=dev),
+               "evicted": torch.empty(H, N, dtype=torch.int32, device=dev),
+               "counts": torch.empty(H, 5, dtype=torch.int32, device=dev)}
+    cs = cache.struct()
+    wsp, wsn = _workspace(lib.fastar_tempcache_workspace(H, N, cache.cap, P), dev, ws)
+    check("fastar_tempcache_update", lib.fastar_tempcache_update(
+        ctypes.byref(cs), _ptr(q), _ptr(q_ids), _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), N, P,
+        tau, step, _ptr(best_in), _ptr(cos_in), _ptr(res.get("best")), _ptr(res.get("cos")),
+        _ptr(res.get("dest")), _ptr(res.get("evicted")), _ptr(res.get("counts")), wsp, wsn,
+        _stream(dev)))
+    return res
+
+
+class kernel_timer:
+    """Context manager around fastar_timer_start/stop: ``.times`` maps each kernel
+    name to (launches, total_ms) measured with HIP events on the launch stream."""
+
+    def __enter__(self):
+        check("fastar_timer_start", load().fastar_timer_start())
+        self.times: Dict[str, Tuple[int, float]] = {}
+        return self
+
+    def __exit__(self, *exc):
+        buf = (_lib.FastarKernelTime * 64)()
+        n = load().fastar_timer_stop(buf, 64)
+        for i in range(min(n, 64)):
+            self.times[buf[i].name.decode()] = (buf[i].launches, buf[i].total_ms)
+        return False

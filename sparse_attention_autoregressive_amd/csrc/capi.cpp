@@ -1,0 +1,489 @@
+// C ABI of the FAST-AR attention step: argument validation, workspace layout
+// and kernel sequencing.  Nothing here allocates device memory or waits on the
+// device (except fastar_timer_stop, which waits for its own events).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/fastar.h"
+#include "launch.hpp"
+
+namespace fastar {
+
+// ------------------------------------------------------------------ timer
+namespace {
+struct TimerRec {
+    const char* name;
+    hipEvent_t a, b;
+};
+bool g_timer_on = false;
+bool g_pending = false;
+std::vector<TimerRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_pool_used = 0;
+
+hipEvent_t pool_get() {
+    if (g_pool_used < g_pool.size()) return g_pool[g_pool_used++];
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_pool.push_back(e);
+    ++g_pool_used;
+    return e;
+}
+}  // namespace
+
+void timer_begin(const char* name, hipStream_t s) {
+    g_pending = false;
+    if (!g_timer_on || g_recs.size() >= FASTAR_TIMER_MAX) return;
+    hipEvent_t a = pool_get(), b = pool_get();
+    if (!a || !b || hipEventRecord(a, s) != hipSuccess) return;
+    g_recs.push_back({name, a, b});
+    g_pending = true;
+}
+
+void timer_end(hipStream_t s) {
+    if (!g_pending) return;
+    (void)hipEventRecord(g_recs.back().b, s);
+    g_pending = false;
+}
+
+}  // namespace fastar
+
+using namespace fastar;
+
+namespace {
+
+// Workspace carving: the size queries and the calls run the same plan, one with
+// a null base (sizing), one with the caller's pointer.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(long long count) {
+        const size_t bytes = static_cast<size_t>(count > 0 ? count : 0) * sizeof(T);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += (bytes + 255) & ~static_cast<size_t>(255);
+        return p;
+    }
+};
+
+SortBufs carve_sort(Carver& c, int H, long long nmax, int P, bool with_wt, bool with_off_perm) {
+    SortBufs s;
+    const int B = 1 << P;
+    s.max_tiles = sort_tiles(nmax);
+    s.perm_stride = static_cast<int>(nmax);
+    s.hist = c.take<int32_t>(static_cast<long long>(H) * s.max_tiles * B);
+    if (with_off_perm) {
+        s.off = c.take<int32_t>(static_cast<long long>(H) * (B + 1));
+        s.perm = c.take<int32_t>(static_cast<long long>(H) * nmax);
+    }
+    if (with_wt) s.wt = c.take<int32_t>(static_cast<long long>(H) * (B + 1));
+    return s;
+}
+
+struct AnnsaWs {
+    SortBufs q, k;
+};
+AnnsaWs carve_annsa(Carver& c, int H, int Nq, int cap, int Ncur, int P) {
+    AnnsaWs w;
+    w.q = carve_sort(c, H, Nq, P, true, true);
+    w.k = carve_sort(c, H, static_cast<long long>(cap) + Ncur, P, false, true);
+    return w;
+}
+
+struct AnncaWs {
+    int32_t* idx;
+    int32_t* cnt;
+};
+AnncaWs carve_annca(Carver& c, int H, int F, int L) {
+    AnncaWs w;
+    w.idx = c.take<int32_t>(static_cast<long long>(H) * F * L);
+    w.cnt = c.take<int32_t>(static_cast<long long>(H) * F);
+    return w;
+}
+
+struct TcWs {
+    SortBufs q, k;
+    int32_t *claim, *best, *upos, *ev, *dest;
+    float* cosv;
+};
+TcWs carve_tc(Carver& c, int H, int N, int cap, int P) {
+    TcWs w;
+    w.q = carve_sort(c, H, N, P, true, true);
+    w.k = carve_sort(c, H, cap, P, false, true);
+    const long long HN = static_cast<long long>(H) * N;
+    w.claim = c.take<int32_t>(static_cast<long long>(H) * cap);
+    w.best = c.take<int32_t>(HN);
+    w.cosv = c.take<float>(HN);
+    w.upos = c.take<int32_t>(HN);
+    w.ev = c.take<int32_t>(HN);
+    w.dest = c.take<int32_t>(HN);
+    return w;
+}
+
+bool dtype_ok(int dt) { return dt == FASTAR_F32 || dt == FASTAR_BF16; }
+bool d_ok(int d) { return d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool planes_ok(int P) { return P >= 0 && P <= FASTAR_MAX_PLANES; }
+
+// Tensor pointer rule: required when the tensor is non-empty, 16-byte aligned when given.
+bool tensor_ok(const void* p, long long elems) {
+    if (elems <= 0) return p == nullptr || aligned16(p);
+    return p != nullptr && aligned16(p);
+}
+bool small_ok(const void* p, long long elems) { return elems <= 0 || p != nullptr; }
+bool fits_i32(long long v) { return v >= 0 && v < (1ll << 31); }
+
+fastar_status hip_status(hipError_t e) { return e == hipSuccess ? FASTAR_OK : FASTAR_EHIP; }
+
+bool cache_ok(const fastar_cache* c, int H, int d, int dtype) {
+    if (!c) return true;
+    if (c->H != H || c->d != d || c->dtype != dtype || c->cap < 0) return false;
+    const long long rows = static_cast<long long>(H) * c->cap;
+    if (!fits_i32(rows * d)) return false;
+    return tensor_ok(c->k, rows * d) && tensor_ok(c->v, rows * d) && small_ok(c->ids, rows) &&
+           small_ok(c->ts, rows) && small_ok(c->n_valid, H);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fastar_status_string(int32_t status) {
+    switch (status) {
+        case FASTAR_OK: return "FASTAR_OK";
+        case FASTAR_EINVAL: return "FASTAR_EINVAL";
+        case FASTAR_EDTYPE: return "FASTAR_EDTYPE";
+        case FASTAR_ESHAPE: return "FASTAR_ESHAPE";
+        case FASTAR_EWORKSPACE: return "FASTAR_EWORKSPACE";
+        case FASTAR_ECAPACITY: return "FASTAR_ECAPACITY";
+        case FASTAR_EHIP: return "FASTAR_EHIP";
+        default: return "FASTAR_UNKNOWN";
+    }
+}
+
+int32_t fastar_abi_version(void) { return FASTAR_ABI_VERSION; }
+
+// ------------------------------------------------------------------ hash
+fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
+                              const float* planes, int32_t P, uint16_t* ids, void* stream) {
+    if (!dtype_ok(dtype)) return FASTAR_EDTYPE;
+    if (H < 0 || N < 0) return FASTAR_EINVAL;
+    if (!d_ok(d) || P < 0 || P > FASTAR_MAX_HASH_PLANES) return FASTAR_ESHAPE;
+    const long long HN = static_cast<long long>(H) * N;
+    if (!fits_i32(HN * d)) return FASTAR_EINVAL;
+    if (!tensor_ok(x, HN * d) || !small_ok(ids, HN)) return FASTAR_EINVAL;
+    if (!tensor_ok(planes, (HN > 0 ? static_cast<long long>(H) * P * d : 0))) return FASTAR_EINVAL;
+    if (HN == 0) return FASTAR_OK;
+    return hip_status(launch_hash(x, dtype == FASTAR_BF16, H, N, d, planes, P, ids,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ bucket sort
+size_t fastar_bucket_sort_workspace(int32_t H, int32_t N, int32_t P) {
+    if (H < 0 || N < 0 || !planes_ok(P)) return 0;
+    Carver c(nullptr);
+    carve_sort(c, H, N, P, false, false);
+    return c.off;
+}
+
+fastar_status fastar_bucket_sort(const uint16_t* ids, int32_t H, int32_t N, int32_t P,
+                                 int32_t* off, int32_t* perm, void* ws, size_t ws_bytes,
+                                 void* stream) {
+    if (H < 0 || N < 0) return FASTAR_EINVAL;
+    if (!planes_ok(P)) return FASTAR_ESHAPE;
+    const long long HN = static_cast<long long>(H) * N;
+    if (!fits_i32(HN)) return FASTAR_EINVAL;
+    if (!small_ok(ids, HN) || !small_ok(perm, HN) || !small_ok(off, H)) return FASTAR_EINVAL;
+    const size_t need = fastar_bucket_sort_workspace(H, N, P);
+    if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
+    if (H == 0) return FASTAR_OK;
+    Carver c(ws);
+    SortBufs b = carve_sort(c, H, N, P, false, false);
+    b.off = off;
+    b.perm = perm;
+    IdSet s;
+    s.a = ids;
+    s.a_stride = N;
+    s.a_fixed = N;
+    return hip_status(launch_bucket_sort(H, P, 1, &s, &b, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ AnnSA
+size_t fastar_annsa_workspace(int32_t H, int32_t Nq, int32_t cap, int32_t Ncur, int32_t P) {
+    if (H < 0 || Nq < 0 || cap < 0 || Ncur < 0 || !planes_ok(P)) return 0;
+    Carver c(nullptr);
+    carve_annsa(c, H, Nq, cap, Ncur, P);
+    return c.off;
+}
+
+fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                   int32_t d, int32_t dtype, const fastar_cache* cache,
+                                   const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
+                                   int32_t Ncur, int32_t P, float scale, void* out,
+                                   int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                   void* stream) {
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return FASTAR_EDTYPE;
+    if (H < 0 || Nq < 0 || Ncur < 0 || !std::isfinite(scale)) return FASTAR_EINVAL;
+    if (!d_ok(d) || !planes_ok(P)) return FASTAR_ESHAPE;
+    if (cache && (cache->H != H || cache->d != d)) return FASTAR_ESHAPE;
+    if (cache && cache->dtype != dtype) return FASTAR_EDTYPE;
+    if (!cache_ok(cache, H, d, dtype)) return FASTAR_EINVAL;
+    const long long HQ = static_cast<long long>(H) * Nq, HC = static_cast<long long>(H) * Ncur;
+    const int cap = cache ? cache->cap : 0;
+    if (!fits_i32(HQ * d) || !fits_i32(HC * d) || !fits_i32(static_cast<long long>(H) * (cap + static_cast<long long>(Ncur))))
+        return FASTAR_EINVAL;
+    if (!tensor_ok(q, HQ * d) || !small_ok(q_ids, HQ) || !tensor_ok(out, HQ * d)) return FASTAR_EINVAL;
+    if (!tensor_ok(k_cur, HC * d) || !tensor_ok(v_cur, HC * d) || !small_ok(kcur_ids, HC))
+        return FASTAR_EINVAL;
+    const size_t need = fastar_annsa_workspace(H, Nq, cap, Ncur, P);
+    if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
+    if (HQ == 0) return FASTAR_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carver c(ws);
+    AnnsaWs w = carve_annsa(c, H, Nq, cap, Ncur, P);
+    IdSet sets[2];
+    sets[0].a = q_ids;
+    sets[0].a_stride = Nq;
+    sets[0].a_fixed = Nq;
+    if (cache) {
+        sets[1].a = cache->ids;
+        sets[1].a_stride = cap;
+        sets[1].a_nvalid = cache->n_valid;
+        sets[1].a_cap = cap;
+    }
+    sets[1].b = kcur_ids;
+    sets[1].b_stride = Ncur;
+    sets[1].nb = Ncur;
+    SortBufs bufs[2] = {w.q, w.k};
+    hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, s);
+    if (e != hipSuccess) return FASTAR_EHIP;
+
+    AttnParams p;
+    p.q = q;
+    p.Nq = Nq;
+    p.ka = cache ? cache->k : k_cur;
+    p.va = cache ? cache->v : v_cur;
+    p.a_rows = cap;
+    p.kb = k_cur;
+    p.vb = v_cur;
+    p.b_rows = Ncur;
+    p.n_valid = cache ? cache->n_valid : nullptr;
+    p.cap = cap;
+    p.qoff = w.q.off;
+    p.qperm = w.q.perm;
+    p.qperm_stride = w.q.perm_stride;
+    p.koff = w.k.off;
+    p.kperm = w.k.perm;
+    p.kperm_stride = w.k.perm_stride;
+    p.wt = w.q.wt;
+    p.B = 1 << P;
+    p.max_items = (Nq + kQTile - 1) / kQTile + p.B;
+    p.out = out;
+    p.lse = lse;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return hip_status(launch_attn(MODE_SA, dtype == FASTAR_BF16, d, out_dtype == FASTAR_BF16, H, p, s));
+}
+
+// ------------------------------------------------------------------ AnnCA
+size_t fastar_annca_workspace(int32_t H, int32_t Nq, int32_t frame_len, int32_t L, int32_t P) {
+    if (H < 0 || Nq < 0 || L < 0 || frame_len <= 0 || !planes_ok(P)) return 0;
+    Carver c(nullptr);
+    carve_annca(c, H, Nq / frame_len, L);
+    return c.off;
+}
+
+fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                   int32_t frame_len, int32_t d, int32_t dtype, const void* kp,
+                                   const void* vp, const uint16_t* kp_ids, int32_t L, int32_t P,
+                                   float scale, void* out, int32_t out_dtype, uint8_t* keep,
+                                   int32_t* keep_count, void* ws, size_t ws_bytes, void* stream) {
+    if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return FASTAR_EDTYPE;
+    if (H < 0 || Nq < 0 || L < 0 || !std::isfinite(scale)) return FASTAR_EINVAL;
+    if (!d_ok(d) || !planes_ok(P) || frame_len <= 0 || Nq % frame_len != 0) return FASTAR_ESHAPE;
+    const long long HQ = static_cast<long long>(H) * Nq, HL = static_cast<long long>(H) * L;
+    const int F = Nq / frame_len;
+    if (!fits_i32(HQ * d) || !fits_i32(HL * d) || !fits_i32(static_cast<long long>(H) * F * L))
+        return FASTAR_EINVAL;
+    if (!tensor_ok(q, HQ * d) || !small_ok(q_ids, HQ) || !tensor_ok(out, HQ * d)) return FASTAR_EINVAL;
+    if (!tensor_ok(kp, HL * d) || !tensor_ok(vp, HL * d) || !small_ok(kp_ids, HL)) return FASTAR_EINVAL;
+    const size_t need = fastar_annca_workspace(H, Nq, frame_len, L, P);
+    if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
+    if (HQ == 0) return FASTAR_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Carver c(ws);
+    AnncaWs w = carve_annca(c, H, F, L);
+    hipError_t e = launch_annca_select(q_ids, kp_ids, H, Nq, frame_len, L, P, w.idx, w.cnt, keep,
+                                       keep_count, s);
+    if (e != hipSuccess) return FASTAR_EHIP;
+    AttnParams p;
+    p.q = q;
+    p.Nq = Nq;
+    p.ka = kp;
+    p.va = vp;
+    p.a_rows = L;
+    p.ca_idx = w.idx;
+    p.ca_cnt = w.cnt;
+    p.frame_len = frame_len;
+    p.F = F;
+    p.L = L;
+    p.out = out;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return hip_status(launch_attn(MODE_CA, dtype == FASTAR_BF16, d, out_dtype == FASTAR_BF16, H, p, s));
+}
+
+// ------------------------------------------------------------------ TempCache
+size_t fastar_tempcache_workspace(int32_t H, int32_t N, int32_t cap, int32_t P) {
+    if (H < 0 || N < 0 || cap < 0 || !planes_ok(P)) return 0;
+    Carver c(nullptr);
+    carve_tc(c, H, N, cap, P);
+    return c.off;
+}
+
+fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
+                                      const uint16_t* q_ids, const void* k_cur, const void* v_cur,
+                                      const uint16_t* kcur_ids, int32_t N, int32_t P, float tau,
+                                      int32_t step, const int32_t* best_in, const float* cos_in,
+                                      int32_t* best, float* best_cos, int32_t* dest,
+                                      int32_t* evicted, int32_t* counts, void* ws,
+                                      size_t ws_bytes, void* stream) {
+    if (!cache) return FASTAR_EINVAL;
+    const int H = cache->H, d = cache->d, dtype = cache->dtype, cap = cache->cap;
+    if (!dtype_ok(dtype)) return FASTAR_EDTYPE;
+    if (H < 0 || N < 0 || cap < 0 || std::isnan(tau)) return FASTAR_EINVAL;
+    if (!d_ok(d) || !planes_ok(P)) return FASTAR_ESHAPE;
+    if (!cache_ok(cache, H, d, dtype)) return FASTAR_EINVAL;
+    if (H > 0 && (!cache->ids || !cache->ts || !cache->n_valid || (cap > 0 && (!cache->k || !cache->v))))
+        return FASTAR_EINVAL;
+    if ((best_in == nullptr) != (cos_in == nullptr)) return FASTAR_EINVAL;
+    if (N > cap) return FASTAR_ECAPACITY;
+    const long long HN = static_cast<long long>(H) * N;
+    if (!fits_i32(HN * d)) return FASTAR_EINVAL;
+    if (!tensor_ok(q, HN * d) || !small_ok(q_ids, HN) || !tensor_ok(k_cur, HN * d) ||
+        !tensor_ok(v_cur, HN * d) || !small_ok(kcur_ids, HN))
+        return FASTAR_EINVAL;
+    const size_t need = fastar_tempcache_workspace(H, N, cap, P);
+    if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
+    if (H == 0) return FASTAR_OK;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf = dtype == FASTAR_BF16;
+    Carver c(ws);
+    TcWs w = carve_tc(c, H, N, cap, P);
+    hipError_t e = launch_fill_i32(w.claim, static_cast<long long>(H) * cap, -1, s);
+    if (e != hipSuccess) return FASTAR_EHIP;
+
+    const int32_t* bestp;
+    const float* cosp;
+    if (best_in) {
+        bestp = best_in;
+        cosp = cos_in;
+        e = launch_tc_claim(best_in, cos_in, cache->n_valid, cap, H, N, tau, w.claim, s);
+        if (e == hipSuccess && best && HN > 0)
+            e = hipMemcpyAsync(best, best_in, HN * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && best_cos && HN > 0)
+            e = hipMemcpyAsync(best_cos, cos_in, HN * sizeof(float), hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return FASTAR_EHIP;
+    } else {
+        int32_t* bo = best ? best : w.best;
+        float* co = best_cos ? best_cos : w.cosv;
+        bestp = bo;
+        cosp = co;
+        IdSet sets[2];
+        sets[0].a = q_ids;
+        sets[0].a_stride = N;
+        sets[0].a_fixed = N;
+        sets[1].a = cache->ids;
+        sets[1].a_stride = cap;
+        sets[1].a_nvalid = cache->n_valid;
+        sets[1].a_cap = cap;
+        SortBufs bufs[2] = {w.q, w.k};
+        e = launch_bucket_sort(H, P, 2, sets, bufs, s);
+        if (e != hipSuccess) return FASTAR_EHIP;
+        AttnParams p;
+        p.q = q;
+        p.Nq = N;
+        p.ka = cache->k;
+        p.a_rows = cap;
+        p.n_valid = cache->n_valid;
+        p.cap = cap;
+        p.qoff = w.q.off;
+        p.qperm = w.q.perm;
+        p.qperm_stride = w.q.perm_stride;
+        p.koff = w.k.off;
+        p.kperm = w.k.perm;
+        p.kperm_stride = w.k.perm_stride;
+        p.wt = w.q.wt;
+        p.B = 1 << P;
+        p.max_items = (N + kQTile - 1) / kQTile + p.B;
+        p.best = bo;
+        p.bcos = co;
+        p.claim = w.claim;
+        p.tau = tau;
+        e = launch_attn(MODE_TOP1, bf, d, false, H, p, s);
+        if (e != hipSuccess) return FASTAR_EHIP;
+    }
+
+    TcSelectParams sp;
+    sp.best = bestp;
+    sp.cosv = cosp;
+    sp.claim = w.claim;
+    sp.ts = cache->ts;
+    sp.n_valid = cache->n_valid;
+    sp.upos = w.upos;
+    sp.ev = w.ev;
+    sp.dest = dest ? dest : w.dest;
+    sp.evicted = evicted;
+    sp.counts = counts;
+    sp.H = H;
+    sp.N = N;
+    sp.cap = cap;
+    sp.tau = tau;
+    e = launch_tc_select(sp, s);
+    if (e != hipSuccess) return FASTAR_EHIP;
+    return hip_status(launch_tc_scatter(bf, d, H, N, cap, sp.dest, k_cur, v_cur, kcur_ids, step,
+                                        cache->k, cache->v, cache->ids, cache->ts, s));
+}
+
+// ------------------------------------------------------------------ timer
+fastar_status fastar_timer_start(void) {
+    g_recs.clear();
+    g_pool_used = 0;
+    g_timer_on = true;
+    return FASTAR_OK;
+}
+
+int32_t fastar_timer_stop(fastar_kernel_time* out, int32_t max) {
+    g_timer_on = false;
+    g_pending = false;
+    std::vector<fastar_kernel_time> agg;
+    for (const TimerRec& r : g_recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess) continue;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) continue;
+        size_t i = 0;
+        for (; i < agg.size(); ++i)
+            if (std::strncmp(agg[i].name, r.name, sizeof(agg[i].name)) == 0) break;
+        if (i == agg.size()) {
+            fastar_kernel_time k;
+            std::memset(&k, 0, sizeof(k));
+            std::strncpy(k.name, r.name, sizeof(k.name) - 1);
+            agg.push_back(k);
+        }
+        agg[i].launches += 1;
+        agg[i].total_ms += ms;
+    }
+    g_recs.clear();
+    g_pool_used = 0;
+    const int n = static_cast<int>(agg.size());
+    for (int i = 0; i < n && i < max && out; ++i) out[i] = agg[i];
+    return n;
+}
+
+}  // extern "C"

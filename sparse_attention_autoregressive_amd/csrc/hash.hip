@@ -1,0 +1,102 @@
+// Random-hyperplane bucket ids (the LSH that places queries, cache keys,
+// current keys and prompt keys in one shared bucket space; FAST-AR summary,
+// "2. Core Components", parts A and B).
+//
+// HBM-bound: every element of x is read once.  Each group of d/8 lanes owns one
+// vector; lane ``seg`` always handles the same 8 coordinates, so its slice of
+// every hyperplane lives in registers for the whole kernel (no LDS traffic per
+// element).  Partial projections are summed across the group with DPP row
+// butterflies, which leave the same fp32 sum in every lane of the group.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fastar {
+
+template <typename T, int D, int MAXP>
+__global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x,
+                                                   const float* __restrict__ planes, int N, int P,
+                                                   uint16_t* __restrict__ ids) {
+    constexpr int LPV = D / 8;         // lanes per vector
+    constexpr int VPB = 256 / LPV;     // vectors per block per step
+    constexpr int UNROLL = 4;
+    const int h = blockIdx.y;
+    const int seg = threadIdx.x % LPV;
+    const int vslot = threadIdx.x / LPV;
+
+    float pl[MAXP][8];
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        if (p < P) {
+            const float* src = planes + (static_cast<size_t>(h) * P + p) * D + seg * 8;
+            float4 a = *reinterpret_cast<const float4*>(src);
+            float4 b = *reinterpret_cast<const float4*>(src + 4);
+            pl[p][0] = a.x; pl[p][1] = a.y; pl[p][2] = a.z; pl[p][3] = a.w;
+            pl[p][4] = b.x; pl[p][5] = b.y; pl[p][6] = b.z; pl[p][7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pl[p][e] = 0.f;
+        }
+    }
+
+    const T* xh = x + static_cast<size_t>(h) * N * D;
+    uint16_t* idh = ids + static_cast<size_t>(h) * N;
+    for (int base = blockIdx.x * VPB * UNROLL; base < N; base += gridDim.x * VPB * UNROLL) {
+        float v[UNROLL][8];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int i = base + u * VPB + vslot;
+            if (i < N) {
+                load8_f32(xh + static_cast<size_t>(i) * D + seg * 8, v[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int i = base + u * VPB + vslot;
+            uint32_t id = 0;
+#pragma unroll
+            for (int p = 0; p < MAXP; ++p) {
+                if (p < P) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s = __builtin_fmaf(v[u][e], pl[p][e], s);
+                    s = group_sum<(LPV < 16 ? LPV : 16)>(s);
+                    id |= static_cast<uint32_t>(s >= 0.f) << p;
+                }
+            }
+            if (seg == 0 && i < N) idh[i] = static_cast<uint16_t>(id);
+        }
+    }
+}
+
+template <typename T, int D>
+static hipError_t hash_dispatch_p(const void* x, int H, int N, const float* planes, int P,
+                                  uint16_t* ids, hipStream_t s) {
+    constexpr int VPB = 256 / (D / 8);
+    int blocks = (N + VPB * 4 - 1) / (VPB * 4);
+    if (blocks < 1) blocks = 1;
+    dim3 grid(blocks, H);
+    timer_begin("ann_hash", s);
+    if (P <= 8)
+        hipLaunchKernelGGL((hash_kernel<T, D, 8>), grid, dim3(256), 0, s,
+                           static_cast<const T*>(x), planes, N, P, ids);
+    else
+        hipLaunchKernelGGL((hash_kernel<T, D, 16>), grid, dim3(256), 0, s,
+                           static_cast<const T*>(x), planes, N, P, ids);
+    timer_end(s);
+    return hipGetLastError();
+}
+
+hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const float* planes, int P,
+                       uint16_t* ids, hipStream_t s) {
+    if (N == 0 || H == 0) return hipSuccess;
+    if (bf16)
+        return d == 64 ? hash_dispatch_p<uint16_t, 64>(x, H, N, planes, P, ids, s)
+                       : hash_dispatch_p<uint16_t, 128>(x, H, N, planes, P, ids, s);
+    return d == 64 ? hash_dispatch_p<float, 64>(x, H, N, planes, P, ids, s)
+                   : hash_dispatch_p<float, 128>(x, H, N, planes, P, ids, s);
+}
+
+}  // namespace fastar

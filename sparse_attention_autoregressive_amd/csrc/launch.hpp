@@ -1,0 +1,128 @@
+// Host-side launchers of the FAST-AR kernels (defined in the .hip files),
+// called by the C ABI after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fastar {
+
+// Per-kernel timing hooks (capi.cpp); no-ops unless fastar_timer_start is active.
+void timer_begin(const char* name, hipStream_t s);
+void timer_end(hipStream_t s);
+
+// ------------------------------------------------------------------ hash
+hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const float* planes, int P,
+                       uint16_t* ids, hipStream_t s);
+
+// ------------------------------------------------------------------ sort
+// A set of ids per head: the first part (source a) holds either ``a_fixed``
+// ids or, when ``a_nvalid`` is set, clamp(a_nvalid[h], 0, a_cap) ids; the
+// second part (source b) holds ``nb`` ids.  Element e of the set is a[e] for
+// e < na, b[e - na] otherwise.
+struct IdSet {
+    const uint16_t* a = nullptr;
+    int a_stride = 0;          // ids per head in a's array
+    int a_fixed = 0;
+    const int32_t* a_nvalid = nullptr;
+    int a_cap = 0;
+    const uint16_t* b = nullptr;
+    int b_stride = 0;
+    int nb = 0;
+};
+
+struct SortBufs {
+    int32_t* hist = nullptr;    // [H][max_tiles][B] scratch (tile counts, then tile bases)
+    int32_t* off = nullptr;     // [H][B+1]
+    int32_t* perm = nullptr;    // [H][perm_stride]
+    int32_t* wt = nullptr;      // [H][B+1] prefix of ceil(count/64) per bucket, or null
+    int max_tiles = 0;
+    int perm_stride = 0;
+};
+
+constexpr int kSortTile = 1024;
+__host__ __device__ inline int sort_tiles(long long n) { return static_cast<int>((n + kSortTile - 1) / kSortTile); }
+
+// Sorts one or two sets (nsets = 1 or 2) per head, in three launches.
+hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
+                              hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+enum AttnMode { MODE_SA = 0, MODE_CA = 1, MODE_TOP1 = 2 };
+
+struct AttnParams {
+    const void* q = nullptr;        // [H][Nq][D]
+    int Nq = 0;
+    // key/value rows: source a (cache slots, or prompt rows), source b (current chunk)
+    const void* ka = nullptr;
+    const void* va = nullptr;
+    int a_rows = 0;                 // rows per head in source a
+    const void* kb = nullptr;
+    const void* vb = nullptr;
+    int b_rows = 0;
+    const int32_t* n_valid = nullptr;
+    int cap = 0;
+    // bucket tables (SA, TOP1)
+    const int32_t* qoff = nullptr;
+    const int32_t* qperm = nullptr;
+    int qperm_stride = 0;
+    const int32_t* koff = nullptr;
+    const int32_t* kperm = nullptr;
+    int kperm_stride = 0;
+    const int32_t* wt = nullptr;
+    int B = 1;
+    int max_items = 0;              // grid.x for SA/TOP1
+    // prompt selection (CA)
+    const int32_t* ca_idx = nullptr;
+    const int32_t* ca_cnt = nullptr;
+    int frame_len = 0;
+    int F = 0;
+    int L = 0;
+    // outputs
+    void* out = nullptr;
+    float* lse = nullptr;
+    int32_t* best = nullptr;
+    float* bcos = nullptr;
+    int32_t* claim = nullptr;
+    float tau = 0.f;
+    float scale_log2 = 0.f;
+};
+
+constexpr int kQTile = 64;   // queries per attention block
+
+hipError_t launch_attn(int mode, bool bf16, int d, bool out_bf16, int H, const AttnParams& p,
+                       hipStream_t s);
+
+// ------------------------------------------------------------------ AnnCA selection
+hipError_t launch_annca_select(const uint16_t* q_ids, const uint16_t* kp_ids, int H, int Nq,
+                               int frame_len, int L, int P, int32_t* idx, int32_t* cnt,
+                               uint8_t* keep, int32_t* keep_count, hipStream_t s);
+
+// ------------------------------------------------------------------ TempCache
+hipError_t launch_fill_i32(int32_t* p, long long n, int32_t v, hipStream_t s);
+
+hipError_t launch_tc_claim(const int32_t* best, const float* cosv, const int32_t* n_valid,
+                           int cap, int H, int N, float tau, int32_t* claim, hipStream_t s);
+
+struct TcSelectParams {
+    const int32_t* best;     // [H][N]
+    const float* cosv;       // [H][N]
+    const int32_t* claim;    // [H][cap]
+    const int32_t* ts;       // [H][cap]
+    int32_t* n_valid;        // [H] read, then updated
+    int32_t* upos;           // [H][N] scratch
+    int32_t* ev;             // [H][N] scratch: evicted slots, ascending
+    int32_t* dest;           // [H][N] output (scratch or caller's)
+    int32_t* evicted;        // [H][N] caller output or null
+    int32_t* counts;         // [H][5] caller output or null
+    int H, N, cap;
+    float tau;
+};
+hipError_t launch_tc_select(const TcSelectParams& p, hipStream_t s);
+
+hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int32_t* dest,
+                             const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
+                             int32_t step, void* ck, void* cv, uint16_t* cids, int32_t* cts,
+                             hipStream_t s);
+
+}  // namespace fastar

@@ -1,0 +1,178 @@
+// Stable counting sort of token indices by bucket id: the block-sparse layout
+// that bucket attention gathers from (FAST-AR summary, "2. Core Components",
+// part C).  Three launches, every count stays on the device:
+//
+//   sort_hist    one block per 1024-id tile: LDS histogram -> hist[h][tile][b]
+//   sort_scan    one block per head and set: per-bucket exclusive prefix over
+//                tiles (in place) plus a block scan over buckets -> off[h][b];
+//                optionally the prefix of ceil(count/64), the attention work list
+//   sort_scatter one block per tile: stable rank of every id inside its tile
+//                (wave ballots on the P id bits give the rank among equal ids of
+//                the wave; LDS counters tagged by round carry it across waves
+//                and rounds), then perm[off + tile base + rank] = index.
+//
+// The result is unique (a stable sort), so it is bit-identical run to run.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fastar {
+
+struct SortArgs {
+    IdSet set[2];
+    SortBufs buf[2];
+    int B;
+    int P;
+};
+
+__device__ __forceinline__ int set_count(const IdSet& s, int h, int& na) {
+    na = s.a_nvalid ? clamp_n(s.a_nvalid, h, s.a_cap) : s.a_fixed;
+    return na + s.nb;
+}
+
+__device__ __forceinline__ int set_id(const IdSet& s, int h, int na, int e) {
+    return e < na ? s.a[static_cast<size_t>(h) * s.a_stride + e]
+                  : s.b[static_cast<size_t>(h) * s.b_stride + (e - na)];
+}
+
+__global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
+    __shared__ int cnt[1024];
+    const IdSet& S = a.set[blockIdx.z];
+    const SortBufs& O = a.buf[blockIdx.z];
+    const int h = blockIdx.y, t = blockIdx.x, B = a.B;
+    int na;
+    const int n = set_count(S, h, na);
+    if (t * kSortTile >= n) return;
+    for (int b = threadIdx.x; b < B; b += 256) cnt[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortTile / 256; ++r) {
+        const int e = t * kSortTile + r * 256 + threadIdx.x;
+        if (e < n) atomicAdd(&cnt[set_id(S, h, na, e) & (B - 1)], 1);
+    }
+    __syncthreads();
+    int* dst = O.hist + (static_cast<size_t>(h) * O.max_tiles + t) * B;
+    for (int b = threadIdx.x; b < B; b += 256) dst[b] = cnt[b];
+}
+
+__global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
+    __shared__ int smem[16];
+    const IdSet& S = a.set[blockIdx.y];
+    const SortBufs& O = a.buf[blockIdx.y];
+    const int h = blockIdx.x, B = a.B, b = threadIdx.x;
+    int na;
+    const int n = set_count(S, h, na);
+    const int ntiles = sort_tiles(n);
+    int* hist = O.hist + static_cast<size_t>(h) * O.max_tiles * B;
+    int run = 0;
+    if (b < B) {
+        for (int t = 0; t < ntiles; ++t) {
+            const int c = hist[static_cast<size_t>(t) * B + b];
+            hist[static_cast<size_t>(t) * B + b] = run;
+            run += c;
+        }
+    }
+    int total;
+    const int excl = block_exclusive_scan<1024>(b < B ? run : 0, smem, total);
+    if (b < B) {
+        for (int t = 0; t < ntiles; ++t) hist[static_cast<size_t>(t) * B + b] += excl;
+        O.off[static_cast<size_t>(h) * (B + 1) + b] = excl;
+    }
+    if (b == 0) O.off[static_cast<size_t>(h) * (B + 1) + B] = total;
+    if (O.wt) {
+        const int tiles = (b < B) ? (run + kQTile - 1) / kQTile : 0;
+        int wtotal;
+        const int wex = block_exclusive_scan<1024>(tiles, smem, wtotal);
+        if (b < B) O.wt[static_cast<size_t>(h) * (B + 1) + b] = wex;
+        if (b == 0) O.wt[static_cast<size_t>(h) * (B + 1) + B] = wtotal;
+    }
+}
+
+__global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
+    __shared__ int run[1024];
+    __shared__ int base[1024];
+    __shared__ uint32_t wcnt[4][1024];
+    const IdSet& S = a.set[blockIdx.z];
+    const SortBufs& O = a.buf[blockIdx.z];
+    const int h = blockIdx.y, t = blockIdx.x, B = a.B, P = a.P;
+    int na;
+    const int n = set_count(S, h, na);
+    if (t * kSortTile >= n) return;
+    const int* tb = O.hist + (static_cast<size_t>(h) * O.max_tiles + t) * B;
+    for (int b = threadIdx.x; b < B; b += 256) {
+        run[b] = 0;
+        base[b] = tb[b];
+        wcnt[0][b] = wcnt[1][b] = wcnt[2][b] = wcnt[3][b] = 0;
+    }
+    __syncthreads();
+    const int lane = lane_id();
+    const int w = threadIdx.x / kWave;
+    int32_t* perm = O.perm + static_cast<size_t>(h) * O.perm_stride;
+#pragma unroll 1
+    for (int r = 0; r < kSortTile / 256; ++r) {
+        const int e = t * kSortTile + r * 256 + threadIdx.x;
+        const bool valid = e < n;
+        const int id = valid ? (set_id(S, h, na, e) & (B - 1)) : 0;
+        uint64_t mask = __ballot(valid);
+        for (int p = 0; p < P; ++p) {
+            const bool bit = (id >> p) & 1;
+            const uint64_t bb = __ballot(bit);
+            mask &= bit ? bb : ~bb;
+        }
+        const int rank_w = __popcll(mask & lanemask_lt());
+        const uint32_t tag = static_cast<uint32_t>(r + 1) << 16;
+        if (valid && rank_w == 0) wcnt[w][id] = tag | static_cast<uint32_t>(__popcll(mask));
+        __syncthreads();
+        int rank = 0;
+        bool last = false;
+        if (valid) {
+            int pre = run[id];
+            last = (mask >> lane) == 1;
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t x = wcnt[v][id];
+                const bool cur = (x & 0xFFFF0000u) == tag;
+                if (v < w && cur) pre += static_cast<int>(x & 0xFFFFu);
+                if (v > w && cur) last = false;
+            }
+            rank = pre + rank_w;
+        }
+        __syncthreads();
+        if (valid) {
+            if (last) run[id] = rank + 1;
+            perm[base[id] + rank] = e;
+        }
+    }
+}
+
+hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
+                              hipStream_t s) {
+    SortArgs a;
+    a.B = 1 << P;
+    a.P = P;
+    int max_tiles = 0;
+    for (int i = 0; i < nsets; ++i) {
+        a.set[i] = sets[i];
+        a.buf[i] = bufs[i];
+        if (bufs[i].max_tiles > max_tiles) max_tiles = bufs[i].max_tiles;
+    }
+    if (nsets == 1) {
+        a.set[1] = a.set[0];
+        a.buf[1] = a.buf[0];
+    }
+    if (H == 0) return hipSuccess;
+    if (max_tiles > 0) {
+        timer_begin("sort_hist", s);
+        hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
+        timer_end(s);
+    }
+    timer_begin("sort_scan", s);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(H, nsets), dim3(1024), 0, s, a);
+    timer_end(s);
+    if (max_tiles > 0) {
+        timer_begin("sort_scatter", s);
+        hipLaunchKernelGGL(sort_scatter_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
+        timer_end(s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace fastar

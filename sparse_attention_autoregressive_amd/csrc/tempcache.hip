@@ -1,0 +1,295 @@
+// TempCache commit (FAST-AR blog, "1. TempCache"; summary, "2. Core
+// Components" A): after the top-1 search has written best/cos and claimed the
+// matched slots (atomicMax of the token index, so the most recent token wins
+// regardless of scheduling), one block per head
+//   1. ranks the unmatched tokens in token order (block scan),
+//   2. counts the refreshed slots,
+//   3. if the cache overflows, selects the e non-refreshed slots with the
+//      smallest (timestamp, slot) by a radix select on the timestamps
+//      (8-bit digits of ts - min(ts); one pass when timestamps span < 256)
+//      and lists them in slot order (two block scans),
+//   4. writes every token's destination slot, the eviction list, the counts
+//      and the new valid-slot count;
+// then a gather-free copy kernel moves the winning tokens' rows into place.
+// Every decision is integer or a single fp32 compare, so results are
+// deterministic.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fastar {
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, long long n, int32_t v) {
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, long long n, int32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    long long blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    timer_begin("fill", s);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n, v);
+    timer_end(s);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void tc_claim_kernel(const int32_t* __restrict__ best,
+                                                       const float* __restrict__ cosv,
+                                                       const int32_t* __restrict__ n_valid, int cap,
+                                                       int N, float tau, int32_t* __restrict__ claim) {
+    const int h = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= N) return;
+    const int n = clamp_n(n_valid, h, cap);
+    const size_t qi = static_cast<size_t>(h) * N + i;
+    const int b = best[qi];
+    if (b >= 0 && b < n && cosv[qi] >= tau) atomicMax(&claim[static_cast<size_t>(h) * cap + b], i);
+}
+
+hipError_t launch_tc_claim(const int32_t* best, const float* cosv, const int32_t* n_valid, int cap,
+                           int H, int N, float tau, int32_t* claim, hipStream_t s) {
+    if (H == 0 || N == 0) return hipSuccess;
+    timer_begin("tempcache_claim", s);
+    hipLaunchKernelGGL(tc_claim_kernel, dim3((N + 255) / 256, H), dim3(256), 0, s, best, cosv,
+                       n_valid, cap, N, tau, claim);
+    timer_end(s);
+    return hipGetLastError();
+}
+
+namespace {
+constexpr int SEL_NT = 1024;
+constexpr int SEL_ITEMS = 32;
+constexpr int SEL_CHUNK = SEL_NT * SEL_ITEMS;
+
+__device__ __forceinline__ uint32_t ts_key(int32_t t) { return static_cast<uint32_t>(t) ^ 0x80000000u; }
+
+__device__ __forceinline__ uint32_t block_min_max(uint32_t v, bool want_max, uint32_t* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = __shfl_xor(v, off);
+        v = want_max ? (o > v ? o : v) : (o < v ? o : v);
+    }
+    const int w = threadIdx.x / kWave;
+    if (lane_id() == 0) red[w] = v;
+    __syncthreads();
+    uint32_t r = red[0];
+    for (int i = 1; i < SEL_NT / kWave; ++i) r = want_max ? (red[i] > r ? red[i] : r) : (red[i] < r ? red[i] : r);
+    __syncthreads();
+    return r;
+}
+}  // namespace
+
+__global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams p) {
+    __shared__ int smem[SEL_NT / kWave];
+    __shared__ uint32_t red[SEL_NT / kWave];
+    __shared__ int hist[256];
+    __shared__ int bcast[2];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int cap = p.cap, N = p.N;
+    const int n = clamp_n(p.n_valid, h, cap);
+    const int32_t* best = p.best + static_cast<size_t>(h) * N;
+    const float* cosv = p.cosv + static_cast<size_t>(h) * N;
+    const int32_t* claim = p.claim + static_cast<size_t>(h) * cap;
+    const int32_t* ts = p.ts + static_cast<size_t>(h) * cap;
+    int32_t* upos = p.upos + static_cast<size_t>(h) * N;
+    int32_t* ev = p.ev + static_cast<size_t>(h) * N;
+    int32_t* dest = p.dest + static_cast<size_t>(h) * N;
+
+    // 1. rank the unmatched tokens in token order
+    int u = 0;
+    for (int c0 = 0; c0 < N; c0 += SEL_CHUNK) {
+        const int base = c0 + tid * SEL_ITEMS;
+        uint32_t flags = 0;
+        int local = 0;
+#pragma unroll 8
+        for (int k = 0; k < SEL_ITEMS; ++k) {
+            const int i = base + k;
+            if (i < N) {
+                const int b = best[i];
+                const bool m = b >= 0 && b < n && cosv[i] >= p.tau;
+                if (!m) { flags |= 1u << k; ++local; }
+            }
+        }
+        int total;
+        int pos = u + block_exclusive_scan<SEL_NT>(local, smem, total);
+        for (int k = 0; k < SEL_ITEMS; ++k) {
+            const int i = base + k;
+            if (i < N) upos[i] = ((flags >> k) & 1) ? pos++ : -1;
+        }
+        u += total;
+    }
+
+    // 2. refreshed slots
+    int rloc = 0;
+    for (int j = tid; j < n; j += SEL_NT) rloc += claim[j] >= 0;
+    int refreshed;
+    (void)block_exclusive_scan<SEL_NT>(rloc, smem, refreshed);
+
+    const int e = max(0, n + u - cap);
+    const int appended = u - e;
+
+    // 3. the e oldest non-refreshed slots (ties: lower slot), ascending
+    if (e > 0) {
+        uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
+        for (int j = tid; j < n; j += SEL_NT) {
+            if (claim[j] < 0) {
+                const uint32_t k = ts_key(ts[j]);
+                lmin = k < lmin ? k : lmin;
+                lmax = k > lmax ? k : lmax;
+            }
+        }
+        const uint32_t kmin = block_min_max(lmin, false, red);
+        const uint32_t kmax = block_min_max(lmax, true, red);
+        uint32_t prefix = 0;
+        int need = e;
+        if (kmax != kmin) {
+            const uint32_t range = kmax - kmin;
+            const int nbits = 32 - __clz(static_cast<int>(range));
+            for (int shift = ((nbits - 1) / 8) * 8; shift >= 0; shift -= 8) {
+                if (tid < 256) hist[tid] = 0;
+                __syncthreads();
+                for (int j = tid; j < n; j += SEL_NT) {
+                    if (claim[j] < 0) {
+                        const uint32_t rel = ts_key(ts[j]) - kmin;
+                        const uint32_t hi = (shift + 8 >= 32) ? 0u : (rel >> (shift + 8));
+                        if (hi == prefix) atomicAdd(&hist[(rel >> shift) & 255u], 1);
+                    }
+                }
+                __syncthreads();
+                if (tid == 0) {
+                    int cum = 0, dgt = 0;
+                    for (; dgt < 255; ++dgt) {
+                        if (cum + hist[dgt] >= need) break;
+                        cum += hist[dgt];
+                    }
+                    bcast[0] = dgt;
+                    bcast[1] = need - cum;
+                }
+                __syncthreads();
+                prefix = (prefix << 8) | static_cast<uint32_t>(bcast[0]);
+                need = bcast[1];
+                __syncthreads();
+            }
+        }
+        const uint32_t tstar = kmin + prefix;
+        int carry_eq = 0, carry_sel = 0;
+        for (int c0 = 0; c0 < n; c0 += SEL_CHUNK) {
+            const int base = c0 + tid * SEL_ITEMS;
+            uint32_t ltf = 0, eqf = 0;
+            int eqc = 0;
+#pragma unroll 8
+            for (int k = 0; k < SEL_ITEMS; ++k) {
+                const int j = base + k;
+                if (j < n && claim[j] < 0) {
+                    const uint32_t key = ts_key(ts[j]);
+                    if (key < tstar) ltf |= 1u << k;
+                    else if (key == tstar) { eqf |= 1u << k; ++eqc; }
+                }
+            }
+            int eqtot;
+            int er = carry_eq + block_exclusive_scan<SEL_NT>(eqc, smem, eqtot);
+            uint32_t self = 0;
+            int selc = 0;
+            for (int k = 0; k < SEL_ITEMS; ++k) {
+                if ((ltf >> k) & 1) { self |= 1u << k; ++selc; }
+                else if ((eqf >> k) & 1) {
+                    if (er < need) { self |= 1u << k; ++selc; }
+                    ++er;
+                }
+            }
+            int seltot;
+            int pos = carry_sel + block_exclusive_scan<SEL_NT>(selc, smem, seltot);
+            for (int k = 0; k < SEL_ITEMS; ++k)
+                if ((self >> k) & 1) {
+                    if (pos < e) ev[pos] = base + k;     // e <= N: never past the row
+                    ++pos;
+                }
+            carry_eq += eqtot;
+            carry_sel += seltot;
+        }
+    }
+    __syncthreads();
+
+    // 4. destinations, eviction list, counts
+    for (int i = tid; i < N; i += SEL_NT) {
+        const int k = upos[i];
+        int dst;
+        if (k < 0) {
+            const int b = best[i];
+            dst = (claim[b] == i) ? b : -1;
+        } else {
+            dst = (k < appended) ? n + k : ev[k - appended];
+        }
+        dest[i] = (dst >= 0 && dst < cap) ? dst : -1;
+    }
+    if (p.evicted)
+        for (int k = tid; k < N; k += SEL_NT)
+            p.evicted[static_cast<size_t>(h) * N + k] = (k < e) ? ev[k] : -1;
+    if (tid == 0) {
+        if (p.counts) {
+            int32_t* c = p.counts + static_cast<size_t>(h) * 5;
+            c[0] = N - u;
+            c[1] = refreshed;
+            c[2] = (N - u) - refreshed;
+            c[3] = appended;
+            c[4] = e;
+        }
+        p.n_valid[h] = n + appended;
+    }
+}
+
+hipError_t launch_tc_select(const TcSelectParams& p, hipStream_t s) {
+    if (p.H == 0) return hipSuccess;
+    timer_begin("tempcache_select", s);
+    hipLaunchKernelGGL(tc_select_kernel, dim3(p.H), dim3(SEL_NT), 0, s, p);
+    timer_end(s);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void tc_scatter_kernel(
+    const int32_t* __restrict__ dest, const T* __restrict__ kc, const T* __restrict__ vc,
+    const uint16_t* __restrict__ kids, int32_t step, T* __restrict__ ck, T* __restrict__ cv,
+    uint16_t* __restrict__ cids, int32_t* __restrict__ cts, int N, int cap) {
+    constexpr int CPR = D * static_cast<int>(sizeof(T)) / 16;
+    const int h = blockIdx.y;
+    const int i = blockIdx.x * 4 + threadIdx.x / 64;
+    const int l = threadIdx.x % 64;
+    if (i >= N) return;
+    const size_t ti = static_cast<size_t>(h) * N + i;
+    const int d = dest[ti];
+    if (d < 0 || d >= cap) return;
+    const size_t si = static_cast<size_t>(h) * cap + d;
+    for (int c = l; c < 2 * CPR; c += 64) {
+        const bool isv = c >= CPR;
+        const int cc = isv ? c - CPR : c;
+        const uint4* src = reinterpret_cast<const uint4*>((isv ? vc : kc) + ti * D) + cc;
+        uint4* dst = reinterpret_cast<uint4*>((isv ? cv : ck) + si * D) + cc;
+        *dst = *src;
+    }
+    if (l == 0) {
+        cids[si] = kids[ti];
+        cts[si] = step;
+    }
+}
+
+hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int32_t* dest,
+                             const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
+                             int32_t step, void* ck, void* cv, uint16_t* cids, int32_t* cts,
+                             hipStream_t s) {
+    if (H == 0 || N == 0) return hipSuccess;
+    dim3 grid((N + 3) / 4, H);
+    timer_begin("tempcache_scatter", s);
+#define FASTAR_SCATTER(T, DD)                                                                     \
+    hipLaunchKernelGGL((tc_scatter_kernel<T, DD>), grid, dim3(256), 0, s, dest,                  \
+                       static_cast<const T*>(k_cur), static_cast<const T*>(v_cur), kcur_ids, step, \
+                       static_cast<T*>(ck), static_cast<T*>(cv), cids, cts, N, cap)
+    if (bf16) {
+        if (d == 64) FASTAR_SCATTER(uint16_t, 64); else FASTAR_SCATTER(uint16_t, 128);
+    } else {
+        if (d == 64) FASTAR_SCATTER(float, 64); else FASTAR_SCATTER(float, 128);
+    }
+#undef FASTAR_SCATTER
+    timer_end(s);
+    return hipGetLastError();
+}
+
+}  // namespace fastar

@@ -1,0 +1,137 @@
+"""C ABI on the host (no GPU): the library loads, exports every entry point that
+include/fastar.h declares, and rejects bad arguments with the documented
+status before launching anything.  Fake device pointers used here are never
+dereferenced: each call below fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_autoregressive_amd import _lib
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "fastar.h")
+FAKE = 0x100000          # 16-byte aligned, never dereferenced
+MISALIGNED = 0x100008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fastar_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.fastar_abi_version() == 1
+    for code, name in [(0, "FASTAR_OK"), (-1, "FASTAR_EINVAL"), (-2, "FASTAR_EDTYPE"),
+                       (-3, "FASTAR_ESHAPE"), (-4, "FASTAR_EWORKSPACE"), (-5, "FASTAR_ECAPACITY"),
+                       (-6, "FASTAR_EHIP")]:
+        assert lib.fastar_status_string(code).decode() == name
+    assert lib.fastar_status_string(99).decode() == "FASTAR_UNKNOWN"
+
+
+def test_hash_validation(lib):
+    h = lib.fastar_ann_hash
+    assert h(FAKE, 7, 1, 4, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EDTYPE
+    assert h(FAKE, 0, 1, 4, 96, FAKE, 4, FAKE, None) == _lib.FASTAR_ESHAPE
+    assert h(FAKE, 0, 1, 4, 64, FAKE, 17, FAKE, None) == _lib.FASTAR_ESHAPE
+    assert h(FAKE, 0, 1, -1, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EINVAL
+    assert h(None, 0, 1, 4, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EINVAL
+    assert h(MISALIGNED, 0, 1, 4, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EINVAL
+    assert h(FAKE, 0, 1, 4, 64, None, 4, FAKE, None) == _lib.FASTAR_EINVAL
+    assert h(FAKE, 1, 1, 4, 128, FAKE, 4, None, None) == _lib.FASTAR_EINVAL
+    # empty work is a no-op that succeeds without touching the device
+    assert h(None, 0, 0, 4, 64, None, 4, None, None) == _lib.FASTAR_OK
+    assert h(None, 1, 3, 0, 128, None, 4, None, None) == _lib.FASTAR_OK
+
+
+def test_workspace_queries(lib):
+    a = lib.fastar_annsa_workspace(12, 4680, 32760, 4680, 7)
+    assert a > 12 * (4680 + 32760 + 4680) * 4
+    assert lib.fastar_annsa_workspace(12, 4680, 32760, 4680, 8) > a
+    assert lib.fastar_annsa_workspace(1, 10, 0, 0, 11) == 0          # P out of range
+    assert lib.fastar_tempcache_workspace(12, 4680, 32760, 7) > 12 * 32760 * 4
+    assert lib.fastar_annca_workspace(12, 4680, 1560, 512, 7) >= 12 * 3 * 512 * 4
+    assert lib.fastar_bucket_sort_workspace(2, 1000, 5) > 0
+    assert lib.fastar_bucket_sort_workspace(2, 0, 5) == 0
+
+
+def _cache(H=1, cap=64, d=64, dtype=0):
+    return _lib.FastarCache(H, cap, d, dtype, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_annsa_validation(lib):
+    f = lib.fastar_annsa_forward
+    need = lib.fastar_annsa_workspace(1, 32, 64, 16, 4)
+    c = _cache()
+    args = lambda **kw: [kw.get("q", FAKE), FAKE, 1, 32, kw.get("d", 64), kw.get("dt", 0),
+                         kw.get("cache", ctypes.byref(c)), FAKE, FAKE, FAKE, 16, kw.get("P", 4),
+                         kw.get("scale", 0.125), FAKE, kw.get("odt", 0), None, FAKE,
+                         kw.get("ws", need), None]
+    assert f(*args(ws=need - 1)) == _lib.FASTAR_EWORKSPACE
+    assert f(*args(P=11)) == _lib.FASTAR_ESHAPE
+    assert f(*args(d=80)) == _lib.FASTAR_ESHAPE
+    assert f(*args(dt=1)) == _lib.FASTAR_EDTYPE          # cache is fp32
+    assert f(*args(odt=5)) == _lib.FASTAR_EDTYPE
+    assert f(*args(scale=float("nan"))) == _lib.FASTAR_EINVAL
+    assert f(*args(q=MISALIGNED)) == _lib.FASTAR_EINVAL
+    c2 = _cache(H=2)
+    assert f(*args(cache=ctypes.byref(c2))) == _lib.FASTAR_ESHAPE
+
+
+def test_annca_validation(lib):
+    f = lib.fastar_annca_forward
+    need = lib.fastar_annca_workspace(1, 30, 10, 8, 4)
+    base = [FAKE, FAKE, 1, 30, 10, 64, 0, FAKE, FAKE, FAKE, 8, 4, 0.125, FAKE, 0, None, None]
+    assert f(*(base + [FAKE, need - 1, None])) == _lib.FASTAR_EWORKSPACE
+    bad = list(base); bad[4] = 7                         # 7 does not divide 30
+    assert f(*(bad + [FAKE, need, None])) == _lib.FASTAR_ESHAPE
+    bad = list(base); bad[4] = 0
+    assert f(*(bad + [FAKE, need, None])) == _lib.FASTAR_ESHAPE
+    bad = list(base); bad[7] = None                      # prompt keys missing
+    assert f(*(bad + [FAKE, need, None])) == _lib.FASTAR_EINVAL
+
+
+def test_tempcache_validation(lib):
+    f = lib.fastar_tempcache_update
+    c = _cache(cap=64)
+    need = lib.fastar_tempcache_workspace(1, 32, 64, 4)
+    def call(N=32, cache=c, tau=0.9, best_in=None, cos_in=None, ws=need, P=4):
+        return f(ctypes.byref(cache) if cache is not None else None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 N, P, tau, 3, best_in, cos_in, None, None, None, None, None, FAKE, ws, None)
+    assert call(ws=need - 1) == _lib.FASTAR_EWORKSPACE
+    assert call(N=65) == _lib.FASTAR_ECAPACITY
+    assert call(tau=float("nan")) == _lib.FASTAR_EINVAL
+    assert call(best_in=FAKE) == _lib.FASTAR_EINVAL      # best without cos
+    assert call(cache=None) == _lib.FASTAR_EINVAL
+    assert call(P=12) == _lib.FASTAR_ESHAPE
+    bad = _cache(cap=64, dtype=3)
+    assert call(cache=bad) == _lib.FASTAR_EDTYPE
+
+
+def test_bucket_sort_validation(lib):
+    f = lib.fastar_bucket_sort
+    need = lib.fastar_bucket_sort_workspace(2, 100, 5)
+    assert f(FAKE, 2, 100, 5, FAKE, FAKE, FAKE, need - 1, None) == _lib.FASTAR_EWORKSPACE
+    assert f(FAKE, 2, 100, 11, FAKE, FAKE, FAKE, need, None) == _lib.FASTAR_ESHAPE
+    assert f(None, 2, 100, 5, FAKE, FAKE, FAKE, need, None) == _lib.FASTAR_EINVAL
+
+
+def test_timer_without_launches(lib):
+    assert lib.fastar_timer_start() == 0
+    buf = (_lib.FastarKernelTime * 4)()
+    assert lib.fastar_timer_stop(buf, 4) == 0

@@ -1,0 +1,73 @@
+"""GPU parity of fastar_annca_forward against the oracle: keep masks and counts
+bit-exact, outputs within tolerance; workloads as generated (nearly every
+prompt token kept), constructed ids that prune most of the prompt, frames with
+nothing kept, and an empty prompt."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_autoregressive_amd as fa
+from oracle import annca as o_annca
+from tests.gpu_util import assert_attention_close, dev, dev_ids, prepared, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check(prep, q_ids, kp_ids, P, what, out_dtype=torch.float32, kp=None, vp=None):
+    st, cfg = prep["step"], prep["cfg"]
+    kp = st.kp if kp is None else kp
+    vp = st.vp if vp is None else vp
+    out, keep, cnt = fa.annca_forward(dev(st.q, cfg.dtype), dev_ids(q_ids), cfg.frame_len,
+                                      dev(kp, cfg.dtype), dev(vp, cfg.dtype), dev_ids(kp_ids), P,
+                                      out_dtype=out_dtype)
+    Os, Ks = [], []
+    for h in range(cfg.H):
+        O, keep_ref = o_annca(st.q[h], q_ids[h], cfg.frame_len, kp[h], vp[h], kp_ids[h], st.scale)
+        Os.append(O)
+        Ks.append(keep_ref)
+    keep_ref = np.stack(Ks)
+    assert np.array_equal(keep.cpu().numpy().astype(bool), keep_ref), what
+    assert np.array_equal(cnt.cpu().numpy(), keep_ref.sum(-1)), what
+    assert_attention_close(out, np.stack(Os), cfg.dtype, what)
+    return keep_ref
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_bf16", "wan13_bf16"])
+def test_annca_matches_oracle(name):
+    require_gpu()
+    prep = prepared(name)
+    keep = run_and_check(prep, prep["q_ids"], prep["kp_ids"], prep["cfg"].P, f"annca {name}")
+    print(f"annca {name}: kept {keep.mean():.3f}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "wan13_bf16"])
+def test_annca_pruned(name):
+    require_gpu()
+    prep = prepared(name)
+    cfg = prep["cfg"]
+    rng = np.random.default_rng(1)
+    B = 1 << cfg.P
+    F = cfg.Nq // cfg.frame_len
+    q_ids = np.empty_like(prep["q_ids"])
+    for f in range(F):   # each frame occupies its own small set of buckets
+        lo = (f * 5) % max(1, B - 8)
+        q_ids[:, f * cfg.frame_len:(f + 1) * cfg.frame_len] = rng.integers(lo, lo + 6, size=(cfg.H, cfg.frame_len))
+    kp_ids = rng.integers(0, B, size=prep["kp_ids"].shape).astype(np.uint16)
+    keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, cfg.P, f"pruned {name}")
+    assert 0 < keep.mean() < 0.5
+    keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, cfg.P, f"pruned bf16 out {name}",
+                         out_dtype=torch.bfloat16)
+
+
+def test_annca_nothing_kept_and_empty_prompt():
+    require_gpu()
+    prep = prepared("single_bf16")
+    cfg = prep["cfg"]
+    q_ids = np.zeros_like(prep["q_ids"])
+    kp_ids = np.ones_like(prep["kp_ids"])
+    keep = run_and_check(prep, q_ids, kp_ids, cfg.P, "nothing kept")
+    assert not keep.any()
+    st = prep["step"]
+    empty = np.zeros((cfg.H, 0, cfg.d), np.float32)
+    run_and_check(prep, prep["q_ids"], np.zeros((cfg.H, 0), np.uint16), cfg.P, "empty prompt",
+                  kp=empty, vp=empty)

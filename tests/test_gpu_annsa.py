@@ -1,0 +1,121 @@
+"""GPU parity of fastar_annsa_forward against the oracle (same inputs, the
+oracle's bucket ids), at the tiny fp32, single-head bf16 and full Wan-1.3B-like
+shapes, plus one bucket (dense attention), a partly filled cache, no cache,
+empty buckets, bf16 outputs and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_autoregressive_amd as fa
+from oracle import annsa as o_annsa, key_context
+from tests.gpu_util import (LSE_ABS, assert_attention_close, dev, dev_ids, device_cache,
+                            prepared, require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_annsa(prep, n, q_ids=None, kcur_ids=None, cache_ids=None, heads=None, use_cache=True):
+    st, cfg = prep["step"], prep["cfg"]
+    q_ids = prep["q_ids"] if q_ids is None else q_ids
+    kcur_ids = prep["k_cur_ids"] if kcur_ids is None else kcur_ids
+    cache_ids = prep["cache_ids"] if cache_ids is None else cache_ids
+    Os, Ls = [], []
+    for h in (range(cfg.H) if heads is None else heads):
+        nn = n if use_cache else 0
+        K, V, kid = key_context(st.cache_k[h], st.cache_v[h], cache_ids[h], nn, st.k_cur[h],
+                                st.v_cur[h], kcur_ids[h])
+        O, L = o_annsa(st.q[h], q_ids[h], K, V, kid, st.scale)
+        Os.append(O)
+        Ls.append(L)
+    return np.stack(Os), np.stack(Ls)
+
+
+def check_lse(lse_gpu, lse_ref):
+    g = lse_gpu.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(g), fin)
+    assert (np.isneginf(g) == np.isneginf(lse_ref)).all()
+    if fin.any():
+        assert np.abs(g[fin] - lse_ref[fin]).max() <= LSE_ABS
+
+
+def run(prep, cache=None, q_ids=None, kcur_ids=None, P=None, out_dtype=torch.float32):
+    st, cfg = prep["step"], prep["cfg"]
+    q_ids = prep["q_ids"] if q_ids is None else q_ids
+    kcur_ids = prep["k_cur_ids"] if kcur_ids is None else kcur_ids
+    return fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(q_ids), dev(st.k_cur, cfg.dtype),
+                            dev(st.v_cur, cfg.dtype), dev_ids(kcur_ids), cfg.P if P is None else P,
+                            cache=cache, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_bf16", "wan13_bf16"])
+def test_annsa_matches_oracle(name):
+    require_gpu()
+    prep = prepared(name)
+    cfg = prep["cfg"]
+    out, lse = run(prep, cache=device_cache(prep))
+    O, L = oracle_annsa(prep, cfg.n0)
+    err = assert_attention_close(out, O, cfg.dtype, f"annsa {name}")
+    check_lse(lse, L)
+    print(f"annsa {name}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_bf16"])
+def test_annsa_one_bucket_is_dense(name):
+    require_gpu()
+    prep = prepared(name)
+    st, cfg = prep["step"], prep["cfg"]
+    z = lambda a: np.zeros_like(a)
+    cache = device_cache(prep)
+    cache.ids.zero_()
+    out, lse = run(prep, cache=cache, q_ids=z(prep["q_ids"]), kcur_ids=z(prep["k_cur_ids"]), P=0)
+    O, L = oracle_annsa(prep, cfg.n0, q_ids=z(prep["q_ids"]), kcur_ids=z(prep["k_cur_ids"]),
+                        cache_ids=z(prep["cache_ids"]))
+    assert_attention_close(out, O, cfg.dtype, f"dense {name}")
+    check_lse(lse, L)
+
+
+def test_annsa_partial_cache_and_no_cache():
+    require_gpu()
+    prep = prepared("single_bf16")
+    cfg = prep["cfg"]
+    n = cfg.cap // 2 + 37
+    out, lse = run(prep, cache=device_cache(prep, n=n))
+    O, L = oracle_annsa(prep, n)
+    assert_attention_close(out, O, cfg.dtype, "partial cache")
+    check_lse(lse, L)
+    out, lse = run(prep, cache=None)
+    O, L = oracle_annsa(prep, 0, use_cache=False)
+    assert_attention_close(out, O, cfg.dtype, "no cache")
+    check_lse(lse, L)
+
+
+def test_annsa_empty_buckets():
+    require_gpu()
+    prep = prepared("tiny_f32")
+    st, cfg = prep["step"], prep["cfg"]
+    rng = np.random.default_rng(0)
+    q_ids = rng.integers(0, 16, size=prep["q_ids"].shape).astype(np.uint16)
+    k_ids = rng.integers(0, 8, size=prep["k_cur_ids"].shape).astype(np.uint16)
+    c_ids = rng.integers(0, 8, size=prep["cache_ids"].shape).astype(np.uint16)
+    cache = device_cache(prep)
+    cache.ids.copy_(dev_ids(c_ids))
+    out, lse = run(prep, cache=cache, q_ids=q_ids, kcur_ids=k_ids)
+    O, L = oracle_annsa(prep, cfg.n0, q_ids=q_ids, kcur_ids=k_ids, cache_ids=c_ids)
+    assert np.isneginf(L).sum() > 50
+    assert_attention_close(out, O, cfg.dtype, "empty buckets")
+    check_lse(lse, L)
+
+
+def test_annsa_bf16_output_and_determinism():
+    require_gpu()
+    prep = prepared("wan13_bf16")
+    cfg = prep["cfg"]
+    cache = device_cache(prep)
+    out_b, _ = run(prep, cache=cache, out_dtype=torch.bfloat16)
+    heads = [0, 5, 11]
+    O, _ = oracle_annsa(prep, cfg.n0, heads=heads)
+    assert_attention_close(out_b[heads], O, cfg.dtype, "bf16 out")
+    a, la = run(prep, cache=cache)
+    b, lb = run(prep, cache=cache)
+    assert torch.equal(a, b) and torch.equal(la, lb)

@@ -1,0 +1,69 @@
+"""GPU parity of fastar_ann_hash and fastar_bucket_sort against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_autoregressive_amd as fa
+from oracle import ann_hash as o_hash, bucket_sort as o_sort
+from tests.gpu_util import (assert_ids_match, dev, dev_ids, host_ids, prepared, require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_bf16", "wan13_bf16"])
+def test_hash_matches_oracle_on_workloads(name):
+    require_gpu()
+    prep = prepared(name)
+    st, cfg = prep["step"], prep["cfg"]
+    planes = torch.from_numpy(st.planes).cuda()
+    flagged = 0
+    for key, arr in (("q", st.q), ("k_cur", st.k_cur), ("cache", st.cache_k), ("kp", st.kp)):
+        ids = host_ids(fa.ann_hash(dev(arr, cfg.dtype), planes))
+        flagged += assert_ids_match(ids, prep[key + "_ids"], prep[key + "_tie"], f"{name}/{key}")
+    torch.cuda.synchronize()
+    print(f"{name}: {flagged} flagged ids differ (allowed)")
+
+
+@pytest.mark.parametrize("dtype,d,P,N", [("f32", 64, 0, 100), ("f32", 128, 16, 333),
+                                         ("bf16", 64, 9, 1025), ("bf16", 128, 16, 4097),
+                                         ("bf16", 128, 1, 1)])
+def test_hash_random_shapes(dtype, d, P, N):
+    require_gpu()
+    rng = np.random.default_rng(N + P)
+    H = 3
+    x = rng.standard_normal((H, N, d)).astype(np.float32)
+    if dtype == "bf16":
+        from workloads import bf16_round
+        x = bf16_round(x)
+    planes = rng.standard_normal((H, P, d)).astype(np.float32)
+    ids = host_ids(fa.ann_hash(dev(x, dtype), torch.from_numpy(planes).cuda()))
+    for h in range(H):
+        ref, tie = o_hash(x[h], planes[h])
+        assert_ids_match(ids[h], ref, tie, f"head {h}")
+
+
+@pytest.mark.parametrize("P,N", [(0, 17), (3, 0), (5, 1), (7, 1023), (7, 1025), (7, 37440),
+                                 (10, 5000), (8, 4096)])
+def test_bucket_sort_bit_exact(P, N):
+    require_gpu()
+    rng = np.random.default_rng(10 * P + N)
+    H = 4
+    # skewed bucket sizes, like the workloads' clusters
+    w = rng.dirichlet(np.full(1 << P, 0.3))
+    ids = rng.choice(1 << P, size=(H, N), p=w).astype(np.uint16)
+    off, perm = fa.bucket_sort(dev_ids(ids), P)
+    off2, perm2 = fa.bucket_sort(dev_ids(ids), P)
+    off, perm = off.cpu().numpy(), perm.cpu().numpy()
+    for h in range(H):
+        ro, rp = o_sort(ids[h], P)
+        assert np.array_equal(off[h], ro)
+        assert np.array_equal(perm[h], rp)
+    assert torch.equal(off2.cpu(), torch.from_numpy(off)) and torch.equal(perm2.cpu(), torch.from_numpy(perm))
+
+
+def test_bucket_sort_ignores_high_bits():
+    require_gpu()
+    ids = np.array([[5, 5 + 8, 2, 2 + 64, 7]], np.uint16)
+    off, perm = fa.bucket_sort(dev_ids(ids), 3)
+    ro, rp = o_sort(ids[0] & 7, 3)
+    assert np.array_equal(off.cpu().numpy()[0], ro) and np.array_equal(perm.cpu().numpy()[0], rp)
