@@ -1,0 +1,223 @@
+"""Benchmark of one FAST-AR attention step on one MI355X.
+
+A step is the whole hot path over one chunk of the Wan-1.3B-like layer
+(12 heads x d=128, bf16; a 3-frame chunk of 4680 tokens; a full 32760-slot
+cache; 7 hyperplanes = 128 buckets; 512 prompt tokens):
+
+    ann_hash(q), ann_hash(k_cur), ann_hash(prompt k)
+    annsa_forward   (bucket sort + gathered MFMA attention over [cache ; chunk])
+    annca_forward   (prompt selection + cross-attention over the kept tokens)
+    tempcache_update(bucket sort + top-1 search + claim/select + row scatter)
+
+Inputs are seeded synthetic tensors, resident in HBM before the timed region.
+Every timed step starts from its own pristine copy of the cache (the commit
+mutates it), so each step sees exactly the same workload.
+
+Output: one JSON line.  ``value`` is the achieved bf16 TFLOP/s on kept pairs,
+4*d*(AnnSA kept pairs + AnnCA kept pairs) / step time; ``ms_per_step`` is the
+step latency.  ``roofline`` describes the dominant kernel (AnnSA's bucket
+attention, HBM-bound): algorithmic bytes per launch / its mean duration from
+HIP events on its launch stream.  ``cpu_baseline`` times the CPU oracle on a
+bounded sample of heads of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+
+# rocprofv3 FETCH_SIZE+WRITE_SIZE of the AnnSA attention kernel at this
+# workload, scaled by the copy-kernel calibration; None until measured for the
+# current kernel.
+ANNSA_TRAFFIC_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="wan13_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU-oracle sample budget (heads are added until it is spent)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(every head is independent; see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_autoregressive_amd as fa
+    from workloads import CONFIGS, f32_to_bf16_bits, make_step
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = make_step(cfg, args.seed)
+
+    def to_dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+
+    H, Nq, d, cap, P = cfg.H, cfg.Nq, cfg.d, cfg.cap, cfg.P
+    q, kc, vc = to_dev(st.q), to_dev(st.k_cur), to_dev(st.v_cur)
+    kp, vp = to_dev(st.kp), to_dev(st.vp)
+    planes = torch.from_numpy(st.planes).to(dev)
+    base = fa.KVCache(k=to_dev(st.cache_k), v=to_dev(st.cache_v),
+                      ids=torch.empty(H, cap, dtype=torch.int16, device=dev),
+                      ts=torch.from_numpy(st.cache_ts).to(dev),
+                      n_valid=torch.from_numpy(st.n_valid).to(dev))
+    fa.ann_hash(base.k, planes, ids=base.ids)          # cached keys carry their bucket ids
+
+    n_copies = args.warmup + 2 * args.steps
+    caches = [fa.KVCache(k=base.k.clone(), v=base.v.clone(), ids=base.ids.clone(),
+                         ts=base.ts.clone(), n_valid=base.n_valid.clone()) for _ in range(n_copies)]
+    out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    lib = fa.load()
+    ws = {
+        "sa": torch.empty(lib.fastar_annsa_workspace(H, Nq, cap, Nq, P), dtype=torch.uint8, device=dev),
+        "ca": torch.empty(lib.fastar_annca_workspace(H, Nq, cfg.frame_len, cfg.L, P), dtype=torch.uint8, device=dev),
+        "tc": torch.empty(lib.fastar_tempcache_workspace(H, Nq, cap, P), dtype=torch.uint8, device=dev),
+    }
+    ids = {k: torch.empty(H, n, dtype=torch.int16, device=dev)
+           for k, n in (("q", Nq), ("k", Nq), ("p", cfg.L))}
+    o_sa = torch.empty(H, Nq, d, dtype=out_dt, device=dev)
+    lse = torch.empty(H, Nq, dtype=torch.float32, device=dev)
+    o_ca = torch.empty(H, Nq, d, dtype=out_dt, device=dev)
+
+    def step(cache):
+        fa.ann_hash(q, planes, ids=ids["q"])
+        fa.ann_hash(kc, planes, ids=ids["k"])
+        fa.ann_hash(kp, planes, ids=ids["p"])
+        fa.annsa_forward(q, ids["q"], kc, vc, ids["k"], P, cache=cache, out=o_sa, lse=lse, ws=ws["sa"])
+        _, keep, cnt = fa.annca_forward(q, ids["q"], cfg.frame_len, kp, vp, ids["p"], P, out=o_ca,
+                                        ws=ws["ca"])
+        res = fa.tempcache_update(cache, q, ids["q"], kc, vc, ids["k"], P, cfg.tau, st.step,
+                                  outputs=False, ws=ws["tc"])
+        return cnt
+
+    it = iter(caches)
+    for _ in range(args.warmup):
+        cnt = step(next(it))
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        cnt = step(next(it))
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # ---- the same K steps again with per-kernel HIP events (launch stream)
+    with fa.kernel_timer() as kt:
+        for _ in range(args.steps):
+            step(next(it))
+    torch.cuda.synchronize()
+    kernel_ms = {k: v[1] / max(1, v[0]) for k, v in kt.times.items()}
+    kernel_launches = {k: v[0] // args.steps for k, v in kt.times.items()}
+
+    # ---- work accounting (not timed): kept pairs and algorithmic bytes
+    B = 1 << P
+    qi = ids["q"].long() & 0xFFFF
+    ki = torch.cat([base.ids.long() & 0xFFFF, ids["k"].long() & 0xFFFF], dim=1)
+    nqb = torch.stack([torch.bincount(qi[h], minlength=B) for h in range(H)]).double()
+    nkb = torch.stack([torch.bincount(ki[h], minlength=B) for h in range(H)]).double()
+    sa_pairs = float((nqb * nkb).sum())
+    ca_pairs = float(cnt.double().sum() * cfg.frame_len)
+    flops = 4.0 * d * (sa_pairs + ca_pairs)
+    value_tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    esz = 2 if cfg.dtype == "bf16" else 4
+    osz = 4 if out_dt == torch.float32 else 2
+    keys_read = float((nkb * (nqb > 0)).sum())                 # each kept key row once
+    sa_bytes = Nq * H * d * esz + keys_read * 2 * d * esz + Nq * H * (d * osz + 4)
+    attn_ms = kernel_ms.get("annsa_attn")
+    achieved = sa_bytes / (attn_ms * 1e-3) / 1e9 if attn_ms else None
+    roofline = {"kernel": "annsa_attn", "bound": "hbm", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                "traffic": ANNSA_TRAFFIC_BYTES, "algorithmic_bytes": sa_bytes,
+                "mean_ms": attn_ms}
+
+    line = {
+        "metric": "attention step latency (ms) + achieved bf16 TFLOP/s on kept pairs, Wan-1.3B chunk",
+        "value": value_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {H} heads x d={d}, chunk {cfg.Fq} frames x "
+                               f"{cfg.frame_len} = {Nq} tokens, cache {cap} slots (full), "
+                               f"P={P} ({B} buckets), prompt {cfg.L}, tau={cfg.tau}",
+                   "out_dtype": args.out_dtype, "seed": args.seed},
+        "roofline": roofline,
+        "kernel_ms": kernel_ms, "kernel_launches_per_step": kernel_launches,
+        "kept_pairs": {"annsa": sa_pairs, "annca": ca_pairs,
+                       "annsa_frac_of_dense": sa_pairs / (H * Nq * (cap + Nq))},
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds, line)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, seed, budget_s, line):
+    """The oracle (unchanged) on whole heads of the same workload until the
+    budget is spent; scaled to TFLOP/s on kept pairs."""
+    import numpy as np
+    from oracle import ann_hash, attention_step
+    from workloads import make_step
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:                                        # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    t_total, pairs, heads = 0.0, 0.0, 0
+    h = 0
+    while t_total < budget_s and heads < 16 * cfg.H:
+        st = make_step(cfg, seed, heads=range(h, h + 1))
+        cid = np.stack([ann_hash(st.cache_k[0], st.planes[0])[0]])
+        t0 = time.perf_counter()
+        r = attention_step(st.q, st.k_cur, st.v_cur, st.cache_k, st.cache_v, cid, st.cache_ts,
+                           st.n_valid, st.planes, st.kp, st.vp, cfg.frame_len, cfg.tau, st.step)
+        t_total += time.perf_counter() - t0
+        qi = r["q_ids"][0].astype(np.int64)
+        ki = np.concatenate([cid[0], r["kcur_ids"][0]]).astype(np.int64)
+        B = 1 << cfg.P
+        pairs += float((np.bincount(qi, minlength=B) * np.bincount(ki, minlength=B)).sum())
+        pairs += float(r["keep"][0].sum() * cfg.frame_len)
+        heads += 1
+        h = (h + 1) % cfg.H
+    value = 4.0 * cfg.d * pairs / t_total / 1e12
+    return {"value": value, "unit": "TFLOP/s", "cores": min(cores, threads) if threads else cores,
+            "kind": "oracle",
+            "sample": f"{heads} head-passes (heads cycled, {cfg.H} per step) of the same step "
+                      f"(hash + AnnSA + AnnCA + TempCache), "
+                      f"{t_total:.1f} s on the host; BLAS threads {threads}, affinity cores {cores}",
+            "ms_per_step_equiv": t_total / heads * cfg.H * 1e3}
+
+
+if __name__ == "__main__":
+    main()
