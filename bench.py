@@ -5,9 +5,10 @@ A step is the whole hot path over one chunk of the Wan-1.3B-like layer
 cache; 7 hyperplanes = 128 buckets; 512 prompt tokens):
 
     ann_hash(q), ann_hash(k_cur), ann_hash(prompt k)
-    annsa_forward   (bucket sort + gathered MFMA attention over [cache ; chunk])
+    annsa_forward   (bucket sort + gathered MFMA attention over [cache ; chunk];
+                     the same pass returns TempCache's top-1 for every query)
     annca_forward   (prompt selection + cross-attention over the kept tokens)
-    tempcache_update(bucket sort + top-1 search + claim/select + row scatter)
+    tempcache_update(claims from that top-1 + select + row scatter)
 
 Inputs are seeded synthetic tensors, resident in HBM before the timed region.
 Every timed step starts from its own pristine copy of the cache (the commit
@@ -83,15 +84,12 @@ def main():
     q, kc, vc = to_dev(st.q), to_dev(st.k_cur), to_dev(st.v_cur)
     kp, vp = to_dev(st.kp), to_dev(st.vp)
     planes = torch.from_numpy(st.planes).to(dev)
-    base = fa.KVCache(k=to_dev(st.cache_k), v=to_dev(st.cache_v),
-                      ids=torch.empty(H, cap, dtype=torch.int16, device=dev),
-                      ts=torch.from_numpy(st.cache_ts).to(dev),
-                      n_valid=torch.from_numpy(st.n_valid).to(dev))
-    fa.ann_hash(base.k, planes, ids=base.ids)          # cached keys carry their bucket ids
-
+    # cached keys carry their bucket ids and norms
+    base = fa.KVCache.from_keys(to_dev(st.cache_k), to_dev(st.cache_v),
+                                torch.from_numpy(st.cache_ts).to(dev),
+                                torch.from_numpy(st.n_valid).to(dev), planes)
     n_copies = args.warmup + 2 * args.steps
-    caches = [fa.KVCache(k=base.k.clone(), v=base.v.clone(), ids=base.ids.clone(),
-                         ts=base.ts.clone(), n_valid=base.n_valid.clone()) for _ in range(n_copies)]
+    caches = [base.clone() for _ in range(n_copies)]
     out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
     lib = fa.load()
     ws = {
@@ -104,16 +102,19 @@ def main():
     o_sa = torch.empty(H, Nq, d, dtype=out_dt, device=dev)
     lse = torch.empty(H, Nq, dtype=torch.float32, device=dev)
     o_ca = torch.empty(H, Nq, d, dtype=out_dt, device=dev)
+    best = torch.empty(H, Nq, dtype=torch.int32, device=dev)
+    bcos = torch.empty(H, Nq, dtype=torch.float32, device=dev)
 
     def step(cache):
         fa.ann_hash(q, planes, ids=ids["q"])
         fa.ann_hash(kc, planes, ids=ids["k"])
         fa.ann_hash(kp, planes, ids=ids["p"])
-        fa.annsa_forward(q, ids["q"], kc, vc, ids["k"], P, cache=cache, out=o_sa, lse=lse, ws=ws["sa"])
+        fa.annsa_forward(q, ids["q"], kc, vc, ids["k"], P, cache=cache, out=o_sa, lse=lse,
+                         ws=ws["sa"], search=True, best=best, best_cos=bcos)
         _, keep, cnt = fa.annca_forward(q, ids["q"], cfg.frame_len, kp, vp, ids["p"], P, out=o_ca,
                                         ws=ws["ca"])
-        res = fa.tempcache_update(cache, q, ids["q"], kc, vc, ids["k"], P, cfg.tau, st.step,
-                                  outputs=False, ws=ws["tc"])
+        fa.tempcache_update(cache, q, ids["q"], kc, vc, ids["k"], P, cfg.tau, st.step,
+                            best_in=best, cos_in=bcos, outputs=False, ws=ws["tc"])
         return cnt
 
     it = iter(caches)
@@ -153,7 +154,12 @@ def main():
     esz = 2 if cfg.dtype == "bf16" else 4
     osz = 4 if out_dt == torch.float32 else 2
     keys_read = float((nkb * (nqb > 0)).sum())                 # each kept key row once
-    sa_bytes = Nq * H * d * esz + keys_read * 2 * d * esz + Nq * H * (d * osz + 4)
+    ci = base.ids.long() & 0xFFFF
+    nkc = torch.stack([torch.bincount(ci[h], minlength=B) for h in range(H)]).double()
+    cached_read = float((nkc * (nqb > 0)).sum())                # their norms, for the search
+    # Q in; K and V of every kept key; O, lse, best slot and cosine out; key norms
+    sa_bytes = (Nq * H * d * esz + keys_read * 2 * d * esz + Nq * H * (d * osz + 4 + 8)
+                + cached_read * 4)
     attn_ms = kernel_ms.get("annsa_attn")
     achieved = sa_bytes / (attn_ms * 1e-3) / 1e9 if attn_ms else None
     roofline = {"kernel": "annsa_attn", "bound": "hbm", "achieved": achieved,

@@ -52,7 +52,7 @@ extern "C" {
 
 typedef enum {
     FASTAR_OK = 0,
-    FASTAR_EINVAL = -1,      /* null pointer, negative size, non-finite scalar */
+    FASTAR_EINVAL = -1,      /* null pointer, negative size, bad scalar (non-finite, scale <= 0) */
     FASTAR_EDTYPE = -2,      /* unknown dtype, or dtypes that must agree do not */
     FASTAR_ESHAPE = -3,      /* d not 64/128, P out of range, frame_len not dividing Nq, H mismatch */
     FASTAR_EWORKSPACE = -4,  /* workspace smaller than the query returned (or NULL with size > 0) */
@@ -67,9 +67,13 @@ typedef enum { FASTAR_F32 = 0, FASTAR_BF16 = 1 } fastar_dtype;
  *   k, v     [H][cap][d] of ``dtype``
  *   ids      [H][cap]  bucket id of the key held in each slot
  *   ts       [H][cap]  timestamp (step) at which each slot was written
+ *   knorm    [H][cap]  fp32 norm |k| of the key held in each slot (the
+ *                      TempCache cosine search divides by it)
  *   n_valid  [H]       number of valid slots; slots 0..n_valid[h]-1 are valid.
  * n_valid stays on the device so that a step never waits on the host; values
- * outside [0, cap] are clamped when read. */
+ * outside [0, cap] are clamped when read.  fastar_tempcache_update maintains
+ * every field; a cache filled by other means gets ids and knorm from
+ * fastar_ann_hash on its keys. */
 typedef struct {
     int32_t H;
     int32_t cap;
@@ -80,6 +84,7 @@ typedef struct {
     uint16_t* ids;
     int32_t* ts;
     int32_t* n_valid;
+    float* knorm;
 } fastar_cache;
 
 /* Status name, e.g. "FASTAR_ESHAPE" (static storage, never NULL). */
@@ -94,12 +99,14 @@ int32_t fastar_abi_version(void);
  *
  * x       [H][N][d] of ``dtype``      planes  [H][P][d] fp32
  * ids     [H][N] uint16 (output)
+ * norms   [H][N] fp32 (output, may be NULL): |x[h][i]|, in the same pass
  * P in [0, 16]; P = 0 puts every token in bucket 0.  The projection is
  * accumulated in fp32; a projection within fp32 rounding of 0 may take either
  * sign.
  * ------------------------------------------------------------------------ */
 fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
-                              const float* planes, int32_t P, uint16_t* ids, void* stream);
+                              const float* planes, int32_t P, uint16_t* ids, float* norms,
+                              void* stream);
 
 /* ------------------------------------------------------------------------
  * Stable grouping of tokens by bucket -- the block-sparse layout AnnSA runs
@@ -129,9 +136,16 @@ fastar_status fastar_bucket_sort(const uint16_t* ids, int32_t H, int32_t N, int3
  * cache     host pointer, may be NULL (no cached keys); its H, d and dtype
  *           must equal the call's
  * k_cur, v_cur [H][Ncur][d] of ``dtype``, kcur_ids [H][Ncur]; Ncur may be 0
- * scale     softmax scale (finite); 1/sqrt(d) is the usual value
+ * scale     softmax scale, finite and > 0; 1/sqrt(d) is the usual value
  * out       [H][Nq][d] of ``out_dtype`` (FASTAR_F32 or FASTAR_BF16)
  * lse       [H][Nq] fp32, may be NULL
+ * best, best_cos  [H][Nq] int32 / fp32, may be NULL (both or neither): the
+ *           same pass also returns TempCache's top-1 for each query -- the
+ *           cached slot j < n_valid with ids[j] == q_ids[i] of largest
+ *           cos(q_i, k_j) = <q_i,k_j> / (|q_i| knorm[j]) (ties: lowest slot;
+ *           a zero norm gives 0), or -1 and -inf when the bucket holds no
+ *           cached key -- ready to pass to fastar_tempcache_update as
+ *           best_in/cos_in.
  * ws        workspace of fastar_annsa_workspace(H, Nq, cap, Ncur, P) bytes,
  *           cap = cache ? cache->cap : 0
  * Products are bf16 x bf16 (or fp32 x fp32) on the matrix cores with fp32
@@ -142,8 +156,8 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
                                    int32_t d, int32_t dtype, const fastar_cache* cache,
                                    const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
                                    int32_t Ncur, int32_t P, float scale, void* out,
-                                   int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
-                                   void* stream);
+                                   int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * AnnCA: frame-relevant prompt pruning + cross-attention (blog, "2. AnnCA";
@@ -156,7 +170,7 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
  * out        [H][Nq][d] of ``out_dtype``
  * keep       [H][F][L] uint8 (0/1), may be NULL
  * keep_count [H][F] int32, may be NULL
- * frame_len must divide Nq.  L may be 0.
+ * frame_len must divide Nq.  L may be 0.  scale: finite and > 0.
  * ------------------------------------------------------------------------ */
 size_t fastar_annca_workspace(int32_t H, int32_t Nq, int32_t frame_len, int32_t L, int32_t P);
 fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
@@ -169,13 +183,15 @@ fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t
  * TempCache commit of one chunk (blog, "1. TempCache"; summary, Core
  * Components A).  Per head, with n = n_valid[h] before the call:
  *  1. top-1: for each current token i, best[i] = the valid slot j < n with
- *     ids[j] == q_ids[i] maximising cos(q_i, k_j) (ties: lowest j; a zero
- *     norm gives cosine 0); -1 and cos = -inf if the bucket has no slot.
- *     Skipped when best_in and cos_in are given (then those are used; a
- *     best_in value outside [0, n) means "no candidate").
+ *     ids[j] == q_ids[i] maximising cos(q_i, k_j) = <q_i,k_j>/(|q_i| knorm[j])
+ *     (ties: lowest j; a zero norm gives cosine 0); -1 and cos = -inf if the
+ *     bucket has no slot.  Skipped when best_in and cos_in are given (then
+ *     those are used -- e.g. fastar_annsa_forward's best/best_cos; a best_in
+ *     value outside [0, n) means "no candidate").
  *  2. matched[i] = best[i] >= 0 && cos[i] >= tau.  Each matched slot is
  *     refreshed with the current token of largest index that matched it
- *     (k, v, id <- the token's k_cur, v_cur, kcur_id; ts <- step); the other
+ *     (k, v, id <- the token's k_cur, v_cur, kcur_id; ts <- step; knorm <-
+ *     |k_cur|); the other
  *     tokens that matched the same slot are dropped (merged away).
  *  3. the u unmatched tokens, in token order, fill slots n, n+1, ... up to
  *     cap, then the e = max(0, n + u - cap) non-refreshed slots with the

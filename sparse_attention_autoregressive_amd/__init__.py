@@ -60,6 +60,7 @@ class KVCache:
     ids: torch.Tensor        # [H, cap] int16 (uint16 bit pattern)
     ts: torch.Tensor         # [H, cap] int32
     n_valid: torch.Tensor    # [H] int32
+    knorm: torch.Tensor      # [H, cap] float32, |k| of each slot's key
 
     @classmethod
     def empty(cls, H: int, cap: int, d: int, dtype=torch.bfloat16, device="cuda") -> "KVCache":
@@ -67,7 +68,22 @@ class KVCache:
                    v=torch.zeros(H, cap, d, dtype=dtype, device=device),
                    ids=torch.zeros(H, cap, dtype=torch.int16, device=device),
                    ts=torch.zeros(H, cap, dtype=torch.int32, device=device),
-                   n_valid=torch.zeros(H, dtype=torch.int32, device=device))
+                   n_valid=torch.zeros(H, dtype=torch.int32, device=device),
+                   knorm=torch.zeros(H, cap, dtype=torch.float32, device=device))
+
+    @classmethod
+    def from_keys(cls, k: torch.Tensor, v: torch.Tensor, ts: torch.Tensor, n_valid: torch.Tensor,
+                  planes: torch.Tensor) -> "KVCache":
+        """A cache holding ``k``/``v`` with bucket ids and norms computed by ann_hash."""
+        H, cap, _ = k.shape
+        c = cls(k=k, v=v, ids=torch.empty(H, cap, dtype=torch.int16, device=k.device), ts=ts,
+                n_valid=n_valid, knorm=torch.empty(H, cap, dtype=torch.float32, device=k.device))
+        ann_hash(k, planes, ids=c.ids, norms=c.knorm)
+        return c
+
+    def clone(self) -> "KVCache":
+        return KVCache(k=self.k.clone(), v=self.v.clone(), ids=self.ids.clone(),
+                       ts=self.ts.clone(), n_valid=self.n_valid.clone(), knorm=self.knorm.clone())
 
     @property
     def H(self) -> int:
@@ -82,14 +98,15 @@ class KVCache:
         return self.k.shape[2]
 
     def struct(self) -> _lib.FastarCache:
-        for t in (self.k, self.v, self.ids, self.ts, self.n_valid):
+        for t in (self.k, self.v, self.ids, self.ts, self.n_valid, self.knorm):
             if not t.is_contiguous():
                 raise ValueError("cache tensors must be contiguous")
         if self.ids.dtype != torch.int16 or self.ts.dtype != torch.int32 \
-                or self.n_valid.dtype != torch.int32:
-            raise TypeError("cache ids must be int16, ts and n_valid int32")
+                or self.n_valid.dtype != torch.int32 or self.knorm.dtype != torch.float32:
+            raise TypeError("cache ids must be int16, ts and n_valid int32, knorm float32")
         return _lib.FastarCache(self.H, self.cap, self.d, _dtype_code(self.k), _ptr(self.k),
-                                _ptr(self.v), _ptr(self.ids), _ptr(self.ts), _ptr(self.n_valid))
+                                _ptr(self.v), _ptr(self.ids), _ptr(self.ts), _ptr(self.n_valid),
+                                _ptr(self.knorm))
 
 
 def _ids_check(ids: torch.Tensor, shape) -> None:
@@ -97,8 +114,10 @@ def _ids_check(ids: torch.Tensor, shape) -> None:
         raise ValueError(f"ids must be int16 of shape {tuple(shape)}, got {ids.dtype} {tuple(ids.shape)}")
 
 
-def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Bucket ids [H, N] (int16 holding uint16 bits) of x [H, N, d] under planes [H, P, d] fp32."""
+def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] = None,
+             norms: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Bucket ids [H, N] (int16 holding uint16 bits) of x [H, N, d] under planes [H, P, d]
+    fp32; with ``norms`` ([H, N] float32) also writes |x|."""
     H, N, d = x.shape
     P = planes.shape[1]
     if planes.dtype != torch.float32 or tuple(planes.shape) != (H, P, d):
@@ -106,8 +125,10 @@ def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] 
     if ids is None:
         ids = torch.empty(H, N, dtype=torch.int16, device=x.device)
     _ids_check(ids, (H, N))
+    if norms is not None and (norms.dtype != torch.float32 or tuple(norms.shape) != (H, N)):
+        raise ValueError("norms must be float32 [H, N]")
     check("fastar_ann_hash", load().fastar_ann_hash(_ptr(x), _dtype_code(x), H, N, d, _ptr(planes),
-                                                    P, _ptr(ids), _stream(x.device)))
+                                                    P, _ptr(ids), _ptr(norms), _stream(x.device)))
     return ids
 
 
@@ -128,8 +149,11 @@ def annsa_forward(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor, v_c
                   kcur_ids: torch.Tensor, P: int, cache: Optional[KVCache] = None,
                   scale: Optional[float] = None, out_dtype=torch.float32,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                  want_lse: bool = True, ws: Optional[torch.Tensor] = None):
-    """Bucket-restricted self-attention over [cache ; current chunk]: (out, lse)."""
+                  want_lse: bool = True, ws: Optional[torch.Tensor] = None,
+                  search: bool = False, best: Optional[torch.Tensor] = None,
+                  best_cos: Optional[torch.Tensor] = None):
+    """Bucket-restricted self-attention over [cache ; current chunk]: (out, lse), or
+    (out, lse, best, best_cos) with ``search`` (TempCache's top-1 from the same pass)."""
     H, Nq, d = q.shape
     Ncur = k_cur.shape[1]
     _ids_check(q_ids, (H, Nq))
@@ -142,14 +166,20 @@ def annsa_forward(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor, v_c
         out = torch.empty(H, Nq, d, dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(H, Nq, dtype=torch.float32, device=q.device)
+    if search:
+        if best is None:
+            best = torch.empty(H, Nq, dtype=torch.int32, device=q.device)
+        if best_cos is None:
+            best_cos = torch.empty(H, Nq, dtype=torch.float32, device=q.device)
     cs = cache.struct() if cache is not None else None
     cap = cache.cap if cache is not None else 0
     wsp, wsn = _workspace(lib.fastar_annsa_workspace(H, Nq, cap, Ncur, P), q.device, ws)
     check("fastar_annsa_forward", lib.fastar_annsa_forward(
         _ptr(q), _ptr(q_ids), H, Nq, d, _dtype_code(q), ctypes.byref(cs) if cs else None,
         _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), Ncur, P, scale, _ptr(out), _dtype_code(out),
-        _ptr(lse), wsp, wsn, _stream(q.device)))
-    return out, lse
+        _ptr(lse), _ptr(best) if search else None, _ptr(best_cos) if search else None,
+        wsp, wsn, _stream(q.device)))
+    return (out, lse, best, best_cos) if search else (out, lse)
 
 
 def annca_forward(q: torch.Tensor, q_ids: torch.Tensor, frame_len: int, kp: torch.Tensor,

@@ -28,7 +28,8 @@ FASTAR_TIMER_MAX = 8192
 class FastarCache(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("cap", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("ids", ctypes.c_void_p), ("ts", ctypes.c_void_p), ("n_valid", ctypes.c_void_p)]
+                ("ids", ctypes.c_void_p), ("ts", ctypes.c_void_p), ("n_valid", ctypes.c_void_p),
+                ("knorm", ctypes.c_void_p)]
 
 
 class FastarKernelTime(ctypes.Structure):
@@ -41,12 +42,13 @@ _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c
 SIGNATURES = {
     "fastar_status_string": (ctypes.c_char_p, [_i32]),
     "fastar_abi_version": (_i32, []),
-    "fastar_ann_hash": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
+    "fastar_ann_hash": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "fastar_bucket_sort_workspace": (_sz, [_i32, _i32, _i32]),
     "fastar_bucket_sort": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "fastar_annsa_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "fastar_annsa_forward": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(FastarCache),
-                                    _vp, _vp, _vp, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _sz, _vp]),
+                                    _vp, _vp, _vp, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _vp,
+                                    _vp, _sz, _vp]),
     "fastar_annca_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "fastar_annca_forward": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                     _i32, _f32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),

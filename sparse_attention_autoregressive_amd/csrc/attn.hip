@@ -3,12 +3,15 @@
 //  MODE_SA   AnnSA: one block per (head, bucket, 64-query slice).  Queries are
 //            the bucket's current-chunk queries, keys the bucket's members of
 //            [cache slots ; current chunk] (FAST-AR blog, "3. AnnSA"; summary,
-//            "2. Core Components" C).  Softmax attention + log-sum-exp.
+//            "2. Core Components" C).  Softmax attention + log-sum-exp.  With
+//            SEARCH the same pass also finds each query's most similar cached
+//            key (TempCache's top-1, blog "1. TempCache"; summary A): those
+//            keys are exactly the cached members of the query's bucket, whose
+//            dot products the attention computes anyway.
 //  MODE_CA   AnnCA: one block per (head, frame, 64 consecutive queries); keys
 //            are the frame's kept prompt tokens (blog, "2. AnnCA"; summary B).
-//  MODE_TOP1 TempCache search: same blocks as SA over old-cache keys only;
-//            instead of a softmax each query keeps its best cosine and slot
-//            (blog, "1. TempCache"; summary A), then claims the slot.
+//  MODE_TOP1 TempCache search alone: the SA blocks over cached keys only, no
+//            softmax; each query keeps its best cosine and slot and claims it.
 //
 // Layout of the work inside a block (256 threads = 4 waves, wave w owns the
 // block's queries 16w..16w+15; lane l serves query l%16 and "lane group"
@@ -18,14 +21,24 @@
 //    and four keys per 16-key block: the row max / sum of the online softmax
 //    then need only two cross-lane steps (lanes l, l^16, l^32, l^48), and the
 //    probabilities are already laid out as the B operand of O^T = V^T P^T.
-//  * K tiles of 64 rows sit row-major in LDS (A operand of S^T, 16 contiguous
-//    bytes per lane).  For bf16, V tiles are stored transposed in LDS with the
-//    keys of each 32-key group permuted so that lane group g reads its eight
-//    keys {4g..4g+3, 16+4g..16+4g+3} as 16 contiguous bytes -- the same keys
-//    its probabilities cover.  For fp32 (16x16x4 MFMA) V stays row-major.
-//  * Global K/V rows are gathered through the index list with 16-byte loads
-//    (16 lanes cover one 256-byte bf16 row), one tile ahead of the compute,
-//    and the index list itself two tiles ahead.
+//  * K and V tiles of 64 rows sit row-major in LDS (16-byte, bank-conflict-free
+//    stores; rows padded by 16 bytes).  K fragments (A operand of S^T) are 16
+//    contiguous bytes per lane.  The bf16 V^T fragments come from gfx950's
+//    LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane
+//    i receives element i%4 of the 8-byte chunks addressed by lanes
+//    4k + i/4 (k = 0..3), so when lane j points at V[key0 + j/4][d0 + 4(j%4)]
+//    lane i gets dim d0+i of keys key0..key0+3.  Two such reads give lane group
+//    g the keys {4g..4g+3, 16+4g..16+4g+3} of a 32-key group -- exactly the
+//    keys its probabilities cover in the B operand.  For fp32 (16x16x4 MFMA)
+//    V is read row-major.
+//  * The item's key indices are staged in LDS; K/V rows are gathered with
+//    16-byte loads (16 lanes cover one 256-byte bf16 row) into two register
+//    stages, so two tiles are in flight while the third is computed on.
+//  * SA/TOP1 blocks read their work item (query slice, key range) from a table
+//    the bucket sort writes, longest key lists first, with heads fastest in the
+//    launch order, so the largest buckets never form the tail of the launch.
+//  * The search uses the cached keys' norms kept in the cache, so a cosine is
+//    one product per (query, key): dot * (1/|q|) * (1/|k|).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,14 +47,15 @@ namespace fastar {
 namespace {
 
 constexpr int KT = 64;            // keys per LDS tile
+constexpr int KCH = 1024;         // key indices staged in LDS at a time
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// Position of key kk (0..63) in a transposed-V row: within each 32-key group,
-// keys 4g..4g+3 go to 8g..8g+3 and keys 16+4g..16+4g+3 to 8g+4..8g+7.
-__device__ __forceinline__ int vt_pos(int kk) {
-    const int grp = kk >> 5, r = kk & 31, quad = r >> 2;
-    const int base = quad < 4 ? 8 * quad : 8 * (quad - 4) + 4;
-    return grp * 32 + base + (r & 3);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 4 bf16 of V^T through the LDS transpose read (see the header comment).
+__device__ __forceinline__ v4i16 lds_read_tr(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<void*>(p)));
 }
 
 template <typename T, int D, int MODE>
@@ -52,28 +66,26 @@ struct Tile {
     static constexpr int CPR = D / EPC;                 // chunks per row
     static constexpr int UNITS = (KT / 4) * CPR;        // (4-row quad, chunk) units
     static constexpr int UPT = (UNITS + 255) / 256;     // units per thread
-    static constexpr int KSTR = D + (BF ? 8 : 4);            // padded K row (elements)
-    static constexpr int VTSTR = KT + 8;                // bf16 transposed V row
-    static constexpr int VRSTR = D + 4;                 // fp32 row-major V row
-    static constexpr int VSIZE = HAS_V ? (BF ? D * VTSTR : KT * VRSTR) : 1;
+    static constexpr int STR = D + EPC;                 // padded row (elements), K and V
 };
 
 }  // namespace
 
-template <typename T, int D, int MODE, typename OT>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
+template <typename T, int D, int MODE, bool SEARCH, typename OT>
+__device__ __forceinline__ void attn_body(const AttnParams& p) {
     using TL = Tile<T, D, MODE>;
     constexpr bool BF = TL::BF;
     constexpr bool HAS_V = TL::HAS_V;
     constexpr int UPT = TL::UPT, CPR = TL::CPR, EPC = TL::EPC;
-    constexpr int KSTR = TL::KSTR, VTSTR = TL::VTSTR, VRSTR = TL::VRSTR;
+    constexpr int STR = TL::STR;
     constexpr int NDB = D / 16;                          // 16-wide output blocks
     constexpr int NKS = BF ? D / 32 : D / 4;             // k-steps of S^T
 
-    __shared__ __align__(16) T Ks[KT * KSTR];
-    __shared__ __align__(16) T Vs[TL::VSIZE];
-    __shared__ float knorm[MODE == MODE_TOP1 ? KT : 1];
-    __shared__ int kslot[MODE == MODE_TOP1 ? KT : 1];
+    __shared__ __align__(16) T Ks[KT * STR];
+    __shared__ __align__(16) T Vs[HAS_V ? KT * STR : 1];
+    __shared__ __align__(16) int kslot[SEARCH ? KT : 4];
+    __shared__ __align__(16) float kinv[SEARCH ? KT : 4];
+    __shared__ int kidx[KCH];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -90,24 +102,14 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
         nk = p.ca_cnt[h * p.F + f];
         klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
     } else {
-        h = blockIdx.y;
-        const int item = blockIdx.x;
-        const int B = p.B;
-        const int32_t* wt = p.wt + static_cast<size_t>(h) * (B + 1);
-        if (item >= wt[B]) return;
-        int lo = 0, hi = B - 1;                 // last bucket with wt[b] <= item
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (wt[mid] <= item) lo = mid; else hi = mid - 1;
-        }
-        const int b = lo;
-        const int32_t* qo = p.qoff + static_cast<size_t>(h) * (B + 1);
-        const int qs = qo[b] + (item - wt[b]) * kQTile;
-        q_count = min(kQTile, qo[b + 1] - qs);
-        qlist = p.qperm + static_cast<size_t>(h) * p.qperm_stride + qs;
-        const int32_t* ko = p.koff + static_cast<size_t>(h) * (B + 1);
-        nk = ko[b + 1] - ko[b];
-        klist = p.kperm + static_cast<size_t>(h) * p.kperm_stride + ko[b];
+        h = blockIdx.x;                          // heads fastest: the longest items
+        const int item = blockIdx.y;            // of every head dispatch first
+        const int4 it = p.items[static_cast<size_t>(h) * p.max_items + item];
+        if (it.y <= 0) return;
+        q_count = it.y;
+        qlist = p.qperm + static_cast<size_t>(h) * p.qperm_stride + it.x;
+        nk = it.w;
+        klist = p.kperm + static_cast<size_t>(h) * p.kperm_stride + it.z;
         na = clamp_n(p.n_valid, h, p.cap);
     }
 
@@ -122,6 +124,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
     const T* va = HAS_V ? static_cast<const T*>(p.va) + static_cast<size_t>(h) * p.a_rows * D : nullptr;
     const T* kb = p.kb ? static_cast<const T*>(p.kb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
     const T* vb = (HAS_V && p.vb) ? static_cast<const T*>(p.vb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
+    const float* kn_h = SEARCH ? p.knorm + static_cast<size_t>(h) * p.a_rows : nullptr;
 
     // ---------------------------------------------------------------- Q fragments
     // B operand of S^T: lane holds Q[query l%16][k-slice of group g].
@@ -131,14 +134,13 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
     if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            uint4 r = make_uint4(0, 0, 0, 0);
-            if (qvalid) r = *reinterpret_cast<const uint4*>(qh + static_cast<size_t>(qrow) * D + ks * 32 + 8 * g);
+            u32x4 r = {0u, 0u, 0u, 0u};
+            if (qvalid) r = *reinterpret_cast<const u32x4*>(qh + static_cast<size_t>(qrow) * D + ks * 32 + 8 * g);
             qf_b[ks] = __builtin_bit_cast(bf16x8_t, r);
-            if constexpr (MODE == MODE_TOP1) {
-                const uint32_t wv[4] = {r.x, r.y, r.z, r.w};
+            if constexpr (SEARCH) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float lo = __uint_as_float(wv[i] << 16), hi = __uint_as_float(wv[i] & 0xFFFF0000u);
+                    const float lo = __uint_as_float(r[i] << 16), hi = __uint_as_float(r[i] & 0xFFFF0000u);
                     qsq = __builtin_fmaf(lo, lo, qsq);
                     qsq = __builtin_fmaf(hi, hi, qsq);
                 }
@@ -148,126 +150,79 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             qf_f[ks] = qvalid ? reinterpret_cast<const float*>(qh)[static_cast<size_t>(qrow) * D + ks * 4 + g] : 0.f;
-            if constexpr (MODE == MODE_TOP1) qsq = __builtin_fmaf(qf_f[ks], qf_f[ks], qsq);
+            if constexpr (SEARCH) qsq = __builtin_fmaf(qf_f[ks], qf_f[ks], qsq);
         }
     }
-    float qnorm = 0.f;
-    if constexpr (MODE == MODE_TOP1) {
+    float qinv = 0.f;
+    if constexpr (SEARCH) {
         qsq += __shfl_xor(qsq, 16);
         qsq += __shfl_xor(qsq, 32);
-        qnorm = __builtin_sqrtf(qsq);
+        const float qn = __builtin_sqrtf(qsq);
+        qinv = qn > 0.f ? 1.f / qn : 0.f;
     }
 
-    // ---------------------------------------------------------------- tile loads
-    int ix[UPT][4];
-    int ixk[MODE == MODE_TOP1 ? UPT : 1][4];   // indices of the tile held in kreg
-    uint4 kreg[UPT][4];
-    uint4 vreg[HAS_V ? UPT : 1][4];
-
-    auto load_idx = [&](int tile) {
-#pragma unroll
-        for (int k = 0; k < UPT; ++k) {
-            const int u = tid + k * 256;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = tile * KT + 4 * (u / CPR) + e;
-                ix[k][e] = (u < TL::UNITS && r < nk) ? klist[r] : -1;
-            }
+    // ---------------------------------------------------------------- key indices
+    // The item's key list is staged in LDS (KCH entries at a time, coalesced),
+    // so the gathers below never wait on a dependent index load.  Entries past
+    // the end repeat the last key, so every lane of a partial tile still
+    // gathers a valid row (its score is masked).
+    auto stage_idx = [&](int first) __attribute__((always_inline)) {
+        for (int i = tid; i < KCH; i += 256) {
+            const int r = first + i;
+            kidx[i] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
         }
     };
-    auto load_kv = [&]() {
+
+    // ---------------------------------------------------------------- tile loads
+    // A stage holds one 64-key tile in registers between its global gather and
+    // its LDS store; two stages alternate so that two tiles are in flight
+    // while a third is computed on.
+    struct Stage {
+        u32x4 k[UPT][4];
+        u32x4 v[HAS_V ? UPT : 1][4];
+        int slot[SEARCH ? UPT : 1][4];
+        float kn[SEARCH ? UPT : 1][4];
+    };
+    auto load_kv = [&](Stage& S, int tile) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < UPT; ++k) {
             const int u = tid + k * 256;
+            if constexpr (TL::UNITS % 256 != 0)             // (bf16, d=64: half the threads)
+                if (u >= TL::UNITS) continue;
             const int chunk = u % CPR;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = ix[k][e];
-                uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
-                if (j >= 0) {
-                    const bool from_a = (MODE == MODE_CA || MODE == MODE_TOP1) || j < na;
-                    const size_t row = from_a ? static_cast<size_t>(j) : static_cast<size_t>(j - na);
-                    const T* kr_p = (from_a ? ka : kb) + row * D + chunk * EPC;
-                    kr = *reinterpret_cast<const uint4*>(kr_p);
-                    if constexpr (HAS_V) {
-                        const T* vr_p = (from_a ? va : vb) + row * D + chunk * EPC;
-                        vr = *reinterpret_cast<const uint4*>(vr_p);
-                    }
+                const int r = tile * KT + 4 * (u / CPR) + e;
+                const int j = kidx[r % KCH];
+                const bool from_a = (MODE == MODE_CA || MODE == MODE_TOP1) || j < na;
+                const size_t row = from_a ? static_cast<size_t>(j) : static_cast<size_t>(j - na);
+                S.k[k][e] = *reinterpret_cast<const u32x4*>((from_a ? ka : kb) + row * D + chunk * EPC);
+                if constexpr (HAS_V)
+                    S.v[k][e] = *reinterpret_cast<const u32x4*>((from_a ? va : vb) + row * D + chunk * EPC);
+                if constexpr (SEARCH) {
+                    S.slot[k][e] = j;
+                    S.kn[k][e] = (chunk == 0 && from_a) ? kn_h[j] : 0.f;
                 }
-                kreg[k][e] = kr;
-                if constexpr (HAS_V) vreg[k][e] = vr;
-                if constexpr (MODE == MODE_TOP1) ixk[k][e] = j;
             }
         }
     };
-    auto store_lds = [&]() {
+    auto store_lds = [&](const Stage& S) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < UPT; ++k) {
             const int u = tid + k * 256;
-            if (u >= TL::UNITS) continue;
+            if constexpr (TL::UNITS % 256 != 0)
+                if (u >= TL::UNITS) continue;
             const int quad = u / CPR, chunk = u % CPR;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 4 * quad + e;
-                *reinterpret_cast<uint4*>(&Ks[row * KSTR + chunk * EPC]) = kreg[k][e];
-                if constexpr (HAS_V && !BF)
-                    *reinterpret_cast<uint4*>(&Vs[row * VRSTR + chunk * EPC]) = vreg[k][e];
-            }
-            if constexpr (HAS_V && BF) {
-                // 4 keys x 8 dims -> 8 transposed rows of 4 keys (8 bytes each)
-                const int pos = vt_pos(4 * quad);
-                const uint32_t a0[4] = {vreg[k][0].x, vreg[k][0].y, vreg[k][0].z, vreg[k][0].w};
-                const uint32_t a1[4] = {vreg[k][1].x, vreg[k][1].y, vreg[k][1].z, vreg[k][1].w};
-                const uint32_t a2[4] = {vreg[k][2].x, vreg[k][2].y, vreg[k][2].z, vreg[k][2].w};
-                const uint32_t a3[4] = {vreg[k][3].x, vreg[k][3].y, vreg[k][3].z, vreg[k][3].w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // dims 2i (low halves) and 2i+1 (high halves)
-                    const uint32_t lo01 = (a0[i] & 0xFFFFu) | (a1[i] << 16);
-                    const uint32_t lo23 = (a2[i] & 0xFFFFu) | (a3[i] << 16);
-                    const uint32_t hi01 = (a0[i] >> 16) | (a1[i] & 0xFFFF0000u);
-                    const uint32_t hi23 = (a2[i] >> 16) | (a3[i] & 0xFFFF0000u);
-                    const int d0 = chunk * 8 + 2 * i;
-                    *reinterpret_cast<uint2*>(&Vs[d0 * VTSTR + pos]) = make_uint2(lo01, lo23);
-                    *reinterpret_cast<uint2*>(&Vs[(d0 + 1) * VTSTR + pos]) = make_uint2(hi01, hi23);
-                }
-            }
-            if constexpr (MODE == MODE_TOP1) {
-                // squared norms of the 4 rows: this lane's chunk, then the lanes
-                // of the same quad (CPR consecutive lanes)
-                float sq[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint4 r = kreg[k][e];
-                    const uint32_t wv[4] = {r.x, r.y, r.z, r.w};
-                    float s = 0.f;
-                    if constexpr (BF) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float lo = __uint_as_float(wv[i] << 16), hi = __uint_as_float(wv[i] & 0xFFFF0000u);
-                            s = __builtin_fmaf(lo, lo, s);
-                            s = __builtin_fmaf(hi, hi, s);
-                        }
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float x = __uint_as_float(wv[i]);
-                            s = __builtin_fmaf(x, x, s);
-                        }
-                    }
-                    if constexpr (CPR >= 16) {
-                        s = group_sum<16>(s);
-                        if constexpr (CPR == 32) s += __shfl_xor(s, 16);
-                    } else {
-                        s = group_sum<8>(s);
-                    }
-                    sq[e] = s;
-                }
-                if (chunk == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        knorm[4 * quad + e] = __builtin_sqrtf(sq[e]);
-                        kslot[4 * quad + e] = ixk[k][e];
+                *reinterpret_cast<u32x4*>(&Ks[row * STR + chunk * EPC]) = S.k[k][e];
+                if constexpr (HAS_V)
+                    *reinterpret_cast<u32x4*>(&Vs[row * STR + chunk * EPC]) = S.v[k][e];
+                if constexpr (SEARCH) {
+                    if (chunk == 0) {
+                        kslot[row] = S.slot[k][e];
+                        kinv[row] = S.kn[k][e] > 0.f ? 1.f / S.kn[k][e] : 0.f;
                     }
                 }
             }
@@ -278,94 +233,98 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
     f32x4 o[HAS_V ? NDB : 1];
 #pragma unroll
     for (int i = 0; i < (HAS_V ? NDB : 1); ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = kNegInf, l_run = 0.f;             // softmax state (log2 domain)
+    float m_run = kNegInf, l_run = 0.f;             // softmax state: raw-score max, sum
     float best_c = kNegInf;
-    int best_s = 0x7FFFFFFF;                        // TOP1 state
+    int best_s = 0x7FFFFFFF;                        // search state
 
     const int nt = (nk + KT - 1) / KT;
-    if (nt > 0) {
-        load_idx(0);
-        load_kv();
-        if (nt > 1) load_idx(1);
-    }
-#pragma unroll 1
-    for (int t = 0; t < nt; ++t) {
-        __syncthreads();
-        store_lds();
-        __syncthreads();
-        if (t + 1 < nt) {
-            load_kv();
-            if (t + 2 < nt) load_idx(t + 2);
-        }
-        if (!wave_active) continue;
 
+    auto compute = [&](int t) __attribute__((always_inline)) {
         // ---- S^T = K Q^T for the 4 key blocks of the tile
         f32x4 s[4];
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
             s[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const T* krow = &Ks[(kb4 * 16 + c16) * KSTR];
+            const T* krow = &Ks[(kb4 * 16 + c16) * STR];
             if constexpr (BF) {
+                bf16x8_t a[NKS];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(krow + ks * 32 + 8 * g);
-                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf_b[ks], s[kb4], 0, 0, 0);
-                }
+                for (int ks = 0; ks < NKS; ++ks)
+                    a[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 32 + 8 * g);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qf_b[ks], s[kb4], 0, 0, 0);
             } else {
+                float a[NKS];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const float a = reinterpret_cast<const float*>(krow)[ks * 4 + g];
-                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf_f[ks], s[kb4], 0, 0, 0);
-                }
+                for (int ks = 0; ks < NKS; ++ks) a[ks] = reinterpret_cast<const float*>(krow)[ks * 4 + g];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], qf_f[ks], s[kb4], 0, 0, 0);
             }
         }
         const int kbase = t * KT;
+        const bool full = kbase + KT <= nk;                    // wave-uniform
 
-        if constexpr (MODE == MODE_TOP1) {
+        // ---- TempCache search over this tile's cached keys (sorted first, so a
+        // tile whose first key is current holds no cached key)
+        if constexpr (SEARCH) {
+            if (MODE == MODE_TOP1 || kslot[0] < na) {
 #pragma unroll
-            for (int kb4 = 0; kb4 < 4; ++kb4) {
+                for (int kb4 = 0; kb4 < 4; ++kb4) {
+                    const int4 sl = *reinterpret_cast<const int4*>(&kslot[kb4 * 16 + 4 * g]);
+                    const float4 iv = *reinterpret_cast<const float4*>(&kinv[kb4 * 16 + 4 * g]);
+                    const int slv[4] = {sl.x, sl.y, sl.z, sl.w};
+                    const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kk = kb4 * 16 + 4 * g + r;
-                    if (kbase + kk < nk) {
-                        const float den = qnorm * knorm[kk];
-                        const float c = den > 0.f ? s[kb4][r] / den : 0.f;
-                        if (c > best_c) { best_c = c; best_s = kslot[kk]; }
+                    for (int r = 0; r < 4; ++r) {
+                        const int kk = kb4 * 16 + 4 * g + r;
+                        const bool ok = (MODE == MODE_TOP1 || slv[r] < na) && (full || kbase + kk < nk);
+                        const float cs = s[kb4][r] * qinv * ivv[r];
+                        if (ok && cs > best_c) { best_c = cs; best_s = slv[r]; }
                     }
                 }
             }
-        } else {
-            // ---- online softmax (log2 domain), one query per lane
+        }
+
+        if constexpr (HAS_V) {
+            // ---- online softmax, one query per lane.  The running max is kept
+            // in raw score units; the scale folds into the exponent:
+            // p = 2^(s*c - m*c), c = scale * log2(e) > 0.
+            if (!full) {
+#pragma unroll
+                for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (kbase + kb4 * 16 + 4 * g + r >= nk) s[kb4][r] = kNegInf;
+            }
             float tmax = kNegInf;
 #pragma unroll
-            for (int kb4 = 0; kb4 < 4; ++kb4) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kk = kb4 * 16 + 4 * g + r;
-                    const float v = (kbase + kk < nk) ? s[kb4][r] * p.scale_log2 : kNegInf;
-                    s[kb4][r] = v;
-                    tmax = fmaxf(tmax, v);
-                }
-            }
+            for (int kb4 = 0; kb4 < 4; ++kb4)
+                tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb4][0], s[kb4][1]), fmaxf(s[kb4][2], s[kb4][3])));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
             const float m_new = fmaxf(m_run, tmax);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_use);
+            const float c = p.scale_log2;
+            const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
             float psum = 0.f;
 #pragma unroll
             for (int kb4 = 0; kb4 < 4; ++kb4) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(s[kb4][r] - m_use);
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb4][r], c, -mc));
                     s[kb4][r] = e;
                     psum += e;
                 }
             }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
+            if (__ballot(m_new > m_run) != 0) {                 // some lane's max grew
+                const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, c, -mc));
+                l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+                for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            }
+            l_run += psum;
+            m_run = m_new;
 
             // ---- O^T += V^T P^T
             if constexpr (BF) {
@@ -377,10 +336,18 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
                         pb[r] = static_cast<__bf16>(s[2 * kg][r]);
                         pb[4 + r] = static_cast<__bf16>(s[2 * kg + 1][r]);
                     }
+                    // lane j of group g addresses V[kg*32 + 4g + j/4][db*16 + 4(j%4)]
+                    const T* vb0 = &Vs[(kg * 32 + 4 * g + (c16 >> 2)) * STR + 4 * (c16 & 3)];
+                    v4i16 lo[NDB], hi[NDB];
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                            &Vs[(db * 16 + c16) * VTSTR + kg * 32 + 8 * g]);
+                        lo[db] = lds_read_tr(vb0 + db * 16);
+                        hi[db] = lds_read_tr(vb0 + 16 * STR + db * 16);
+                    }
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const bf16x8_t a = __builtin_bit_cast(
+                            bf16x8_t, __builtin_shufflevector(lo[db], hi[db], 0, 1, 2, 3, 4, 5, 6, 7));
                         o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[db], 0, 0, 0);
                     }
                 }
@@ -389,7 +356,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
                 for (int kb4 = 0; kb4 < 4; ++kb4) {
 #pragma unroll
                     for (int st = 0; st < 4; ++st) {
-                        const float* vrow = reinterpret_cast<const float*>(&Vs[(kb4 * 16 + 4 * g + st) * VRSTR]);
+                        const float* vrow = reinterpret_cast<const float*>(&Vs[(kb4 * 16 + 4 * g + st) * STR]);
 #pragma unroll
                         for (int db = 0; db < NDB; ++db)
                             o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[db * 16 + c16], s[kb4][st], o[db], 0, 0, 0);
@@ -397,10 +364,40 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
                 }
             }
         }
+    };
+
+    // One pipeline step on tile t held in stage S: store it, refill S with
+    // tile t+2, compute on tile t.  Tile t+1 stays in flight in the other stage.
+    auto step = [&](Stage& S, int t) __attribute__((always_inline)) {
+        if (t >= nt) return;                              // block-uniform
+        __syncthreads();
+        store_lds(S);
+        __syncthreads();
+        if (t + 2 < nt) {
+            if (((t + 2) * KT) % KCH == 0) {        // next index chunk
+                stage_idx((t + 2) * KT);
+                __syncthreads();
+            }
+            load_kv(S, t + 2);
+        }
+        if (wave_active) compute(t);
+    };
+
+    Stage A, B;
+    stage_idx(0);
+    __syncthreads();
+    if (nt > 0) load_kv(A, 0);
+    if (nt > 1) load_kv(B, 1);
+    // Each stage is named in exactly one place of a fixed pair of steps, so
+    // both keep fixed registers.  A step past the last tile does nothing.
+#pragma unroll 1
+    for (int t = 0; t < nt; t += 2) {
+        step(A, t);
+        step(B, t + 1);
     }
 
     // ---------------------------------------------------------------- epilogue
-    if constexpr (MODE == MODE_TOP1) {
+    if constexpr (SEARCH) {
 #pragma unroll
         for (int off = 16; off <= 32; off <<= 1) {
             const float oc = __shfl_xor(best_c, off);
@@ -412,10 +409,11 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
             const size_t qi = static_cast<size_t>(h) * p.Nq + qrow;
             p.best[qi] = found ? best_s : -1;
             p.bcos[qi] = found ? best_c : kNegInf;
-            if (found && best_c >= p.tau)
+            if (MODE == MODE_TOP1 && found && best_c >= p.tau)
                 atomicMax(&p.claim[static_cast<size_t>(h) * p.cap + best_s], qrow);
         }
-    } else {
+    }
+    if constexpr (HAS_V) {
         float l_tot = l_run + __shfl_xor(l_run, 16);
         l_tot += __shfl_xor(l_tot, 32);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -425,7 +423,7 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
             for (int db = 0; db < NDB; ++db) {
                 const f32x4 v = o[db] * inv;
                 if constexpr (sizeof(OT) == 4) {
-                    *reinterpret_cast<float4*>(orow + db * 16 + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+                    *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g) = v;
                 } else {
                     const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
                     const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
@@ -434,24 +432,50 @@ __global__ __launch_bounds__(256) void attn_kernel(const AttnParams p) {
             }
             if (MODE == MODE_SA && p.lse && g == 0)
                 p.lse[static_cast<size_t>(h) * p.Nq + qrow] =
-                    l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : kNegInf;
+                    l_tot > 0.f ? (m_run * p.scale_log2 + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : kNegInf;
         }
     }
 }
 
+// K+V modes keep two prefetched tiles of K and V in registers: up to 256
+// registers per lane, i.e. 2 waves per SIMD (two blocks per CU, each with two
+// 32 KB tiles in flight).
+template <typename T, int D, int MODE, bool SEARCH, typename OT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_kv_kernel(const AttnParams p) {
+    attn_body<T, D, MODE, SEARCH, OT>(p);
+}
+
+// The search alone stages K only and runs at the occupancy its registers allow.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_top1_kernel(const AttnParams p) {
+    attn_body<T, D, MODE_TOP1, true, float>(p);
+}
+
+namespace {
+
 template <typename T, int D, int MODE, typename OT>
-static void attn_go(int H, const AttnParams& p, hipStream_t s) {
+void attn_go(int H, const AttnParams& p, hipStream_t s) {
     dim3 grid;
     if constexpr (MODE == MODE_CA)
         grid = dim3((p.frame_len + kQTile - 1) / kQTile, p.F, H);
     else
-        grid = dim3(p.max_items, H);
+        grid = dim3(H, p.max_items);
     if (grid.x == 0 || grid.y == 0 || grid.z == 0) return;
-    hipLaunchKernelGGL((attn_kernel<T, D, MODE, OT>), grid, dim3(256), 0, s, p);
+    if constexpr (MODE == MODE_TOP1) {
+        hipLaunchKernelGGL((attn_top1_kernel<T, D>), grid, dim3(256), 0, s, p);
+    } else if constexpr (MODE == MODE_SA) {
+        if (p.best)
+            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, true, OT>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, false, OT>), grid, dim3(256), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_CA, false, OT>), grid, dim3(256), 0, s, p);
+    }
 }
 
 template <int MODE>
-static void attn_dispatch(bool bf16, int d, bool out_bf16, int H, const AttnParams& p, hipStream_t s) {
+void attn_dispatch(bool bf16, int d, bool out_bf16, int H, const AttnParams& p, hipStream_t s) {
     if (bf16) {
         if (d == 64) {
             out_bf16 ? attn_go<uint16_t, 64, MODE, uint16_t>(H, p, s) : attn_go<uint16_t, 64, MODE, float>(H, p, s);
@@ -466,6 +490,8 @@ static void attn_dispatch(bool bf16, int d, bool out_bf16, int H, const AttnPara
         }
     }
 }
+
+}  // namespace
 
 hipError_t launch_attn(int mode, bool bf16, int d, bool out_bf16, int H, const AttnParams& p,
                        hipStream_t s) {

@@ -8,7 +8,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/fastar.h"
+#include "fastar.h"
 #include "launch.hpp"
 
 namespace fastar {
@@ -71,7 +71,7 @@ struct Carver {
     }
 };
 
-SortBufs carve_sort(Carver& c, int H, long long nmax, int P, bool with_wt, bool with_off_perm) {
+SortBufs carve_sort(Carver& c, int H, long long nmax, int P, bool with_off_perm) {
     SortBufs s;
     const int B = 1 << P;
     s.max_tiles = sort_tiles(nmax);
@@ -81,17 +81,25 @@ SortBufs carve_sort(Carver& c, int H, long long nmax, int P, bool with_wt, bool 
         s.off = c.take<int32_t>(static_cast<long long>(H) * (B + 1));
         s.perm = c.take<int32_t>(static_cast<long long>(H) * nmax);
     }
-    if (with_wt) s.wt = c.take<int32_t>(static_cast<long long>(H) * (B + 1));
     return s;
+}
+
+ItemTable carve_items(Carver& c, int H, long long nq, int P) {
+    ItemTable t;
+    t.max_items = max_attn_items(nq, 1 << P);
+    t.items = c.take<int4>(static_cast<long long>(H) * t.max_items);
+    return t;
 }
 
 struct AnnsaWs {
     SortBufs q, k;
+    ItemTable it;
 };
 AnnsaWs carve_annsa(Carver& c, int H, int Nq, int cap, int Ncur, int P) {
     AnnsaWs w;
-    w.q = carve_sort(c, H, Nq, P, true, true);
-    w.k = carve_sort(c, H, static_cast<long long>(cap) + Ncur, P, false, true);
+    w.q = carve_sort(c, H, Nq, P, true);
+    w.k = carve_sort(c, H, static_cast<long long>(cap) + Ncur, P, true);
+    w.it = carve_items(c, H, Nq, P);
     return w;
 }
 
@@ -108,13 +116,15 @@ AnncaWs carve_annca(Carver& c, int H, int F, int L) {
 
 struct TcWs {
     SortBufs q, k;
+    ItemTable it;
     int32_t *claim, *best, *upos, *ev, *dest;
     float* cosv;
 };
 TcWs carve_tc(Carver& c, int H, int N, int cap, int P) {
     TcWs w;
-    w.q = carve_sort(c, H, N, P, true, true);
-    w.k = carve_sort(c, H, cap, P, false, true);
+    w.q = carve_sort(c, H, N, P, true);
+    w.k = carve_sort(c, H, cap, P, true);
+    w.it = carve_items(c, H, N, P);
     const long long HN = static_cast<long long>(H) * N;
     w.claim = c.take<int32_t>(static_cast<long long>(H) * cap);
     w.best = c.take<int32_t>(HN);
@@ -146,7 +156,7 @@ bool cache_ok(const fastar_cache* c, int H, int d, int dtype) {
     const long long rows = static_cast<long long>(H) * c->cap;
     if (!fits_i32(rows * d)) return false;
     return tensor_ok(c->k, rows * d) && tensor_ok(c->v, rows * d) && small_ok(c->ids, rows) &&
-           small_ok(c->ts, rows) && small_ok(c->n_valid, H);
+           small_ok(c->ts, rows) && small_ok(c->knorm, rows) && small_ok(c->n_valid, H);
 }
 
 }  // namespace
@@ -170,7 +180,8 @@ int32_t fastar_abi_version(void) { return FASTAR_ABI_VERSION; }
 
 // ------------------------------------------------------------------ hash
 fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
-                              const float* planes, int32_t P, uint16_t* ids, void* stream) {
+                              const float* planes, int32_t P, uint16_t* ids, float* norms,
+                              void* stream) {
     if (!dtype_ok(dtype)) return FASTAR_EDTYPE;
     if (H < 0 || N < 0) return FASTAR_EINVAL;
     if (!d_ok(d) || P < 0 || P > FASTAR_MAX_HASH_PLANES) return FASTAR_ESHAPE;
@@ -179,7 +190,7 @@ fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N
     if (!tensor_ok(x, HN * d) || !small_ok(ids, HN)) return FASTAR_EINVAL;
     if (!tensor_ok(planes, (HN > 0 ? static_cast<long long>(H) * P * d : 0))) return FASTAR_EINVAL;
     if (HN == 0) return FASTAR_OK;
-    return hip_status(launch_hash(x, dtype == FASTAR_BF16, H, N, d, planes, P, ids,
+    return hip_status(launch_hash(x, dtype == FASTAR_BF16, H, N, d, planes, P, ids, norms,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -187,7 +198,7 @@ fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N
 size_t fastar_bucket_sort_workspace(int32_t H, int32_t N, int32_t P) {
     if (H < 0 || N < 0 || !planes_ok(P)) return 0;
     Carver c(nullptr);
-    carve_sort(c, H, N, P, false, false);
+    carve_sort(c, H, N, P, false);
     return c.off;
 }
 
@@ -203,14 +214,15 @@ fastar_status fastar_bucket_sort(const uint16_t* ids, int32_t H, int32_t N, int3
     if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
     if (H == 0) return FASTAR_OK;
     Carver c(ws);
-    SortBufs b = carve_sort(c, H, N, P, false, false);
+    SortBufs b = carve_sort(c, H, N, P, false);
     b.off = off;
     b.perm = perm;
     IdSet s;
     s.a = ids;
     s.a_stride = N;
     s.a_fixed = N;
-    return hip_status(launch_bucket_sort(H, P, 1, &s, &b, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_bucket_sort(H, P, 1, &s, &b, nullptr, nullptr, 0,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------ AnnSA
@@ -225,10 +237,10 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
                                    int32_t d, int32_t dtype, const fastar_cache* cache,
                                    const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
                                    int32_t Ncur, int32_t P, float scale, void* out,
-                                   int32_t out_dtype, float* lse, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
+                                   void* ws, size_t ws_bytes, void* stream) {
     if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return FASTAR_EDTYPE;
-    if (H < 0 || Nq < 0 || Ncur < 0 || !std::isfinite(scale)) return FASTAR_EINVAL;
+    if (H < 0 || Nq < 0 || Ncur < 0 || !std::isfinite(scale) || !(scale > 0.f)) return FASTAR_EINVAL;
     if (!d_ok(d) || !planes_ok(P)) return FASTAR_ESHAPE;
     if (cache && (cache->H != H || cache->d != d)) return FASTAR_ESHAPE;
     if (cache && cache->dtype != dtype) return FASTAR_EDTYPE;
@@ -240,6 +252,8 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
     if (!tensor_ok(q, HQ * d) || !small_ok(q_ids, HQ) || !tensor_ok(out, HQ * d)) return FASTAR_EINVAL;
     if (!tensor_ok(k_cur, HC * d) || !tensor_ok(v_cur, HC * d) || !small_ok(kcur_ids, HC))
         return FASTAR_EINVAL;
+    if ((best == nullptr) != (best_cos == nullptr)) return FASTAR_EINVAL;
+    if (best && cache && H > 0 && cap > 0 && !cache->knorm) return FASTAR_EINVAL;
     const size_t need = fastar_annsa_workspace(H, Nq, cap, Ncur, P);
     if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
     if (HQ == 0) return FASTAR_OK;
@@ -261,7 +275,7 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
     sets[1].b_stride = Ncur;
     sets[1].nb = Ncur;
     SortBufs bufs[2] = {w.q, w.k};
-    hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, s);
+    hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, nullptr, 0, s);
     if (e != hipSuccess) return FASTAR_EHIP;
 
     AttnParams p;
@@ -275,17 +289,17 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
     p.b_rows = Ncur;
     p.n_valid = cache ? cache->n_valid : nullptr;
     p.cap = cap;
-    p.qoff = w.q.off;
     p.qperm = w.q.perm;
     p.qperm_stride = w.q.perm_stride;
-    p.koff = w.k.off;
     p.kperm = w.k.perm;
     p.kperm_stride = w.k.perm_stride;
-    p.wt = w.q.wt;
-    p.B = 1 << P;
-    p.max_items = (Nq + kQTile - 1) / kQTile + p.B;
+    p.items = w.it.items;
+    p.max_items = w.it.max_items;
     p.out = out;
     p.lse = lse;
+    p.best = best;
+    p.bcos = best_cos;
+    p.knorm = cache ? cache->knorm : nullptr;
     p.scale_log2 = scale * 1.4426950408889634f;
     return hip_status(launch_attn(MODE_SA, dtype == FASTAR_BF16, d, out_dtype == FASTAR_BF16, H, p, s));
 }
@@ -304,7 +318,7 @@ fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t
                                    float scale, void* out, int32_t out_dtype, uint8_t* keep,
                                    int32_t* keep_count, void* ws, size_t ws_bytes, void* stream) {
     if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return FASTAR_EDTYPE;
-    if (H < 0 || Nq < 0 || L < 0 || !std::isfinite(scale)) return FASTAR_EINVAL;
+    if (H < 0 || Nq < 0 || L < 0 || !std::isfinite(scale) || !(scale > 0.f)) return FASTAR_EINVAL;
     if (!d_ok(d) || !planes_ok(P) || frame_len <= 0 || Nq % frame_len != 0) return FASTAR_ESHAPE;
     const long long HQ = static_cast<long long>(H) * Nq, HL = static_cast<long long>(H) * L;
     const int F = Nq / frame_len;
@@ -359,7 +373,8 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     if (H < 0 || N < 0 || cap < 0 || std::isnan(tau)) return FASTAR_EINVAL;
     if (!d_ok(d) || !planes_ok(P)) return FASTAR_ESHAPE;
     if (!cache_ok(cache, H, d, dtype)) return FASTAR_EINVAL;
-    if (H > 0 && (!cache->ids || !cache->ts || !cache->n_valid || (cap > 0 && (!cache->k || !cache->v))))
+    if (H > 0 && (!cache->ids || !cache->ts || !cache->n_valid ||
+                  (cap > 0 && (!cache->k || !cache->v || !cache->knorm))))
         return FASTAR_EINVAL;
     if ((best_in == nullptr) != (cos_in == nullptr)) return FASTAR_EINVAL;
     if (N > cap) return FASTAR_ECAPACITY;
@@ -376,15 +391,17 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     const bool bf = dtype == FASTAR_BF16;
     Carver c(ws);
     TcWs w = carve_tc(c, H, N, cap, P);
-    hipError_t e = launch_fill_i32(w.claim, static_cast<long long>(H) * cap, -1, s);
-    if (e != hipSuccess) return FASTAR_EHIP;
+    hipError_t e = hipSuccess;
+    const long long claims = static_cast<long long>(H) * cap;
 
     const int32_t* bestp;
     const float* cosp;
     if (best_in) {
         bestp = best_in;
         cosp = cos_in;
-        e = launch_tc_claim(best_in, cos_in, cache->n_valid, cap, H, N, tau, w.claim, s);
+        e = launch_fill_i32(w.claim, claims, -1, s);
+        if (e == hipSuccess)
+            e = launch_tc_claim(best_in, cos_in, cache->n_valid, cap, H, N, tau, w.claim, s);
         if (e == hipSuccess && best && HN > 0)
             e = hipMemcpyAsync(best, best_in, HN * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess && best_cos && HN > 0)
@@ -404,7 +421,7 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
         sets[1].a_nvalid = cache->n_valid;
         sets[1].a_cap = cap;
         SortBufs bufs[2] = {w.q, w.k};
-        e = launch_bucket_sort(H, P, 2, sets, bufs, s);
+        e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, w.claim, claims, s);
         if (e != hipSuccess) return FASTAR_EHIP;
         AttnParams p;
         p.q = q;
@@ -413,15 +430,13 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
         p.a_rows = cap;
         p.n_valid = cache->n_valid;
         p.cap = cap;
-        p.qoff = w.q.off;
         p.qperm = w.q.perm;
         p.qperm_stride = w.q.perm_stride;
-        p.koff = w.k.off;
         p.kperm = w.k.perm;
         p.kperm_stride = w.k.perm_stride;
-        p.wt = w.q.wt;
-        p.B = 1 << P;
-        p.max_items = (N + kQTile - 1) / kQTile + p.B;
+        p.items = w.it.items;
+        p.max_items = w.it.max_items;
+        p.knorm = cache->knorm;
         p.best = bo;
         p.bcos = co;
         p.claim = w.claim;
@@ -448,7 +463,7 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     e = launch_tc_select(sp, s);
     if (e != hipSuccess) return FASTAR_EHIP;
     return hip_status(launch_tc_scatter(bf, d, H, N, cap, sp.dest, k_cur, v_cur, kcur_ids, step,
-                                        cache->k, cache->v, cache->ids, cache->ts, s));
+                                        cache->k, cache->v, cache->ids, cache->ts, cache->knorm, s));
 }
 
 // ------------------------------------------------------------------ timer

@@ -6,7 +6,9 @@
 // vector; lane ``seg`` always handles the same 8 coordinates, so its slice of
 // every hyperplane lives in registers for the whole kernel (no LDS traffic per
 // element).  Partial projections are summed across the group with DPP row
-// butterflies, which leave the same fp32 sum in every lane of the group.
+// butterflies, which leave the same fp32 sum in every lane of the group.  The
+// same pass can also return each vector's norm (a cache keeps its keys'
+// norms for the TempCache cosine search).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -15,7 +17,8 @@ namespace fastar {
 template <typename T, int D, int MAXP>
 __global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x,
                                                    const float* __restrict__ planes, int N, int P,
-                                                   uint16_t* __restrict__ ids) {
+                                                   uint16_t* __restrict__ ids,
+                                                   float* __restrict__ norms) {
     constexpr int LPV = D / 8;         // lanes per vector
     constexpr int VPB = 256 / LPV;     // vectors per block per step
     constexpr int UNROLL = 4;
@@ -67,13 +70,20 @@ __global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x,
                 }
             }
             if (seg == 0 && i < N) idh[i] = static_cast<uint16_t>(id);
+            if (norms) {                                   // |x|, the cache keeps it per slot
+                float sq = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(v[u][e], v[u][e], sq);
+                sq = group_sum<(LPV < 16 ? LPV : 16)>(sq);
+                if (seg == 0 && i < N) norms[static_cast<size_t>(h) * N + i] = __builtin_sqrtf(sq);
+            }
         }
     }
 }
 
 template <typename T, int D>
 static hipError_t hash_dispatch_p(const void* x, int H, int N, const float* planes, int P,
-                                  uint16_t* ids, hipStream_t s) {
+                                  uint16_t* ids, float* norms, hipStream_t s) {
     constexpr int VPB = 256 / (D / 8);
     int blocks = (N + VPB * 4 - 1) / (VPB * 4);
     if (blocks < 1) blocks = 1;
@@ -81,22 +91,22 @@ static hipError_t hash_dispatch_p(const void* x, int H, int N, const float* plan
     timer_begin("ann_hash", s);
     if (P <= 8)
         hipLaunchKernelGGL((hash_kernel<T, D, 8>), grid, dim3(256), 0, s,
-                           static_cast<const T*>(x), planes, N, P, ids);
+                           static_cast<const T*>(x), planes, N, P, ids, norms);
     else
         hipLaunchKernelGGL((hash_kernel<T, D, 16>), grid, dim3(256), 0, s,
-                           static_cast<const T*>(x), planes, N, P, ids);
+                           static_cast<const T*>(x), planes, N, P, ids, norms);
     timer_end(s);
     return hipGetLastError();
 }
 
 hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const float* planes, int P,
-                       uint16_t* ids, hipStream_t s) {
+                       uint16_t* ids, float* norms, hipStream_t s) {
     if (N == 0 || H == 0) return hipSuccess;
     if (bf16)
-        return d == 64 ? hash_dispatch_p<uint16_t, 64>(x, H, N, planes, P, ids, s)
-                       : hash_dispatch_p<uint16_t, 128>(x, H, N, planes, P, ids, s);
-    return d == 64 ? hash_dispatch_p<float, 64>(x, H, N, planes, P, ids, s)
-                   : hash_dispatch_p<float, 128>(x, H, N, planes, P, ids, s);
+        return d == 64 ? hash_dispatch_p<uint16_t, 64>(x, H, N, planes, P, ids, norms, s)
+                       : hash_dispatch_p<uint16_t, 128>(x, H, N, planes, P, ids, norms, s);
+    return d == 64 ? hash_dispatch_p<float, 64>(x, H, N, planes, P, ids, norms, s)
+                   : hash_dispatch_p<float, 128>(x, H, N, planes, P, ids, norms, s);
 }
 
 }  // namespace fastar

@@ -13,7 +13,7 @@ void timer_end(hipStream_t s);
 
 // ------------------------------------------------------------------ hash
 hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const float* planes, int P,
-                       uint16_t* ids, hipStream_t s);
+                       uint16_t* ids, float* norms, hipStream_t s);
 
 // ------------------------------------------------------------------ sort
 // A set of ids per head: the first part (source a) holds either ``a_fixed``
@@ -35,16 +35,33 @@ struct SortBufs {
     int32_t* hist = nullptr;    // [H][max_tiles][B] scratch (tile counts, then tile bases)
     int32_t* off = nullptr;     // [H][B+1]
     int32_t* perm = nullptr;    // [H][perm_stride]
-    int32_t* wt = nullptr;      // [H][B+1] prefix of ceil(count/64) per bucket, or null
     int max_tiles = 0;
     int perm_stride = 0;
 };
 
 constexpr int kSortTile = 1024;
+constexpr int kQTile = 64;   // queries per attention block
 __host__ __device__ inline int sort_tiles(long long n) { return static_cast<int>((n + kSortTile - 1) / kSortTile); }
 
-// Sorts one or two sets (nsets = 1 or 2) per head, in three launches.
+// Attention work items built from a (query set, key set) pair of groupings:
+// one item per (bucket, 64-query slice) with at least one query, in bucket
+// order: x = first query position in the query permutation, y = number of
+// queries (0 marks padding), z = first key position, w = number of keys.
+struct ItemTable {
+    int4* items = nullptr;      // [H][max_items]
+    int max_items = 0;
+};
+// Upper bound on the number of items of one head (a multiple of 8).
+inline int max_attn_items(long long nq, int B) {
+    long long m = (nq + kQTile - 1) / kQTile + B;
+    return static_cast<int>((m + 7) / 8 * 8);
+}
+
+// Sorts one or two sets (nsets = 1 or 2) per head, in three launches.  With
+// ``items`` set (two sets: queries, keys) the scan also writes the attention
+// work list.  ``clear`` (optional) is filled with -1 by the first launch.
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
+                              const ItemTable* items, int32_t* clear, long long clear_n,
                               hipStream_t s);
 
 // ------------------------------------------------------------------ attention
@@ -62,16 +79,14 @@ struct AttnParams {
     int b_rows = 0;
     const int32_t* n_valid = nullptr;
     int cap = 0;
-    // bucket tables (SA, TOP1)
-    const int32_t* qoff = nullptr;
+    const float* knorm = nullptr;   // [H][a_rows] key norms of source a (search)
+    // bucket groupings and work items (SA, TOP1)
     const int32_t* qperm = nullptr;
     int qperm_stride = 0;
-    const int32_t* koff = nullptr;
     const int32_t* kperm = nullptr;
     int kperm_stride = 0;
-    const int32_t* wt = nullptr;
-    int B = 1;
-    int max_items = 0;              // grid.x for SA/TOP1
+    const int4* items = nullptr;
+    int max_items = 0;              // grid.x for SA/TOP1 (a multiple of 8)
     // prompt selection (CA)
     const int32_t* ca_idx = nullptr;
     const int32_t* ca_cnt = nullptr;
@@ -87,8 +102,6 @@ struct AttnParams {
     float tau = 0.f;
     float scale_log2 = 0.f;
 };
-
-constexpr int kQTile = 64;   // queries per attention block
 
 hipError_t launch_attn(int mode, bool bf16, int d, bool out_bf16, int H, const AttnParams& p,
                        hipStream_t s);
@@ -123,6 +136,6 @@ hipError_t launch_tc_select(const TcSelectParams& p, hipStream_t s);
 hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int32_t* dest,
                              const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
                              int32_t step, void* ck, void* cv, uint16_t* cids, int32_t* cts,
-                             hipStream_t s);
+                             float* cnorm, hipStream_t s);
 
 }  // namespace fastar

@@ -3,9 +3,11 @@
 // part C).  Three launches, every count stays on the device:
 //
 //   sort_hist    one block per 1024-id tile: LDS histogram -> hist[h][tile][b]
-//   sort_scan    one block per head and set: per-bucket exclusive prefix over
-//                tiles (in place) plus a block scan over buckets -> off[h][b];
-//                optionally the prefix of ceil(count/64), the attention work list
+//                (the blocks also clear an optional caller array to -1)
+//   sort_scan    one block per head: per-bucket exclusive prefix over tiles (in
+//                place) plus a block scan over buckets -> off[h][b], for each
+//                set; optionally the attention work list (one item per bucket
+//                and 64-query slice, longest key lists first)
 //   sort_scatter one block per tile: stable rank of every id inside its tile
 //                (wave ballots on the P id bits give the rank among equal ids of
 //                the wave; LDS counters tagged by round carry it across waves
@@ -20,8 +22,12 @@ namespace fastar {
 struct SortArgs {
     IdSet set[2];
     SortBufs buf[2];
+    int nsets;
     int B;
     int P;
+    ItemTable items;
+    int32_t* clear;
+    long long clear_n;
 };
 
 __device__ __forceinline__ int set_count(const IdSet& s, int h, int& na) {
@@ -36,6 +42,11 @@ __device__ __forceinline__ int set_id(const IdSet& s, int h, int na, int e) {
 
 __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
     __shared__ int cnt[1024];
+    if (a.clear) {      // a scratch array the caller needs at -1 (TempCache claims)
+        const long long nb = static_cast<long long>(gridDim.x) * gridDim.y * gridDim.z;
+        const long long bid = blockIdx.x + static_cast<long long>(gridDim.x) * (blockIdx.y + static_cast<long long>(gridDim.y) * blockIdx.z);
+        for (long long i = bid * 256 + threadIdx.x; i < a.clear_n; i += nb * 256) a.clear[i] = -1;
+    }
     const IdSet& S = a.set[blockIdx.z];
     const SortBufs& O = a.buf[blockIdx.z];
     const int h = blockIdx.y, t = blockIdx.x, B = a.B;
@@ -54,36 +65,78 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
     for (int b = threadIdx.x; b < B; b += 256) dst[b] = cnt[b];
 }
 
+// One block per head.  Thread (part, b) owns bucket b over a contiguous range
+// of tiles (1024 / B parts), so every tile count is read by one thread and the
+// loads of a part are independent.
 __global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
+    __shared__ int part_sum[1024];
     __shared__ int smem[16];
-    const IdSet& S = a.set[blockIdx.y];
-    const SortBufs& O = a.buf[blockIdx.y];
-    const int h = blockIdx.x, B = a.B, b = threadIdx.x;
-    int na;
-    const int n = set_count(S, h, na);
-    const int ntiles = sort_tiles(n);
-    int* hist = O.hist + static_cast<size_t>(h) * O.max_tiles * B;
-    int run = 0;
-    if (b < B) {
-        for (int t = 0; t < ntiles; ++t) {
-            const int c = hist[static_cast<size_t>(t) * B + b];
-            hist[static_cast<size_t>(t) * B + b] = run;
+    __shared__ int offs[2][1025];
+    const int h = blockIdx.x, B = a.B, tid = threadIdx.x;
+    const int parts = 1024 / B;
+    const int b = tid % B, part = tid / B;
+    for (int si = 0; si < a.nsets; ++si) {
+        const IdSet& S = a.set[si];
+        const SortBufs& O = a.buf[si];
+        int na;
+        const int n = set_count(S, h, na);
+        const int ntiles = sort_tiles(n);
+        const int tpp = (ntiles + parts - 1) / parts;
+        const int t0 = min(ntiles, part * tpp), t1 = min(ntiles, t0 + tpp);
+        int* hist = O.hist + static_cast<size_t>(h) * O.max_tiles * B + b;
+        int sum = 0;
+#pragma unroll 4
+        for (int t = t0; t < t1; ++t) sum += hist[static_cast<size_t>(t) * B];
+        part_sum[part * B + b] = sum;
+        __syncthreads();
+        int pre = 0, tot = 0;
+        for (int q = 0; q < parts; ++q) {
+            const int v = part_sum[q * B + b];
+            pre += (q < part) ? v : 0;
+            tot += v;
+        }
+        int total;
+        const int excl = block_exclusive_scan<1024>(part == 0 ? tot : 0, smem, total);
+        if (part == 0) offs[si][b] = excl;
+        if (tid == 0) offs[si][B] = total;
+        __syncthreads();
+        int run = offs[si][b] + pre;
+        for (int t = t0; t < t1; ++t) {
+            const int c = hist[static_cast<size_t>(t) * B];
+            hist[static_cast<size_t>(t) * B] = run;
             run += c;
         }
+        if (part == 0) O.off[static_cast<size_t>(h) * (B + 1) + b] = offs[si][b];
+        if (tid == 0) O.off[static_cast<size_t>(h) * (B + 1) + B] = total;
     }
-    int total;
-    const int excl = block_exclusive_scan<1024>(b < B ? run : 0, smem, total);
-    if (b < B) {
-        for (int t = 0; t < ntiles; ++t) hist[static_cast<size_t>(t) * B + b] += excl;
-        O.off[static_cast<size_t>(h) * (B + 1) + b] = excl;
-    }
-    if (b == 0) O.off[static_cast<size_t>(h) * (B + 1) + B] = total;
-    if (O.wt) {
-        const int tiles = (b < B) ? (run + kQTile - 1) / kQTile : 0;
-        int wtotal;
-        const int wex = block_exclusive_scan<1024>(tiles, smem, wtotal);
-        if (b < B) O.wt[static_cast<size_t>(h) * (B + 1) + b] = wex;
-        if (b == 0) O.wt[static_cast<size_t>(h) * (B + 1) + B] = wtotal;
+    if (a.items.items && a.nsets == 2) {
+        // Items in decreasing order of key count (ties: lower bucket first), so
+        // the longest items start first.  rank[b] = position of bucket b.
+        __shared__ int slot_tiles[1024];
+        const int qc = (part == 0) ? offs[0][b + 1] - offs[0][b] : 0;
+        const int kn = (part == 0) ? offs[1][b + 1] - offs[1][b] : 0;
+        const int tiles = (qc + kQTile - 1) / kQTile;
+        int rank = 0;
+        if (part == 0) {
+            for (int c = 0; c < B; ++c) {
+                const int kc = offs[1][c + 1] - offs[1][c];
+                rank += (kc > kn) || (kc == kn && c < b);
+            }
+            slot_tiles[rank] = tiles;
+        }
+        __syncthreads();
+        int ntot;
+        const int first_by_rank = block_exclusive_scan<1024>(part == 0 ? slot_tiles[b] : 0, smem, ntot);
+        if (part == 0) slot_tiles[b] = first_by_rank;          // start of rank b
+        __syncthreads();
+        int4* it = a.items.items + static_cast<size_t>(h) * a.items.max_items;
+        if (part == 0) {
+            const int first = slot_tiles[rank];
+            const int ks = offs[1][b];
+            for (int c = 0; c < tiles; ++c)
+                it[first + c] = make_int4(offs[0][b] + c * kQTile, min(kQTile, qc - c * kQTile), ks, kn);
+        }
+        for (int i = ntot + tid; i < a.items.max_items; i += 1024) it[i] = make_int4(0, 0, 0, 0);
     }
 }
 
@@ -144,10 +197,15 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
 }
 
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
+                              const ItemTable* items, int32_t* clear, long long clear_n,
                               hipStream_t s) {
     SortArgs a;
+    a.nsets = nsets;
     a.B = 1 << P;
     a.P = P;
+    a.items = items ? *items : ItemTable();
+    a.clear = clear_n > 0 ? clear : nullptr;
+    a.clear_n = clear_n;
     int max_tiles = 0;
     for (int i = 0; i < nsets; ++i) {
         a.set[i] = sets[i];
@@ -159,13 +217,12 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
         a.buf[1] = a.buf[0];
     }
     if (H == 0) return hipSuccess;
-    if (max_tiles > 0) {
-        timer_begin("sort_hist", s);
-        hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
-        timer_end(s);
-    }
+    // the histogram launch also clears ``clear``: keep at least one block
+    timer_begin("sort_hist", s);
+    hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles > 0 ? max_tiles : 1, H, nsets), dim3(256), 0, s, a);
+    timer_end(s);
     timer_begin("sort_scan", s);
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(H, nsets), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(sort_scan_kernel, dim3(H), dim3(1024), 0, s, a);
     timer_end(s);
     if (max_tiles > 0) {
         timer_begin("sort_scatter", s);

@@ -2,15 +2,18 @@
 // Components" A): after the top-1 search has written best/cos and claimed the
 // matched slots (atomicMax of the token index, so the most recent token wins
 // regardless of scheduling), one block per head
-//   1. ranks the unmatched tokens in token order (block scan),
-//   2. counts the refreshed slots,
-//   3. if the cache overflows, selects the e non-refreshed slots with the
+//   1. resolves the matched tokens (winner -> its slot, others dropped), counts
+//      the winners (= refreshed slots) and ranks the unmatched tokens in token
+//      order with one block scan,
+//   2. if the cache overflows, selects the e non-refreshed slots with the
 //      smallest (timestamp, slot) by a radix select on the timestamps
 //      (8-bit digits of ts - min(ts); one pass when timestamps span < 256)
-//      and lists them in slot order (two block scans),
-//   4. writes every token's destination slot, the eviction list, the counts
+//      and lists them in slot order (two block scans); slot data are loaded
+//      once per 32768-slot chunk, 32 consecutive slots per thread,
+//   3. writes the unmatched tokens' destinations, the eviction list, the counts
 //      and the new valid-slot count;
-// then a gather-free copy kernel moves the winning tokens' rows into place.
+// then a copy kernel moves the written tokens' rows into place (32 lanes per
+// token, 16 bytes each) and records each written key's norm.
 // Every decision is integer or a single fp32 compare, so results are
 // deterministic.
 #include "common.hpp"
@@ -56,8 +59,10 @@ hipError_t launch_tc_claim(const int32_t* best, const float* cosv, const int32_t
 
 namespace {
 constexpr int SEL_NT = 1024;
-constexpr int SEL_ITEMS = 32;
-constexpr int SEL_CHUNK = SEL_NT * SEL_ITEMS;
+constexpr int TOK_ITEMS = 8;                      // tokens per thread per chunk
+constexpr int TOK_CHUNK = SEL_NT * TOK_ITEMS;     // < 65536: packed counters fit 16 bits
+constexpr int SLOT_ITEMS = 32;                    // slots per thread per chunk
+constexpr int SLOT_CHUNK = SEL_NT * SLOT_ITEMS;
 
 __device__ __forceinline__ uint32_t ts_key(int32_t t) { return static_cast<uint32_t>(t) ^ 0x80000000u; }
 
@@ -75,6 +80,42 @@ __device__ __forceinline__ uint32_t block_min_max(uint32_t v, bool want_max, uin
     __syncthreads();
     return r;
 }
+
+// This thread's SLOT_ITEMS consecutive slots of a chunk: timestamp keys and a
+// bit mask of the eviction candidates (valid, not refreshed).  All loads are
+// issued before any is used.
+struct SlotChunk {
+    uint32_t key[SLOT_ITEMS];
+    uint32_t cand;
+    int base;
+    __device__ __forceinline__ void load(const int32_t* claim, const int32_t* ts, int n, int c0) {
+        base = c0 + static_cast<int>(threadIdx.x) * SLOT_ITEMS;
+        int cl[SLOT_ITEMS];
+        const bool vec = base + SLOT_ITEMS <= n &&
+                         ((reinterpret_cast<uintptr_t>(claim + base) | reinterpret_cast<uintptr_t>(ts + base)) & 15) == 0;
+        if (vec) {
+#pragma unroll
+            for (int k = 0; k < SLOT_ITEMS; k += 4) {
+                const int4 c = *reinterpret_cast<const int4*>(claim + base + k);
+                const int4 t = *reinterpret_cast<const int4*>(ts + base + k);
+                cl[k] = c.x; cl[k + 1] = c.y; cl[k + 2] = c.z; cl[k + 3] = c.w;
+                key[k] = ts_key(t.x); key[k + 1] = ts_key(t.y);
+                key[k + 2] = ts_key(t.z); key[k + 3] = ts_key(t.w);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < SLOT_ITEMS; ++k) {
+                const int j = base + k;
+                cl[k] = (j < n) ? claim[j] : 0;
+                key[k] = (j < n) ? ts_key(ts[j]) : 0u;
+            }
+        }
+        cand = 0;
+#pragma unroll
+        for (int k = 0; k < SLOT_ITEMS; ++k)
+            if (base + k < n && cl[k] < 0) cand |= 1u << k;
+    }
+};
 }  // namespace
 
 __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams p) {
@@ -93,48 +134,70 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     int32_t* ev = p.ev + static_cast<size_t>(h) * N;
     int32_t* dest = p.dest + static_cast<size_t>(h) * N;
 
-    // 1. rank the unmatched tokens in token order
-    int u = 0;
-    for (int c0 = 0; c0 < N; c0 += SEL_CHUNK) {
-        const int base = c0 + tid * SEL_ITEMS;
-        uint32_t flags = 0;
-        int local = 0;
-#pragma unroll 8
-        for (int k = 0; k < SEL_ITEMS; ++k) {
+    // 1. tokens: matched ones get their slot (winner) or -1 (dropped); the
+    //    unmatched are ranked in token order.  One scan carries both counts:
+    //    unmatched in the low 16 bits, winners (= refreshed slots) above.
+    int u = 0, refreshed = 0;
+    for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
+        const int base = c0 + tid * TOK_ITEMS;
+        int bi[TOK_ITEMS];
+        float ci[TOK_ITEMS];
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k) {
             const int i = base + k;
-            if (i < N) {
-                const int b = best[i];
-                const bool m = b >= 0 && b < n && cosv[i] >= p.tau;
-                if (!m) { flags |= 1u << k; ++local; }
+            bi[k] = (i < N) ? best[i] : -1;
+            ci[k] = (i < N) ? cosv[i] : 0.f;
+        }
+        uint32_t um = 0;
+        int local = 0, wins = 0;
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k) {
+            const int i = base + k;
+            if (i >= N) continue;
+            const bool m = bi[k] >= 0 && bi[k] < n && ci[k] >= p.tau;
+            if (!m) {
+                um |= 1u << k;
+                ++local;
+            } else {
+                const bool win = claim[bi[k]] == i;
+                wins += win;
+                dest[i] = win ? bi[k] : -1;
             }
         }
         int total;
-        int pos = u + block_exclusive_scan<SEL_NT>(local, smem, total);
-        for (int k = 0; k < SEL_ITEMS; ++k) {
+        const int excl = block_exclusive_scan<SEL_NT>(local | (wins << 16), smem, total);
+        int pos = u + (excl & 0xFFFF);
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k) {
             const int i = base + k;
-            if (i < N) upos[i] = ((flags >> k) & 1) ? pos++ : -1;
+            if (i < N) upos[i] = ((um >> k) & 1) ? pos++ : -1;
         }
-        u += total;
+        u += total & 0xFFFF;
+        refreshed += total >> 16;
     }
-
-    // 2. refreshed slots
-    int rloc = 0;
-    for (int j = tid; j < n; j += SEL_NT) rloc += claim[j] >= 0;
-    int refreshed;
-    (void)block_exclusive_scan<SEL_NT>(rloc, smem, refreshed);
 
     const int e = max(0, n + u - cap);
     const int appended = u - e;
 
-    // 3. the e oldest non-refreshed slots (ties: lower slot), ascending
+    // 2. the e oldest non-refreshed slots (ties: lower slot), ascending
     if (e > 0) {
-        uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
-        for (int j = tid; j < n; j += SEL_NT) {
-            if (claim[j] < 0) {
-                const uint32_t k = ts_key(ts[j]);
-                lmin = k < lmin ? k : lmin;
-                lmax = k > lmax ? k : lmax;
+        SlotChunk sc;
+        int cached = -1;
+        auto chunk = [&](int c0) {
+            if (cached != c0) {
+                sc.load(claim, ts, n, c0);
+                cached = c0;
             }
+        };
+        uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
+        for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
+            chunk(c0);
+#pragma unroll
+            for (int k = 0; k < SLOT_ITEMS; ++k)
+                if ((sc.cand >> k) & 1) {
+                    lmin = sc.key[k] < lmin ? sc.key[k] : lmin;
+                    lmax = sc.key[k] > lmax ? sc.key[k] : lmax;
+                }
         }
         const uint32_t kmin = block_min_max(lmin, false, red);
         const uint32_t kmax = block_min_max(lmax, true, red);
@@ -146,12 +209,28 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
             for (int shift = ((nbits - 1) / 8) * 8; shift >= 0; shift -= 8) {
                 if (tid < 256) hist[tid] = 0;
                 __syncthreads();
-                for (int j = tid; j < n; j += SEL_NT) {
-                    if (claim[j] < 0) {
-                        const uint32_t rel = ts_key(ts[j]) - kmin;
-                        const uint32_t hi = (shift + 8 >= 32) ? 0u : (rel >> (shift + 8));
-                        if (hi == prefix) atomicAdd(&hist[(rel >> shift) & 255u], 1);
+                for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
+                    chunk(c0);
+                    // neighbouring slots usually share a timestamp: add runs of
+                    // equal digits with one atomic each
+                    int rd = -1, rc = 0;
+#pragma unroll
+                    for (int k = 0; k < SLOT_ITEMS; ++k) {
+                        if ((sc.cand >> k) & 1) {
+                            const uint32_t rel = sc.key[k] - kmin;
+                            const uint32_t hi = (shift + 8 >= 32) ? 0u : (rel >> (shift + 8));
+                            if (hi == prefix) {
+                                const int dg = static_cast<int>((rel >> shift) & 255u);
+                                if (dg != rd) {
+                                    if (rc) atomicAdd(&hist[rd], rc);
+                                    rd = dg;
+                                    rc = 0;
+                                }
+                                ++rc;
+                            }
+                        }
                     }
+                    if (rc) atomicAdd(&hist[rd], rc);
                 }
                 __syncthreads();
                 if (tid == 0) {
@@ -171,24 +250,23 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         }
         const uint32_t tstar = kmin + prefix;
         int carry_eq = 0, carry_sel = 0;
-        for (int c0 = 0; c0 < n; c0 += SEL_CHUNK) {
-            const int base = c0 + tid * SEL_ITEMS;
+        for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
+            chunk(c0);
             uint32_t ltf = 0, eqf = 0;
             int eqc = 0;
-#pragma unroll 8
-            for (int k = 0; k < SEL_ITEMS; ++k) {
-                const int j = base + k;
-                if (j < n && claim[j] < 0) {
-                    const uint32_t key = ts_key(ts[j]);
-                    if (key < tstar) ltf |= 1u << k;
-                    else if (key == tstar) { eqf |= 1u << k; ++eqc; }
+#pragma unroll
+            for (int k = 0; k < SLOT_ITEMS; ++k) {
+                if ((sc.cand >> k) & 1) {
+                    if (sc.key[k] < tstar) ltf |= 1u << k;
+                    else if (sc.key[k] == tstar) { eqf |= 1u << k; ++eqc; }
                 }
             }
             int eqtot;
             int er = carry_eq + block_exclusive_scan<SEL_NT>(eqc, smem, eqtot);
             uint32_t self = 0;
             int selc = 0;
-            for (int k = 0; k < SEL_ITEMS; ++k) {
+#pragma unroll
+            for (int k = 0; k < SLOT_ITEMS; ++k) {
                 if ((ltf >> k) & 1) { self |= 1u << k; ++selc; }
                 else if ((eqf >> k) & 1) {
                     if (er < need) { self |= 1u << k; ++selc; }
@@ -197,9 +275,10 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
             }
             int seltot;
             int pos = carry_sel + block_exclusive_scan<SEL_NT>(selc, smem, seltot);
-            for (int k = 0; k < SEL_ITEMS; ++k)
+#pragma unroll
+            for (int k = 0; k < SLOT_ITEMS; ++k)
                 if ((self >> k) & 1) {
-                    if (pos < e) ev[pos] = base + k;     // e <= N: never past the row
+                    if (pos < e) ev[pos] = sc.base + k;     // e <= N: never past the row
                     ++pos;
                 }
             carry_eq += eqtot;
@@ -208,16 +287,11 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     }
     __syncthreads();
 
-    // 4. destinations, eviction list, counts
+    // 3. unmatched tokens: appended slots first, then the evicted ones
     for (int i = tid; i < N; i += SEL_NT) {
         const int k = upos[i];
-        int dst;
-        if (k < 0) {
-            const int b = best[i];
-            dst = (claim[b] == i) ? b : -1;
-        } else {
-            dst = (k < appended) ? n + k : ev[k - appended];
-        }
+        if (k < 0) continue;
+        const int dst = (k < appended) ? n + k : ev[k - appended];
         dest[i] = (dst >= 0 && dst < cap) ? dst : -1;
     }
     if (p.evicted)
@@ -248,40 +322,57 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void tc_scatter_kernel(
     const int32_t* __restrict__ dest, const T* __restrict__ kc, const T* __restrict__ vc,
     const uint16_t* __restrict__ kids, int32_t step, T* __restrict__ ck, T* __restrict__ cv,
-    uint16_t* __restrict__ cids, int32_t* __restrict__ cts, int N, int cap) {
+    uint16_t* __restrict__ cids, int32_t* __restrict__ cts, float* __restrict__ cnorm, int N,
+    int cap) {
     constexpr int CPR = D * static_cast<int>(sizeof(T)) / 16;
     const int h = blockIdx.y;
-    const int i = blockIdx.x * 4 + threadIdx.x / 64;
-    const int l = threadIdx.x % 64;
+    const int i = blockIdx.x * 8 + threadIdx.x / 32;
+    const int l = threadIdx.x % 32;
     if (i >= N) return;
     const size_t ti = static_cast<size_t>(h) * N + i;
     const int d = dest[ti];
-    if (d < 0 || d >= cap) return;
+    if (d < 0 || d >= cap) return;                      // 32-lane group uniform
     const size_t si = static_cast<size_t>(h) * cap + d;
-    for (int c = l; c < 2 * CPR; c += 64) {
+    float sq = 0.f;                                     // |k| for the slot
+    for (int c = l; c < 2 * CPR; c += 32) {
         const bool isv = c >= CPR;
         const int cc = isv ? c - CPR : c;
-        const uint4* src = reinterpret_cast<const uint4*>((isv ? vc : kc) + ti * D) + cc;
-        uint4* dst = reinterpret_cast<uint4*>((isv ? cv : ck) + si * D) + cc;
-        *dst = *src;
+        const u32x4 x = *(reinterpret_cast<const u32x4*>((isv ? vc : kc) + ti * D) + cc);
+        *(reinterpret_cast<u32x4*>((isv ? cv : ck) + si * D) + cc) = x;
+        if (!isv) {
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xFFFF0000u);
+                    sq = __builtin_fmaf(lo, lo, sq);
+                    sq = __builtin_fmaf(hi, hi, sq);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sq = __builtin_fmaf(__uint_as_float(x[i]), __uint_as_float(x[i]), sq);
+            }
+        }
     }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) sq += __shfl_xor(sq, off, 32);
     if (l == 0) {
         cids[si] = kids[ti];
         cts[si] = step;
+        cnorm[si] = __builtin_sqrtf(sq);
     }
 }
 
 hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int32_t* dest,
                              const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
                              int32_t step, void* ck, void* cv, uint16_t* cids, int32_t* cts,
-                             hipStream_t s) {
+                             float* cnorm, hipStream_t s) {
     if (H == 0 || N == 0) return hipSuccess;
-    dim3 grid((N + 3) / 4, H);
+    dim3 grid((N + 7) / 8, H);
     timer_begin("tempcache_scatter", s);
 #define FASTAR_SCATTER(T, DD)                                                                     \
     hipLaunchKernelGGL((tc_scatter_kernel<T, DD>), grid, dim3(256), 0, s, dest,                  \
                        static_cast<const T*>(k_cur), static_cast<const T*>(v_cur), kcur_ids, step, \
-                       static_cast<T*>(ck), static_cast<T*>(cv), cids, cts, N, cap)
+                       static_cast<T*>(ck), static_cast<T*>(cv), cids, cts, cnorm, N, cap)
     if (bf16) {
         if (d == 64) FASTAR_SCATTER(uint16_t, 64); else FASTAR_SCATTER(uint16_t, 128);
     } else {

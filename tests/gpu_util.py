@@ -111,10 +111,15 @@ def prepared(name: str, seed: int = 0, **overrides):
 
 
 def device_cache(prep, n=None):
-    """KVCache on the device holding the step's initial cache (ids from the oracle)."""
-    from sparse_attention_autoregressive_amd import KVCache
+    """KVCache on the device holding the step's initial cache: bucket ids from the
+    oracle (the same inputs both sides get), key norms from the library's hash."""
+    import sparse_attention_autoregressive_amd as fa
     st, cfg = prep["step"], prep["cfg"]
     n_valid = st.n_valid if n is None else np.full(cfg.H, n, np.int32)
-    return KVCache(k=dev(st.cache_k, cfg.dtype), v=dev(st.cache_v, cfg.dtype),
-                   ids=dev_ids(prep["cache_ids"]), ts=torch.from_numpy(st.cache_ts).cuda(),
-                   n_valid=torch.from_numpy(np.ascontiguousarray(n_valid, np.int32)).cuda())
+    k = dev(st.cache_k, cfg.dtype)
+    knorm = torch.empty(cfg.H, cfg.cap, dtype=torch.float32, device="cuda")
+    fa.ann_hash(k, torch.from_numpy(st.planes).cuda(), norms=knorm)
+    return fa.KVCache(k=k, v=dev(st.cache_v, cfg.dtype), ids=dev_ids(prep["cache_ids"]),
+                      ts=torch.from_numpy(st.cache_ts).cuda(),
+                      n_valid=torch.from_numpy(np.ascontiguousarray(n_valid, np.int32)).cuda(),
+                      knorm=knorm)

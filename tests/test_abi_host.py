@@ -46,17 +46,17 @@ def test_status_strings_and_version(lib):
 
 def test_hash_validation(lib):
     h = lib.fastar_ann_hash
-    assert h(FAKE, 7, 1, 4, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EDTYPE
-    assert h(FAKE, 0, 1, 4, 96, FAKE, 4, FAKE, None) == _lib.FASTAR_ESHAPE
-    assert h(FAKE, 0, 1, 4, 64, FAKE, 17, FAKE, None) == _lib.FASTAR_ESHAPE
-    assert h(FAKE, 0, 1, -1, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EINVAL
-    assert h(None, 0, 1, 4, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EINVAL
-    assert h(MISALIGNED, 0, 1, 4, 64, FAKE, 4, FAKE, None) == _lib.FASTAR_EINVAL
-    assert h(FAKE, 0, 1, 4, 64, None, 4, FAKE, None) == _lib.FASTAR_EINVAL
-    assert h(FAKE, 1, 1, 4, 128, FAKE, 4, None, None) == _lib.FASTAR_EINVAL
+    assert h(FAKE, 7, 1, 4, 64, FAKE, 4, FAKE, None, None) == _lib.FASTAR_EDTYPE
+    assert h(FAKE, 0, 1, 4, 96, FAKE, 4, FAKE, None, None) == _lib.FASTAR_ESHAPE
+    assert h(FAKE, 0, 1, 4, 64, FAKE, 17, FAKE, None, None) == _lib.FASTAR_ESHAPE
+    assert h(FAKE, 0, 1, -1, 64, FAKE, 4, FAKE, None, None) == _lib.FASTAR_EINVAL
+    assert h(None, 0, 1, 4, 64, FAKE, 4, FAKE, None, None) == _lib.FASTAR_EINVAL
+    assert h(MISALIGNED, 0, 1, 4, 64, FAKE, 4, FAKE, None, None) == _lib.FASTAR_EINVAL
+    assert h(FAKE, 0, 1, 4, 64, None, 4, FAKE, None, None) == _lib.FASTAR_EINVAL
+    assert h(FAKE, 1, 1, 4, 128, FAKE, 4, None, None, None) == _lib.FASTAR_EINVAL
     # empty work is a no-op that succeeds without touching the device
-    assert h(None, 0, 0, 4, 64, None, 4, None, None) == _lib.FASTAR_OK
-    assert h(None, 1, 3, 0, 128, None, 4, None, None) == _lib.FASTAR_OK
+    assert h(None, 0, 0, 4, 64, None, 4, None, None, None) == _lib.FASTAR_OK
+    assert h(None, 1, 3, 0, 128, None, 4, None, None, None) == _lib.FASTAR_OK
 
 
 def test_workspace_queries(lib):
@@ -70,8 +70,8 @@ def test_workspace_queries(lib):
     assert lib.fastar_bucket_sort_workspace(2, 0, 5) == 0
 
 
-def _cache(H=1, cap=64, d=64, dtype=0):
-    return _lib.FastarCache(H, cap, d, dtype, FAKE, FAKE, FAKE, FAKE, FAKE)
+def _cache(H=1, cap=64, d=64, dtype=0, knorm=FAKE):
+    return _lib.FastarCache(H, cap, d, dtype, FAKE, FAKE, FAKE, FAKE, FAKE, knorm)
 
 
 def test_annsa_validation(lib):
@@ -80,7 +80,8 @@ def test_annsa_validation(lib):
     c = _cache()
     args = lambda **kw: [kw.get("q", FAKE), FAKE, 1, 32, kw.get("d", 64), kw.get("dt", 0),
                          kw.get("cache", ctypes.byref(c)), FAKE, FAKE, FAKE, 16, kw.get("P", 4),
-                         kw.get("scale", 0.125), FAKE, kw.get("odt", 0), None, FAKE,
+                         kw.get("scale", 0.125), FAKE, kw.get("odt", 0), None,
+                         kw.get("best", None), kw.get("bcos", None), FAKE,
                          kw.get("ws", need), None]
     assert f(*args(ws=need - 1)) == _lib.FASTAR_EWORKSPACE
     assert f(*args(P=11)) == _lib.FASTAR_ESHAPE
@@ -88,9 +89,14 @@ def test_annsa_validation(lib):
     assert f(*args(dt=1)) == _lib.FASTAR_EDTYPE          # cache is fp32
     assert f(*args(odt=5)) == _lib.FASTAR_EDTYPE
     assert f(*args(scale=float("nan"))) == _lib.FASTAR_EINVAL
+    assert f(*args(scale=0.0)) == _lib.FASTAR_EINVAL
+    assert f(*args(scale=-0.5)) == _lib.FASTAR_EINVAL
     assert f(*args(q=MISALIGNED)) == _lib.FASTAR_EINVAL
     c2 = _cache(H=2)
     assert f(*args(cache=ctypes.byref(c2))) == _lib.FASTAR_ESHAPE
+    assert f(*args(best=FAKE)) == _lib.FASTAR_EINVAL                 # best without cos
+    c3 = _cache(knorm=None)
+    assert f(*args(best=FAKE, bcos=FAKE, cache=ctypes.byref(c3))) == _lib.FASTAR_EINVAL
 
 
 def test_annca_validation(lib):
@@ -121,6 +127,7 @@ def test_tempcache_validation(lib):
     assert call(P=12) == _lib.FASTAR_ESHAPE
     bad = _cache(cap=64, dtype=3)
     assert call(cache=bad) == _lib.FASTAR_EDTYPE
+    assert call(cache=_cache(cap=64, knorm=None)) == _lib.FASTAR_EINVAL   # norms are needed
 
 
 def test_bucket_sort_validation(lib):

@@ -42,6 +42,24 @@ def test_hash_random_shapes(dtype, d, P, N):
         assert_ids_match(ids[h], ref, tie, f"head {h}")
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_hash_norms(dtype, d):
+    """The optional norm output equals |x| (fp32 sum of squares of the stored values)."""
+    require_gpu()
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((2, 777, d)).astype(np.float32) * 3
+    if dtype == "bf16":
+        from workloads import bf16_round
+        x = bf16_round(x)
+    x[0, 5] = 0.0
+    norms = torch.empty(2, 777, dtype=torch.float32, device="cuda")
+    fa.ann_hash(dev(x, dtype), torch.from_numpy(rng.standard_normal((2, 3, d)).astype(np.float32)).cuda(),
+                norms=norms)
+    ref = np.linalg.norm(x.astype(np.float64), axis=2)
+    np.testing.assert_allclose(norms.cpu().numpy(), ref, rtol=2e-6, atol=0)
+    assert norms[0, 5].item() == 0.0
+
+
 @pytest.mark.parametrize("P,N", [(0, 17), (3, 0), (5, 1), (7, 1023), (7, 1025), (7, 37440),
                                  (10, 5000), (8, 4096)])
 def test_bucket_sort_bit_exact(P, N):

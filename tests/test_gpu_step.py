@@ -15,32 +15,35 @@ from workloads import CONFIGS, make_step
 pytestmark = pytest.mark.gpu
 
 
-def gpu_step(st, cfg):
+def gpu_step(st, cfg, fused):
     planes = torch.from_numpy(st.planes).cuda()
     q, kc, vc = dev(st.q, cfg.dtype), dev(st.k_cur, cfg.dtype), dev(st.v_cur, cfg.dtype)
-    cache = fa.KVCache(k=dev(st.cache_k, cfg.dtype), v=dev(st.cache_v, cfg.dtype),
-                       ids=torch.empty(cfg.H, cfg.cap, dtype=torch.int16, device="cuda"),
-                       ts=torch.from_numpy(st.cache_ts).cuda(),
-                       n_valid=torch.from_numpy(st.n_valid).cuda())
-    fa.ann_hash(cache.k, planes, ids=cache.ids)
+    cache = fa.KVCache.from_keys(dev(st.cache_k, cfg.dtype), dev(st.cache_v, cfg.dtype),
+                                 torch.from_numpy(st.cache_ts).cuda(),
+                                 torch.from_numpy(st.n_valid).cuda(), planes)
     q_ids = fa.ann_hash(q, planes)
     k_ids = fa.ann_hash(kc, planes)
     kp = dev(st.kp, cfg.dtype)
     p_ids = fa.ann_hash(kp, planes)
-    o_sa, lse = fa.annsa_forward(q, q_ids, kc, vc, k_ids, cfg.P, cache=cache)
+    if fused:       # the attention pass also returns TempCache's top-1
+        o_sa, lse, best, cos = fa.annsa_forward(q, q_ids, kc, vc, k_ids, cfg.P, cache=cache, search=True)
+    else:
+        o_sa, lse = fa.annsa_forward(q, q_ids, kc, vc, k_ids, cfg.P, cache=cache)
+        best = cos = None
     o_ca, keep, cnt = fa.annca_forward(q, q_ids, cfg.frame_len, kp, dev(st.vp, cfg.dtype), p_ids, cfg.P)
-    tc = fa.tempcache_update(cache, q, q_ids, kc, vc, k_ids, cfg.P, cfg.tau, st.step)
+    tc = fa.tempcache_update(cache, q, q_ids, kc, vc, k_ids, cfg.P, cfg.tau, st.step,
+                             best_in=best, cos_in=cos)
     torch.cuda.synchronize()
     return dict(q_ids=host_ids(q_ids), k_ids=host_ids(k_ids), p_ids=host_ids(p_ids), o_sa=o_sa,
                 lse=lse, o_ca=o_ca, keep=keep, tc=tc, cache=cache)
 
 
-@pytest.mark.parametrize("seed", [0, 2, 4])
-def test_end_to_end_tiny_exact(seed):
+@pytest.mark.parametrize("seed,fused", [(0, False), (2, False), (4, False), (0, True), (2, True)])
+def test_end_to_end_tiny_exact(seed, fused):
     require_gpu()
     cfg = CONFIGS["tiny_f32"]
     st = make_step(cfg, seed)
-    g = gpu_step(st, cfg)
+    g = gpu_step(st, cfg, fused)
     cache_ids = np.stack([ann_hash(st.cache_k[h], st.planes[h])[0] for h in range(cfg.H)])
     r = attention_step(st.q, st.k_cur, st.v_cur, st.cache_k, st.cache_v, cache_ids, st.cache_ts,
                        st.n_valid, st.planes, st.kp, st.vp, cfg.frame_len, cfg.tau, st.step)

@@ -70,6 +70,44 @@ def test_top1_matches_oracle(name):
     print(f"top1 {name}: {ties} argmax near-ties (validated)")
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "single_bf16", "wan13_bf16"])
+def test_fused_search_in_annsa_matches_oracle(name):
+    """annsa_forward's search output (TempCache's top-1 from the attention pass)
+    against the oracle's top-1; the attention output is unchanged by it."""
+    require_gpu()
+    prep = prepared(name)
+    st, cfg = prep["step"], prep["cfg"]
+    cache = device_cache(prep)
+    args = (dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
+            dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), cfg.P)
+    out, lse, best_t, cos_t = fa.annsa_forward(*args, cache=cache, search=True)
+    out0, lse0 = fa.annsa_forward(*args, cache=cache)
+    assert torch.equal(out, out0) and torch.equal(lse, lse0)
+    best = best_t.cpu().numpy()
+    cos = cos_t.cpu().numpy().astype(np.float64)
+    for h, (ob, oc, tie, near) in enumerate(oracle_top1(prep, cfg.n0)):
+        ok = ~tie
+        assert np.array_equal(best[h][ok], ob[ok]), f"head {h}"
+        for i in np.nonzero(tie)[0]:
+            assert best[h][i] in near[i]
+        fin = np.isfinite(oc)
+        assert np.array_equal(np.isfinite(cos[h]), fin)
+        assert np.abs(cos[h][fin] - oc[fin]).max() <= COS_ABS
+
+
+def test_commit_keeps_key_norms():
+    """After a commit every valid slot's knorm is the norm of the key it holds."""
+    require_gpu()
+    prep = prepared("single_bf16")
+    cfg = prep["cfg"]
+    cache = device_cache(prep)
+    call(prep, cache, cfg.tau)
+    k = cache.k.float().cpu().numpy().astype(np.float64)
+    n = int(cache.n_valid[0])
+    np.testing.assert_allclose(cache.knorm.cpu().numpy()[0, :n], np.linalg.norm(k[0, :n], axis=1),
+                               rtol=2e-6, atol=0)
+
+
 def _commit_case(prep, cache_dev, n, tau, ts=None, step=None):
     st, cfg = prep["step"], prep["cfg"]
     step = st.step if step is None else step
