@@ -11,7 +11,7 @@
 //  MODE_CA   AnnCA: one block per (head, frame, 64 consecutive queries); keys
 //            are the frame's kept prompt tokens (blog, "2. AnnCA"; summary B).
 //  MODE_TOP1 TempCache search alone: the SA blocks over cached keys only, no
-//            softmax; each query keeps its best cosine and slot and claims it.
+//            softmax; each query keeps its best cosine and slot.
 //
 // Layout of the work inside a block (256 threads = 4 waves, wave w owns the
 // block's queries 16w..16w+15; lane l serves query l%16 and "lane group"
@@ -409,8 +409,6 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
             const size_t qi = static_cast<size_t>(h) * p.Nq + qrow;
             p.best[qi] = found ? best_s : -1;
             p.bcos[qi] = found ? best_c : kNegInf;
-            if (MODE == MODE_TOP1 && found && best_c >= p.tau)
-                atomicMax(&p.claim[static_cast<size_t>(h) * p.cap + best_s], qrow);
         }
     }
     if constexpr (HAS_V) {

@@ -118,6 +118,7 @@ struct TcWs {
     SortBufs q, k;
     ItemTable it;
     int32_t *claim, *best, *upos, *ev, *dest;
+    uint32_t* refreshed;
     float* cosv;
 };
 TcWs carve_tc(Carver& c, int H, int N, int cap, int P) {
@@ -127,6 +128,7 @@ TcWs carve_tc(Carver& c, int H, int N, int cap, int P) {
     w.it = carve_items(c, H, N, P);
     const long long HN = static_cast<long long>(H) * N;
     w.claim = c.take<int32_t>(static_cast<long long>(H) * cap);
+    w.refreshed = c.take<uint32_t>(static_cast<long long>(H) * ((cap + 31) / 32));
     w.best = c.take<int32_t>(HN);
     w.cosv = c.take<float>(HN);
     w.upos = c.take<int32_t>(HN);
@@ -221,8 +223,7 @@ fastar_status fastar_bucket_sort(const uint16_t* ids, int32_t H, int32_t N, int3
     s.a = ids;
     s.a_stride = N;
     s.a_fixed = N;
-    return hip_status(launch_bucket_sort(H, P, 1, &s, &b, nullptr, nullptr, 0,
-                                         static_cast<hipStream_t>(stream)));
+    return hip_status(launch_bucket_sort(H, P, 1, &s, &b, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------ AnnSA
@@ -275,7 +276,7 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
     sets[1].b_stride = Ncur;
     sets[1].nb = Ncur;
     SortBufs bufs[2] = {w.q, w.k};
-    hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, nullptr, 0, s);
+    hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, s);
     if (e != hipSuccess) return FASTAR_EHIP;
 
     AttnParams p;
@@ -392,17 +393,13 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     Carver c(ws);
     TcWs w = carve_tc(c, H, N, cap, P);
     hipError_t e = hipSuccess;
-    const long long claims = static_cast<long long>(H) * cap;
 
     const int32_t* bestp;
     const float* cosp;
     if (best_in) {
         bestp = best_in;
         cosp = cos_in;
-        e = launch_fill_i32(w.claim, claims, -1, s);
-        if (e == hipSuccess)
-            e = launch_tc_claim(best_in, cos_in, cache->n_valid, cap, H, N, tau, w.claim, s);
-        if (e == hipSuccess && best && HN > 0)
+        if (best && HN > 0)
             e = hipMemcpyAsync(best, best_in, HN * sizeof(int32_t), hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess && best_cos && HN > 0)
             e = hipMemcpyAsync(best_cos, cos_in, HN * sizeof(float), hipMemcpyDeviceToDevice, s);
@@ -421,7 +418,7 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
         sets[1].a_nvalid = cache->n_valid;
         sets[1].a_cap = cap;
         SortBufs bufs[2] = {w.q, w.k};
-        e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, w.claim, claims, s);
+        e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, s);
         if (e != hipSuccess) return FASTAR_EHIP;
         AttnParams p;
         p.q = q;
@@ -439,8 +436,6 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
         p.knorm = cache->knorm;
         p.best = bo;
         p.bcos = co;
-        p.claim = w.claim;
-        p.tau = tau;
         e = launch_attn(MODE_TOP1, bf, d, false, H, p, s);
         if (e != hipSuccess) return FASTAR_EHIP;
     }
@@ -449,6 +444,7 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     sp.best = bestp;
     sp.cosv = cosp;
     sp.claim = w.claim;
+    sp.refreshed = w.refreshed;
     sp.ts = cache->ts;
     sp.n_valid = cache->n_valid;
     sp.upos = w.upos;

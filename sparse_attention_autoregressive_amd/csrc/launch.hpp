@@ -59,10 +59,9 @@ inline int max_attn_items(long long nq, int B) {
 
 // Sorts one or two sets (nsets = 1 or 2) per head, in three launches.  With
 // ``items`` set (two sets: queries, keys) the scan also writes the attention
-// work list.  ``clear`` (optional) is filled with -1 by the first launch.
+// work list.
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
-                              const ItemTable* items, int32_t* clear, long long clear_n,
-                              hipStream_t s);
+                              const ItemTable* items, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
 enum AttnMode { MODE_SA = 0, MODE_CA = 1, MODE_TOP1 = 2 };
@@ -98,8 +97,6 @@ struct AttnParams {
     float* lse = nullptr;
     int32_t* best = nullptr;
     float* bcos = nullptr;
-    int32_t* claim = nullptr;
-    float tau = 0.f;
     float scale_log2 = 0.f;
 };
 
@@ -111,16 +108,12 @@ hipError_t launch_annca_select(const uint16_t* q_ids, const uint16_t* kp_ids, in
                                int frame_len, int L, int P, int32_t* idx, int32_t* cnt,
                                uint8_t* keep, int32_t* keep_count, hipStream_t s);
 
-// ------------------------------------------------------------------ TempCache
-hipError_t launch_fill_i32(int32_t* p, long long n, int32_t v, hipStream_t s);
-
-hipError_t launch_tc_claim(const int32_t* best, const float* cosv, const int32_t* n_valid,
-                           int cap, int H, int N, float tau, int32_t* claim, hipStream_t s);
-
+// ------------------------------------------------------------------ TempCache commit
 struct TcSelectParams {
     const int32_t* best;     // [H][N]
     const float* cosv;       // [H][N]
-    const int32_t* claim;    // [H][cap]
+    int32_t* claim;          // [H][cap] scratch; only the entries of matched slots are used
+    uint32_t* refreshed;     // [H][ceil(cap/32)] scratch bitmap
     const int32_t* ts;       // [H][cap]
     int32_t* n_valid;        // [H] read, then updated
     int32_t* upos;           // [H][N] scratch

@@ -3,7 +3,6 @@
 // part C).  Three launches, every count stays on the device:
 //
 //   sort_hist    one block per 1024-id tile: LDS histogram -> hist[h][tile][b]
-//                (the blocks also clear an optional caller array to -1)
 //   sort_scan    one block per head: per-bucket exclusive prefix over tiles (in
 //                place) plus a block scan over buckets -> off[h][b], for each
 //                set; optionally the attention work list (one item per bucket
@@ -26,8 +25,6 @@ struct SortArgs {
     int B;
     int P;
     ItemTable items;
-    int32_t* clear;
-    long long clear_n;
 };
 
 __device__ __forceinline__ int set_count(const IdSet& s, int h, int& na) {
@@ -42,11 +39,6 @@ __device__ __forceinline__ int set_id(const IdSet& s, int h, int na, int e) {
 
 __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
     __shared__ int cnt[1024];
-    if (a.clear) {      // a scratch array the caller needs at -1 (TempCache claims)
-        const long long nb = static_cast<long long>(gridDim.x) * gridDim.y * gridDim.z;
-        const long long bid = blockIdx.x + static_cast<long long>(gridDim.x) * (blockIdx.y + static_cast<long long>(gridDim.y) * blockIdx.z);
-        for (long long i = bid * 256 + threadIdx.x; i < a.clear_n; i += nb * 256) a.clear[i] = -1;
-    }
     const IdSet& S = a.set[blockIdx.z];
     const SortBufs& O = a.buf[blockIdx.z];
     const int h = blockIdx.y, t = blockIdx.x, B = a.B;
@@ -197,15 +189,12 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
 }
 
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
-                              const ItemTable* items, int32_t* clear, long long clear_n,
-                              hipStream_t s) {
+                              const ItemTable* items, hipStream_t s) {
     SortArgs a;
     a.nsets = nsets;
     a.B = 1 << P;
     a.P = P;
     a.items = items ? *items : ItemTable();
-    a.clear = clear_n > 0 ? clear : nullptr;
-    a.clear_n = clear_n;
     int max_tiles = 0;
     for (int i = 0; i < nsets; ++i) {
         a.set[i] = sets[i];
@@ -217,10 +206,11 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
         a.buf[1] = a.buf[0];
     }
     if (H == 0) return hipSuccess;
-    // the histogram launch also clears ``clear``: keep at least one block
-    timer_begin("sort_hist", s);
-    hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles > 0 ? max_tiles : 1, H, nsets), dim3(256), 0, s, a);
-    timer_end(s);
+    if (max_tiles > 0) {
+        timer_begin("sort_hist", s);
+        hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
+        timer_end(s);
+    }
     timer_begin("sort_scan", s);
     hipLaunchKernelGGL(sort_scan_kernel, dim3(H), dim3(1024), 0, s, a);
     timer_end(s);

@@ -1,67 +1,33 @@
 // TempCache commit (FAST-AR blog, "1. TempCache"; summary, "2. Core
-// Components" A): after the top-1 search has written best/cos and claimed the
-// matched slots (atomicMax of the token index, so the most recent token wins
-// regardless of scheduling), one block per head
-//   1. resolves the matched tokens (winner -> its slot, others dropped), counts
-//      the winners (= refreshed slots) and ranks the unmatched tokens in token
-//      order with one block scan,
-//   2. if the cache overflows, selects the e non-refreshed slots with the
+// Components" A).  Given each current token's top-1 (best slot, cosine), one
+// block per head
+//   1. resets the claim entries of the slots this chunk matched and lets every
+//      matched token claim its slot with atomicMax of its index, so the most
+//      recent token wins regardless of scheduling,
+//   2. resolves the matched tokens (winner -> its slot, marked in a bitmap of
+//      refreshed slots; others dropped), counts the winners and ranks the
+//      unmatched tokens in token order with one block scan,
+//   3. if the cache overflows, selects the e non-refreshed slots with the
 //      smallest (timestamp, slot) by a radix select on the timestamps
 //      (8-bit digits of ts - min(ts); one pass when timestamps span < 256)
 //      and lists them in slot order (two block scans); slot data are loaded
-//      once per 32768-slot chunk, 32 consecutive slots per thread,
-//   3. writes the unmatched tokens' destinations, the eviction list, the counts
+//      once per 32768-slot chunk, 32 consecutive slots (one bitmap word) per
+//      thread,
+//   4. writes the unmatched tokens' destinations, the eviction list, the counts
 //      and the new valid-slot count;
 // then a copy kernel moves the written tokens' rows into place (32 lanes per
-// token, 16 bytes each) and records each written key's norm.
-// Every decision is integer or a single fp32 compare, so results are
-// deterministic.
+// token, 16 bytes each) and records each written key's norm.  Every decision
+// is integer or a single fp32 compare, so results are deterministic.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace fastar {
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, long long n, int32_t v) {
-    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n; i += 256ll * gridDim.x) p[i] = v;
-}
-
-hipError_t launch_fill_i32(int32_t* p, long long n, int32_t v, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    long long blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    timer_begin("fill", s);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n, v);
-    timer_end(s);
-    return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void tc_claim_kernel(const int32_t* __restrict__ best,
-                                                       const float* __restrict__ cosv,
-                                                       const int32_t* __restrict__ n_valid, int cap,
-                                                       int N, float tau, int32_t* __restrict__ claim) {
-    const int h = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= N) return;
-    const int n = clamp_n(n_valid, h, cap);
-    const size_t qi = static_cast<size_t>(h) * N + i;
-    const int b = best[qi];
-    if (b >= 0 && b < n && cosv[qi] >= tau) atomicMax(&claim[static_cast<size_t>(h) * cap + b], i);
-}
-
-hipError_t launch_tc_claim(const int32_t* best, const float* cosv, const int32_t* n_valid, int cap,
-                           int H, int N, float tau, int32_t* claim, hipStream_t s) {
-    if (H == 0 || N == 0) return hipSuccess;
-    timer_begin("tempcache_claim", s);
-    hipLaunchKernelGGL(tc_claim_kernel, dim3((N + 255) / 256, H), dim3(256), 0, s, best, cosv,
-                       n_valid, cap, N, tau, claim);
-    timer_end(s);
-    return hipGetLastError();
-}
-
 namespace {
 constexpr int SEL_NT = 1024;
 constexpr int TOK_ITEMS = 8;                      // tokens per thread per chunk
 constexpr int TOK_CHUNK = SEL_NT * TOK_ITEMS;     // < 65536: packed counters fit 16 bits
-constexpr int SLOT_ITEMS = 32;                    // slots per thread per chunk
+constexpr int SLOT_ITEMS = 32;                    // slots per thread per chunk (one bitmap word)
 constexpr int SLOT_CHUNK = SEL_NT * SLOT_ITEMS;
 
 __device__ __forceinline__ uint32_t ts_key(int32_t t) { return static_cast<uint32_t>(t) ^ 0x80000000u; }
@@ -81,41 +47,9 @@ __device__ __forceinline__ uint32_t block_min_max(uint32_t v, bool want_max, uin
     return r;
 }
 
-// This thread's SLOT_ITEMS consecutive slots of a chunk: timestamp keys and a
-// bit mask of the eviction candidates (valid, not refreshed).  All loads are
-// issued before any is used.
-struct SlotChunk {
-    uint32_t key[SLOT_ITEMS];
-    uint32_t cand;
-    int base;
-    __device__ __forceinline__ void load(const int32_t* claim, const int32_t* ts, int n, int c0) {
-        base = c0 + static_cast<int>(threadIdx.x) * SLOT_ITEMS;
-        int cl[SLOT_ITEMS];
-        const bool vec = base + SLOT_ITEMS <= n &&
-                         ((reinterpret_cast<uintptr_t>(claim + base) | reinterpret_cast<uintptr_t>(ts + base)) & 15) == 0;
-        if (vec) {
-#pragma unroll
-            for (int k = 0; k < SLOT_ITEMS; k += 4) {
-                const int4 c = *reinterpret_cast<const int4*>(claim + base + k);
-                const int4 t = *reinterpret_cast<const int4*>(ts + base + k);
-                cl[k] = c.x; cl[k + 1] = c.y; cl[k + 2] = c.z; cl[k + 3] = c.w;
-                key[k] = ts_key(t.x); key[k + 1] = ts_key(t.y);
-                key[k + 2] = ts_key(t.z); key[k + 3] = ts_key(t.w);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < SLOT_ITEMS; ++k) {
-                const int j = base + k;
-                cl[k] = (j < n) ? claim[j] : 0;
-                key[k] = (j < n) ? ts_key(ts[j]) : 0u;
-            }
-        }
-        cand = 0;
-#pragma unroll
-        for (int k = 0; k < SLOT_ITEMS; ++k)
-            if (base + k < n && cl[k] < 0) cand |= 1u << k;
-    }
-};
+__device__ __forceinline__ bool is_matched(int b, float c, int n, float tau) {
+    return b >= 0 && b < n && c >= tau;
+}
 }  // namespace
 
 __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams p) {
@@ -128,13 +62,28 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     const int n = clamp_n(p.n_valid, h, cap);
     const int32_t* best = p.best + static_cast<size_t>(h) * N;
     const float* cosv = p.cosv + static_cast<size_t>(h) * N;
-    const int32_t* claim = p.claim + static_cast<size_t>(h) * cap;
+    int32_t* claim = p.claim + static_cast<size_t>(h) * cap;
+    uint32_t* refr = p.refreshed + static_cast<size_t>(h) * ((cap + 31) / 32);
     const int32_t* ts = p.ts + static_cast<size_t>(h) * cap;
     int32_t* upos = p.upos + static_cast<size_t>(h) * N;
     int32_t* ev = p.ev + static_cast<size_t>(h) * N;
     int32_t* dest = p.dest + static_cast<size_t>(h) * N;
 
-    // 1. tokens: matched ones get their slot (winner) or -1 (dropped); the
+    // 1. claims.  Only the entries of matched slots are reset, so the claim
+    //    array never needs a full clear.
+    for (int w = tid; w < (n + 31) / 32; w += SEL_NT) refr[w] = 0u;
+    for (int i = tid; i < N; i += SEL_NT) {
+        const int b = best[i];
+        if (is_matched(b, cosv[i], n, p.tau)) claim[b] = -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < N; i += SEL_NT) {
+        const int b = best[i];
+        if (is_matched(b, cosv[i], n, p.tau)) atomicMax(&claim[b], i);
+    }
+    __syncthreads();
+
+    // 2. tokens: matched ones get their slot (winner) or -1 (dropped); the
     //    unmatched are ranked in token order.  One scan carries both counts:
     //    unmatched in the low 16 bits, winners (= refreshed slots) above.
     int u = 0, refreshed = 0;
@@ -154,12 +103,12 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         for (int k = 0; k < TOK_ITEMS; ++k) {
             const int i = base + k;
             if (i >= N) continue;
-            const bool m = bi[k] >= 0 && bi[k] < n && ci[k] >= p.tau;
-            if (!m) {
+            if (!is_matched(bi[k], ci[k], n, p.tau)) {
                 um |= 1u << k;
                 ++local;
             } else {
                 const bool win = claim[bi[k]] == i;
+                if (win) atomicOr(&refr[bi[k] >> 5], 1u << (bi[k] & 31));
                 wins += win;
                 dest[i] = win ? bi[k] : -1;
             }
@@ -175,28 +124,45 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         u += total & 0xFFFF;
         refreshed += total >> 16;
     }
+    __syncthreads();                    // the refreshed bitmap is complete
 
     const int e = max(0, n + u - cap);
     const int appended = u - e;
 
-    // 2. the e oldest non-refreshed slots (ties: lower slot), ascending
+    // 3. the e oldest non-refreshed slots (ties: lower slot), ascending
     if (e > 0) {
-        SlotChunk sc;
-        int cached = -1;
-        auto chunk = [&](int c0) {
-            if (cached != c0) {
-                sc.load(claim, ts, n, c0);
-                cached = c0;
+        uint32_t key[SLOT_ITEMS];
+        uint32_t cand = 0;
+        int sbase = 0, cached = -1;
+        auto load = [&](int c0) __attribute__((always_inline)) {
+            if (cached == c0) return;
+            cached = c0;
+            sbase = c0 + tid * SLOT_ITEMS;
+            const bool vec = sbase + SLOT_ITEMS <= n &&
+                             (reinterpret_cast<uintptr_t>(ts + sbase) & 15) == 0;
+            if (vec) {
+#pragma unroll
+                for (int k = 0; k < SLOT_ITEMS; k += 4) {
+                    const int4 t = *reinterpret_cast<const int4*>(ts + sbase + k);
+                    key[k] = ts_key(t.x); key[k + 1] = ts_key(t.y);
+                    key[k + 2] = ts_key(t.z); key[k + 3] = ts_key(t.w);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < SLOT_ITEMS; ++k) key[k] = (sbase + k < n) ? ts_key(ts[sbase + k]) : 0u;
             }
+            const int left = n - sbase;
+            const uint32_t valid = left >= SLOT_ITEMS ? 0xFFFFFFFFu : (left > 0 ? (1u << left) - 1u : 0u);
+            cand = valid ? (~refr[sbase >> 5] & valid) : 0u;
         };
         uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
         for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
-            chunk(c0);
+            load(c0);
 #pragma unroll
             for (int k = 0; k < SLOT_ITEMS; ++k)
-                if ((sc.cand >> k) & 1) {
-                    lmin = sc.key[k] < lmin ? sc.key[k] : lmin;
-                    lmax = sc.key[k] > lmax ? sc.key[k] : lmax;
+                if ((cand >> k) & 1) {
+                    lmin = key[k] < lmin ? key[k] : lmin;
+                    lmax = key[k] > lmax ? key[k] : lmax;
                 }
         }
         const uint32_t kmin = block_min_max(lmin, false, red);
@@ -210,14 +176,14 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
                 if (tid < 256) hist[tid] = 0;
                 __syncthreads();
                 for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
-                    chunk(c0);
+                    load(c0);
                     // neighbouring slots usually share a timestamp: add runs of
                     // equal digits with one atomic each
                     int rd = -1, rc = 0;
 #pragma unroll
                     for (int k = 0; k < SLOT_ITEMS; ++k) {
-                        if ((sc.cand >> k) & 1) {
-                            const uint32_t rel = sc.key[k] - kmin;
+                        if ((cand >> k) & 1) {
+                            const uint32_t rel = key[k] - kmin;
                             const uint32_t hi = (shift + 8 >= 32) ? 0u : (rel >> (shift + 8));
                             if (hi == prefix) {
                                 const int dg = static_cast<int>((rel >> shift) & 255u);
@@ -233,14 +199,14 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
                     if (rc) atomicAdd(&hist[rd], rc);
                 }
                 __syncthreads();
-                if (tid == 0) {
-                    int cum = 0, dgt = 0;
-                    for (; dgt < 255; ++dgt) {
-                        if (cum + hist[dgt] >= need) break;
-                        cum += hist[dgt];
-                    }
-                    bcast[0] = dgt;
-                    bcast[1] = need - cum;
+                // the digit holding the need-th candidate: a scan over the 256
+                // bins, owned by the one thread whose bin straddles it
+                const int v = tid < 256 ? hist[tid] : 0;
+                int tot;
+                const int ex = block_exclusive_scan<SEL_NT>(v, smem, tot);
+                if (tid < 256 && ex < need && need <= ex + v) {
+                    bcast[0] = tid;
+                    bcast[1] = need - ex;
                 }
                 __syncthreads();
                 prefix = (prefix << 8) | static_cast<uint32_t>(bcast[0]);
@@ -251,14 +217,14 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         const uint32_t tstar = kmin + prefix;
         int carry_eq = 0, carry_sel = 0;
         for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
-            chunk(c0);
+            load(c0);
             uint32_t ltf = 0, eqf = 0;
             int eqc = 0;
 #pragma unroll
             for (int k = 0; k < SLOT_ITEMS; ++k) {
-                if ((sc.cand >> k) & 1) {
-                    if (sc.key[k] < tstar) ltf |= 1u << k;
-                    else if (sc.key[k] == tstar) { eqf |= 1u << k; ++eqc; }
+                if ((cand >> k) & 1) {
+                    if (key[k] < tstar) ltf |= 1u << k;
+                    else if (key[k] == tstar) { eqf |= 1u << k; ++eqc; }
                 }
             }
             int eqtot;
@@ -278,7 +244,7 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
 #pragma unroll
             for (int k = 0; k < SLOT_ITEMS; ++k)
                 if ((self >> k) & 1) {
-                    if (pos < e) ev[pos] = sc.base + k;     // e <= N: never past the row
+                    if (pos < e) ev[pos] = sbase + k;     // e <= N: never past the row
                     ++pos;
                 }
             carry_eq += eqtot;
@@ -287,7 +253,7 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     }
     __syncthreads();
 
-    // 3. unmatched tokens: appended slots first, then the evicted ones
+    // 4. unmatched tokens: appended slots first, then the evicted ones
     for (int i = tid; i < N; i += SEL_NT) {
         const int k = upos[i];
         if (k < 0) continue;
