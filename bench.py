@@ -10,6 +10,12 @@ cache; 7 hyperplanes = 128 buckets; 512 prompt tokens):
     annca_forward   (prompt selection + cross-attention over the kept tokens)
     tempcache_update(claims from that top-1 + select + row scatter)
 
+The step runs on two streams: AnnCA (independent of the cache) overlaps the
+TempCache commit, whose select phase keeps only one CU per head busy.  The
+headline issues the calls one by one; ``ms_per_step_graph`` replays the same
+step captured as a HIP graph (one graph per cache copy) and
+``ms_per_step_eager_one_stream`` issues the calls on one stream.
+
 Inputs are seeded synthetic tensors, resident in HBM before the timed region.
 Every timed step starts from its own pristine copy of the cache (the commit
 mutates it), so each step sees exactly the same workload.
@@ -18,7 +24,8 @@ Output: one JSON line.  ``value`` is the achieved bf16 TFLOP/s on kept pairs,
 4*d*(AnnSA kept pairs + AnnCA kept pairs) / step time; ``ms_per_step`` is the
 step latency.  ``roofline`` describes the dominant kernel (AnnSA's bucket
 attention, HBM-bound): algorithmic bytes per launch / its mean duration from
-HIP events on its launch stream.  ``cpu_baseline`` times the CPU oracle on a
+HIP events on its launch stream, taken in a one-stream pass where every
+kernel runs alone.  ``cpu_baseline`` times the CPU oracle on a
 bounded sample of heads of the same workload.
 """
 from __future__ import annotations
@@ -88,54 +95,52 @@ def main():
     base = fa.KVCache.from_keys(to_dev(st.cache_k), to_dev(st.cache_v),
                                 torch.from_numpy(st.cache_ts).to(dev),
                                 torch.from_numpy(st.n_valid).to(dev), planes)
-    n_copies = args.warmup + 2 * args.steps
-    caches = [base.clone() for _ in range(n_copies)]
     out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
-    lib = fa.load()
-    ws = {
-        "sa": torch.empty(lib.fastar_annsa_workspace(H, Nq, cap, Nq, P), dtype=torch.uint8, device=dev),
-        "ca": torch.empty(lib.fastar_annca_workspace(H, Nq, cfg.frame_len, cfg.L, P), dtype=torch.uint8, device=dev),
-        "tc": torch.empty(lib.fastar_tempcache_workspace(H, Nq, cap, P), dtype=torch.uint8, device=dev),
-    }
-    ids = {k: torch.empty(H, n, dtype=torch.int16, device=dev)
-           for k, n in (("q", Nq), ("k", Nq), ("p", cfg.L))}
-    o_sa = torch.empty(H, Nq, d, dtype=out_dt, device=dev)
-    lse = torch.empty(H, Nq, dtype=torch.float32, device=dev)
-    o_ca = torch.empty(H, Nq, d, dtype=out_dt, device=dev)
-    best = torch.empty(H, Nq, dtype=torch.int32, device=dev)
-    bcos = torch.empty(H, Nq, dtype=torch.float32, device=dev)
-
-    def step(cache):
-        fa.ann_hash(q, planes, ids=ids["q"])
-        fa.ann_hash(kc, planes, ids=ids["k"])
-        fa.ann_hash(kp, planes, ids=ids["p"])
-        fa.annsa_forward(q, ids["q"], kc, vc, ids["k"], P, cache=cache, out=o_sa, lse=lse,
-                         ws=ws["sa"], search=True, best=best, best_cos=bcos)
-        _, keep, cnt = fa.annca_forward(q, ids["q"], cfg.frame_len, kp, vp, ids["p"], P, out=o_ca,
-                                        ws=ws["ca"])
-        fa.tempcache_update(cache, q, ids["q"], kc, vc, ids["k"], P, cfg.tau, st.step,
-                            best_in=best, cos_in=bcos, outputs=False, ws=ws["tc"])
-        return cnt
-
+    from sparse_attention_autoregressive_amd.step import AttentionStep
+    mk = lambda overlap: AttentionStep(H, Nq, d, cap, P, cfg.frame_len, cfg.L, cfg.tau,
+                                       out_dtype=out_dt, device=dev, overlap=overlap)
+    two, one = mk(True), mk(False)
+    ids = two.ids
+    # every step commits into its own pristine copy of the cache
+    n_copies = 3 * args.warmup + 4 * args.steps
+    caches = [base.clone() for _ in range(n_copies)]
     it = iter(caches)
+    run = lambda s, c: s(c, q, kc, vc, kp, vp, planes, st.step)
+
     for _ in range(args.warmup):
-        cnt = step(next(it))
+        run(two, next(it))
+        run(one, next(it))
+    torch.cuda.synchronize()
+    # one captured graph per cache copy (addresses are baked into a graph)
+    graphs = [two.graph(next(it), q, kc, vc, kp, vp, planes, st.step)
+              for _ in range(args.warmup + args.steps)]
+    for g in graphs[:args.warmup]:
+        g.replay()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        cnt = step(next(it))
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    def timed(fn):
+        main = torch.cuda.current_stream(dev)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(main)
+        for i in range(args.steps):
+            fn(i)
+        t1.record(main)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
 
-    # ---- the same K steps again with per-kernel HIP events (launch stream)
+    # ---- timed regions: K two-stream steps issued call by call (the headline);
+    # the same step as K graph replays, and issued on one stream
+    ms_graph = timed(lambda i: graphs[args.warmup + i].replay())
+    ms_per_step = timed(lambda i: run(two, next(it)))
+    ms_one_stream = timed(lambda i: run(one, next(it)))
+    cnt = two.keep_count
+
+    # ---- K eager one-stream steps again with per-kernel HIP events: every
+    # kernel runs alone, so its mean duration is its own
     with fa.kernel_timer() as kt:
         for _ in range(args.steps):
-            step(next(it))
+            run(one, next(it))
     torch.cuda.synchronize()
     kernel_ms = {k: v[1] / max(1, v[0]) for k, v in kt.times.items()}
     kernel_launches = {k: v[0] // args.steps for k, v in kt.times.items()}
@@ -171,12 +176,14 @@ def main():
     line = {
         "metric": "attention step latency (ms) + achieved bf16 TFLOP/s on kept pairs, Wan-1.3B chunk",
         "value": value_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "ms_per_step_graph": ms_graph,
+        "ms_per_step_eager_one_stream": ms_one_stream,
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {H} heads x d={d}, chunk {cfg.Fq} frames x "
                                f"{cfg.frame_len} = {Nq} tokens, cache {cap} slots (full), "
                                f"P={P} ({B} buckets), prompt {cfg.L}, tau={cfg.tau}",
-                   "out_dtype": args.out_dtype, "seed": args.seed},
+                   "out_dtype": args.out_dtype, "seed": args.seed, "streams": 2},
         "roofline": roofline,
         "kernel_ms": kernel_ms, "kernel_launches_per_step": kernel_launches,
         "kept_pairs": {"annsa": sa_pairs, "annca": ca_pairs,

@@ -185,7 +185,8 @@ def annsa_forward(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor, v_c
 def annca_forward(q: torch.Tensor, q_ids: torch.Tensor, frame_len: int, kp: torch.Tensor,
                   vp: torch.Tensor, kp_ids: torch.Tensor, P: int, scale: Optional[float] = None,
                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
-                  want_keep: bool = True, ws: Optional[torch.Tensor] = None):
+                  want_keep: bool = True, ws: Optional[torch.Tensor] = None,
+                  keep: Optional[torch.Tensor] = None, keep_count: Optional[torch.Tensor] = None):
     """Frame-pruned cross-attention: (out, keep [H, F, L] uint8, keep_count [H, F])."""
     H, Nq, d = q.shape
     L = kp.shape[1]
@@ -196,8 +197,15 @@ def annca_forward(q: torch.Tensor, q_ids: torch.Tensor, frame_len: int, kp: torc
     lib = load()
     if out is None:
         out = torch.empty(H, Nq, d, dtype=out_dtype, device=q.device)
-    keep = torch.empty(H, F, L, dtype=torch.uint8, device=q.device) if want_keep else None
-    cnt = torch.empty(H, F, dtype=torch.int32, device=q.device) if want_keep else None
+    if keep is None and want_keep:
+        keep = torch.empty(H, F, L, dtype=torch.uint8, device=q.device)
+    cnt = keep_count
+    if cnt is None and want_keep:
+        cnt = torch.empty(H, F, dtype=torch.int32, device=q.device)
+    if keep is not None and (keep.dtype != torch.uint8 or tuple(keep.shape) != (H, F, L)):
+        raise ValueError("keep must be uint8 [H, F, L]")
+    if cnt is not None and (cnt.dtype != torch.int32 or tuple(cnt.shape) != (H, F)):
+        raise ValueError("keep_count must be int32 [H, F]")
     wsp, wsn = _workspace(lib.fastar_annca_workspace(H, Nq, frame_len, L, P), q.device, ws)
     check("fastar_annca_forward", lib.fastar_annca_forward(
         _ptr(q), _ptr(q_ids), H, Nq, frame_len, d, _dtype_code(q), _ptr(kp), _ptr(vp),

@@ -6,7 +6,8 @@
 //      recent token wins regardless of scheduling,
 //   2. resolves the matched tokens (winner -> its slot, marked in a bitmap of
 //      refreshed slots; others dropped), counts the winners and ranks the
-//      unmatched tokens in token order with one block scan,
+//      unmatched tokens in token order with one block scan (ranks stay in
+//      registers when the chunk fits one pass of the block),
 //   3. if the cache overflows, selects the e non-refreshed slots with the
 //      smallest (timestamp, slot) by a radix select on the timestamps
 //      (8-bit digits of ts - min(ts); one pass when timestamps span < 256)
@@ -69,17 +70,39 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     int32_t* ev = p.ev + static_cast<size_t>(h) * N;
     int32_t* dest = p.dest + static_cast<size_t>(h) * N;
 
+    // Token data are held in registers, TOK_ITEMS consecutive tokens per
+    // thread; with N <= TOK_CHUNK (one chunk) every phase reuses one load.
+    // Each phase issues all its loads before its first store, so the round
+    // trips overlap (the stores could alias the loaded arrays).
+    int bi[TOK_ITEMS], up[TOK_ITEMS];
+    float ci[TOK_ITEMS];
+    int tok_c0 = -1;
+    auto load_tok = [&](int c0) __attribute__((always_inline)) {
+        if (tok_c0 == c0) return;
+        tok_c0 = c0;
+        const int base = c0 + tid * TOK_ITEMS;
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k) bi[k] = (base + k < N) ? best[base + k] : -1;
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k) ci[k] = (base + k < N) ? cosv[base + k] : 0.f;
+    };
+
     // 1. claims.  Only the entries of matched slots are reset, so the claim
     //    array never needs a full clear.
     for (int w = tid; w < (n + 31) / 32; w += SEL_NT) refr[w] = 0u;
-    for (int i = tid; i < N; i += SEL_NT) {
-        const int b = best[i];
-        if (is_matched(b, cosv[i], n, p.tau)) claim[b] = -1;
+    for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
+        load_tok(c0);
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k)
+            if (is_matched(bi[k], ci[k], n, p.tau)) claim[bi[k]] = -1;
     }
     __syncthreads();
-    for (int i = tid; i < N; i += SEL_NT) {
-        const int b = best[i];
-        if (is_matched(b, cosv[i], n, p.tau)) atomicMax(&claim[b], i);
+    for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
+        load_tok(c0);
+        const int base = c0 + tid * TOK_ITEMS;
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k)
+            if (is_matched(bi[k], ci[k], n, p.tau)) atomicMax(&claim[bi[k]], base + k);
     }
     __syncthreads();
 
@@ -88,26 +111,21 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     //    unmatched in the low 16 bits, winners (= refreshed slots) above.
     int u = 0, refreshed = 0;
     for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
+        load_tok(c0);
         const int base = c0 + tid * TOK_ITEMS;
-        int bi[TOK_ITEMS];
-        float ci[TOK_ITEMS];
+        int cl[TOK_ITEMS];
 #pragma unroll
-        for (int k = 0; k < TOK_ITEMS; ++k) {
-            const int i = base + k;
-            bi[k] = (i < N) ? best[i] : -1;
-            ci[k] = (i < N) ? cosv[i] : 0.f;
-        }
-        uint32_t um = 0;
+        for (int k = 0; k < TOK_ITEMS; ++k)
+            cl[k] = (base + k < N && is_matched(bi[k], ci[k], n, p.tau)) ? claim[bi[k]] : -2;
         int local = 0, wins = 0;
 #pragma unroll
         for (int k = 0; k < TOK_ITEMS; ++k) {
             const int i = base + k;
             if (i >= N) continue;
-            if (!is_matched(bi[k], ci[k], n, p.tau)) {
-                um |= 1u << k;
+            if (cl[k] == -2) {
                 ++local;
             } else {
-                const bool win = claim[bi[k]] == i;
+                const bool win = cl[k] == i;
                 if (win) atomicOr(&refr[bi[k] >> 5], 1u << (bi[k] & 31));
                 wins += win;
                 dest[i] = win ? bi[k] : -1;
@@ -119,7 +137,8 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
 #pragma unroll
         for (int k = 0; k < TOK_ITEMS; ++k) {
             const int i = base + k;
-            if (i < N) upos[i] = ((um >> k) & 1) ? pos++ : -1;
+            up[k] = (i < N && cl[k] == -2) ? pos++ : -1;
+            if (i < N && N > TOK_CHUNK) upos[i] = up[k];
         }
         u += total & 0xFFFF;
         refreshed += total >> 16;
@@ -254,11 +273,19 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     __syncthreads();
 
     // 4. unmatched tokens: appended slots first, then the evicted ones
-    for (int i = tid; i < N; i += SEL_NT) {
-        const int k = upos[i];
-        if (k < 0) continue;
-        const int dst = (k < appended) ? n + k : ev[k - appended];
-        dest[i] = (dst >= 0 && dst < cap) ? dst : -1;
+    for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
+        const int base = c0 + tid * TOK_ITEMS;
+        if (N > TOK_CHUNK) {
+#pragma unroll
+            for (int k = 0; k < TOK_ITEMS; ++k) up[k] = (base + k < N) ? upos[base + k] : -1;
+        }
+        int dst[TOK_ITEMS];
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k)
+            dst[k] = up[k] < 0 ? -2 : (up[k] < appended ? n + up[k] : ev[up[k] - appended]);
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k)
+            if (dst[k] != -2) dest[base + k] = (dst[k] >= 0 && dst[k] < cap) ? dst[k] : -1;
     }
     if (p.evicted)
         for (int k = tid; k < N; k += SEL_NT)

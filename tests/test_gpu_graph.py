@@ -1,0 +1,117 @@
+"""The step orchestrator (two streams, HIP graph capture) on the GPU.
+
+* the two-stream step on the tiny workload agrees with the oracle's end-to-end
+  step exactly as the one-stream calls do (integers exact, floats within the
+  attention tolerances);
+* one-stream and two-stream eager steps give bit-identical results;
+* a captured step, replayed several times with eager work (cache restore,
+  output poisoning) and synchronisation between the replays, reproduces the
+  eager step bit for bit on every replay.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_autoregressive_amd as fa
+from oracle import ann_hash, attention_step
+from sparse_attention_autoregressive_amd.step import AttentionStep
+from tests.gpu_util import LSE_ABS, assert_attention_close, dev, host_ids, require_gpu
+from workloads import CONFIGS, make_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg, seed):
+    st = make_step(cfg, seed)
+    planes = torch.from_numpy(st.planes).cuda()
+    t = dict(q=dev(st.q, cfg.dtype), k_cur=dev(st.k_cur, cfg.dtype), v_cur=dev(st.v_cur, cfg.dtype),
+             kp=dev(st.kp, cfg.dtype), vp=dev(st.vp, cfg.dtype), planes=planes)
+    base = fa.KVCache.from_keys(dev(st.cache_k, cfg.dtype), dev(st.cache_v, cfg.dtype),
+                                torch.from_numpy(st.cache_ts).cuda(),
+                                torch.from_numpy(st.n_valid).cuda(), planes)
+    return st, t, base
+
+
+def _stepper(cfg, overlap):
+    return AttentionStep(cfg.H, cfg.Nq, cfg.d, cfg.cap, cfg.P, cfg.frame_len, cfg.L, cfg.tau,
+                         overlap=overlap)
+
+
+def _run(stepper, cache, t, step):
+    stepper(cache, t["q"], t["k_cur"], t["v_cur"], t["kp"], t["vp"], t["planes"], step)
+
+
+def _snapshot(s, cache):
+    torch.cuda.synchronize()
+    out = {k: v.clone() for k, v in (("o_sa", s.o_sa), ("lse", s.lse), ("o_ca", s.o_ca),
+                                      ("best", s.best), ("best_cos", s.best_cos), ("keep", s.keep),
+                                      ("keep_count", s.keep_count))}
+    for k, v in s.ids.items():
+        out["ids_" + k] = v.clone()
+    for k in ("k", "v", "ids", "ts", "n_valid", "knorm"):
+        out["cache_" + k] = getattr(cache, k).clone()
+    return out
+
+
+def _assert_same(a, b, what):
+    for k in a:
+        assert torch.equal(a[k], b[k]), f"{what}: {k} differs"
+
+
+@pytest.mark.parametrize("seed", [0, 2])
+def test_two_stream_step_matches_oracle(seed):
+    require_gpu()
+    cfg = CONFIGS["tiny_f32"]
+    st, t, base = _inputs(cfg, seed)
+    s = _stepper(cfg, overlap=True)
+    cache = base.clone()
+    _run(s, cache, t, st.step)
+    torch.cuda.synchronize()
+    cache_ids = np.stack([ann_hash(st.cache_k[h], st.planes[h])[0] for h in range(cfg.H)])
+    r = attention_step(st.q, st.k_cur, st.v_cur, st.cache_k, st.cache_v, cache_ids, st.cache_ts,
+                       st.n_valid, st.planes, st.kp, st.vp, cfg.frame_len, cfg.tau, st.step)
+    assert np.array_equal(host_ids(s.ids["q"])[0], r["q_ids"][0])
+    assert np.array_equal(host_ids(s.ids["k"])[0], r["kcur_ids"][0])
+    assert np.array_equal(host_ids(s.ids["p"])[0], r["kp_ids"][0])
+    assert_attention_close(s.o_sa, np.stack(r["o_sa"]), cfg.dtype, "annsa")
+    assert np.abs(s.lse.cpu().numpy() - np.stack(r["lse"])).max() <= LSE_ABS
+    assert np.array_equal(s.keep.cpu().numpy().astype(bool), np.stack(r["keep"]))
+    assert_attention_close(s.o_ca, np.stack(r["o_ca"]), cfg.dtype, "annca")
+    tc = r["tc"][0]
+    assert not tc["argmax_tie"].any() and not tc["thr_tie"].any()
+    assert np.array_equal(s.best[0].cpu().numpy(), tc["best"])
+    assert int(cache.n_valid[0]) == tc["n"]
+    assert np.array_equal(cache.k[0].cpu().numpy(), tc["cache"]["k"].astype(np.float32))
+    assert np.array_equal(host_ids(cache.ids)[0], tc["cache"]["ids"])
+    assert np.array_equal(cache.ts[0].cpu().numpy(), tc["cache"]["ts"])
+
+
+@pytest.mark.parametrize("name", ["single_bf16", "wan13_bf16"])
+def test_graph_replays_match_eager(name):
+    require_gpu()
+    cfg = CONFIGS[name]
+    st, t, base = _inputs(cfg, 0)
+
+    one = _stepper(cfg, overlap=False)
+    c1 = base.clone()
+    _run(one, c1, t, st.step)
+    ref = _snapshot(one, c1)
+
+    two = _stepper(cfg, overlap=True)
+    c2 = base.clone()
+    _run(two, c2, t, st.step)
+    _assert_same(ref, _snapshot(two, c2), "two streams vs one")
+
+    cg = base.clone()
+    g = two.graph(cg, t["q"], t["k_cur"], t["v_cur"], t["kp"], t["vp"], t["planes"], st.step)
+    for r in range(3):
+        # eager work between replays: restore the cache, poison every output
+        for k in ("k", "v", "ids", "ts", "n_valid", "knorm"):
+            getattr(cg, k).copy_(getattr(base, k))
+        for buf in (two.o_sa, two.lse, two.o_ca, two.best_cos):
+            buf.fill_(float("nan"))
+        for buf in (two.best, two.keep, two.keep_count, *two.ids.values()):
+            buf.fill_(-1 if buf.dtype != torch.uint8 else 255)
+        torch.cuda.synchronize()
+        g.replay()
+        _assert_same(ref, _snapshot(two, cg), f"replay {r}")

@@ -235,3 +235,39 @@ def test_rollout_stays_bit_identical():
         assert np.array_equal(got["k"][0], state["k"].astype(np.float32)), f"chunk {c}"
         assert np.array_equal(got["ts"][0], state["ts"]), f"chunk {c}"
         assert np.array_equal(got["ids"][0], state["ids"]), f"chunk {c}"
+
+
+@pytest.mark.parametrize("pool", [0, 50])
+def test_commit_bit_exact_multi_chunk(pool):
+    """N above one block pass of tokens (8192) and a cache above one pass of
+    slots (32768), full and partial heads; with ``pool`` = 50 thousands of
+    tokens claim the same few slots."""
+    require_gpu()
+    from workloads import commit_case
+    H, N, cap, d, P, tau, step = 2, 9000, 40000, 64, 5, 0.95, 1000
+    n_valid = np.array([cap, cap - 3000], np.int32)
+    c = commit_case(11 + pool, H, N, cap, d, n_valid, P, pool=pool)
+    cache = fa.KVCache(k=torch.from_numpy(c["cache_k"]).cuda(), v=torch.from_numpy(c["cache_v"]).cuda(),
+                       ids=dev_ids(c["cache_ids"]), ts=torch.from_numpy(c["cache_ts"]).cuda(),
+                       n_valid=torch.from_numpy(n_valid).cuda(),
+                       knorm=torch.zeros(H, cap, dtype=torch.float32, device="cuda"))
+    kc = torch.from_numpy(c["k_cur"]).cuda()
+    res = fa.tempcache_update(cache, kc, dev_ids(c["kcur_ids"]), kc,
+                              torch.from_numpy(c["v_cur"]).cuda(), dev_ids(c["kcur_ids"]), P, tau,
+                              step, best_in=torch.from_numpy(c["best"]).cuda(),
+                              cos_in=torch.from_numpy(c["cos"]).cuda())
+    got = cache_host(cache, "f32")
+    for h in range(H):
+        ref = tempcache_commit({"k": c["cache_k"][h], "v": c["cache_v"][h], "ids": c["cache_ids"][h],
+                                "ts": c["cache_ts"][h]}, int(n_valid[h]), c["k_cur"][h],
+                               c["v_cur"][h], c["kcur_ids"][h], c["best"][h],
+                               c["cos"][h].astype(np.float64), float(np.float32(tau)), step)
+        assert ref["counts"][4] > 0 and ref["counts"][1] > 0
+        assert np.array_equal(res["dest"][h].cpu().numpy(), ref["dest"]), f"dest head {h}"
+        assert np.array_equal(res["evicted"][h].cpu().numpy(), ref["evicted"]), f"evicted head {h}"
+        assert np.array_equal(res["counts"][h].cpu().numpy(), ref["counts"]), f"counts head {h}"
+        assert got["n"][h] == ref["n"]
+        assert np.array_equal(got["k"][h], ref["cache"]["k"]), f"k head {h}"
+        assert np.array_equal(got["v"][h], ref["cache"]["v"]), f"v head {h}"
+        assert np.array_equal(got["ids"][h], ref["cache"]["ids"]), f"ids head {h}"
+        assert np.array_equal(got["ts"][h], ref["cache"]["ts"]), f"ts head {h}"

@@ -47,3 +47,14 @@ def test_rollout_first_chunk_is_the_step_chunk():
     assert c1["step"] == cfg.Fc + cfg.Fq
     moved = np.abs(c1["k_cur"] - c0["k_cur"]).max(axis=2) > 1.0
     assert 0 < moved.mean() < 0.2          # ~5% of positions re-drawn
+
+
+def test_commit_case_is_seeded_and_in_range():
+    from workloads import commit_case
+    a = commit_case(3, 2, 100, 300, 64, [300, 200], 5, pool=10)
+    b = commit_case(3, 2, 100, 300, 64, [300, 200], 5, pool=10)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert a["cache_ids"].max() < 32 and a["kcur_ids"].max() < 32
+    assert (a["best"][1] < 10).all() and (a["best"] >= -1).all()
+    assert a["cos"].dtype == np.float32 and a["cache_k"].shape == (2, 300, 64)

@@ -288,3 +288,38 @@ def rollout_chunks(cfg: WorkloadConfig, n_chunks: int, seed: int = 0,
                 s.planes_and_prompt()   # keep the stream aligned with make_step
         yield dict(q=_round(cfg, np.stack(qs)), k_cur=_round(cfg, np.stack(ks)),
                    v_cur=_round(cfg, np.stack(vs)), step=cfg.Fc + c * cfg.Fq)
+
+
+def commit_case(seed: int, H: int, N: int, cap: int, d: int, n_valid, P: int,
+                match_frac: float = 0.5, pool: int = 0, ts_span: int = 64) -> dict:
+    """Random inputs for a cache commit taken on its own: a cache of ``cap``
+    slots per head (``n_valid[h]`` of them valid, timestamps drawn from
+    ``ts_span`` values so many are equal), a chunk of N tokens with bucket ids,
+    and per-token (best slot, cosine) pairs standing in for a search result.
+    About ``match_frac`` of the cosines lie in [0.95, 1], the rest in [-1, 0.9].
+    With ``pool`` > 0 the best slots are drawn from the first ``pool`` valid
+    slots so that many tokens name the same slot; some tokens get no slot (-1).
+    All float arrays are float32; ids are uint16 values below 2**P."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7919])))
+    n_valid = np.broadcast_to(np.asarray(n_valid, np.int32), (H,)).copy()
+    f = np.float32
+    out = dict(
+        cache_k=rng.standard_normal((H, cap, d)).astype(f),
+        cache_v=rng.standard_normal((H, cap, d)).astype(f),
+        cache_ids=rng.integers(0, 1 << P, (H, cap)).astype(np.uint16),
+        cache_ts=rng.integers(0, ts_span, (H, cap)).astype(np.int32),
+        k_cur=rng.standard_normal((H, N, d)).astype(f),
+        v_cur=rng.standard_normal((H, N, d)).astype(f),
+        kcur_ids=rng.integers(0, 1 << P, (H, N)).astype(np.uint16),
+        n_valid=n_valid)
+    best = np.empty((H, N), np.int32)
+    cos = np.empty((H, N), f)
+    for h in range(H):
+        n = int(n_valid[h])
+        hi = max(1, min(pool, n) if pool > 0 else n)
+        best[h] = rng.integers(0, hi, N) if n > 0 else -1
+        best[h][rng.random(N) < 0.02] = -1
+        m = rng.random(N) < match_frac
+        cos[h] = np.where(m, rng.uniform(0.95, 1.0, N), rng.uniform(-1.0, 0.9, N)).astype(f)
+    out["best"], out["cos"] = best, cos
+    return out
