@@ -31,7 +31,8 @@
  *    negative status means nothing was enqueued and nothing was modified.
  *    FASTAR_EHIP reports a HIP launch error after validation; outputs (and,
  *    for fastar_tempcache_update, the cache) are then undefined.
- *  - Sizes are int32; every tensor must hold fewer than 2^31 elements.
+ *  - Sizes are int32; every tensor must hold fewer than 2^31 elements, and
+ *    one head's rows of a K or V tensor fewer than 2^32 bytes (FASTAR_EINVAL).
  *  - Pointers to d-wide tensors (activations, cache K/V, planes) must be
  *    16-byte aligned (FASTAR_EINVAL otherwise); a tensor with no elements
  *    may be passed as NULL.

@@ -1,6 +1,6 @@
 // Gathered block attention on the matrix cores, three uses:
 //
-//  MODE_SA   AnnSA: one block per (head, bucket, 64-query slice).  Queries are
+//  MODE_SA   AnnSA: work items are (head, bucket, 64-query slice).  Queries are
 //            the bucket's current-chunk queries, keys the bucket's members of
 //            [cache slots ; current chunk] (FAST-AR blog, "3. AnnSA"; summary,
 //            "2. Core Components" C).  Softmax attention + log-sum-exp.  With
@@ -10,35 +10,38 @@
 //            dot products the attention computes anyway.
 //  MODE_CA   AnnCA: one block per (head, frame, 64 consecutive queries); keys
 //            are the frame's kept prompt tokens (blog, "2. AnnCA"; summary B).
-//  MODE_TOP1 TempCache search alone: the SA blocks over cached keys only, no
+//  MODE_TOP1 TempCache search alone: the SA items over cached keys only, no
 //            softmax; each query keeps its best cosine and slot.
 //
-// Layout of the work inside a block (256 threads = 4 waves, wave w owns the
-// block's queries 16w..16w+15; lane l serves query l%16 and "lane group"
+// Layout of the work on one 64-query item (256 threads = 4 waves, wave w owns
+// the item's queries 16w..16w+15; lane l serves query l%16 and "lane group"
 // g = l/16):
 //  * scores are computed transposed, S^T = K Q^T, so that MFMA's output layout
 //    (lane holds rows 4g..4g+3 of column l%16) gives every lane a single query
 //    and four keys per 16-key block: the row max / sum of the online softmax
 //    then need only two cross-lane steps (lanes l, l^16, l^32, l^48), and the
 //    probabilities are already laid out as the B operand of O^T = V^T P^T.
-//  * K and V tiles of 64 rows sit row-major in LDS (16-byte, bank-conflict-free
-//    stores; rows padded by 16 bytes).  K fragments (A operand of S^T) are 16
-//    contiguous bytes per lane.  The bf16 V^T fragments come from gfx950's
-//    LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane
-//    i receives element i%4 of the 8-byte chunks addressed by lanes
-//    4k + i/4 (k = 0..3), so when lane j points at V[key0 + j/4][d0 + 4(j%4)]
-//    lane i gets dim d0+i of keys key0..key0+3.  Two such reads give lane group
-//    g the keys {4g..4g+3, 16+4g..16+4g+3} of a 32-key group -- exactly the
-//    keys its probabilities cover in the B operand.  For fp32 (16x16x4 MFMA)
-//    V is read row-major.
+//  * K and V tiles of 64 rows sit row-major in LDS (16-byte stores, rows
+//    padded).  K fragments (A operand of S^T) are 16 contiguous bytes per lane.
+//    The bf16 V^T fragments come from gfx950's LDS transpose read
+//    (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+//    i%4 of the 8-byte chunks addressed by lanes 4k + i/4 (k = 0..3), so when
+//    lane j points at V[key0 + j/4][d0 + 4(j%4)] lane i gets dim d0+i of keys
+//    key0..key0+3.  Two such reads give lane group g the keys
+//    {4g..4g+3, 16+4g..16+4g+3} of a 32-key group -- exactly the keys its
+//    probabilities cover in the B operand.  For fp32 (16x16x4 MFMA) V is read
+//    row-major.
 //  * The item's key indices are staged in LDS; K/V rows are gathered with
 //    16-byte loads (16 lanes cover one 256-byte bf16 row) into two register
-//    stages, so two tiles are in flight while the third is computed on.
-//  * SA/TOP1 blocks read their work item (query slice, key range) from a table
-//    the bucket sort writes, longest key lists first, with heads fastest in the
-//    launch order, so the largest buckets never form the tail of the launch.
+//    stages, so two tiles are in flight while a third is computed on.
 //  * The search uses the cached keys' norms kept in the cache, so a cosine is
-//    one product per (query, key): dot * (1/|q|) * (1/|k|).
+//    one product per (query, key): dot * (1/|k|), times 1/|q| at the end.
+//
+// Every use launches one block per item, heads fastest in the launch order;
+// SA / TOP1 items come from a table the bucket sort writes with the longest
+// key lists first, so the largest buckets never form the tail of the launch.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -66,78 +69,95 @@ struct Tile {
     static constexpr int CPR = D / EPC;                 // chunks per row
     static constexpr int UNITS = (KT / 4) * CPR;        // (4-row quad, chunk) units
     static constexpr int UPT = (UNITS + 255) / 256;     // units per thread
-    static constexpr int STR = D + EPC;                 // padded row (elements), K and V
+    // Padded rows.  K rows step 4 banks (mod 64), so the 16 rows one K-fragment
+    // read touches cover all 64 banks.  bf16 V rows step 8 banks, so the 4 rows
+    // x 4 8-byte columns of a transpose read (and the 4 lane groups, 4 rows
+    // apart) fall on distinct banks.
+    static constexpr int STRK = D + EPC;
+    static constexpr int STRV = BF ? D + 2 * EPC : D + EPC;
+    static constexpr int ROWB = D * static_cast<int>(sizeof(T));   // bytes per global row
+    static constexpr int NDB = D / 16;                  // 16-wide output blocks
+    static constexpr int NKS = BF ? D / 32 : D / 4;     // k-steps of S^T
 };
 
-}  // namespace
-
-template <typename T, int D, int MODE, bool SEARCH, typename OT>
-__device__ __forceinline__ void attn_body(const AttnParams& p) {
+// The pieces every kernel below is built from.
+template <typename T, int D, int MODE, bool SEARCH>
+struct Blk {
     using TL = Tile<T, D, MODE>;
-    constexpr bool BF = TL::BF;
-    constexpr bool HAS_V = TL::HAS_V;
-    constexpr int UPT = TL::UPT, CPR = TL::CPR, EPC = TL::EPC;
-    constexpr int STR = TL::STR;
-    constexpr int NDB = D / 16;                          // 16-wide output blocks
-    constexpr int NKS = BF ? D / 32 : D / 4;             // k-steps of S^T
+    static constexpr bool BF = TL::BF, HAS_V = TL::HAS_V;
+    static constexpr int UPT = TL::UPT, CPR = TL::CPR, EPC = TL::EPC;
+    static constexpr int STRK = TL::STRK, STRV = TL::STRV, ROWB = TL::ROWB;
+    static constexpr int NDB = TL::NDB, NKS = TL::NKS;
 
-    __shared__ __align__(16) T Ks[KT * STR];
-    __shared__ __align__(16) T Vs[HAS_V ? KT * STR : 1];
-    __shared__ __align__(16) int kslot[SEARCH ? KT : 4];
-    __shared__ __align__(16) float kinv[SEARCH ? KT : 4];
-    __shared__ int kidx[KCH];
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 4, c16 = lane & 15;
-
-    // ---------------------------------------------------------------- work
-    int h, q_count, nk, na = 0, qbase = 0;
-    const int32_t* qlist = nullptr;
-    const int32_t* klist;
-    if constexpr (MODE == MODE_CA) {
-        h = blockIdx.z;
-        const int f = blockIdx.y, c = blockIdx.x;
-        qbase = f * p.frame_len + c * kQTile;
-        q_count = min(kQTile, p.frame_len - c * kQTile);
-        nk = p.ca_cnt[h * p.F + f];
-        klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
-    } else {
-        h = blockIdx.x;                          // heads fastest: the longest items
-        const int item = blockIdx.y;            // of every head dispatch first
-        const int4 it = p.items[static_cast<size_t>(h) * p.max_items + item];
-        if (it.y <= 0) return;
-        q_count = it.y;
-        qlist = p.qperm + static_cast<size_t>(h) * p.qperm_stride + it.x;
-        nk = it.w;
-        klist = p.kperm + static_cast<size_t>(h) * p.kperm_stride + it.z;
-        na = clamp_n(p.n_valid, h, p.cap);
-    }
-
-    const int ql = w * 16 + c16;
-    const bool qvalid = ql < q_count;
-    const bool wave_active = w * 16 < q_count;
-    int qrow = 0;
-    if (qvalid) qrow = (MODE == MODE_CA) ? qbase + ql : qlist[ql];
-
-    const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
-    const T* ka = static_cast<const T*>(p.ka) + static_cast<size_t>(h) * p.a_rows * D;
-    const T* va = HAS_V ? static_cast<const T*>(p.va) + static_cast<size_t>(h) * p.a_rows * D : nullptr;
-    const T* kb = p.kb ? static_cast<const T*>(p.kb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
-    const T* vb = (HAS_V && p.vb) ? static_cast<const T*>(p.vb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
-    const float* kn_h = SEARCH ? p.knorm + static_cast<size_t>(h) * p.a_rows : nullptr;
-
-    // ---------------------------------------------------------------- Q fragments
     // B operand of S^T: lane holds Q[query l%16][k-slice of group g].
-    bf16x8_t qf_b[BF ? NKS : 1];
-    float qf_f[BF ? 1 : NKS];
-    float qsq = 0.f;
-    if constexpr (BF) {
+    struct QF {
+        bf16x8_t b[BF ? NKS : 1];
+        float f[BF ? 1 : NKS];
+        float inv;                  // 1/|q| (search only)
+    };
+    // One 64-key tile between its global gather and its LDS store.  (Its key
+    // slots, for the search, wait in an LDS array of the stage, ``slots``.)
+    struct Stage {
+        u32x4 k[UPT][4];
+        u32x4 v[HAS_V ? UPT : 1][4];
+        float kn[SEARCH ? UPT : 1][4];
+        int* slots;
+    };
+    // Running state of one query (per lane; the four lane groups of a query
+    // hold disjoint keys and are merged at the end).
+    struct Acc {
+        f32x4 o[HAS_V ? NDB : 1];
+        float m, l;                 // softmax: raw-score max, sum
+        float bc;                   // search: best dot/|k|
+        int bs;                     //         and its slot
+        __device__ __forceinline__ void reset() {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            u32x4 r = {0u, 0u, 0u, 0u};
-            if (qvalid) r = *reinterpret_cast<const u32x4*>(qh + static_cast<size_t>(qrow) * D + ks * 32 + 8 * g);
-            qf_b[ks] = __builtin_bit_cast(bf16x8_t, r);
-            if constexpr (SEARCH) {
+            for (int i = 0; i < (HAS_V ? NDB : 1); ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m = kNegInf;
+            l = 0.f;
+            bc = kNegInf;
+            bs = 0x7FFFFFFF;
+        }
+    };
+    struct Smem {
+        T* Ks;
+        T* Vs;
+        int* kslot;
+        float* kinv;
+    };
+    // Where one head's keys live: index j < na is row j of (ka, va), else row
+    // j - na of (kb, vb).  kn holds the cached keys' norms.
+    struct Src {
+        const T* ka;
+        const T* va;
+        const T* kb;
+        const T* vb;
+        const float* kn;
+        int na;
+    };
+
+    // Issues the loads of a query row's fragments (``row`` null: a padding lane).
+    static __device__ __forceinline__ void load_q(QF& q, const T* row, int g) {
+        if constexpr (BF) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                u32x4 r = {0u, 0u, 0u, 0u};
+                if (row) r = *reinterpret_cast<const u32x4*>(row + ks * 32 + 8 * g);
+                q.b[ks] = __builtin_bit_cast(bf16x8_t, r);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) q.f[ks] = row ? reinterpret_cast<const float*>(row)[ks * 4 + g] : 0.f;
+        }
+    }
+    // 1/|q| from the fragments (all lanes of the wave take part).
+    static __device__ __forceinline__ void finish_q(QF& q) {
+        if constexpr (!SEARCH) return;
+        float qsq = 0.f;
+        if constexpr (BF) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const u32x4 r = __builtin_bit_cast(u32x4, q.b[ks]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float lo = __uint_as_float(r[i] << 16), hi = __uint_as_float(r[i] & 0xFFFF0000u);
@@ -145,45 +165,33 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
                     qsq = __builtin_fmaf(hi, hi, qsq);
                 }
             }
-        }
-    } else {
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qf_f[ks] = qvalid ? reinterpret_cast<const float*>(qh)[static_cast<size_t>(qrow) * D + ks * 4 + g] : 0.f;
-            if constexpr (SEARCH) qsq = __builtin_fmaf(qf_f[ks], qf_f[ks], qsq);
+            for (int ks = 0; ks < NKS; ++ks) qsq = __builtin_fmaf(q.f[ks], q.f[ks], qsq);
         }
-    }
-    float qinv = 0.f;
-    if constexpr (SEARCH) {
         qsq += __shfl_xor(qsq, 16);
         qsq += __shfl_xor(qsq, 32);
         const float qn = __builtin_sqrtf(qsq);
-        qinv = qn > 0.f ? 1.f / qn : 0.f;
+        q.inv = qn > 0.f ? 1.f / qn : 0.f;
     }
 
-    // ---------------------------------------------------------------- key indices
-    // The item's key list is staged in LDS (KCH entries at a time, coalesced),
-    // so the gathers below never wait on a dependent index load.  Entries past
-    // the end repeat the last key, so every lane of a partial tile still
-    // gathers a valid row (its score is masked).
-    auto stage_idx = [&](int first) __attribute__((always_inline)) {
-        for (int i = tid; i < KCH; i += 256) {
-            const int r = first + i;
-            kidx[i] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+    // Gathers tile ``tile`` of the key list staged in ``kidx``.  Rows of a tile
+    // come from the cache part or the current chunk; the key list holds cached
+    // keys first, so at most one tile per item mixes the two, and every other
+    // tile gathers from one base pointer held in scalar registers with a
+    // 32-bit byte offset per row.
+    static __device__ __forceinline__ void load_tile(Stage& S, const int* kidx, int tile, const Src& sr,
+                                                     int tid) {
+        int jf = 0, jl = 0;
+        if constexpr (MODE == MODE_SA) {
+            jf = __builtin_amdgcn_readfirstlane(kidx[(tile * KT) % KCH]);
+            jl = __builtin_amdgcn_readfirstlane(kidx[(tile * KT + KT - 1) % KCH]);
         }
-    };
-
-    // ---------------------------------------------------------------- tile loads
-    // A stage holds one 64-key tile in registers between its global gather and
-    // its LDS store; two stages alternate so that two tiles are in flight
-    // while a third is computed on.
-    struct Stage {
-        u32x4 k[UPT][4];
-        u32x4 v[HAS_V ? UPT : 1][4];
-        int slot[SEARCH ? UPT : 1][4];
-        float kn[SEARCH ? UPT : 1][4];
-    };
-    auto load_kv = [&](Stage& S, int tile) __attribute__((always_inline)) {
+        const bool all_a = MODE != MODE_SA || jl < sr.na;        // scalar
+        const bool all_b = MODE == MODE_SA && jf >= sr.na;
+        const char* kbase = reinterpret_cast<const char*>(all_a ? sr.ka : sr.kb);
+        const char* vbase = HAS_V ? reinterpret_cast<const char*>(all_a ? sr.va : sr.vb) : nullptr;
+        const int sub = all_a ? 0 : sr.na;
 #pragma unroll
         for (int k = 0; k < UPT; ++k) {
             const int u = tid + k * 256;
@@ -194,19 +202,49 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
             for (int e = 0; e < 4; ++e) {
                 const int r = tile * KT + 4 * (u / CPR) + e;
                 const int j = kidx[r % KCH];
-                const bool from_a = (MODE == MODE_CA || MODE == MODE_TOP1) || j < na;
-                const size_t row = from_a ? static_cast<size_t>(j) : static_cast<size_t>(j - na);
-                S.k[k][e] = *reinterpret_cast<const u32x4*>((from_a ? ka : kb) + row * D + chunk * EPC);
-                if constexpr (HAS_V)
-                    S.v[k][e] = *reinterpret_cast<const u32x4*>((from_a ? va : vb) + row * D + chunk * EPC);
+                if (all_a || all_b) {
+                    const uint32_t off = static_cast<uint32_t>(j - sub) * ROWB + chunk * 16;
+                    S.k[k][e] = *reinterpret_cast<const u32x4*>(kbase + off);
+                    if constexpr (HAS_V) S.v[k][e] = *reinterpret_cast<const u32x4*>(vbase + off);
+                } else {
+                    const bool from_a = j < sr.na;
+                    const uint32_t off = static_cast<uint32_t>(from_a ? j : j - sr.na) * ROWB + chunk * 16;
+                    S.k[k][e] = *reinterpret_cast<const u32x4*>(
+                        reinterpret_cast<const char*>(from_a ? sr.ka : sr.kb) + off);
+                    if constexpr (HAS_V)
+                        S.v[k][e] = *reinterpret_cast<const u32x4*>(
+                            reinterpret_cast<const char*>(from_a ? sr.va : sr.vb) + off);
+                }
                 if constexpr (SEARCH) {
-                    S.slot[k][e] = j;
-                    S.kn[k][e] = (chunk == 0 && from_a) ? kn_h[j] : 0.f;
+                    // every lane of a row loads the same norm and writes the
+                    // same slot (no branches in the load sequence); current-
+                    // chunk keys read a clamped cached index, masked at the store
+                    if (MODE != MODE_SA || sr.na > 0)                  // uniform
+                        S.kn[k][e] = sr.kn[MODE != MODE_SA || j < sr.na ? j : sr.na - 1];
+                    else
+                        S.kn[k][e] = 0.f;
+                    S.slots[4 * (u / CPR) + e] = j;
                 }
             }
         }
-    };
-    auto store_lds = [&](const Stage& S) __attribute__((always_inline)) {
+    }
+
+    // Gives a stage that receives no tile a defined value without memory
+    // traffic, so the stage's registers are written on every path (a stage
+    // kept from an earlier step on one path makes the compiler copy it, and a
+    // copy waits for every load in flight).
+    static __device__ __forceinline__ void clear_stage(Stage& S) {
+#pragma unroll
+        for (int k = 0; k < UPT; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                S.k[k][e] = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (HAS_V) S.v[k][e] = u32x4{0u, 0u, 0u, 0u};
+                if constexpr (SEARCH) S.kn[k][e] = 0.f;
+            }
+    }
+
+    static __device__ __forceinline__ void store_tile(const Stage& S, const Smem& sm, int na, int tid) {
 #pragma unroll
         for (int k = 0; k < UPT; ++k) {
             const int u = tid + k * 256;
@@ -216,74 +254,76 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 4 * quad + e;
-                *reinterpret_cast<u32x4*>(&Ks[row * STR + chunk * EPC]) = S.k[k][e];
+                *reinterpret_cast<u32x4*>(&sm.Ks[row * STRK + chunk * EPC]) = S.k[k][e];
                 if constexpr (HAS_V)
-                    *reinterpret_cast<u32x4*>(&Vs[row * STR + chunk * EPC]) = S.v[k][e];
+                    *reinterpret_cast<u32x4*>(&sm.Vs[row * STRV + chunk * EPC]) = S.v[k][e];
                 if constexpr (SEARCH) {
-                    if (chunk == 0) {
-                        kslot[row] = S.slot[k][e];
-                        kinv[row] = S.kn[k][e] > 0.f ? 1.f / S.kn[k][e] : 0.f;
-                    }
+                    const int j = S.slots[row];
+                    const float kn = S.kn[k][e];
+                    sm.kslot[row] = j;
+                    sm.kinv[row] = (MODE == MODE_TOP1 || j < na) && kn > 0.f ? __builtin_amdgcn_rcpf(kn) : 0.f;
                 }
             }
         }
-    };
+    }
 
-    // ---------------------------------------------------------------- state
-    f32x4 o[HAS_V ? NDB : 1];
-#pragma unroll
-    for (int i = 0; i < (HAS_V ? NDB : 1); ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = kNegInf, l_run = 0.f;             // softmax state: raw-score max, sum
-    float best_c = kNegInf;
-    int best_s = 0x7FFFFFFF;                        // search state
-
-    const int nt = (nk + KT - 1) / KT;
-
-    auto compute = [&](int t) __attribute__((always_inline)) {
+    // One 64-key tile (keys kbase.. of an item with nk keys, the first na of
+    // the head's index space cached) against the wave's 16 queries.
+    static __device__ __forceinline__ void compute_tile(Acc& a, const QF& q, const Smem& sm, int kbase,
+                                                        int nk, int na, float scale_log2, int g, int c16) {
         // ---- S^T = K Q^T for the 4 key blocks of the tile
         f32x4 s[4];
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
             s[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const T* krow = &Ks[(kb4 * 16 + c16) * STR];
+            const T* krow = &sm.Ks[(kb4 * 16 + c16) * STRK];
             if constexpr (BF) {
-                bf16x8_t a[NKS];
+                bf16x8_t af[NKS];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    a[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 32 + 8 * g);
+                    af[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 32 + 8 * g);
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qf_b[ks], s[kb4], 0, 0, 0);
+                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], q.b[ks], s[kb4], 0, 0, 0);
             } else {
-                float a[NKS];
+                float af[NKS];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) a[ks] = reinterpret_cast<const float*>(krow)[ks * 4 + g];
+                for (int ks = 0; ks < NKS; ++ks) af[ks] = reinterpret_cast<const float*>(krow)[ks * 4 + g];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[ks], qf_f[ks], s[kb4], 0, 0, 0);
+                    s[kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ks], q.f[ks], s[kb4], 0, 0, 0);
             }
         }
-        const int kbase = t * KT;
-        const bool full = kbase + KT <= nk;                    // wave-uniform
+        const bool full = kbase + KT <= nk;                    // uniform
 
         // ---- TempCache search over this tile's cached keys (sorted first, so a
-        // tile whose first key is current holds no cached key)
+        // tile whose first key is current holds no cached key).  The running
+        // best compares dot * (1/|k|); 1/|q| > 0 is applied once at the end.
         if constexpr (SEARCH) {
-            if (MODE == MODE_TOP1 || kslot[0] < na) {
+            if (MODE == MODE_TOP1 || sm.kslot[0] < na) {
+                // uniform: a full tile of cached keys needs no per-key masks
+                const bool clean = full && (MODE == MODE_TOP1 || sm.kslot[KT - 1] < na);
+                auto scan = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-                for (int kb4 = 0; kb4 < 4; ++kb4) {
-                    const int4 sl = *reinterpret_cast<const int4*>(&kslot[kb4 * 16 + 4 * g]);
-                    const float4 iv = *reinterpret_cast<const float4*>(&kinv[kb4 * 16 + 4 * g]);
-                    const int slv[4] = {sl.x, sl.y, sl.z, sl.w};
-                    const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
+                    for (int kb4 = 0; kb4 < 4; ++kb4) {
+                        const int4 sl = *reinterpret_cast<const int4*>(&sm.kslot[kb4 * 16 + 4 * g]);
+                        const float4 iv = *reinterpret_cast<const float4*>(&sm.kinv[kb4 * 16 + 4 * g]);
+                        const int slv[4] = {sl.x, sl.y, sl.z, sl.w};
+                        const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int kk = kb4 * 16 + 4 * g + r;
-                        const bool ok = (MODE == MODE_TOP1 || slv[r] < na) && (full || kbase + kk < nk);
-                        const float cs = s[kb4][r] * qinv * ivv[r];
-                        if (ok && cs > best_c) { best_c = cs; best_s = slv[r]; }
+                        for (int r = 0; r < 4; ++r) {
+                            const float cs = s[kb4][r] * ivv[r];
+                            bool ok = cs > a.bc;
+                            if constexpr (decltype(masked)::value)
+                                ok = ok && (MODE == MODE_TOP1 || slv[r] < na) &&
+                                     kbase + kb4 * 16 + 4 * g + r < nk;
+                            a.bc = ok ? cs : a.bc;
+                            a.bs = ok ? slv[r] : a.bs;
+                        }
                     }
-                }
+                };
+                if (clean) scan(std::false_type{});
+                else scan(std::true_type{});
             }
         }
 
@@ -304,8 +344,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
                 tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb4][0], s[kb4][1]), fmaxf(s[kb4][2], s[kb4][3])));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float m_new = fmaxf(m_run, tmax);
-            const float c = p.scale_log2;
+            const float m_new = fmaxf(a.m, tmax);
+            const float c = scale_log2;
             const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
             float psum = 0.f;
 #pragma unroll
@@ -317,14 +357,14 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
                     psum += e;
                 }
             }
-            if (__ballot(m_new > m_run) != 0) {                 // some lane's max grew
-                const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, c, -mc));
-                l_run *= alpha;
+            if (__ballot(m_new > a.m) != 0) {                   // some lane's max grew
+                const float alpha = (a.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(a.m, c, -mc));
+                a.l *= alpha;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+                for (int db = 0; db < NDB; ++db) a.o[db] *= alpha;
             }
-            l_run += psum;
-            m_run = m_new;
+            a.l += psum;
+            a.m = m_new;
 
             // ---- O^T += V^T P^T
             if constexpr (BF) {
@@ -337,18 +377,18 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
                         pb[4 + r] = static_cast<__bf16>(s[2 * kg + 1][r]);
                     }
                     // lane j of group g addresses V[kg*32 + 4g + j/4][db*16 + 4(j%4)]
-                    const T* vb0 = &Vs[(kg * 32 + 4 * g + (c16 >> 2)) * STR + 4 * (c16 & 3)];
+                    const T* vb0 = &sm.Vs[(kg * 32 + 4 * g + (c16 >> 2)) * STRV + 4 * (c16 & 3)];
                     v4i16 lo[NDB], hi[NDB];
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
                         lo[db] = lds_read_tr(vb0 + db * 16);
-                        hi[db] = lds_read_tr(vb0 + 16 * STR + db * 16);
+                        hi[db] = lds_read_tr(vb0 + 16 * STRV + db * 16);
                     }
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
-                        const bf16x8_t a = __builtin_bit_cast(
+                        const bf16x8_t av = __builtin_bit_cast(
                             bf16x8_t, __builtin_shufflevector(lo[db], hi[db], 0, 1, 2, 3, 4, 5, 6, 7));
-                        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[db], 0, 0, 0);
+                        a.o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, a.o[db], 0, 0, 0);
                     }
                 }
             } else {
@@ -356,88 +396,174 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
                 for (int kb4 = 0; kb4 < 4; ++kb4) {
 #pragma unroll
                     for (int st = 0; st < 4; ++st) {
-                        const float* vrow = reinterpret_cast<const float*>(&Vs[(kb4 * 16 + 4 * g + st) * STR]);
+                        const float* vrow = reinterpret_cast<const float*>(&sm.Vs[(kb4 * 16 + 4 * g + st) * STRV]);
 #pragma unroll
                         for (int db = 0; db < NDB; ++db)
-                            o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[db * 16 + c16], s[kb4][st], o[db], 0, 0, 0);
+                            a.o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[db * 16 + c16], s[kb4][st], a.o[db], 0, 0, 0);
                     }
                 }
             }
         }
+    }
+
+    // Merges the four lane groups of each query and writes its results
+    // (all lanes of the wave take part in the merge).  Row pointers are those
+    // of the lane's query; ``qvalid`` false for padding lanes.
+    template <typename OT>
+    static __device__ __forceinline__ void finish(Acc& a, const QF& q, bool qvalid, int g, OT* orow,
+                                                  float* lse, int32_t* best, float* bcos, float scale_log2) {
+        if constexpr (SEARCH) {
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float oc = __shfl_xor(a.bc, off);
+                const int os = __shfl_xor(a.bs, off);
+                if (oc > a.bc || (oc == a.bc && os < a.bs)) { a.bc = oc; a.bs = os; }
+            }
+            if (qvalid && g == 0) {
+                const bool found = a.bs != 0x7FFFFFFF;
+                *best = found ? a.bs : -1;
+                *bcos = found ? a.bc * q.inv : kNegInf;
+            }
+        }
+        if constexpr (HAS_V) {
+            float l_tot = a.l + __shfl_xor(a.l, 16);
+            l_tot += __shfl_xor(l_tot, 32);
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            if (qvalid) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const f32x4 v = a.o[db] * inv;
+                    if constexpr (sizeof(OT) == 4) {
+                        *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g) = v;
+                    } else {
+                        const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+                        const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+                        *reinterpret_cast<uint2*>(orow + db * 16 + 4 * g) = make_uint2(lo, hi);
+                    }
+                }
+                if (MODE == MODE_SA && lse && g == 0)
+                    *lse = l_tot > 0.f ? (a.m * scale_log2 + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f
+                                       : kNegInf;
+            }
+        }
+    }
+
+    static __device__ __forceinline__ Src src_of(const AttnParams& p, int h) {
+        Src s;
+        s.ka = static_cast<const T*>(p.ka) + static_cast<size_t>(h) * p.a_rows * D;
+        s.va = HAS_V ? static_cast<const T*>(p.va) + static_cast<size_t>(h) * p.a_rows * D : nullptr;
+        s.kb = p.kb ? static_cast<const T*>(p.kb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
+        s.vb = (HAS_V && p.vb) ? static_cast<const T*>(p.vb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
+        s.kn = SEARCH ? p.knorm + static_cast<size_t>(h) * p.a_rows : nullptr;
+        s.na = 0;
+        return s;
+    }
+};
+
+}  // namespace
+
+template <typename T, int D, int MODE, bool SEARCH, typename OT>
+__device__ __forceinline__ void attn_body(const AttnParams& p) {
+    using B = Blk<T, D, MODE, SEARCH>;
+    __shared__ __align__(16) T Ks[KT * B::STRK];
+    __shared__ __align__(16) T Vs[B::HAS_V ? KT * B::STRV : 1];
+    __shared__ __align__(16) int kslot[SEARCH ? KT : 4];
+    __shared__ __align__(16) float kinv[SEARCH ? KT : 4];
+    __shared__ int sslot[2][SEARCH ? KT : 1];
+    __shared__ int kidx[KCH];
+    const typename B::Smem sm{Ks, Vs, kslot, kinv};
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+
+    int h, q_count, nk, qbase = 0;
+    const int32_t* qlist = nullptr;
+    const int32_t* klist;
+    if constexpr (MODE == MODE_CA) {
+        h = blockIdx.z;
+        const int f = blockIdx.y, c = blockIdx.x;
+        qbase = f * p.frame_len + c * kQTile;
+        q_count = min(kQTile, p.frame_len - c * kQTile);
+        nk = p.ca_cnt[h * p.F + f];
+        klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
+    } else {
+        h = blockIdx.x;                          // heads fastest: the longest items
+        const int item = blockIdx.y;            // of every head dispatch first
+        const int4 it = p.items[static_cast<size_t>(h) * p.max_items + item];
+        if (it.y <= 0) return;
+        q_count = it.y;
+        qlist = p.qperm + static_cast<size_t>(h) * p.qperm_stride + it.x;
+        nk = it.w;
+        klist = p.kperm + static_cast<size_t>(h) * p.kperm_stride + it.z;
+    }
+    typename B::Src sr = B::src_of(p, h);
+    if constexpr (MODE == MODE_SA) sr.na = clamp_n(p.n_valid, h, p.cap);
+
+    const int ql = w * 16 + c16;
+    const bool qvalid = ql < q_count;
+    const bool wave_active = w * 16 < q_count;
+    int qrow = 0;
+    if (qvalid) qrow = (MODE == MODE_CA) ? qbase + ql : qlist[ql];
+    const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
+
+    typename B::QF qf;
+    B::load_q(qf, qvalid ? qh + static_cast<size_t>(qrow) * D : nullptr, g);
+    B::finish_q(qf);
+
+    // The key list is staged in LDS (KCH entries at a time, coalesced), so the
+    // gathers never wait on a dependent index load.  Entries past the end
+    // repeat the last key, so every lane of a partial tile still gathers a
+    // valid row (its score is masked).
+    auto stage_idx = [&](int first) __attribute__((always_inline)) {
+        for (int i = tid; i < KCH; i += 256) {
+            const int r = first + i;
+            kidx[i] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+        }
     };
+
+    typename B::Acc acc;
+    acc.reset();
+    const int nt = (nk + KT - 1) / KT;
 
     // One pipeline step on tile t held in stage S: store it, refill S with
     // tile t+2, compute on tile t.  Tile t+1 stays in flight in the other stage.
-    auto step = [&](Stage& S, int t) __attribute__((always_inline)) {
+    auto step = [&](typename B::Stage& S, int t) __attribute__((always_inline)) {
         if (t >= nt) return;                              // block-uniform
         __syncthreads();
-        store_lds(S);
+        B::store_tile(S, sm, sr.na, tid);
         __syncthreads();
         if (t + 2 < nt) {
             if (((t + 2) * KT) % KCH == 0) {        // next index chunk
                 stage_idx((t + 2) * KT);
                 __syncthreads();
             }
-            load_kv(S, t + 2);
+            B::load_tile(S, kidx, t + 2, sr, tid);
         }
-        if (wave_active) compute(t);
+        if (wave_active) B::compute_tile(acc, qf, sm, t * KT, nk, sr.na, p.scale_log2, g, c16);
     };
 
-    Stage A, B;
+    typename B::Stage A, Bs;
+    A.slots = sslot[0];
+    Bs.slots = sslot[1];
     stage_idx(0);
     __syncthreads();
-    if (nt > 0) load_kv(A, 0);
-    if (nt > 1) load_kv(B, 1);
+    if (nt > 0) B::load_tile(A, kidx, 0, sr, tid);
+    if (nt > 1) B::load_tile(Bs, kidx, 1, sr, tid);
     // Each stage is named in exactly one place of a fixed pair of steps, so
     // both keep fixed registers.  A step past the last tile does nothing.
 #pragma unroll 1
     for (int t = 0; t < nt; t += 2) {
         step(A, t);
-        step(B, t + 1);
+        step(Bs, t + 1);
     }
 
-    // ---------------------------------------------------------------- epilogue
-    if constexpr (SEARCH) {
-#pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float oc = __shfl_xor(best_c, off);
-            const int os = __shfl_xor(best_s, off);
-            if (oc > best_c || (oc == best_c && os < best_s)) { best_c = oc; best_s = os; }
-        }
-        if (qvalid && g == 0) {
-            const bool found = best_s != 0x7FFFFFFF;
-            const size_t qi = static_cast<size_t>(h) * p.Nq + qrow;
-            p.best[qi] = found ? best_s : -1;
-            p.bcos[qi] = found ? best_c : kNegInf;
-        }
-    }
-    if constexpr (HAS_V) {
-        float l_tot = l_run + __shfl_xor(l_run, 16);
-        l_tot += __shfl_xor(l_tot, 32);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qvalid) {
-            OT* orow = static_cast<OT*>(p.out) + (static_cast<size_t>(h) * p.Nq + qrow) * D;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const f32x4 v = o[db] * inv;
-                if constexpr (sizeof(OT) == 4) {
-                    *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g) = v;
-                } else {
-                    const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-                    const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-                    *reinterpret_cast<uint2*>(orow + db * 16 + 4 * g) = make_uint2(lo, hi);
-                }
-            }
-            if (MODE == MODE_SA && p.lse && g == 0)
-                p.lse[static_cast<size_t>(h) * p.Nq + qrow] =
-                    l_tot > 0.f ? (m_run * p.scale_log2 + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : kNegInf;
-        }
-    }
+    const size_t qi = static_cast<size_t>(h) * p.Nq + qrow;
+    B::template finish<OT>(acc, qf, qvalid, g, static_cast<OT*>(p.out) + qi * D, p.lse ? p.lse + qi : nullptr,
+                           p.best ? p.best + qi : nullptr, p.bcos ? p.bcos + qi : nullptr, p.scale_log2);
 }
 
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
-// registers per lane, i.e. 2 waves per SIMD (two blocks per CU, each with two
-// 32 KB tiles in flight).
+// registers per lane, i.e. 2 waves per SIMD.
 template <typename T, int D, int MODE, bool SEARCH, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kv_kernel(const AttnParams p) {
@@ -491,9 +617,11 @@ void attn_dispatch(bool bf16, int d, bool out_bf16, int H, const AttnParams& p, 
 
 }  // namespace
 
-hipError_t launch_attn(int mode, bool bf16, int d, bool out_bf16, int H, const AttnParams& p,
+hipError_t launch_attn(int mode, bool bf16, int d, bool out_bf16, int H, const AttnParams& params,
                        hipStream_t s) {
     if (H == 0) return hipSuccess;
+    AttnParams p = params;
+    p.H = H;
     switch (mode) {
         case MODE_SA:
             timer_begin("annsa_attn", s);

@@ -149,6 +149,10 @@ bool tensor_ok(const void* p, long long elems) {
 }
 bool small_ok(const void* p, long long elems) { return elems <= 0 || p != nullptr; }
 bool fits_i32(long long v) { return v >= 0 && v < (1ll << 31); }
+// One head's rows of a K/V tensor are addressed with 32-bit byte offsets.
+bool head_bytes_ok(long long rows, int d, int dtype) {
+    return rows * d * (dtype == FASTAR_BF16 ? 2 : 4) < (1ll << 32);
+}
 
 fastar_status hip_status(hipError_t e) { return e == hipSuccess ? FASTAR_OK : FASTAR_EHIP; }
 
@@ -250,6 +254,7 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
     const int cap = cache ? cache->cap : 0;
     if (!fits_i32(HQ * d) || !fits_i32(HC * d) || !fits_i32(static_cast<long long>(H) * (cap + static_cast<long long>(Ncur))))
         return FASTAR_EINVAL;
+    if (!head_bytes_ok(cap, d, dtype) || !head_bytes_ok(Ncur, d, dtype)) return FASTAR_EINVAL;
     if (!tensor_ok(q, HQ * d) || !small_ok(q_ids, HQ) || !tensor_ok(out, HQ * d)) return FASTAR_EINVAL;
     if (!tensor_ok(k_cur, HC * d) || !tensor_ok(v_cur, HC * d) || !small_ok(kcur_ids, HC))
         return FASTAR_EINVAL;
@@ -325,6 +330,7 @@ fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t
     const int F = Nq / frame_len;
     if (!fits_i32(HQ * d) || !fits_i32(HL * d) || !fits_i32(static_cast<long long>(H) * F * L))
         return FASTAR_EINVAL;
+    if (!head_bytes_ok(L, d, dtype)) return FASTAR_EINVAL;
     if (!tensor_ok(q, HQ * d) || !small_ok(q_ids, HQ) || !tensor_ok(out, HQ * d)) return FASTAR_EINVAL;
     if (!tensor_ok(kp, HL * d) || !tensor_ok(vp, HL * d) || !small_ok(kp_ids, HL)) return FASTAR_EINVAL;
     const size_t need = fastar_annca_workspace(H, Nq, frame_len, L, P);
@@ -380,7 +386,7 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     if ((best_in == nullptr) != (cos_in == nullptr)) return FASTAR_EINVAL;
     if (N > cap) return FASTAR_ECAPACITY;
     const long long HN = static_cast<long long>(H) * N;
-    if (!fits_i32(HN * d)) return FASTAR_EINVAL;
+    if (!fits_i32(HN * d) || !head_bytes_ok(cap, d, dtype)) return FASTAR_EINVAL;
     if (!tensor_ok(q, HN * d) || !small_ok(q_ids, HN) || !tensor_ok(k_cur, HN * d) ||
         !tensor_ok(v_cur, HN * d) || !small_ok(kcur_ids, HN))
         return FASTAR_EINVAL;

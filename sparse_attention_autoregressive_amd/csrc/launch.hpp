@@ -67,6 +67,7 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
 enum AttnMode { MODE_SA = 0, MODE_CA = 1, MODE_TOP1 = 2 };
 
 struct AttnParams {
+    int H = 0;                      // heads (set by launch_attn)
     const void* q = nullptr;        // [H][Nq][D]
     int Nq = 0;
     // key/value rows: source a (cache slots, or prompt rows), source b (current chunk)
@@ -85,7 +86,7 @@ struct AttnParams {
     const int32_t* kperm = nullptr;
     int kperm_stride = 0;
     const int4* items = nullptr;
-    int max_items = 0;              // grid.x for SA/TOP1 (a multiple of 8)
+    int max_items = 0;              // work-list entries per head (a multiple of 8)
     // prompt selection (CA)
     const int32_t* ca_idx = nullptr;
     const int32_t* ca_cnt = nullptr;
