@@ -74,31 +74,33 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
+// Inclusive prefix sum over the 64 lanes of a wave (V = int or uint32_t;
+// unsigned sums wrap, which packed counters rely on).
+template <typename V = int>
+__device__ __forceinline__ V wave_inclusive_scan(V v) {
     const int l = lane_id();
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
-        int t = __shfl_up(v, off, kWave);
+        V t = __shfl_up(v, off, kWave);
         if (l >= off) v += t;
     }
     return v;
 }
 
 // Exclusive prefix sum over a block of NT threads; ``total`` receives the sum.
-// ``smem`` needs NT/64 ints.  Contains two __syncthreads.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* smem, int& total) {
+// ``smem`` needs NT/64 elements.  Contains two __syncthreads.
+template <int NT, typename V = int>
+__device__ __forceinline__ V block_exclusive_scan(V v, V* smem, V& total) {
     constexpr int NW = NT / kWave;
     const int w = threadIdx.x / kWave;
-    int inc = wave_inclusive_scan(v);
+    V inc = wave_inclusive_scan<V>(v);
     if (lane_id() == kWave - 1) smem[w] = inc;
     __syncthreads();
-    int before = 0, sum = 0;
+    V before = 0, sum = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        int s = smem[i];
-        before += (i < w) ? s : 0;
+        V s = smem[i];
+        before += (i < w) ? s : V(0);
         sum += s;
     }
     __syncthreads();

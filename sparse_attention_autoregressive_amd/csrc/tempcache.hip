@@ -30,22 +30,33 @@ constexpr int TOK_ITEMS = 8;                      // tokens per thread per chunk
 constexpr int TOK_CHUNK = SEL_NT * TOK_ITEMS;     // < 65536: packed counters fit 16 bits
 constexpr int SLOT_ITEMS = 32;                    // slots per thread per chunk (one bitmap word)
 constexpr int SLOT_CHUNK = SEL_NT * SLOT_ITEMS;
+// Caches up to this many slots keep the select's claim table and refreshed
+// bitmap in LDS (4 bytes + 1 bit per slot: 132 KiB at the limit).
+constexpr int kLdsClaimSlots = 32768;
 
 __device__ __forceinline__ uint32_t ts_key(int32_t t) { return static_cast<uint32_t>(t) ^ 0x80000000u; }
 
-__device__ __forceinline__ uint32_t block_min_max(uint32_t v, bool want_max, uint32_t* red) {
+// Block-wide min and max of one value per thread, reduced together.
+__device__ __forceinline__ void block_min_max(uint32_t& mn, uint32_t& mx, uint32_t* red) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t o = __shfl_xor(v, off);
-        v = want_max ? (o > v ? o : v) : (o < v ? o : v);
+        const uint32_t a = __shfl_xor(mn, off), b = __shfl_xor(mx, off);
+        mn = a < mn ? a : mn;
+        mx = b > mx ? b : mx;
     }
     const int w = threadIdx.x / kWave;
-    if (lane_id() == 0) red[w] = v;
+    if (lane_id() == 0) {
+        red[2 * w] = mn;
+        red[2 * w + 1] = mx;
+    }
     __syncthreads();
-    uint32_t r = red[0];
-    for (int i = 1; i < SEL_NT / kWave; ++i) r = want_max ? (red[i] > r ? red[i] : r) : (red[i] < r ? red[i] : r);
+    mn = red[0];
+    mx = red[1];
+    for (int i = 1; i < SEL_NT / kWave; ++i) {
+        mn = red[2 * i] < mn ? red[2 * i] : mn;
+        mx = red[2 * i + 1] > mx ? red[2 * i + 1] : mx;
+    }
     __syncthreads();
-    return r;
 }
 
 __device__ __forceinline__ bool is_matched(int b, float c, int n, float tau) {
@@ -53,18 +64,30 @@ __device__ __forceinline__ bool is_matched(int b, float c, int n, float tau) {
 }
 }  // namespace
 
+// LDSC: the claim table (one int per slot) and the refreshed bitmap live in
+// LDS (dynamic, cap <= kLdsClaimSlots); otherwise in the workspace.
+template <bool LDSC>
 __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams p) {
+    extern __shared__ int dyn_lds[];
     __shared__ int smem[SEL_NT / kWave];
-    __shared__ uint32_t red[SEL_NT / kWave];
+    __shared__ uint32_t red[2 * (SEL_NT / kWave)];
     __shared__ int hist[256];
     __shared__ int bcast[2];
     const int h = blockIdx.x, tid = threadIdx.x;
     const int cap = p.cap, N = p.N;
     const int n = clamp_n(p.n_valid, h, cap);
+    const int words = (cap + 31) / 32;
     const int32_t* best = p.best + static_cast<size_t>(h) * N;
     const float* cosv = p.cosv + static_cast<size_t>(h) * N;
-    int32_t* claim = p.claim + static_cast<size_t>(h) * cap;
-    uint32_t* refr = p.refreshed + static_cast<size_t>(h) * ((cap + 31) / 32);
+    int32_t* claim;
+    uint32_t* refr;
+    if constexpr (LDSC) {
+        claim = dyn_lds;
+        refr = reinterpret_cast<uint32_t*>(dyn_lds + cap);
+    } else {
+        claim = p.claim + static_cast<size_t>(h) * cap;
+        refr = p.refreshed + static_cast<size_t>(h) * words;
+    }
     const int32_t* ts = p.ts + static_cast<size_t>(h) * cap;
     int32_t* upos = p.upos + static_cast<size_t>(h) * N;
     int32_t* ev = p.ev + static_cast<size_t>(h) * N;
@@ -184,8 +207,8 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
                     lmax = key[k] > lmax ? key[k] : lmax;
                 }
         }
-        const uint32_t kmin = block_min_max(lmin, false, red);
-        const uint32_t kmax = block_min_max(lmax, true, red);
+        uint32_t kmin = lmin, kmax = lmax;
+        block_min_max(kmin, kmax, red);
         uint32_t prefix = 0;
         int need = e;
         if (kmax != kmin) {
@@ -233,41 +256,40 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
                 __syncthreads();
             }
         }
+        // The e selected slots are every candidate below tstar plus the first
+        // ``need`` equal to it, in slot order; one packed scan (below | equal
+        // << 16, unsigned: a field's chunk total reaches at most 32768) gives
+        // every thread its first
+        // list position: (# below before it) + min(# equal before it, need).
         const uint32_t tstar = kmin + prefix;
-        int carry_eq = 0, carry_sel = 0;
+        int carry_lt = 0, carry_eq = 0;
         for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
             load(c0);
             uint32_t ltf = 0, eqf = 0;
-            int eqc = 0;
 #pragma unroll
             for (int k = 0; k < SLOT_ITEMS; ++k) {
                 if ((cand >> k) & 1) {
                     if (key[k] < tstar) ltf |= 1u << k;
-                    else if (key[k] == tstar) { eqf |= 1u << k; ++eqc; }
+                    else if (key[k] == tstar) eqf |= 1u << k;
                 }
             }
-            int eqtot;
-            int er = carry_eq + block_exclusive_scan<SEL_NT>(eqc, smem, eqtot);
-            uint32_t self = 0;
-            int selc = 0;
+            const uint32_t ltc = __popc(ltf), eqc = __popc(eqf);
+            uint32_t tot;
+            const uint32_t ex = block_exclusive_scan<SEL_NT, uint32_t>(
+                ltc | (eqc << 16), reinterpret_cast<uint32_t*>(smem), tot);
+            int er = carry_eq + static_cast<int>(ex >> 16);
+            int pos = carry_lt + static_cast<int>(ex & 0xFFFFu) + min(er, need);
 #pragma unroll
             for (int k = 0; k < SLOT_ITEMS; ++k) {
-                if ((ltf >> k) & 1) { self |= 1u << k; ++selc; }
-                else if ((eqf >> k) & 1) {
-                    if (er < need) { self |= 1u << k; ++selc; }
-                    ++er;
-                }
-            }
-            int seltot;
-            int pos = carry_sel + block_exclusive_scan<SEL_NT>(selc, smem, seltot);
-#pragma unroll
-            for (int k = 0; k < SLOT_ITEMS; ++k)
-                if ((self >> k) & 1) {
+                bool sel = (ltf >> k) & 1;
+                if ((eqf >> k) & 1) sel = er++ < need;
+                if (sel) {
                     if (pos < e) ev[pos] = sbase + k;     // e <= N: never past the row
                     ++pos;
                 }
-            carry_eq += eqtot;
-            carry_sel += seltot;
+            }
+            carry_lt += static_cast<int>(tot & 0xFFFFu);
+            carry_eq += static_cast<int>(tot >> 16);
         }
     }
     __syncthreads();
@@ -306,7 +328,12 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
 hipError_t launch_tc_select(const TcSelectParams& p, hipStream_t s) {
     if (p.H == 0) return hipSuccess;
     timer_begin("tempcache_select", s);
-    hipLaunchKernelGGL(tc_select_kernel, dim3(p.H), dim3(SEL_NT), 0, s, p);
+    if (p.cap <= kLdsClaimSlots) {
+        const size_t bytes = (static_cast<size_t>(p.cap) + (p.cap + 31) / 32) * 4;
+        hipLaunchKernelGGL(tc_select_kernel<true>, dim3(p.H), dim3(SEL_NT), bytes, s, p);
+    } else {
+        hipLaunchKernelGGL(tc_select_kernel<false>, dim3(p.H), dim3(SEL_NT), 0, s, p);
+    }
     timer_end(s);
     return hipGetLastError();
 }
