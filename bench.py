@@ -53,7 +53,7 @@ ANNSA_TRAFFIC_BYTES = None
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="wan13_bf16")
     ap.add_argument("--seed", type=int, default=0)

@@ -45,6 +45,10 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#ifndef CA_WAVES
+#define CA_WAVES 8
+#endif
+
 namespace fastar {
 
 namespace {
@@ -61,14 +65,15 @@ __device__ __forceinline__ v4i16 lds_read_tr(const void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const_cast<void*>(p)));
 }
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, int NT>
 struct Tile {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr bool HAS_V = MODE != MODE_TOP1;
     static constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
     static constexpr int CPR = D / EPC;                 // chunks per row
-    static constexpr int UNITS = (KT / 4) * CPR;        // (4-row quad, chunk) units
-    static constexpr int UPT = (UNITS + 255) / 256;     // units per thread
+    // Thread u of NT gathers chunk u % CPR of the E rows (u / CPR) * E + e.
+    static constexpr int E = KT * CPR / NT;
+    static_assert(E >= 1 && KT * CPR % NT == 0, "tile split");
     // Padded rows.  K rows step 4 banks (mod 64), so the 16 rows one K-fragment
     // read touches cover all 64 banks.  bf16 V rows step 8 banks, so the 4 rows
     // x 4 8-byte columns of a transpose read (and the 4 lane groups, 4 rows
@@ -81,11 +86,11 @@ struct Tile {
 };
 
 // The pieces every kernel below is built from.
-template <typename T, int D, int MODE, bool SEARCH>
+template <typename T, int D, int MODE, bool SEARCH, int NT>
 struct Blk {
-    using TL = Tile<T, D, MODE>;
+    using TL = Tile<T, D, MODE, NT>;
     static constexpr bool BF = TL::BF, HAS_V = TL::HAS_V;
-    static constexpr int UPT = TL::UPT, CPR = TL::CPR, EPC = TL::EPC;
+    static constexpr int E = TL::E, CPR = TL::CPR, EPC = TL::EPC;
     static constexpr int STRK = TL::STRK, STRV = TL::STRV, ROWB = TL::ROWB;
     static constexpr int NDB = TL::NDB, NKS = TL::NKS;
 
@@ -98,9 +103,9 @@ struct Blk {
     // One 64-key tile between its global gather and its LDS store.  (Its key
     // slots, for the search, wait in an LDS array of the stage, ``slots``.)
     struct Stage {
-        u32x4 k[UPT][4];
-        u32x4 v[HAS_V ? UPT : 1][4];
-        float kn[SEARCH ? UPT : 1][4];
+        u32x4 k[E];
+        u32x4 v[HAS_V ? E : 1];
+        float kn[SEARCH ? E : 1];
         int* slots;
     };
     // Running state of one query (per lane; the four lane groups of a query
@@ -192,77 +197,49 @@ struct Blk {
         const char* kbase = reinterpret_cast<const char*>(all_a ? sr.ka : sr.kb);
         const char* vbase = HAS_V ? reinterpret_cast<const char*>(all_a ? sr.va : sr.vb) : nullptr;
         const int sub = all_a ? 0 : sr.na;
+        const int chunk = tid % CPR, rb = tid / CPR;
 #pragma unroll
-        for (int k = 0; k < UPT; ++k) {
-            const int u = tid + k * 256;
-            if constexpr (TL::UNITS % 256 != 0)             // (bf16, d=64: half the threads)
-                if (u >= TL::UNITS) continue;
-            const int chunk = u % CPR;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = tile * KT + 4 * (u / CPR) + e;
-                const int j = kidx[r % KCH];
-                if (all_a || all_b) {
-                    const uint32_t off = static_cast<uint32_t>(j - sub) * ROWB + chunk * 16;
-                    S.k[k][e] = *reinterpret_cast<const u32x4*>(kbase + off);
-                    if constexpr (HAS_V) S.v[k][e] = *reinterpret_cast<const u32x4*>(vbase + off);
-                } else {
-                    const bool from_a = j < sr.na;
-                    const uint32_t off = static_cast<uint32_t>(from_a ? j : j - sr.na) * ROWB + chunk * 16;
-                    S.k[k][e] = *reinterpret_cast<const u32x4*>(
-                        reinterpret_cast<const char*>(from_a ? sr.ka : sr.kb) + off);
-                    if constexpr (HAS_V)
-                        S.v[k][e] = *reinterpret_cast<const u32x4*>(
-                            reinterpret_cast<const char*>(from_a ? sr.va : sr.vb) + off);
-                }
-                if constexpr (SEARCH) {
-                    // every lane of a row loads the same norm and writes the
-                    // same slot (no branches in the load sequence); current-
-                    // chunk keys read a clamped cached index, masked at the store
-                    if (MODE != MODE_SA || sr.na > 0)                  // uniform
-                        S.kn[k][e] = sr.kn[MODE != MODE_SA || j < sr.na ? j : sr.na - 1];
-                    else
-                        S.kn[k][e] = 0.f;
-                    S.slots[4 * (u / CPR) + e] = j;
-                }
+        for (int e = 0; e < E; ++e) {
+            const int row = rb * E + e;
+            const int j = kidx[(tile * KT + row) % KCH];
+            if (all_a || all_b) {
+                const uint32_t off = static_cast<uint32_t>(j - sub) * ROWB + chunk * 16;
+                S.k[e] = *reinterpret_cast<const u32x4*>(kbase + off);
+                if constexpr (HAS_V) S.v[e] = *reinterpret_cast<const u32x4*>(vbase + off);
+            } else {
+                const bool from_a = j < sr.na;
+                const uint32_t off = static_cast<uint32_t>(from_a ? j : j - sr.na) * ROWB + chunk * 16;
+                S.k[e] = *reinterpret_cast<const u32x4*>(
+                    reinterpret_cast<const char*>(from_a ? sr.ka : sr.kb) + off);
+                if constexpr (HAS_V)
+                    S.v[e] = *reinterpret_cast<const u32x4*>(
+                        reinterpret_cast<const char*>(from_a ? sr.va : sr.vb) + off);
+            }
+            if constexpr (SEARCH) {
+                // every lane of a row loads the same norm and writes the
+                // same slot (no branches in the load sequence); current-
+                // chunk keys read a clamped cached index, masked at the store
+                if (MODE != MODE_SA || sr.na > 0)                  // uniform
+                    S.kn[e] = sr.kn[MODE != MODE_SA || j < sr.na ? j : sr.na - 1];
+                else
+                    S.kn[e] = 0.f;
+                S.slots[row] = j;
             }
         }
     }
 
-    // Gives a stage that receives no tile a defined value without memory
-    // traffic, so the stage's registers are written on every path (a stage
-    // kept from an earlier step on one path makes the compiler copy it, and a
-    // copy waits for every load in flight).
-    static __device__ __forceinline__ void clear_stage(Stage& S) {
-#pragma unroll
-        for (int k = 0; k < UPT; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                S.k[k][e] = u32x4{0u, 0u, 0u, 0u};
-                if constexpr (HAS_V) S.v[k][e] = u32x4{0u, 0u, 0u, 0u};
-                if constexpr (SEARCH) S.kn[k][e] = 0.f;
-            }
-    }
-
     static __device__ __forceinline__ void store_tile(const Stage& S, const Smem& sm, int na, int tid) {
+        const int chunk = tid % CPR, rb = tid / CPR;
 #pragma unroll
-        for (int k = 0; k < UPT; ++k) {
-            const int u = tid + k * 256;
-            if constexpr (TL::UNITS % 256 != 0)
-                if (u >= TL::UNITS) continue;
-            const int quad = u / CPR, chunk = u % CPR;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 4 * quad + e;
-                *reinterpret_cast<u32x4*>(&sm.Ks[row * STRK + chunk * EPC]) = S.k[k][e];
-                if constexpr (HAS_V)
-                    *reinterpret_cast<u32x4*>(&sm.Vs[row * STRV + chunk * EPC]) = S.v[k][e];
-                if constexpr (SEARCH) {
-                    const int j = S.slots[row];
-                    const float kn = S.kn[k][e];
-                    sm.kslot[row] = j;
-                    sm.kinv[row] = (MODE == MODE_TOP1 || j < na) && kn > 0.f ? __builtin_amdgcn_rcpf(kn) : 0.f;
-                }
+        for (int e = 0; e < E; ++e) {
+            const int row = rb * E + e;
+            *reinterpret_cast<u32x4*>(&sm.Ks[row * STRK + chunk * EPC]) = S.k[e];
+            if constexpr (HAS_V) *reinterpret_cast<u32x4*>(&sm.Vs[row * STRV + chunk * EPC]) = S.v[e];
+            if constexpr (SEARCH) {
+                const int j = S.slots[row];
+                const float kn = S.kn[e];
+                sm.kslot[row] = j;
+                sm.kinv[row] = (MODE == MODE_TOP1 || j < na) && kn > 0.f ? __builtin_amdgcn_rcpf(kn) : 0.f;
             }
         }
     }
@@ -462,9 +439,13 @@ struct Blk {
 
 }  // namespace
 
-template <typename T, int D, int MODE, bool SEARCH, typename OT>
+// NW waves per block; the item is 16*NW queries (SA / TOP1: the 64-query
+// slices of the bucket sort, NW = 4).
+template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
-    using B = Blk<T, D, MODE, SEARCH>;
+    constexpr int NT = 64 * NW, QT = 16 * NW;
+    static_assert(MODE == MODE_CA || QT == kQTile, "SA / TOP1 items are kQTile queries");
+    using B = Blk<T, D, MODE, SEARCH, NT>;
     __shared__ __align__(16) T Ks[KT * B::STRK];
     __shared__ __align__(16) T Vs[B::HAS_V ? KT * B::STRV : 1];
     __shared__ __align__(16) int kslot[SEARCH ? KT : 4];
@@ -482,8 +463,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     if constexpr (MODE == MODE_CA) {
         h = blockIdx.z;
         const int f = blockIdx.y, c = blockIdx.x;
-        qbase = f * p.frame_len + c * kQTile;
-        q_count = min(kQTile, p.frame_len - c * kQTile);
+        qbase = f * p.frame_len + c * QT;
+        q_count = min(QT, p.frame_len - c * QT);
         nk = p.ca_cnt[h * p.F + f];
         klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
     } else {
@@ -515,7 +496,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     // repeat the last key, so every lane of a partial tile still gathers a
     // valid row (its score is masked).
     auto stage_idx = [&](int first) __attribute__((always_inline)) {
-        for (int i = tid; i < KCH; i += 256) {
+        for (int i = tid; i < KCH; i += NT) {
             const int r = first + i;
             kidx[i] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
         }
@@ -564,25 +545,29 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
 // registers per lane, i.e. 2 waves per SIMD.
-template <typename T, int D, int MODE, bool SEARCH, typename OT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kv_kernel(const AttnParams p) {
-    attn_body<T, D, MODE, SEARCH, OT>(p);
+    attn_body<T, D, MODE, SEARCH, OT, NW>(p);
 }
 
 // The search alone stages K only and runs at the occupancy its registers allow.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_top1_kernel(const AttnParams p) {
-    attn_body<T, D, MODE_TOP1, true, float>(p);
+    attn_body<T, D, MODE_TOP1, true, float, 4>(p);
 }
 
 namespace {
+
+// AnnCA blocks take 16*kCaWaves consecutive queries of a frame: every K/V
+// tile gathered into LDS serves that many queries.
+constexpr int kCaWaves = CA_WAVES;
 
 template <typename T, int D, int MODE, typename OT>
 void attn_go(int H, const AttnParams& p, hipStream_t s) {
     dim3 grid;
     if constexpr (MODE == MODE_CA)
-        grid = dim3((p.frame_len + kQTile - 1) / kQTile, p.F, H);
+        grid = dim3((p.frame_len + 16 * kCaWaves - 1) / (16 * kCaWaves), p.F, H);
     else
         grid = dim3(H, p.max_items);
     if (grid.x == 0 || grid.y == 0 || grid.z == 0) return;
@@ -590,11 +575,12 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
         hipLaunchKernelGGL((attn_top1_kernel<T, D>), grid, dim3(256), 0, s, p);
     } else if constexpr (MODE == MODE_SA) {
         if (p.best)
-            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, true, OT>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, true, OT, 4>), grid, dim3(256), 0, s, p);
         else
-            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, false, OT>), grid, dim3(256), 0, s, p);
+            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, false, OT, 4>), grid, dim3(256), 0, s, p);
     } else {
-        hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_CA, false, OT>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_CA, false, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0,
+                           s, p);
     }
 }
 
