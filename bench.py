@@ -44,10 +44,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 
-# rocprofv3 FETCH_SIZE+WRITE_SIZE of the AnnSA attention kernel at this
-# workload, scaled by the copy-kernel calibration; None until measured for the
-# current kernel.
-ANNSA_TRAFFIC_BYTES = None
+# HBM bytes per launch of the AnnSA attention kernel at the wan13_bf16 workload:
+# rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (KiB per dispatch), the
+# factors being what a 512 MiB device copy reads on the same counters
+# (profiles/step_wan13_hbm_traffic.md).  Valid for the kernel build the
+# counters were taken on; None for other workloads.
+ANNSA_TRAFFIC_BYTES = {"wan13_bf16": 329.6e6}
 
 
 def parse():
@@ -61,11 +63,31 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-oracle sample budget (heads are added until it is spent)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 5 times (the plain copy whose "
+                         "FETCH_SIZE / WRITE_SIZE counters scale the traffic figures), then exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """Five device-to-device copies of ``mib`` MiB: a kernel whose HBM traffic
+    is known exactly (reads = writes = mib MiB per copy)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda").mul_(1.0001)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 5}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(every head is independent; see the sharding note in DESIGN.md)", file=sys.stderr)
@@ -170,7 +192,8 @@ def main():
     roofline = {"kernel": "annsa_attn", "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                "traffic": ANNSA_TRAFFIC_BYTES, "algorithmic_bytes": sa_bytes,
+                "traffic": ANNSA_TRAFFIC_BYTES.get(args.config) if args.out_dtype == "f32" else None,
+                "algorithmic_bytes": sa_bytes,
                 "mean_ms": attn_ms}
 
     line = {
