@@ -63,6 +63,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-oracle sample budget (heads are added until it is spent)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mfma-sweep", action="store_true",
+                    help="only time the bucket-attention kernel at P = 0, 1, 2, 3 and the "
+                         "config's P (one JSON line: TFLOP/s on kept pairs vs the bf16 MFMA peak)")
+    ap.add_argument("--rollout", type=int, default=0, metavar="CHUNKS",
+                    help="only run a rollout of CHUNKS chunks: per-chunk step latency and cache "
+                         "size, next to a dense uncapped-cache baseline (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (the plain copy whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the traffic figures), then exit")
@@ -87,6 +93,12 @@ def main():
     args = parse()
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
+        return
+    if args.mfma_sweep:
+        mfma_sweep(args)
+        return
+    if args.rollout > 0:
+        rollout(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -124,7 +136,7 @@ def main():
     two, one = mk(True), mk(False)
     ids = two.ids
     # every step commits into its own pristine copy of the cache
-    n_copies = 3 * args.warmup + 4 * args.steps
+    n_copies = 3 * args.warmup + 6 * args.steps
     caches = [base.clone() for _ in range(n_copies)]
     it = iter(caches)
     run = lambda s, c: s(c, q, kc, vc, kp, vp, planes, st.step)
@@ -157,6 +169,27 @@ def main():
     ms_per_step = timed(lambda i: run(two, next(it)))
     ms_one_stream = timed(lambda i: run(one, next(it)))
     cnt = two.keep_count
+
+    # ---- latency distribution: K two-stream steps, each between its own
+    # events; warm (back to back) and cold (a 512 MiB write before each step
+    # evicts the 256 MB last-level cache; the write is outside the events)
+    def per_step(cold):
+        main = torch.cuda.current_stream(dev)
+        flush = torch.empty(512 << 18, dtype=torch.float32, device=dev) if cold else None
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            if cold:
+                flush.fill_(1.0)
+            a.record(main)
+            run(two, next(it))
+            b.record(main)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        pick = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
+        return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9)}
+    latency = {"warm": per_step(False), "cold": per_step(True)}
 
     # ---- K eager one-stream steps again with per-kernel HIP events: every
     # kernel runs alone, so its mean duration is its own
@@ -196,6 +229,33 @@ def main():
                 "algorithmic_bytes": sa_bytes,
                 "mean_ms": attn_ms}
 
+    # algorithmic bytes of the other kernels, per step (all launches of the kernel)
+    F = Nq // cfg.frame_len
+    probe = base.clone()                      # one more commit, for the written-token count
+    res = fa.tempcache_update(probe, q, ids["q"], kc, vc, ids["k"], P, cfg.tau, st.step,
+                              best_in=two.best, cos_in=two.best_cos)
+    written = float((res["dest"] >= 0).sum())
+    ca_keys = float(cnt.double().sum())
+    step_bytes = {
+        "ann_hash": (2 * Nq + cfg.L) * H * (d * esz + 2),
+        "sort": 8.0 * H * (2 * Nq + cap),                       # ids read twice, perm written
+        "annca_select": H * (Nq + F * cfg.L) * 2.0 + H * F * cfg.L * 5.0,
+        "annca_attn": Nq * H * (d * esz + d * osz) + ca_keys * 2 * d * esz,
+        "tempcache_select": H * Nq * 12.0 + H * cap * 4.0,      # best, cos in, dest out; ts
+        "tempcache_scatter": written * (4 * d * esz + 10) + H * Nq * 4.0,
+        "annsa_attn": sa_bytes,
+    }
+    step_ms = {
+        "ann_hash": kernel_ms.get("ann_hash", 0) * kernel_launches.get("ann_hash", 0),
+        "sort": sum(kernel_ms.get(k, 0) for k in ("sort_hist", "sort_scan", "sort_scatter")),
+        "annca_select": kernel_ms.get("annca_select"), "annca_attn": kernel_ms.get("annca_attn"),
+        "tempcache_select": kernel_ms.get("tempcache_select"),
+        "tempcache_scatter": kernel_ms.get("tempcache_scatter"), "annsa_attn": attn_ms,
+    }
+    kernel_gbs = {k: {"bytes": step_bytes[k], "GB/s": step_bytes[k] / (step_ms[k] * 1e-3) / 1e9,
+                      "frac_hbm_peak": step_bytes[k] / (step_ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                  for k in step_bytes if step_ms.get(k)}
+
     line = {
         "metric": "attention step latency (ms) + achieved bf16 TFLOP/s on kept pairs, Wan-1.3B chunk",
         "value": value_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -208,7 +268,9 @@ def main():
                                f"P={P} ({B} buckets), prompt {cfg.L}, tau={cfg.tau}",
                    "out_dtype": args.out_dtype, "seed": args.seed, "streams": 2},
         "roofline": roofline,
+        "latency_ms": latency,
         "kernel_ms": kernel_ms, "kernel_launches_per_step": kernel_launches,
+        "kernel_gbs": kernel_gbs,
         "kept_pairs": {"annsa": sa_pairs, "annca": ca_pairs,
                        "annsa_frac_of_dense": sa_pairs / (H * Nq * (cap + Nq))},
     }
@@ -216,6 +278,157 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds, line)
     print(json.dumps(line), flush=True)
+
+
+def _device(cfg, dev):
+    import numpy as np
+    import torch
+    from workloads import f32_to_bf16_bits
+
+    def to_dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    return to_dev
+
+
+def _pairs(qi, ki, B):
+    import torch
+    H = qi.shape[0]
+    nqb = torch.stack([torch.bincount(qi[h].long() & 0xFFFF, minlength=B) for h in range(H)]).double()
+    nkb = torch.stack([torch.bincount(ki[h].long() & 0xFFFF, minlength=B) for h in range(H)]).double()
+    return float((nqb * nkb).sum())
+
+
+def mfma_sweep(args):
+    """Bucket attention (AnnSA without the search) at fewer buckets: P = 0 is
+    dense attention over [cache ; chunk], where the kernel's arithmetic
+    intensity is far above the ridge, so its TFLOP/s on kept pairs against the
+    dense bf16 MFMA peak measures the matrix-core side of the kernel."""
+    import torch
+    import sparse_attention_autoregressive_amd as fa
+    from workloads import CONFIGS, make_step
+    cfg0 = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    lib = fa.load()
+    rows = []
+    for P in sorted({0, 1, 2, 3, cfg0.P}):
+        cfg = cfg0.replace(P=P)
+        st = make_step(cfg, args.seed)
+        to_dev = _device(cfg, dev)
+        H, Nq, d, cap = cfg.H, cfg.Nq, cfg.d, cfg.cap
+        q, kc, vc = to_dev(st.q), to_dev(st.k_cur), to_dev(st.v_cur)
+        planes = torch.from_numpy(st.planes).to(dev)
+        cache = fa.KVCache.from_keys(to_dev(st.cache_k), to_dev(st.cache_v),
+                                     torch.from_numpy(st.cache_ts).to(dev),
+                                     torch.from_numpy(st.n_valid).to(dev), planes)
+        qi, ki = fa.ann_hash(q, planes), fa.ann_hash(kc, planes)
+        ws = torch.empty(lib.fastar_annsa_workspace(H, Nq, cap, Nq, P), dtype=torch.uint8, device=dev)
+        out = torch.empty(H, Nq, d, dtype=torch.float32, device=dev)
+        lse = torch.empty(H, Nq, dtype=torch.float32, device=dev)
+        call = lambda: fa.annsa_forward(q, qi, kc, vc, ki, P, cache=cache, out=out, lse=lse, ws=ws)
+        call()
+        torch.cuda.synchronize()
+        reps = 3 if P == 0 else 10
+        with fa.kernel_timer() as kt:
+            for _ in range(reps):
+                call()
+        torch.cuda.synchronize()
+        launches, total = kt.times["annsa_attn"]
+        ms = total / launches
+        pairs = _pairs(qi, torch.cat([cache.ids, ki], dim=1), 1 << P)
+        tflops = 4.0 * d * pairs / (ms * 1e-3) / 1e12
+        rows.append({"P": P, "buckets": 1 << P, "kept_pairs": pairs, "ms": ms, "TFLOP/s": tflops,
+                     "frac_mfma_peak": tflops / BF16_PEAK_TFLOPS,
+                     "arith_intensity": 4.0 * d * pairs / (
+                         Nq * H * (d * 2 + d * 4 + 4) + float(H * (cap + Nq)) * 4 * d)})
+        print(json.dumps({"progress": "mfma_sweep", "P": P, "ms": ms}), file=sys.stderr, flush=True)
+        del cache, ws, q, kc, vc
+        torch.cuda.empty_cache()
+    print(json.dumps({"mfma_sweep": rows, "kernel": "annsa_attn (no search)", "peak_tflops": BF16_PEAK_TFLOPS,
+                      "config": cfg0.name, "dtype": cfg0.dtype, "out_dtype": "f32"}), flush=True)
+
+
+def rollout(args):
+    """A long rollout on the same layer: every chunk runs the full step on a
+    bounded cache (two streams), each between its own events; beside it a
+    dense baseline (one bucket, no merging, the cache grows by a chunk per
+    step: the same kernels at P = 0) is timed every 10th chunk."""
+    import torch
+    import sparse_attention_autoregressive_amd as fa
+    from sparse_attention_autoregressive_amd.step import AttentionStep
+    from workloads import CONFIGS, make_step, rollout_chunks
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    lib = fa.load()
+    to_dev = _device(cfg, dev)
+    H, Nq, d, cap, P = cfg.H, cfg.Nq, cfg.d, cfg.cap, cfg.P
+    n_chunks = args.rollout
+    st = make_step(cfg, args.seed)
+    planes = torch.from_numpy(st.planes).to(dev)
+    kp, vp = to_dev(st.kp), to_dev(st.vp)
+    cache = fa.KVCache.from_keys(to_dev(st.cache_k), to_dev(st.cache_v),
+                                 torch.from_numpy(st.cache_ts).to(dev),
+                                 torch.from_numpy(st.n_valid).to(dev), planes)
+    stepper = AttentionStep(H, Nq, d, cap, P, cfg.frame_len, cfg.L, cfg.tau, device=dev)
+    # dense baseline: uncapped cache, all ids 0
+    n0 = int(st.n_valid[0])
+    cap_d = n0 + n_chunks * Nq
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dk = torch.zeros(H, cap_d, d, dtype=dt, device=dev)
+    dv = torch.zeros(H, cap_d, d, dtype=dt, device=dev)
+    dk[:, :n0] = cache.k[:, :n0]
+    dv[:, :n0] = cache.v[:, :n0]
+    dense = fa.KVCache(k=dk, v=dv, ids=torch.zeros(H, cap_d, dtype=torch.int16, device=dev),
+                       ts=torch.zeros(H, cap_d, dtype=torch.int32, device=dev),
+                       n_valid=torch.full((H,), n0, dtype=torch.int32, device=dev),
+                       knorm=torch.zeros(H, cap_d, dtype=torch.float32, device=dev))
+    zq = torch.zeros(H, Nq, dtype=torch.int16, device=dev)
+    zp = torch.zeros(H, cfg.L, dtype=torch.int16, device=dev)
+    ws_sa = torch.empty(lib.fastar_annsa_workspace(H, Nq, cap_d, Nq, 0), dtype=torch.uint8, device=dev)
+    ws_ca = torch.empty(lib.fastar_annca_workspace(H, Nq, cfg.frame_len, cfg.L, 0), dtype=torch.uint8,
+                        device=dev)
+    o_sa = torch.empty(H, Nq, d, dtype=torch.float32, device=dev)
+    o_ca = torch.empty_like(o_sa)
+    main = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    fast_ev, dense_ev, slots, dense_slots = [], {}, [], {}
+    n_dense = n0
+    for c, ch in enumerate(rollout_chunks(cfg, n_chunks, args.seed)):
+        q, kc, vc = to_dev(ch["q"]), to_dev(ch["k_cur"]), to_dev(ch["v_cur"])
+        a, b = ev(), ev()
+        a.record(main)
+        stepper(cache, q, kc, vc, kp, vp, planes, ch["step"])
+        b.record(main)
+        fast_ev.append((a, b))
+        slots.append(cache.n_valid)          # read after the loop
+        if c % 10 == 0 or c == n_chunks - 1:
+            a, b = ev(), ev()
+            a.record(main)
+            fa.annsa_forward(q, zq, kc, vc, zq, 0, cache=dense, out=o_sa, ws=ws_sa)
+            fa.annca_forward(q, zq, cfg.frame_len, kp, vp, zp, 0, out=o_ca, ws=ws_ca)
+            b.record(main)
+            dense_ev[c] = (a, b)
+            dense_slots[c] = n_dense
+        dk[:, n_dense:n_dense + Nq] = kc                # the dense cache appends the chunk
+        dv[:, n_dense:n_dense + Nq] = vc
+        n_dense += Nq
+        dense.n_valid.fill_(n_dense)
+        slots[-1] = int(slots[-1].max())        # the bounded cache's valid slots (all heads)
+        if c % 20 == 0:
+            print(json.dumps({"progress": "rollout", "chunk": c}), file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    fast_ms = [a.elapsed_time(b) for a, b in fast_ev]
+    dense_ms = {c: a.elapsed_time(b) for c, (a, b) in dense_ev.items()}
+    row_bytes = d * (2 if cfg.dtype == "bf16" else 4) * 2 * H
+    print(json.dumps({"rollout": {
+        "config": cfg.name, "chunks": n_chunks, "fastar_step_ms": fast_ms,
+        "fastar_cache_slots": slots, "fastar_cache_kv_bytes": cap * row_bytes,
+        "dense_attention_ms": dense_ms, "dense_cache_slots": dense_slots,
+        "dense_cache_kv_bytes_final": n_dense * row_bytes,
+        "note": "FAST-AR: the whole step (hash, AnnSA + search, AnnCA, commit) on a cache capped at "
+                f"{cap} slots; dense: AnnSA + AnnCA at one bucket over the uncapped cache "
+                "(attention only), timed every 10th chunk"}}), flush=True)
 
 
 def cpu_baseline(cfg, seed, budget_s, line):
