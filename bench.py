@@ -392,16 +392,24 @@ def rollout(args):
     o_ca = torch.empty_like(o_sa)
     main = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    fast_ev, dense_ev, slots, dense_slots = [], {}, [], {}
-    n_dense = n0
+    # every chunk is generated and moved to the device first, so the timed
+    # loop never waits on the host (an idle GPU drops its clocks)
+    chunks = []
     for c, ch in enumerate(rollout_chunks(cfg, n_chunks, args.seed)):
-        q, kc, vc = to_dev(ch["q"]), to_dev(ch["k_cur"]), to_dev(ch["v_cur"])
+        chunks.append((to_dev(ch["q"]), to_dev(ch["k_cur"]), to_dev(ch["v_cur"]), ch["step"]))
+        if c % 20 == 0:
+            print(json.dumps({"progress": "rollout inputs", "chunk": c}), file=sys.stderr, flush=True)
+    slots_dev = torch.zeros(n_chunks, H, dtype=torch.int32, device=dev)
+    fast_ev, dense_ev, dense_slots = [], {}, {}
+    n_dense = n0
+    torch.cuda.synchronize()
+    for c, (q, kc, vc, step) in enumerate(chunks):
         a, b = ev(), ev()
         a.record(main)
-        stepper(cache, q, kc, vc, kp, vp, planes, ch["step"])
+        stepper(cache, q, kc, vc, kp, vp, planes, step)
         b.record(main)
         fast_ev.append((a, b))
-        slots.append(cache.n_valid)          # read after the loop
+        slots_dev[c].copy_(cache.n_valid)
         if c % 10 == 0 or c == n_chunks - 1:
             a, b = ev(), ev()
             a.record(main)
@@ -414,10 +422,8 @@ def rollout(args):
         dv[:, n_dense:n_dense + Nq] = vc
         n_dense += Nq
         dense.n_valid.fill_(n_dense)
-        slots[-1] = int(slots[-1].max())        # the bounded cache's valid slots (all heads)
-        if c % 20 == 0:
-            print(json.dumps({"progress": "rollout", "chunk": c}), file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    slots = slots_dev.max(dim=1).values.tolist()
     fast_ms = [a.elapsed_time(b) for a, b in fast_ev]
     dense_ms = {c: a.elapsed_time(b) for c, (a, b) in dense_ev.items()}
     row_bytes = d * (2 if cfg.dtype == "bf16" else 4) * 2 * H

@@ -105,7 +105,7 @@ struct Blk {
     struct Stage {
         u32x4 k[E];
         u32x4 v[HAS_V ? E : 1];
-        float kn[SEARCH ? E : 1];
+        float kn;                   // search: the norm of row (u / CPR) * E + u % CPR (u % CPR < E)
         int* slots;
     };
     // Running state of one query (per lane; the four lane groups of a query
@@ -215,16 +215,19 @@ struct Blk {
                     S.v[e] = *reinterpret_cast<const u32x4*>(
                         reinterpret_cast<const char*>(from_a ? sr.va : sr.vb) + off);
             }
-            if constexpr (SEARCH) {
-                // every lane of a row loads the same norm and writes the
-                // same slot (no branches in the load sequence); current-
-                // chunk keys read a clamped cached index, masked at the store
-                if (MODE != MODE_SA || sr.na > 0)                  // uniform
-                    S.kn[e] = sr.kn[MODE != MODE_SA || j < sr.na ? j : sr.na - 1];
-                else
-                    S.kn[e] = 0.f;
-                S.slots[row] = j;
-            }
+        }
+        if constexpr (SEARCH) {
+            // One norm per thread: lanes u % CPR = e < E take row rb*E + e
+            // (the others repeat row rb*E + E-1), so a tile costs one norm
+            // load per thread, issued without a branch; current-chunk keys
+            // read a clamped cached index and are masked at the store.
+            const int row = rb * E + (chunk < E ? chunk : E - 1);
+            const int j = kidx[(tile * KT + row) % KCH];
+            if (MODE != MODE_SA || sr.na > 0)                      // uniform
+                S.kn = sr.kn[MODE != MODE_SA || j < sr.na ? j : sr.na - 1];
+            else
+                S.kn = 0.f;
+            S.slots[row] = j;
         }
     }
 
@@ -235,11 +238,13 @@ struct Blk {
             const int row = rb * E + e;
             *reinterpret_cast<u32x4*>(&sm.Ks[row * STRK + chunk * EPC]) = S.k[e];
             if constexpr (HAS_V) *reinterpret_cast<u32x4*>(&sm.Vs[row * STRV + chunk * EPC]) = S.v[e];
-            if constexpr (SEARCH) {
+        }
+        if constexpr (SEARCH) {
+            if (chunk < E) {
+                const int row = rb * E + chunk;
                 const int j = S.slots[row];
-                const float kn = S.kn[e];
                 sm.kslot[row] = j;
-                sm.kinv[row] = (MODE == MODE_TOP1 || j < na) && kn > 0.f ? __builtin_amdgcn_rcpf(kn) : 0.f;
+                sm.kinv[row] = (MODE == MODE_TOP1 || j < na) && S.kn > 0.f ? __builtin_amdgcn_rcpf(S.kn) : 0.f;
             }
         }
     }
