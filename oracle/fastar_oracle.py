@@ -22,9 +22,10 @@ Readings of points the pages leave open (each repeated where it is used):
 
 R1  ANN = random-hyperplane (sign) LSH: bit p of a token's bucket id is
     [<x, r_p> >= 0]; plane p is bit p.  Queries, cached keys, current keys
-    and prompt keys are hashed with the same planes of their head ("shared
-    embedding space", summary, Core Components B).
-R2  One hash table, one bucket per token (blog, "3. AnnSA": "same bucket(s)").
+    and prompt keys are hashed with the same planes of their head (the
+    summary, Core Components B, puts queries and prompt keys in one space).
+R2  One hash table, one bucket per token (blog, "3. AnnSA", allows one or
+    several buckets per token; one is the plainest case).
 R3  AnnSA key context = [valid cache slots 0..n-1 ; current chunk in token
     order]; a query attends to every key of its bucket, no causal mask; an
     empty bucket gives O = 0 and lse = -inf; softmax scale is a parameter
@@ -37,8 +38,8 @@ R5  TempCache top-1: cosine between the current query and each cached key of
     Core Components A); candidates are previous-frame keys only (the valid
     cache slots).  Ties go to the lowest slot.  A zero norm gives cosine 0.
 R6  Merge: matched = has a candidate and cosine >= tau (inclusive).  The
-    current token replaces the matched slot ("only the most recent
-    representative stays", blog, "1. TempCache").  When several current
+    current token replaces the matched slot (blog, "1. TempCache": a group of
+    corresponding keys keeps just its newest member).  When several current
     tokens match one slot, the largest token index (the most recent) wins
     and the others are dropped.
 R7  Unmatched tokens are appended in token order; once the cache is full they
@@ -47,6 +48,23 @@ R7  Unmatched tokens are appended in token order; once the cache is full they
     ascending slot order.
 R8  Inserted and refreshed slots get timestamp ``step``.
 R9  A ``best`` value outside [0, n) counts as "no candidate".
+
+Mean-merge variant (summary, Core Components A, Lemma 5.1: identical keys
+merge without error when the values are averaged and the logits shifted by
+the group size).  A cache in this mode carries a group size m_j >= 1 per
+slot:
+
+R10 Slot j stands for m_j tokens with one key; its value is their mean.  The
+    shift is + ln m_j on the logit, which makes it exact: for a group G of
+    identical keys, sum_{t in G} exp(l) v_t = exp(l + ln m) * mean_G(v), and
+    likewise for the softmax denominator.  Current-chunk keys have m = 1.
+R11 Every matched token joins the group of its top-1 slot (none is dropped):
+    with C_j the slot's claimants, v_j <- (m_j v_j + sum_{i in C_j} v_i) /
+    (m_j + |C_j|) and m_j <- m_j + |C_j|.  The key, id and timestamp become
+    those of the most recent claimant, as in R6 (for identical keys the
+    choice is immaterial).
+R12 Appended and replacing tokens start groups of size 1; an evicted slot's
+    group leaves the cache with it.  Selection of the evicted slots is R7's.
 
 Tie flags (the decision is numerically fragile; a parallel fp32 result may
 legitimately differ there): a hash bit whose |<x, r>| / (|x| |r|) < 1e-5; an
@@ -71,7 +89,7 @@ def _f64(a) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# ANN hash  (summary, Core Components A and B: "LSH or quantization"; R1, R2)
+# ANN hash  (summary, Core Components A and B: an LSH or a quantizer; R1, R2)
 # ---------------------------------------------------------------------------
 
 def ann_hash(x, planes) -> Tuple[np.ndarray, np.ndarray]:
@@ -126,18 +144,28 @@ def key_context(cache_k, cache_v, cache_ids, n: int, k_cur, v_cur, kcur_ids):
             np.concatenate([np.asarray(cache_ids[:n]), np.asarray(kcur_ids)]).astype(np.int64))
 
 
+def key_counts(cache_count, n: int, n_cur: int) -> np.ndarray:
+    """Group sizes of AnnSA's key context in merge mode (R10): the valid
+    slots' counts, then 1 for every current-chunk key."""
+    return np.concatenate([np.asarray(cache_count[:n], np.int64), np.ones(n_cur, np.int64)])
+
+
 # ---------------------------------------------------------------------------
 # AnnSA  (blog, "3. AnnSA"; summary, Core Components C; R2, R3)
 # ---------------------------------------------------------------------------
 
-def annsa(q, q_ids, k, v, k_ids, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+def annsa(q, q_ids, k, v, k_ids, scale: float, k_counts=None) -> Tuple[np.ndarray, np.ndarray]:
     """Each query attends only to the keys of its own bucket:
-    O_i = sum_{j: idk_j = idq_i} softmax_j(scale * <q_i, k_j>) v_j,
-    lse_i = log sum_{j in bucket} exp(scale * <q_i, k_j>).
-    Queries whose bucket holds no key get O = 0, lse = -inf."""
+    O_i = sum_{j: idk_j = idq_i} softmax_j(l_ij) v_j,  l_ij = scale * <q_i, k_j>,
+    lse_i = log sum_{j in bucket} exp(l_ij).
+    Queries whose bucket holds no key get O = 0, lse = -inf.
+
+    With ``k_counts`` (group sizes m_j >= 1 of a mean-merged cache, R10) the
+    logit of key j is scale * <q_i, k_j> + ln m_j."""
     Q, K, V = _f64(q), _f64(k), _f64(v)
     qid = np.asarray(q_ids).astype(np.int64)
     kid = np.asarray(k_ids).astype(np.int64)
+    bias = np.zeros(K.shape[0]) if k_counts is None else np.log(_f64(k_counts))
     O = np.zeros((Q.shape[0], V.shape[1]))
     lse = np.full(Q.shape[0], -np.inf)
     for b in np.unique(qid):
@@ -145,7 +173,7 @@ def annsa(q, q_ids, k, v, k_ids, scale: float) -> Tuple[np.ndarray, np.ndarray]:
         kj = np.nonzero(kid == b)[0]
         if kj.size == 0:
             continue
-        S = (Q[qi] @ K[kj].T) * scale
+        S = (Q[qi] @ K[kj].T) * scale + bias[kj][None, :]
         m = S.max(axis=1, keepdims=True)
         E = np.exp(S - m)
         l = E.sum(axis=1, keepdims=True)
@@ -228,7 +256,7 @@ def tempcache_top1(q, q_ids, cache_k, cache_ids, n: int):
 
 
 def tempcache_commit(cache: Dict[str, np.ndarray], n: int, k_cur, v_cur, kcur_ids,
-                     best, cos, tau: float, step: int):
+                     best, cos, tau: float, step: int, merge: bool = False):
     """Apply one chunk's merge/append/evict to one head's cache (R6-R9).
 
     ``cache`` holds ``k``, ``v`` [cap, d], ``ids`` [cap], ``ts`` [cap]; it is
@@ -236,7 +264,12 @@ def tempcache_commit(cache: Dict[str, np.ndarray], n: int, k_cur, v_cur, kcur_id
     after the update), ``dest`` [N] (slot each token was written to, -1 if it
     was merged away), ``evicted`` [N] (-1 padded, ascending slots),
     ``counts`` = (matched, refreshed, dropped, appended, evicted),
-    ``matched`` [N] and ``thr_tie`` [N] (|cos - tau| < 1e-5)."""
+    ``matched`` [N] and ``thr_tie`` [N] (|cos - tau| < 1e-5).
+
+    ``merge`` selects the mean-merge variant (R10-R12): ``cache`` then also
+    holds ``count`` [cap] (group sizes), the new cache's ``v`` is float64 and
+    its ``count`` is updated; slot choice, keys, ids, timestamps, dest,
+    evicted and counts are those of the replacement rule."""
     K, V = cache["k"], cache["v"]
     ids, ts = np.asarray(cache["ids"]), np.asarray(cache["ts"])
     cap = K.shape[0]
@@ -270,13 +303,30 @@ def tempcache_commit(cache: Dict[str, np.ndarray], n: int, k_cur, v_cur, kcur_id
     new = {"k": np.array(K, copy=True), "v": np.array(V, copy=True),
            "ids": np.array(ids, copy=True), "ts": np.array(ts, copy=True)}
     kcur_ids = np.asarray(kcur_ids)
+    if merge:
+        if "count" not in cache:
+            raise ValueError("the mean-merge variant needs the cache's group sizes")
+        m_old = np.asarray(cache["count"], np.int64)
+        new["v"] = _f64(V).copy()
+        new["count"] = m_old.copy()
+        # R11: every claimant joins its slot's group; the group's value is the
+        # mean over old members and claimants, its size grows by the claimants
+        for j in np.nonzero(refreshed)[0]:
+            members = [i for i in range(N) if matched[i] and best[i] == j]
+            total = m_old[j] * _f64(V[j]) + sum(_f64(v_cur[i]) for i in members)
+            new["count"][j] = m_old[j] + len(members)
+            new["v"][j] = total / new["count"][j]
     for i in range(N):
         j = dest[i]
         if j >= 0:
             new["k"][j] = k_cur[i]
-            new["v"][j] = v_cur[i]
             new["ids"][j] = kcur_ids[i]
             new["ts"][j] = step                                # R8
+            if not merge:
+                new["v"][j] = v_cur[i]
+            elif not matched[i]:                               # R12: a new group of one
+                new["v"][j] = v_cur[i]
+                new["count"][j] = 1
     evicted = np.full(N, -1, np.int64)
     evicted[:e] = evicted_slots
     n_matched = int(matched.sum())
@@ -288,10 +338,10 @@ def tempcache_commit(cache: Dict[str, np.ndarray], n: int, k_cur, v_cur, kcur_id
 
 
 def tempcache_update(cache: Dict[str, np.ndarray], n: int, q, q_ids, k_cur, v_cur, kcur_ids,
-                     tau: float, step: int):
-    """Top-1 search, then commit (blog, "1. TempCache")."""
+                     tau: float, step: int, merge: bool = False):
+    """Top-1 search, then commit (blog, "1. TempCache"; ``merge``: R10-R12)."""
     best, cos, tie, near = tempcache_top1(q, q_ids, cache["k"], cache["ids"], n)
-    out = tempcache_commit(cache, n, k_cur, v_cur, kcur_ids, best, cos, tau, step)
+    out = tempcache_commit(cache, n, k_cur, v_cur, kcur_ids, best, cos, tau, step, merge)
     out.update(best=best, cos=cos, argmax_tie=tie, near=near)
     return out
 
@@ -303,8 +353,10 @@ def tempcache_update(cache: Dict[str, np.ndarray], n: int, q, q_ids, k_cur, v_cu
 
 def attention_step(q, k_cur, v_cur, cache_k, cache_v, cache_ids, cache_ts, n_valid,
                    planes, kp, vp, frame_len: int, tau: float, step: int,
-                   scale: Optional[float] = None, heads=None) -> Dict[str, object]:
-    """Runs the whole step head by head; arrays carry a leading head axis."""
+                   scale: Optional[float] = None, heads=None,
+                   cache_count=None) -> Dict[str, object]:
+    """Runs the whole step head by head; arrays carry a leading head axis.
+    ``cache_count`` [H, cap] selects the mean-merge variant (R10-R12)."""
     H = q.shape[0] if heads is None else len(heads)
     heads = range(q.shape[0]) if heads is None else heads
     d = q.shape[2]
@@ -317,10 +369,14 @@ def attention_step(q, k_cur, v_cur, cache_k, cache_v, cache_ids, cache_ts, n_val
         pi, tp = ann_hash(kp[h], planes[h])
         n = int(n_valid[h])
         K, V, kid = key_context(cache_k[h], cache_v[h], cache_ids[h], n, k_cur[h], v_cur[h], ki)
-        o_sa, lse = annsa(q[h], qi, K, V, kid, scale)
+        merge = cache_count is not None
+        cnt = key_counts(cache_count[h], n, k_cur.shape[1]) if merge else None
+        o_sa, lse = annsa(q[h], qi, K, V, kid, scale, cnt)
         o_ca, keep = annca(q[h], qi, frame_len, kp[h], vp[h], pi, scale)
-        tc = tempcache_update({"k": cache_k[h], "v": cache_v[h], "ids": cache_ids[h],
-                               "ts": cache_ts[h]}, n, q[h], qi, k_cur[h], v_cur[h], ki, tau, step)
+        ch = {"k": cache_k[h], "v": cache_v[h], "ids": cache_ids[h], "ts": cache_ts[h]}
+        if merge:
+            ch["count"] = cache_count[h]
+        tc = tempcache_update(ch, n, q[h], qi, k_cur[h], v_cur[h], ki, tau, step, merge)
         for key, val in (("q_ids", qi), ("kcur_ids", ki), ("kp_ids", pi),
                          ("hash_tie", (tq, tk, tp)), ("o_sa", o_sa), ("lse", lse),
                          ("o_ca", o_ca), ("keep", keep), ("tc", tc)):
