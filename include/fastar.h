@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FASTAR_ABI_VERSION 1
+#define FASTAR_ABI_VERSION 2
 #define FASTAR_MAX_PLANES 10      /* bucketed calls: at most 1024 buckets per head */
 #define FASTAR_MAX_HASH_PLANES 16 /* ids are uint16 */
 
@@ -71,10 +71,17 @@ typedef enum { FASTAR_F32 = 0, FASTAR_BF16 = 1 } fastar_dtype;
  *   knorm    [H][cap]  fp32 norm |k| of the key held in each slot (the
  *                      TempCache cosine search divides by it)
  *   n_valid  [H]       number of valid slots; slots 0..n_valid[h]-1 are valid.
+ *   count    [H][cap]  NULL, or the group size m >= 1 of each slot: the cache
+ *                      is then a mean-merged cache (summary, Core Components
+ *                      A, Lemma 5.1), whose slot j stands for m_j tokens that
+ *                      share one key, with v_j their mean value.  Values below
+ *                      1 are read as 1.
  * n_valid stays on the device so that a step never waits on the host; values
  * outside [0, cap] are clamped when read.  fastar_tempcache_update maintains
  * every field; a cache filled by other means gets ids and knorm from
- * fastar_ann_hash on its keys. */
+ * fastar_ann_hash on its keys (and count = 1 for a fresh merged cache).
+ * With count NULL the cache follows the replacement rule: a matched slot takes
+ * the newest token, the other tokens that matched it are dropped. */
 typedef struct {
     int32_t H;
     int32_t cap;
@@ -86,6 +93,7 @@ typedef struct {
     int32_t* ts;
     int32_t* n_valid;
     float* knorm;
+    int32_t* count;           /* NULL: replacement rule; else group sizes (mean merge) */
 } fastar_cache;
 
 /* Status name, e.g. "FASTAR_ESHAPE" (static storage, never NULL). */
@@ -129,9 +137,12 @@ fastar_status fastar_bucket_sort(const uint16_t* ids, int32_t H, int32_t N, int3
  * Components C).  Key context of head h = [cache slots 0..n_valid[h]-1 ;
  * the Ncur current keys in token order].  Query i attends to exactly the
  * context keys whose id equals q_ids[h][i]:
- *   out[h][i] = sum_j softmax_j(scale * <q_i, k_j>) v_j,
- *   lse[h][i] = log sum_j exp(scale * <q_i, k_j>),
+ *   out[h][i] = sum_j softmax_j(l_ij) v_j,   l_ij = scale * <q_i, k_j> + b_j,
+ *   lse[h][i] = log sum_j exp(l_ij),
  * with out = 0 and lse = -inf when the bucket holds no key.  No causal mask.
+ * b_j = 0, except for the slots of a mean-merged cache (cache->count set):
+ * b_j = ln m_j, the group-size shift of Lemma 5.1 (summary, Core Components
+ * A), which makes a slot of m identical keys attend like the m tokens.
  *
  * q         [H][Nq][d] of ``dtype``      q_ids [H][Nq] uint16
  * cache     host pointer, may be NULL (no cached keys); its H, d and dtype
@@ -194,18 +205,29 @@ fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t
  *     (k, v, id <- the token's k_cur, v_cur, kcur_id; ts <- step; knorm <-
  *     |k_cur|); the other
  *     tokens that matched the same slot are dropped (merged away).
+ *     Mean-merged cache (cache->count set; Lemma 5.1, summary, Core
+ *     Components A): every token that matched slot j joins its group instead
+ *     -- with C_j those tokens and m_j the group size,
+ *       v_j <- (m_j v_j + sum_{i in C_j} v_cur_i) / (m_j + |C_j|),
+ *       m_j <- m_j + |C_j|,
+ *     summed in fp32 in ascending token order and rounded once to the cache
+ *     dtype; k, id, ts and knorm are refreshed as above.  Tokens written by
+ *     step 3 start groups of size 1.
  *  3. the u unmatched tokens, in token order, fill slots n, n+1, ... up to
  *     cap, then the e = max(0, n + u - cap) non-refreshed slots with the
  *     smallest (ts, slot), taken in ascending slot order.
  *     n_valid[h] <- min(cap, n + u), so it never exceeds cap.
  * Outputs (each may be NULL):
  *   best [H][N] int32, best_cos [H][N] fp32 (step 1's result, or the inputs),
- *   dest [H][N] int32 (slot written by each token, -1 if dropped),
+ *   dest [H][N] int32 (slot written by each token, -1 if dropped; in a
+ *        mean-merged cache -1 marks a token folded into its slot's group
+ *        without becoming its representative),
  *   evicted [H][N] int32 (replaced slots ascending, -1 padded),
  *   counts [H][5] int32 = {matched, refreshed, dropped, appended, evicted}.
  * Requires N <= cache->cap (else FASTAR_ECAPACITY) and a non-NaN tau.
  * q, k_cur, v_cur are [H][N][d] of cache->dtype; q_ids, kcur_ids [H][N].
- * Slot order, dest, evicted and counts are deterministic.
+ * Slot order, dest, evicted and counts are deterministic, and so are merged
+ * values (a fixed summation order).
  * ------------------------------------------------------------------------ */
 size_t fastar_tempcache_workspace(int32_t H, int32_t N, int32_t cap, int32_t P);
 fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,

@@ -54,36 +54,52 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[Optiona
 
 @dataclass
 class KVCache:
-    """Device tensors of one layer's bounded cache (all heads)."""
+    """Device tensors of one layer's bounded cache (all heads).
+
+    With ``count`` the cache is mean-merged (Lemma 5.1 of the FAST-AR summary,
+    Core Components A): slot j stands for count[h, j] tokens sharing one key
+    and holds their mean value; AnnSA shifts its logits by ln(count) and the
+    commit folds matched tokens into their slot's group.  Without it a
+    matched slot is replaced by the newest token."""
     k: torch.Tensor          # [H, cap, d]
     v: torch.Tensor          # [H, cap, d]
     ids: torch.Tensor        # [H, cap] int16 (uint16 bit pattern)
     ts: torch.Tensor         # [H, cap] int32
     n_valid: torch.Tensor    # [H] int32
     knorm: torch.Tensor      # [H, cap] float32, |k| of each slot's key
+    count: Optional[torch.Tensor] = None   # [H, cap] int32 group sizes (mean merge)
 
     @classmethod
-    def empty(cls, H: int, cap: int, d: int, dtype=torch.bfloat16, device="cuda") -> "KVCache":
+    def empty(cls, H: int, cap: int, d: int, dtype=torch.bfloat16, device="cuda",
+              merge: bool = False) -> "KVCache":
         return cls(k=torch.zeros(H, cap, d, dtype=dtype, device=device),
                    v=torch.zeros(H, cap, d, dtype=dtype, device=device),
                    ids=torch.zeros(H, cap, dtype=torch.int16, device=device),
                    ts=torch.zeros(H, cap, dtype=torch.int32, device=device),
                    n_valid=torch.zeros(H, dtype=torch.int32, device=device),
-                   knorm=torch.zeros(H, cap, dtype=torch.float32, device=device))
+                   knorm=torch.zeros(H, cap, dtype=torch.float32, device=device),
+                   count=torch.ones(H, cap, dtype=torch.int32, device=device) if merge else None)
 
     @classmethod
     def from_keys(cls, k: torch.Tensor, v: torch.Tensor, ts: torch.Tensor, n_valid: torch.Tensor,
-                  planes: torch.Tensor) -> "KVCache":
-        """A cache holding ``k``/``v`` with bucket ids and norms computed by ann_hash."""
+                  planes: torch.Tensor, count: Optional[torch.Tensor] = None) -> "KVCache":
+        """A cache holding ``k``/``v`` with bucket ids and norms computed by
+        ann_hash (``count``: group sizes of a mean-merged cache)."""
         H, cap, _ = k.shape
         c = cls(k=k, v=v, ids=torch.empty(H, cap, dtype=torch.int16, device=k.device), ts=ts,
-                n_valid=n_valid, knorm=torch.empty(H, cap, dtype=torch.float32, device=k.device))
+                n_valid=n_valid, knorm=torch.empty(H, cap, dtype=torch.float32, device=k.device),
+                count=count)
         ann_hash(k, planes, ids=c.ids, norms=c.knorm)
         return c
 
     def clone(self) -> "KVCache":
         return KVCache(k=self.k.clone(), v=self.v.clone(), ids=self.ids.clone(),
-                       ts=self.ts.clone(), n_valid=self.n_valid.clone(), knorm=self.knorm.clone())
+                       ts=self.ts.clone(), n_valid=self.n_valid.clone(), knorm=self.knorm.clone(),
+                       count=None if self.count is None else self.count.clone())
+
+    @property
+    def merge(self) -> bool:
+        return self.count is not None
 
     @property
     def H(self) -> int:
@@ -104,9 +120,12 @@ class KVCache:
         if self.ids.dtype != torch.int16 or self.ts.dtype != torch.int32 \
                 or self.n_valid.dtype != torch.int32 or self.knorm.dtype != torch.float32:
             raise TypeError("cache ids must be int16, ts and n_valid int32, knorm float32")
+        if self.count is not None and (self.count.dtype != torch.int32
+                                       or tuple(self.count.shape) != (self.H, self.cap)):
+            raise TypeError("cache count must be int32 [H, cap]")
         return _lib.FastarCache(self.H, self.cap, self.d, _dtype_code(self.k), _ptr(self.k),
                                 _ptr(self.v), _ptr(self.ids), _ptr(self.ts), _ptr(self.n_valid),
-                                _ptr(self.knorm))
+                                _ptr(self.knorm), _ptr(self.count))
 
 
 def _ids_check(ids: torch.Tensor, shape) -> None:

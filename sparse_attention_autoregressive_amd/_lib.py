@@ -23,13 +23,14 @@ FASTAR_BF16 = 1
 FASTAR_MAX_PLANES = 10
 FASTAR_MAX_HASH_PLANES = 16
 FASTAR_TIMER_MAX = 8192
+FASTAR_ABI_VERSION = 2
 
 
 class FastarCache(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("cap", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("ids", ctypes.c_void_p), ("ts", ctypes.c_void_p), ("n_valid", ctypes.c_void_p),
-                ("knorm", ctypes.c_void_p)]
+                ("knorm", ctypes.c_void_p), ("count", ctypes.c_void_p)]
 
 
 class FastarKernelTime(ctypes.Structure):
@@ -76,6 +77,9 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.fastar_abi_version() != FASTAR_ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {lib.fastar_abi_version()}, the binding "
+                               f"expects {FASTAR_ABI_VERSION}: rebuild the library")
         _lib = lib
     return _lib
 

@@ -36,6 +36,10 @@
 //    stages, so two tiles are in flight while a third is computed on.
 //  * The search uses the cached keys' norms kept in the cache, so a cosine is
 //    one product per (query, key): dot * (1/|k|), times 1/|q| at the end.
+//  * BIAS (AnnSA over a mean-merged cache; summary, "2. Core Components" A,
+//    Lemma 5.1): a cached slot that stands for m tokens adds ln m to its
+//    logits.  The group sizes travel with the tile like the norms, one load
+//    per thread, and become a per-key score offset ln(m) / scale in LDS.
 //
 // Every use launches one block per item, heads fastest in the launch order;
 // SA / TOP1 items come from a table the bucket sort writes with the longest
@@ -86,8 +90,10 @@ struct Tile {
 };
 
 // The pieces every kernel below is built from.
-template <typename T, int D, int MODE, bool SEARCH, int NT>
+template <typename T, int D, int MODE, bool SEARCH, int NT, bool BIAS = false>
 struct Blk {
+    static_assert(!BIAS || MODE == MODE_SA, "group-size offsets are AnnSA's");
+    static constexpr bool SLOTS = SEARCH || BIAS;     // the tile's key indices go to LDS
     using TL = Tile<T, D, MODE, NT>;
     static constexpr bool BF = TL::BF, HAS_V = TL::HAS_V;
     static constexpr int E = TL::E, CPR = TL::CPR, EPC = TL::EPC;
@@ -106,6 +112,7 @@ struct Blk {
         u32x4 k[E];
         u32x4 v[HAS_V ? E : 1];
         float kn;                   // search: the norm of row (u / CPR) * E + u % CPR (u % CPR < E)
+        int kc;                     // bias: that row's group size
         int* slots;
     };
     // Running state of one query (per lane; the four lane groups of a query
@@ -129,6 +136,7 @@ struct Blk {
         T* Vs;
         int* kslot;
         float* kinv;
+        float* kbias;
     };
     // Where one head's keys live: index j < na is row j of (ka, va), else row
     // j - na of (kb, vb).  kn holds the cached keys' norms.
@@ -138,6 +146,7 @@ struct Blk {
         const T* kb;
         const T* vb;
         const float* kn;
+        const int32_t* kcnt;
         int na;
     };
 
@@ -216,22 +225,30 @@ struct Blk {
                         reinterpret_cast<const char*>(from_a ? sr.va : sr.vb) + off);
             }
         }
-        if constexpr (SEARCH) {
-            // One norm per thread: lanes u % CPR = e < E take row rb*E + e
-            // (the others repeat row rb*E + E-1), so a tile costs one norm
-            // load per thread, issued without a branch; current-chunk keys
-            // read a clamped cached index and are masked at the store.
+        if constexpr (SLOTS) {
+            // One norm (and group size) per thread: lanes u % CPR = e < E
+            // take row rb*E + e (the others repeat row rb*E + E-1), so a tile
+            // costs one load per thread, issued without a branch; current-
+            // chunk keys read a clamped cached index and are masked at the
+            // store.
             const int row = rb * E + (chunk < E ? chunk : E - 1);
             const int j = kidx[(tile * KT + row) % KCH];
-            if (MODE != MODE_SA || sr.na > 0)                      // uniform
-                S.kn = sr.kn[MODE != MODE_SA || j < sr.na ? j : sr.na - 1];
-            else
-                S.kn = 0.f;
+            const int jc = MODE != MODE_SA || j < sr.na ? j : sr.na - 1;
+            if constexpr (SEARCH) {
+                if (MODE != MODE_SA || sr.na > 0)                  // uniform
+                    S.kn = sr.kn[jc];
+                else
+                    S.kn = 0.f;
+            }
+            if constexpr (BIAS) S.kc = sr.na > 0 ? sr.kcnt[jc] : 1;
             S.slots[row] = j;
         }
     }
 
-    static __device__ __forceinline__ void store_tile(const Stage& S, const Smem& sm, int na, int tid) {
+    // ``inv_c`` = 1 / (scale * log2 e): a group size m becomes the raw-score
+    // offset log2(m) * inv_c = ln(m) / scale.
+    static __device__ __forceinline__ void store_tile(const Stage& S, const Smem& sm, int na, int tid,
+                                                      float inv_c) {
         const int chunk = tid % CPR, rb = tid / CPR;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -239,12 +256,18 @@ struct Blk {
             *reinterpret_cast<u32x4*>(&sm.Ks[row * STRK + chunk * EPC]) = S.k[e];
             if constexpr (HAS_V) *reinterpret_cast<u32x4*>(&sm.Vs[row * STRV + chunk * EPC]) = S.v[e];
         }
-        if constexpr (SEARCH) {
+        if constexpr (SLOTS) {
             if (chunk < E) {
                 const int row = rb * E + chunk;
                 const int j = S.slots[row];
-                sm.kslot[row] = j;
-                sm.kinv[row] = (MODE == MODE_TOP1 || j < na) && S.kn > 0.f ? __builtin_amdgcn_rcpf(S.kn) : 0.f;
+                if constexpr (SEARCH) {
+                    sm.kslot[row] = j;
+                    sm.kinv[row] = (MODE == MODE_TOP1 || j < na) && S.kn > 0.f ? __builtin_amdgcn_rcpf(S.kn) : 0.f;
+                }
+                if constexpr (BIAS)
+                    sm.kbias[row] = j < na && S.kc > 1
+                                        ? __builtin_amdgcn_logf(static_cast<float>(S.kc)) * inv_c
+                                        : 0.f;
             }
         }
     }
@@ -310,6 +333,18 @@ struct Blk {
         }
 
         if constexpr (HAS_V) {
+            // ---- group-size offsets of a mean-merged cache (after the search,
+            // which compares plain cosines)
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int kb4 = 0; kb4 < 4; ++kb4) {
+                    const float4 b = *reinterpret_cast<const float4*>(&sm.kbias[kb4 * 16 + 4 * g]);
+                    s[kb4][0] += b.x;
+                    s[kb4][1] += b.y;
+                    s[kb4][2] += b.z;
+                    s[kb4][3] += b.w;
+                }
+            }
             // ---- online softmax, one query per lane.  The running max is kept
             // in raw score units; the scale folds into the exponent:
             // p = 2^(s*c - m*c), c = scale * log2(e) > 0.
@@ -437,6 +472,7 @@ struct Blk {
         s.kb = p.kb ? static_cast<const T*>(p.kb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
         s.vb = (HAS_V && p.vb) ? static_cast<const T*>(p.vb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
         s.kn = SEARCH ? p.knorm + static_cast<size_t>(h) * p.a_rows : nullptr;
+        s.kcnt = BIAS ? p.kcount + static_cast<size_t>(h) * p.a_rows : nullptr;
         s.na = 0;
         return s;
     }
@@ -446,18 +482,20 @@ struct Blk {
 
 // NW waves per block; the item is 16*NW queries (SA / TOP1: the 64-query
 // slices of the bucket sort, NW = 4).
-template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW>
+template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
     constexpr int NT = 64 * NW, QT = 16 * NW;
     static_assert(MODE == MODE_CA || QT == kQTile, "SA / TOP1 items are kQTile queries");
-    using B = Blk<T, D, MODE, SEARCH, NT>;
+    using B = Blk<T, D, MODE, SEARCH, NT, BIAS>;
     __shared__ __align__(16) T Ks[KT * B::STRK];
     __shared__ __align__(16) T Vs[B::HAS_V ? KT * B::STRV : 1];
     __shared__ __align__(16) int kslot[SEARCH ? KT : 4];
     __shared__ __align__(16) float kinv[SEARCH ? KT : 4];
-    __shared__ int sslot[2][SEARCH ? KT : 1];
+    __shared__ __align__(16) float kbias[BIAS ? KT : 4];
+    __shared__ int sslot[2][B::SLOTS ? KT : 1];
     __shared__ int kidx[KCH];
-    const typename B::Smem sm{Ks, Vs, kslot, kinv};
+    const typename B::Smem sm{Ks, Vs, kslot, kinv, kbias};
+    const float inv_c = BIAS ? 1.f / p.scale_log2 : 0.f;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -516,7 +554,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     auto step = [&](typename B::Stage& S, int t) __attribute__((always_inline)) {
         if (t >= nt) return;                              // block-uniform
         __syncthreads();
-        B::store_tile(S, sm, sr.na, tid);
+        B::store_tile(S, sm, sr.na, tid, inv_c);
         __syncthreads();
         if (t + 2 < nt) {
             if (((t + 2) * KT) % KCH == 0) {        // next index chunk
@@ -550,10 +588,10 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
 // registers per lane, i.e. 2 waves per SIMD.
-template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW>
+template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kv_kernel(const AttnParams p) {
-    attn_body<T, D, MODE, SEARCH, OT, NW>(p);
+    attn_body<T, D, MODE, SEARCH, OT, NW, BIAS>(p);
 }
 
 // The search alone stages K only and runs at the occupancy its registers allow.
@@ -579,8 +617,13 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
     if constexpr (MODE == MODE_TOP1) {
         hipLaunchKernelGGL((attn_top1_kernel<T, D>), grid, dim3(256), 0, s, p);
     } else if constexpr (MODE == MODE_SA) {
-        if (p.best)
+        const bool bias = p.kcount != nullptr && p.a_rows > 0;
+        if (p.best && bias)
+            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, true, OT, 4, true>), grid, dim3(256), 0, s, p);
+        else if (p.best)
             hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, true, OT, 4>), grid, dim3(256), 0, s, p);
+        else if (bias)
+            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, false, OT, 4, true>), grid, dim3(256), 0, s, p);
         else
             hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, false, OT, 4>), grid, dim3(256), 0, s, p);
     } else {

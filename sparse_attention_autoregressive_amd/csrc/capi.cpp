@@ -118,6 +118,7 @@ struct TcWs {
     SortBufs q, k;
     ItemTable it;
     int32_t *claim, *best, *upos, *ev, *dest;
+    int32_t *grp_cnt, *grp_off, *grp_mem, *grp_pos;   // mean merge
     uint32_t* refreshed;
     float* cosv;
 };
@@ -134,6 +135,10 @@ TcWs carve_tc(Carver& c, int H, int N, int cap, int P) {
     w.upos = c.take<int32_t>(HN);
     w.ev = c.take<int32_t>(HN);
     w.dest = c.take<int32_t>(HN);
+    w.grp_cnt = c.take<int32_t>(HN);
+    w.grp_off = c.take<int32_t>(HN);
+    w.grp_mem = c.take<int32_t>(HN);
+    w.grp_pos = c.take<int32_t>(HN);
     return w;
 }
 
@@ -306,6 +311,7 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
     p.best = best;
     p.bcos = best_cos;
     p.knorm = cache ? cache->knorm : nullptr;
+    p.kcount = cache ? cache->count : nullptr;
     p.scale_log2 = scale * 1.4426950408889634f;
     return hip_status(launch_attn(MODE_SA, dtype == FASTAR_BF16, d, out_dtype == FASTAR_BF16, H, p, s));
 }
@@ -458,12 +464,22 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     sp.dest = dest ? dest : w.dest;
     sp.evicted = evicted;
     sp.counts = counts;
+    const bool merge = cache->count != nullptr && cap > 0;
+    sp.grp_cnt = merge ? w.grp_cnt : nullptr;
+    sp.grp_off = merge ? w.grp_off : nullptr;
+    sp.grp_mem = merge ? w.grp_mem : nullptr;
+    sp.grp_pos = merge ? w.grp_pos : nullptr;
     sp.H = H;
     sp.N = N;
     sp.cap = cap;
     sp.tau = tau;
     e = launch_tc_select(sp, s);
     if (e != hipSuccess) return FASTAR_EHIP;
+    if (merge)
+        return hip_status(launch_tc_merge_scatter(bf, d, H, N, cap, sp.dest, sp.grp_cnt, sp.grp_off,
+                                                  sp.grp_mem, k_cur, v_cur, kcur_ids, step, cache->k,
+                                                  cache->v, cache->ids, cache->ts, cache->knorm,
+                                                  cache->count, s));
     return hip_status(launch_tc_scatter(bf, d, H, N, cap, sp.dest, k_cur, v_cur, kcur_ids, step,
                                         cache->k, cache->v, cache->ids, cache->ts, cache->knorm, s));
 }

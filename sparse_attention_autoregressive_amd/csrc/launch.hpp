@@ -80,6 +80,7 @@ struct AttnParams {
     const int32_t* n_valid = nullptr;
     int cap = 0;
     const float* knorm = nullptr;   // [H][a_rows] key norms of source a (search)
+    const int32_t* kcount = nullptr; // [H][a_rows] group sizes of source a (mean-merged cache)
     // bucket groupings and work items (SA, TOP1)
     const int32_t* qperm = nullptr;
     int qperm_stride = 0;
@@ -122,6 +123,12 @@ struct TcSelectParams {
     int32_t* dest;           // [H][N] output (scratch or caller's)
     int32_t* evicted;        // [H][N] caller output or null
     int32_t* counts;         // [H][5] caller output or null
+    // mean merge only (null otherwise): the matched tokens grouped by the
+    // token that represents their slot
+    int32_t* grp_cnt;        // [H][N] scratch: group size of each representative, else 0
+    int32_t* grp_off;        // [H][N] scratch: exclusive scan of grp_cnt
+    int32_t* grp_mem;        // [H][N] scratch: members of each group (unordered)
+    int32_t* grp_pos;        // [H][N] scratch: a member's position in its group
     int H, N, cap;
     float tau;
 };
@@ -131,5 +138,14 @@ hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int3
                              const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
                              int32_t step, void* ck, void* cv, uint16_t* cids, int32_t* cts,
                              float* cnorm, hipStream_t s);
+// Mean-merge variant of the scatter: representatives fold their group's
+// values into the slot (grp_* as written by the select), the other written
+// tokens start groups of one.
+hipError_t launch_tc_merge_scatter(bool bf16, int d, int H, int N, int cap, const int32_t* dest,
+                                   const int32_t* grp_cnt, const int32_t* grp_off,
+                                   const int32_t* grp_mem, const void* k_cur, const void* v_cur,
+                                   const uint16_t* kcur_ids, int32_t step, void* ck, void* cv,
+                                   uint16_t* cids, int32_t* cts, float* cnorm, int32_t* ccount,
+                                   hipStream_t s);
 
 }  // namespace fastar

@@ -19,6 +19,15 @@
 // then a copy kernel moves the written tokens' rows into place (32 lanes per
 // token, 16 bytes each) and records each written key's norm.  Every decision
 // is integer or a single fp32 compare, so results are deterministic.
+//
+// Mean-merged caches (summary, "2. Core Components" A, Lemma 5.1: a slot
+// holds the mean value of a group of tokens with one key) use the same
+// decisions.  The select also groups the matched tokens by the token that
+// represents their slot (group sizes by integer atomics, offsets by a block
+// scan, members placed at atomic positions), and the merge scatter, one wave
+// per written token, folds a group's values into its slot in ascending token
+// order -- the members are ordered in registers first, so the fp32 sum, and
+// the cache, do not depend on the order the atomics ran in.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -110,9 +119,15 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         for (int k = 0; k < TOK_ITEMS; ++k) ci[k] = (base + k < N) ? cosv[base + k] : 0.f;
     };
 
+    const bool merge = p.grp_cnt != nullptr;                  // uniform
+    int32_t* gcnt = merge ? p.grp_cnt + static_cast<size_t>(h) * N : nullptr;
+    int32_t* gpos = merge ? p.grp_pos + static_cast<size_t>(h) * N : nullptr;
+
     // 1. claims.  Only the entries of matched slots are reset, so the claim
     //    array never needs a full clear.
     for (int w = tid; w < (n + 31) / 32; w += SEL_NT) refr[w] = 0u;
+    if (merge)
+        for (int i = tid; i < N; i += SEL_NT) gcnt[i] = 0;
     for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
         load_tok(c0);
 #pragma unroll
@@ -152,6 +167,8 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
                 if (win) atomicOr(&refr[bi[k] >> 5], 1u << (bi[k] & 31));
                 wins += win;
                 dest[i] = win ? bi[k] : -1;
+                // mean merge: the token joins the group of its slot's winner
+                if (merge) gpos[i] = atomicAdd(&gcnt[cl[k]], 1);
             }
         }
         int total;
@@ -167,6 +184,44 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         refreshed += total >> 16;
     }
     __syncthreads();                    // the refreshed bitmap is complete
+
+    // 2b. mean merge: group offsets (a scan of the group sizes in token
+    //     order), then every matched token is placed in its group
+    if (merge) {
+        int32_t* goff = p.grp_off + static_cast<size_t>(h) * N;
+        int32_t* gmem = p.grp_mem + static_cast<size_t>(h) * N;
+        int carry = 0;
+        for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
+            const int base = c0 + tid * TOK_ITEMS;
+            int cn[TOK_ITEMS], local = 0;
+#pragma unroll
+            for (int k = 0; k < TOK_ITEMS; ++k) {
+                cn[k] = (base + k < N) ? gcnt[base + k] : 0;
+                local += cn[k];
+            }
+            int total;
+            int pos = carry + block_exclusive_scan<SEL_NT>(local, smem, total);
+#pragma unroll
+            for (int k = 0; k < TOK_ITEMS; ++k) {
+                if (base + k < N) goff[base + k] = pos;
+                pos += cn[k];
+            }
+            carry += total;
+        }
+        __syncthreads();
+        for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
+            load_tok(c0);
+            const int base = c0 + tid * TOK_ITEMS;
+#pragma unroll
+            for (int k = 0; k < TOK_ITEMS; ++k) {
+                const int i = base + k;
+                if (i < N && is_matched(bi[k], ci[k], n, p.tau)) {
+                    const int w = claim[bi[k]];
+                    gmem[goff[w] + gpos[i]] = i;
+                }
+            }
+        }
+    }
 
     const int e = max(0, n + u - cap);
     const int appended = u - e;
@@ -399,6 +454,156 @@ hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int3
         if (d == 64) FASTAR_SCATTER(float, 64); else FASTAR_SCATTER(float, 128);
     }
 #undef FASTAR_SCATTER
+    timer_end(s);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ mean merge
+namespace {
+template <typename T>
+__device__ __forceinline__ float elem_f32(T x) {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(x);
+    else return x;
+}
+template <typename T>
+__device__ __forceinline__ T f32_elem(float x) {
+    if constexpr (sizeof(T) == 2) return f32_to_bf16(x);
+    else return x;
+}
+// Minimum over the wave's 64 lanes (every lane ends with it).
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const int o = __shfl_xor(x, off);
+        x = o < x ? o : x;
+    }
+    return x;
+}
+constexpr int kMergeTokensPerBlock = 4;     // one wave per written token
+}  // namespace
+
+// One wave per current token with a destination slot.  Lane l owns elements
+// l*EPL .. l*EPL+EPL-1 of the rows.  The key row, id, timestamp and norm are
+// written as in the replacement scatter.  A token that represents a group of
+// c matched tokens sets the slot's value to (m v + sum of the members'
+// values) / (m + c) in fp32, members taken in ascending token order, and its
+// group size to m + c; any other written token starts a group of one.
+template <typename T, int D>
+__global__ __launch_bounds__(64 * kMergeTokensPerBlock) void tc_merge_scatter_kernel(
+    const int32_t* __restrict__ dest, const int32_t* __restrict__ gcnt, const int32_t* __restrict__ goff,
+    const int32_t* __restrict__ gmem, const T* __restrict__ kc, const T* __restrict__ vc,
+    const uint16_t* __restrict__ kids, int32_t step, T* __restrict__ ck, T* __restrict__ cv,
+    uint16_t* __restrict__ cids, int32_t* __restrict__ cts, float* __restrict__ cnorm,
+    int32_t* __restrict__ ccount, int N, int cap) {
+    constexpr int EPL = D / kWave;
+    static_assert(EPL >= 1 && D % kWave == 0, "row split");
+    const int h = blockIdx.y;
+    const int i = blockIdx.x * kMergeTokensPerBlock + threadIdx.x / kWave;
+    const int l = threadIdx.x % kWave;
+    if (i >= N) return;                                  // wave uniform
+    const size_t ti = static_cast<size_t>(h) * N + i;
+    const int d = dest[ti];
+    if (d < 0 || d >= cap) return;                       // wave uniform
+    const size_t si = static_cast<size_t>(h) * cap + d;
+    const T* vcur_h = vc + static_cast<size_t>(h) * N * D;
+    const int col = l * EPL;
+
+    T kx[EPL];
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        kx[e] = kc[ti * D + col + e];
+        const float f = elem_f32(kx[e]);
+        sq = __builtin_fmaf(f, f, sq);
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ck[si * D + col + e] = kx[e];
+
+    const int c = gcnt[ti];
+    if (c == 0) {                                        // a group of one
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) cv[si * D + col + e] = vc[ti * D + col + e];
+        if (l == 0) ccount[si] = 1;
+    } else {
+        const int m0 = ccount[si];
+        const int m = m0 < 1 ? 1 : m0;
+        float acc[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = static_cast<float>(m) * elem_f32(cv[si * D + col + e]);
+        const int32_t* mem = gmem + static_cast<size_t>(h) * N + goff[ti];
+        auto add_row = [&](int tok) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] += elem_f32(vcur_h[static_cast<size_t>(tok) * D + col + e]);
+        };
+        if (c <= kWave) {
+            // rank each member among the group, then route member r to lane r
+            const int mine = l < c ? mem[l] : 0x7FFFFFFF;
+            int rank = 0;
+            for (int t = 0; t < c; ++t) rank += __shfl(mine, t) < mine ? 1 : 0;
+            const int sorted = __builtin_amdgcn_ds_permute((rank < kWave ? rank : kWave - 1) * 4, mine);
+            constexpr int BT = 8;                        // rows in flight per batch
+            for (int t0 = 0; t0 < c; t0 += BT) {
+                float x[BT][EPL];
+#pragma unroll
+                for (int b = 0; b < BT; ++b) {
+                    const int t = t0 + b < c ? t0 + b : c - 1;
+                    const int tok = __builtin_amdgcn_readlane(sorted, t);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) x[b][e] = elem_f32(vcur_h[static_cast<size_t>(tok) * D + col + e]);
+                }
+#pragma unroll
+                for (int b = 0; b < BT; ++b)
+                    if (t0 + b < c)
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[e] += x[b][e];
+            }
+        } else {
+            // large groups: repeatedly take the smallest member above the last
+            int last = -1;
+            for (int r = 0; r < c; ++r) {
+                int cand = 0x7FFFFFFF;
+                for (int t = l; t < c; t += kWave) {
+                    const int x = mem[t];
+                    cand = (x > last && x < cand) ? x : cand;
+                }
+                last = wave_min(cand);
+                add_row(last);
+            }
+        }
+        const float tot = static_cast<float>(m + c);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) cv[si * D + col + e] = f32_elem<T>(acc[e] / tot);
+        if (l == 0) ccount[si] = m + c;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+    if (l == 0) {
+        cids[si] = kids[ti];
+        cts[si] = step;
+        cnorm[si] = __builtin_sqrtf(sq);
+    }
+}
+
+hipError_t launch_tc_merge_scatter(bool bf16, int d, int H, int N, int cap, const int32_t* dest,
+                                   const int32_t* grp_cnt, const int32_t* grp_off,
+                                   const int32_t* grp_mem, const void* k_cur, const void* v_cur,
+                                   const uint16_t* kcur_ids, int32_t step, void* ck, void* cv,
+                                   uint16_t* cids, int32_t* cts, float* cnorm, int32_t* ccount,
+                                   hipStream_t s) {
+    if (H == 0 || N == 0) return hipSuccess;
+    dim3 grid((N + kMergeTokensPerBlock - 1) / kMergeTokensPerBlock, H);
+    timer_begin("tempcache_merge_scatter", s);
+#define FASTAR_MSCATTER(T, DD)                                                                     \
+    hipLaunchKernelGGL((tc_merge_scatter_kernel<T, DD>), grid, dim3(64 * kMergeTokensPerBlock), 0, s, \
+                       dest, grp_cnt, grp_off, grp_mem, static_cast<const T*>(k_cur),                 \
+                       static_cast<const T*>(v_cur), kcur_ids, step, static_cast<T*>(ck),             \
+                       static_cast<T*>(cv), cids, cts, cnorm, ccount, N, cap)
+    if (bf16) {
+        if (d == 64) FASTAR_MSCATTER(uint16_t, 64); else FASTAR_MSCATTER(uint16_t, 128);
+    } else {
+        if (d == 64) FASTAR_MSCATTER(float, 64); else FASTAR_MSCATTER(float, 128);
+    }
+#undef FASTAR_MSCATTER
     timer_end(s);
     return hipGetLastError();
 }

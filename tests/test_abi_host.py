@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fastar_abi_version() == 1
+    assert lib.fastar_abi_version() == _lib.FASTAR_ABI_VERSION == 2
     for code, name in [(0, "FASTAR_OK"), (-1, "FASTAR_EINVAL"), (-2, "FASTAR_EDTYPE"),
                        (-3, "FASTAR_ESHAPE"), (-4, "FASTAR_EWORKSPACE"), (-5, "FASTAR_ECAPACITY"),
                        (-6, "FASTAR_EHIP")]:
@@ -70,8 +70,8 @@ def test_workspace_queries(lib):
     assert lib.fastar_bucket_sort_workspace(2, 0, 5) == 0
 
 
-def _cache(H=1, cap=64, d=64, dtype=0, knorm=FAKE):
-    return _lib.FastarCache(H, cap, d, dtype, FAKE, FAKE, FAKE, FAKE, FAKE, knorm)
+def _cache(H=1, cap=64, d=64, dtype=0, knorm=FAKE, count=None):
+    return _lib.FastarCache(H, cap, d, dtype, FAKE, FAKE, FAKE, FAKE, FAKE, knorm, count)
 
 
 def test_annsa_validation(lib):
@@ -142,3 +142,26 @@ def test_timer_without_launches(lib):
     assert lib.fastar_timer_start() == 0
     buf = (_lib.FastarKernelTime * 4)()
     assert lib.fastar_timer_stop(buf, 4) == 0
+
+
+def test_cache_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of fastar_cache has the header's size and offsets
+    (a C program built from include/fastar.h prints them)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = tmp_path / "layout.c"
+    names = [n for n, _ in _lib.FastarCache._fields_]
+    body = "".join(f'    printf("%zu\\n", offsetof(fastar_cache, {n}));\n' for n in names)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fastar.h"\n'
+                   'int main(void) {\n    printf("%zu\\n", sizeof(fastar_cache));\n' + body +
+                   '    return 0;\n}\n')
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-I", os.path.join(root, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(_lib.FastarCache)
+    assert out[1:] == [getattr(_lib.FastarCache, n).offset for n in names]

@@ -6,8 +6,8 @@ the storage precision. It contains none of the method's arithmetic: no hashing,
 no attention, no cache policy. Both the CPU oracle and the HIP path consume the
 exact same bytes produced here.
 """
-from .gen import (CONFIGS, WorkloadConfig, Step, make_step, rollout_chunks, commit_case,
+from .gen import (CONFIGS, WorkloadConfig, Step, make_step, rollout_chunks, commit_case, group_sizes,
                   bf16_round, bf16_bits_to_f32, f32_to_bf16_bits)
 
-__all__ = ["CONFIGS", "WorkloadConfig", "Step", "make_step", "rollout_chunks", "commit_case",
+__all__ = ["CONFIGS", "WorkloadConfig", "Step", "make_step", "rollout_chunks", "commit_case", "group_sizes",
            "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits"]

@@ -323,3 +323,15 @@ def commit_case(seed: int, H: int, N: int, cap: int, d: int, n_valid, P: int,
         cos[h] = np.where(m, rng.uniform(0.95, 1.0, N), rng.uniform(-1.0, 0.9, N)).astype(f)
     out["best"], out["cos"] = best, cos
     return out
+
+
+def group_sizes(seed: int, H: int, cap: int, max_m: int = 32) -> np.ndarray:
+    """Group sizes of a mean-merged cache standing in for one that has been
+    merged for a while: ``[H, cap]`` int32 drawn uniformly from 1..max_m
+    (``PCG64(SeedSequence([seed, 104729]))``).  Slot 0 of every head is
+    given ``max_m`` so the largest size always occurs."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 104729])))
+    m = rng.integers(1, max_m + 1, (H, cap)).astype(np.int32)
+    if cap:
+        m[:, 0] = max_m
+    return m
