@@ -15,6 +15,9 @@ TempCache commit, whose select phase keeps only one CU per head busy.  The
 headline issues the calls one by one; ``ms_per_step_graph`` replays the same
 step captured as a HIP graph (one graph per cache copy) and
 ``ms_per_step_eager_one_stream`` issues the calls on one stream.
+``mean_merge`` times the same step on a mean-merged cache (Lemma 5.1 of the
+FAST-AR summary: slots carry group sizes, AnnSA adds ln m to their logits and
+the commit folds matched tokens into their slot's group).
 
 Inputs are seeded synthetic tensors, resident in HBM before the timed region.
 Every timed step starts from its own pristine copy of the cache (the commit
@@ -63,6 +66,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU-oracle sample budget (heads are added until it is spent)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="skip the mean-merged-cache variant of the step")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="only time the bucket-attention kernel at P = 0, 1, 2, 3 and the "
                          "config's P (one JSON line: TFLOP/s on kept pairs vs the bf16 MFMA peak)")
@@ -256,6 +261,45 @@ def main():
                       "frac_hbm_peak": step_bytes[k] / (step_ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS}
                   for k in step_bytes if step_ms.get(k)}
 
+    # ---- the same step on a mean-merged cache (Lemma 5.1 of the FAST-AR
+    # summary): slots carry group sizes (uniform 1..32), AnnSA shifts their
+    # logits by ln m and the commit folds every matched token into its slot
+    merge = None
+    if not args.no_merge:
+        from workloads import group_sizes
+        mbase = base.clone()
+        mbase.count = torch.from_numpy(group_sizes(args.seed, H, cap)).to(dev)
+        mit = iter([mbase.clone() for _ in range(args.warmup + 2 * args.steps)])
+        for _ in range(args.warmup):
+            run(two, next(mit))
+        ms_merge = timed(lambda i: run(two, next(mit)))
+        with fa.kernel_timer() as kt2:
+            for _ in range(args.steps):
+                run(one, next(mit))
+        torch.cuda.synchronize()
+        mk_ms = {k: v[1] / max(1, v[0]) for k, v in kt2.times.items()}
+        mprobe = mbase.clone()
+        mres = fa.tempcache_update(mprobe, q, ids["q"], kc, vc, ids["k"], P, cfg.tau, st.step,
+                                   best_in=two.best, cos_in=two.best_cos)
+        mcounts = mres["counts"].double().sum(0)
+        matched, groups = float(mcounts[0]), float(mcounts[1])
+        mwritten = float((mres["dest"] >= 0).sum())
+        # K row copied, norm/id/ts per written token; a group reads its old value,
+        # its members' values and its size, writes value and size; the other
+        # written tokens copy their value; dest and group size/offset per token
+        mbytes = (mwritten * (2 * d * esz + 10) + groups * (2 * d * esz + 8)
+                  + matched * (d * esz + 4) + (mwritten - groups) * (2 * d * esz + 4)
+                  + H * Nq * 12.0)
+        ms_ms = mk_ms.get("tempcache_merge_scatter")
+        merge = {"ms_per_step": ms_merge, "value_tflops": flops / (ms_merge * 1e-3) / 1e12,
+                 "group_sizes": "uniform 1..32 per slot",
+                 "kernel_ms": mk_ms,
+                 "merge_scatter": {"bytes": mbytes,
+                                   "GB/s": mbytes / (ms_ms * 1e-3) / 1e9 if ms_ms else None,
+                                   "groups": groups, "matched": matched},
+                 "annsa_attn_GB/s": sa_bytes / (mk_ms["annsa_attn"] * 1e-3) / 1e9
+                 if mk_ms.get("annsa_attn") else None}
+
     line = {
         "metric": "attention step latency (ms) + achieved bf16 TFLOP/s on kept pairs, Wan-1.3B chunk",
         "value": value_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -273,6 +317,7 @@ def main():
         "kernel_gbs": kernel_gbs,
         "kept_pairs": {"annsa": sa_pairs, "annca": ca_pairs,
                        "annsa_frac_of_dense": sa_pairs / (H * Nq * (cap + Nq))},
+        "mean_merge": merge,
     }
 
     if not args.no_cpu_baseline:

@@ -42,6 +42,9 @@ constexpr int SLOT_CHUNK = SEL_NT * SLOT_ITEMS;
 // Caches up to this many slots keep the select's claim table and refreshed
 // bitmap in LDS (4 bytes + 1 bit per slot: 132 KiB at the limit).
 constexpr int kLdsClaimSlots = 32768;
+// Dynamic LDS the select may take (the 160 KiB of a workgroup less room for
+// its static arrays, about 1.2 KiB).
+constexpr size_t kSelectDynLds = 160 * 1024 - 2048;
 
 __device__ __forceinline__ uint32_t ts_key(int32_t t) { return static_cast<uint32_t>(t) ^ 0x80000000u; }
 
@@ -75,7 +78,9 @@ __device__ __forceinline__ bool is_matched(int b, float c, int n, float tau) {
 
 // LDSC: the claim table (one int per slot) and the refreshed bitmap live in
 // LDS (dynamic, cap <= kLdsClaimSlots); otherwise in the workspace.
-template <bool LDSC>
+// LDSG (mean merge): the group sizes, then offsets, of the chunk's tokens
+// also live in LDS, after the bitmap; otherwise in the workspace.
+template <bool LDSC, bool LDSG>
 __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams p) {
     extern __shared__ int dyn_lds[];
     __shared__ int smem[SEL_NT / kWave];
@@ -120,8 +125,14 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     };
 
     const bool merge = p.grp_cnt != nullptr;                  // uniform
-    int32_t* gcnt = merge ? p.grp_cnt + static_cast<size_t>(h) * N : nullptr;
+    int32_t* gcnt_out = merge ? p.grp_cnt + static_cast<size_t>(h) * N : nullptr;
     int32_t* gpos = merge ? p.grp_pos + static_cast<size_t>(h) * N : nullptr;
+    int32_t* gcnt;                       // group sizes (in LDS: offsets after the scan)
+    if constexpr (LDSG) gcnt = dyn_lds + (LDSC ? cap + words : 0);
+    else gcnt = gcnt_out;
+    // a matched token's position in its group: in registers when the tokens
+    // fit one chunk, else in the workspace
+    int gp[TOK_ITEMS];
 
     // 1. claims.  Only the entries of matched slots are reset, so the claim
     //    array never needs a full clear.
@@ -168,7 +179,10 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
                 wins += win;
                 dest[i] = win ? bi[k] : -1;
                 // mean merge: the token joins the group of its slot's winner
-                if (merge) gpos[i] = atomicAdd(&gcnt[cl[k]], 1);
+                if (merge) {
+                    gp[k] = atomicAdd(&gcnt[cl[k]], 1);
+                    if (N > TOK_CHUNK) gpos[i] = gp[k];
+                }
             }
         }
         int total;
@@ -188,7 +202,7 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     // 2b. mean merge: group offsets (a scan of the group sizes in token
     //     order), then every matched token is placed in its group
     if (merge) {
-        int32_t* goff = p.grp_off + static_cast<size_t>(h) * N;
+        int32_t* goff_out = p.grp_off + static_cast<size_t>(h) * N;
         int32_t* gmem = p.grp_mem + static_cast<size_t>(h) * N;
         int carry = 0;
         for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
@@ -201,9 +215,17 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
             }
             int total;
             int pos = carry + block_exclusive_scan<SEL_NT>(local, smem, total);
+            // each thread rewrites only its own tokens' entries: in LDS the
+            // sizes become offsets (both go to the workspace for the scatter)
 #pragma unroll
             for (int k = 0; k < TOK_ITEMS; ++k) {
-                if (base + k < N) goff[base + k] = pos;
+                if (base + k < N) {
+                    if constexpr (LDSG) {
+                        gcnt_out[base + k] = cn[k];
+                        gcnt[base + k] = pos;
+                    }
+                    goff_out[base + k] = pos;
+                }
                 pos += cn[k];
             }
             carry += total;
@@ -217,7 +239,8 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
                 const int i = base + k;
                 if (i < N && is_matched(bi[k], ci[k], n, p.tau)) {
                     const int w = claim[bi[k]];
-                    gmem[goff[w] + gpos[i]] = i;
+                    const int off = LDSG ? gcnt[w] : goff_out[w];
+                    gmem[off + (N > TOK_CHUNK ? gpos[i] : gp[k])] = i;
                 }
             }
         }
@@ -383,12 +406,19 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
 hipError_t launch_tc_select(const TcSelectParams& p, hipStream_t s) {
     if (p.H == 0) return hipSuccess;
     timer_begin("tempcache_select", s);
-    if (p.cap <= kLdsClaimSlots) {
-        const size_t bytes = (static_cast<size_t>(p.cap) + (p.cap + 31) / 32) * 4;
-        hipLaunchKernelGGL(tc_select_kernel<true>, dim3(p.H), dim3(SEL_NT), bytes, s, p);
-    } else {
-        hipLaunchKernelGGL(tc_select_kernel<false>, dim3(p.H), dim3(SEL_NT), 0, s, p);
-    }
+    const bool ldsc = p.cap <= kLdsClaimSlots;
+    const size_t claim_bytes = ldsc ? (static_cast<size_t>(p.cap) + (p.cap + 31) / 32) * 4 : 0;
+    const size_t grp_bytes = static_cast<size_t>(p.N) * 4;
+    const bool ldsg = p.grp_cnt != nullptr && claim_bytes + grp_bytes <= kSelectDynLds;
+    const size_t bytes = claim_bytes + (ldsg ? grp_bytes : 0);
+    if (ldsc && ldsg)
+        hipLaunchKernelGGL((tc_select_kernel<true, true>), dim3(p.H), dim3(SEL_NT), bytes, s, p);
+    else if (ldsc)
+        hipLaunchKernelGGL((tc_select_kernel<true, false>), dim3(p.H), dim3(SEL_NT), bytes, s, p);
+    else if (ldsg)
+        hipLaunchKernelGGL((tc_select_kernel<false, true>), dim3(p.H), dim3(SEL_NT), bytes, s, p);
+    else
+        hipLaunchKernelGGL((tc_select_kernel<false, false>), dim3(p.H), dim3(SEL_NT), 0, s, p);
     timer_end(s);
     return hipGetLastError();
 }
@@ -502,7 +532,10 @@ __global__ __launch_bounds__(64 * kMergeTokensPerBlock) void tc_merge_scatter_ke
     const int l = threadIdx.x % kWave;
     if (i >= N) return;                                  // wave uniform
     const size_t ti = static_cast<size_t>(h) * N + i;
+    // the group entries are loaded with dest (not after it): one round trip
     const int d = dest[ti];
+    const int c = gcnt[ti];
+    const int g0 = goff[ti];
     if (d < 0 || d >= cap) return;                       // wave uniform
     const size_t si = static_cast<size_t>(h) * cap + d;
     const T* vcur_h = vc + static_cast<size_t>(h) * N * D;
@@ -519,7 +552,6 @@ __global__ __launch_bounds__(64 * kMergeTokensPerBlock) void tc_merge_scatter_ke
 #pragma unroll
     for (int e = 0; e < EPL; ++e) ck[si * D + col + e] = kx[e];
 
-    const int c = gcnt[ti];
     if (c == 0) {                                        // a group of one
 #pragma unroll
         for (int e = 0; e < EPL; ++e) cv[si * D + col + e] = vc[ti * D + col + e];
@@ -530,7 +562,7 @@ __global__ __launch_bounds__(64 * kMergeTokensPerBlock) void tc_merge_scatter_ke
         float acc[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] = static_cast<float>(m) * elem_f32(cv[si * D + col + e]);
-        const int32_t* mem = gmem + static_cast<size_t>(h) * N + goff[ti];
+        const int32_t* mem = gmem + static_cast<size_t>(h) * N + g0;
         auto add_row = [&](int tok) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[e] += elem_f32(vcur_h[static_cast<size_t>(tok) * D + col + e]);

@@ -154,11 +154,15 @@ def test_merged_commit_partial_cache():
     _merged_commit_case(prep, n, 0.97)
 
 
-def test_merged_commit_large_groups():
-    """9000 tokens, most claiming 50 slots: groups of about a hundred members
-    take the large-group ordering path; caches above one pass of slots."""
+@pytest.mark.parametrize("N,cap", [(9000, 40000), (8000, 32000), (45000, 50000)])
+def test_merged_commit_large_groups(N, cap):
+    """Most tokens claim 50 slots: groups of a hundred members and more take
+    the large-group ordering path.  The shapes cover every placement of the
+    select's tables: claims in the workspace and groups in LDS (40000 slots),
+    claims in LDS and groups in the workspace (32000 slots, 8000 tokens), both
+    in the workspace (50000 slots, 45000 tokens, several token passes)."""
     require_gpu()
-    H, N, cap, d, P, tau, step = 2, 9000, 40000, 64, 5, 0.95, 1000
+    H, d, P, tau, step = 2, 64, 5, 0.95, 1000
     n_valid = np.array([cap, cap - 3000], np.int32)
     c = commit_case(61, H, N, cap, d, n_valid, P, match_frac=0.7, pool=50)
     m = group_sizes(3, H, cap, 200)
