@@ -16,8 +16,8 @@
 //      thread,
 //   4. writes the unmatched tokens' destinations, the eviction list, the counts
 //      and the new valid-slot count;
-// then a copy kernel moves the written tokens' rows into place (32 lanes per
-// token, 16 bytes each) and records each written key's norm.  Every decision
+// then a copy kernel moves the written tokens' rows into place (16 lanes per
+// token) and records each written key's norm.  Every decision
 // is integer or a single fp32 compare, so results are deterministic.
 //
 // Mean-merged caches (summary, "2. Core Components" A, Lemma 5.1: a slot
@@ -423,44 +423,86 @@ hipError_t launch_tc_select(const TcSelectParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ row scatter
+namespace {
+constexpr int kGroupLanes = 16;                       // lanes per written token
+constexpr int kScatterTokensPerBlock = 256 / kGroupLanes;   // tokens per scatter block
+
+// One lane's share of a d-wide row: D/16 consecutive elements, moved as
+// 8, 16 or 32 bytes (the rows are 16-byte aligned).
+template <typename T, int D>
+struct LaneRow {
+    static constexpr int EPL = D / kGroupLanes;
+    static constexpr int W = EPL * static_cast<int>(sizeof(T)) / 4;     // 32-bit words
+    static_assert(W == 2 || W == 4 || W == 8, "lane share");
+    uint32_t w[W];
+    __device__ __forceinline__ void load(const T* row, int gl) {
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(row) + gl * W;
+        if constexpr (W == 2) {
+            const uint2 a = *reinterpret_cast<const uint2*>(p);
+            w[0] = a.x; w[1] = a.y;
+        } else {
+#pragma unroll
+            for (int q = 0; q < W / 4; ++q) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(p + 4 * q);
+                w[4 * q] = a[0]; w[4 * q + 1] = a[1]; w[4 * q + 2] = a[2]; w[4 * q + 3] = a[3];
+            }
+        }
+    }
+    __device__ __forceinline__ void store(T* row, int gl) const {
+        uint32_t* p = reinterpret_cast<uint32_t*>(row) + gl * W;
+        if constexpr (W == 2) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < W / 4; ++q)
+                *reinterpret_cast<u32x4*>(p + 4 * q) = u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+        }
+    }
+    __device__ __forceinline__ float get(int e) const {
+        if constexpr (sizeof(T) == 2) return __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+        else return __uint_as_float(w[e]);
+    }
+    __device__ __forceinline__ void set(int e, float x) {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t b = f32_to_bf16(x);
+            w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0xFFFFu) | (b << 16)) : ((w[e >> 1] & 0xFFFF0000u) | b);
+        } else {
+            w[e] = __float_as_uint(x);
+        }
+    }
+};
+}  // namespace
+
+// Sixteen lanes per current token (four tokens per wave): a written token's
+// key and value rows move to its slot, with its id, the step as timestamp and
+// the key's norm.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tc_scatter_kernel(
     const int32_t* __restrict__ dest, const T* __restrict__ kc, const T* __restrict__ vc,
     const uint16_t* __restrict__ kids, int32_t step, T* __restrict__ ck, T* __restrict__ cv,
     uint16_t* __restrict__ cids, int32_t* __restrict__ cts, float* __restrict__ cnorm, int N,
     int cap) {
-    constexpr int CPR = D * static_cast<int>(sizeof(T)) / 16;
+    using R = LaneRow<T, D>;
     const int h = blockIdx.y;
-    const int i = blockIdx.x * 8 + threadIdx.x / 32;
-    const int l = threadIdx.x % 32;
-    if (i >= N) return;
+    const int gl = threadIdx.x % kGroupLanes;
+    const int i = blockIdx.x * kScatterTokensPerBlock + threadIdx.x / kGroupLanes;
+    if (i >= N) return;                                  // group uniform
     const size_t ti = static_cast<size_t>(h) * N + i;
     const int d = dest[ti];
-    if (d < 0 || d >= cap) return;                      // 32-lane group uniform
+    if (d < 0 || d >= cap) return;                       // group uniform
     const size_t si = static_cast<size_t>(h) * cap + d;
-    float sq = 0.f;                                     // |k| for the slot
-    for (int c = l; c < 2 * CPR; c += 32) {
-        const bool isv = c >= CPR;
-        const int cc = isv ? c - CPR : c;
-        const u32x4 x = *(reinterpret_cast<const u32x4*>((isv ? vc : kc) + ti * D) + cc);
-        *(reinterpret_cast<u32x4*>((isv ? cv : ck) + si * D) + cc) = x;
-        if (!isv) {
-            if constexpr (sizeof(T) == 2) {
+    R kr, vr;
+    kr.load(kc + ti * D, gl);
+    vr.load(vc + ti * D, gl);
+    kr.store(ck + si * D, gl);
+    vr.store(cv + si * D, gl);
+    float sq = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xFFFF0000u);
-                    sq = __builtin_fmaf(lo, lo, sq);
-                    sq = __builtin_fmaf(hi, hi, sq);
-                }
-            } else {
+    for (int e = 0; e < R::EPL; ++e) sq = __builtin_fmaf(kr.get(e), kr.get(e), sq);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sq = __builtin_fmaf(__uint_as_float(x[i]), __uint_as_float(x[i]), sq);
-            }
-        }
-    }
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) sq += __shfl_xor(sq, off, 32);
-    if (l == 0) {
+    for (int off = kGroupLanes / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+    if (gl == 0) {
         cids[si] = kids[ti];
         cts[si] = step;
         cnorm[si] = __builtin_sqrtf(sq);
@@ -472,7 +514,7 @@ hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int3
                              int32_t step, void* ck, void* cv, uint16_t* cids, int32_t* cts,
                              float* cnorm, hipStream_t s) {
     if (H == 0 || N == 0) return hipSuccess;
-    dim3 grid((N + 7) / 8, H);
+    dim3 grid((N + kScatterTokensPerBlock - 1) / kScatterTokensPerBlock, H);
     timer_begin("tempcache_scatter", s);
 #define FASTAR_SCATTER(T, DD)                                                                     \
     hipLaunchKernelGGL((tc_scatter_kernel<T, DD>), grid, dim3(256), 0, s, dest,                  \
@@ -488,128 +530,111 @@ hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int3
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ mean merge
-namespace {
-template <typename T>
-__device__ __forceinline__ float elem_f32(T x) {
-    if constexpr (sizeof(T) == 2) return bf16_to_f32(x);
-    else return x;
-}
-template <typename T>
-__device__ __forceinline__ T f32_elem(float x) {
-    if constexpr (sizeof(T) == 2) return f32_to_bf16(x);
-    else return x;
-}
-// Minimum over the wave's 64 lanes (every lane ends with it).
-__device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const int o = __shfl_xor(x, off);
-        x = o < x ? o : x;
-    }
-    return x;
-}
-constexpr int kMergeTokensPerBlock = 4;     // one wave per written token
-}  // namespace
 
-// One wave per current token with a destination slot.  Lane l owns elements
-// l*EPL .. l*EPL+EPL-1 of the rows.  The key row, id, timestamp and norm are
-// written as in the replacement scatter.  A token that represents a group of
-// c matched tokens sets the slot's value to (m v + sum of the members'
-// values) / (m + c) in fp32, members taken in ascending token order, and its
-// group size to m + c; any other written token starts a group of one.
+// Sixteen lanes per current token with a destination slot (four tokens per
+// wave; every cross-lane step stays inside a token's 16 lanes, whose lanes
+// are active together).  Lane l of a group owns elements l*D/16 .. of each
+// row.  The key row, id, timestamp and norm are written as in the
+// replacement scatter.  A token that represents a group of c matched tokens
+// sets the slot's value to (m v + sum of the members' values) / (m + c) in
+// fp32, members taken in ascending token order, and its group size to m + c;
+// any other written token starts a group of one.
 template <typename T, int D>
-__global__ __launch_bounds__(64 * kMergeTokensPerBlock) void tc_merge_scatter_kernel(
+__global__ __launch_bounds__(256) void tc_merge_scatter_kernel(
     const int32_t* __restrict__ dest, const int32_t* __restrict__ gcnt, const int32_t* __restrict__ goff,
     const int32_t* __restrict__ gmem, const T* __restrict__ kc, const T* __restrict__ vc,
     const uint16_t* __restrict__ kids, int32_t step, T* __restrict__ ck, T* __restrict__ cv,
     uint16_t* __restrict__ cids, int32_t* __restrict__ cts, float* __restrict__ cnorm,
     int32_t* __restrict__ ccount, int N, int cap) {
-    constexpr int EPL = D / kWave;
-    static_assert(EPL >= 1 && D % kWave == 0, "row split");
+    using R = LaneRow<T, D>;
+    constexpr int EPL = R::EPL;
     const int h = blockIdx.y;
-    const int i = blockIdx.x * kMergeTokensPerBlock + threadIdx.x / kWave;
-    const int l = threadIdx.x % kWave;
-    if (i >= N) return;                                  // wave uniform
+    const int gl = threadIdx.x % kGroupLanes;
+    const int gb = (threadIdx.x % kWave) - gl;         // the group's first lane in the wave
+    const int i = blockIdx.x * kScatterTokensPerBlock + threadIdx.x / kGroupLanes;
+    if (i >= N) return;                                  // group uniform
     const size_t ti = static_cast<size_t>(h) * N + i;
     // the group entries are loaded with dest (not after it): one round trip
     const int d = dest[ti];
     const int c = gcnt[ti];
     const int g0 = goff[ti];
-    if (d < 0 || d >= cap) return;                       // wave uniform
+    if (d < 0 || d >= cap) return;                       // group uniform
     const size_t si = static_cast<size_t>(h) * cap + d;
     const T* vcur_h = vc + static_cast<size_t>(h) * N * D;
-    const int col = l * EPL;
 
-    T kx[EPL];
+    R kr;
+    kr.load(kc + ti * D, gl);
+    kr.store(ck + si * D, gl);
     float sq = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        kx[e] = kc[ti * D + col + e];
-        const float f = elem_f32(kx[e]);
-        sq = __builtin_fmaf(f, f, sq);
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) ck[si * D + col + e] = kx[e];
+    for (int e = 0; e < EPL; ++e) sq = __builtin_fmaf(kr.get(e), kr.get(e), sq);
 
     if (c == 0) {                                        // a group of one
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) cv[si * D + col + e] = vc[ti * D + col + e];
-        if (l == 0) ccount[si] = 1;
+        R vr;
+        vr.load(vc + ti * D, gl);
+        vr.store(cv + si * D, gl);
+        if (gl == 0) ccount[si] = 1;
     } else {
         const int m0 = ccount[si];
         const int m = m0 < 1 ? 1 : m0;
+        R old;
+        old.load(cv + si * D, gl);
+        const int32_t* mem = gmem + static_cast<size_t>(h) * N + g0;
         float acc[EPL];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = static_cast<float>(m) * elem_f32(cv[si * D + col + e]);
-        const int32_t* mem = gmem + static_cast<size_t>(h) * N + g0;
-        auto add_row = [&](int tok) __attribute__((always_inline)) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] += elem_f32(vcur_h[static_cast<size_t>(tok) * D + col + e]);
-        };
-        if (c <= kWave) {
-            // rank each member among the group, then route member r to lane r
-            const int mine = l < c ? mem[l] : 0x7FFFFFFF;
+        for (int e = 0; e < EPL; ++e) acc[e] = static_cast<float>(m) * old.get(e);
+        if (c <= kGroupLanes) {
+            // rank each member within the group, then route member r to lane r
+            const int mine = gl < c ? mem[gl] : 0x7FFFFFFF;
             int rank = 0;
-            for (int t = 0; t < c; ++t) rank += __shfl(mine, t) < mine ? 1 : 0;
-            const int sorted = __builtin_amdgcn_ds_permute((rank < kWave ? rank : kWave - 1) * 4, mine);
-            constexpr int BT = 8;                        // rows in flight per batch
+            for (int t = 0; t < c; ++t) rank += __shfl(mine, gb + t) < mine ? 1 : 0;
+            const int slot_lane = gb + (rank < kGroupLanes ? rank : kGroupLanes - 1);
+            const int sorted = __builtin_amdgcn_ds_permute(slot_lane * 4, mine);
+            constexpr int BT = 4;                        // member rows in flight
             for (int t0 = 0; t0 < c; t0 += BT) {
-                float x[BT][EPL];
+                R x[BT];
 #pragma unroll
                 for (int b = 0; b < BT; ++b) {
                     const int t = t0 + b < c ? t0 + b : c - 1;
-                    const int tok = __builtin_amdgcn_readlane(sorted, t);
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) x[b][e] = elem_f32(vcur_h[static_cast<size_t>(tok) * D + col + e]);
+                    x[b].load(vcur_h + static_cast<size_t>(__shfl(sorted, gb + t)) * D, gl);
                 }
 #pragma unroll
                 for (int b = 0; b < BT; ++b)
                     if (t0 + b < c)
 #pragma unroll
-                        for (int e = 0; e < EPL; ++e) acc[e] += x[b][e];
+                        for (int e = 0; e < EPL; ++e) acc[e] += x[b].get(e);
             }
         } else {
             // large groups: repeatedly take the smallest member above the last
             int last = -1;
             for (int r = 0; r < c; ++r) {
                 int cand = 0x7FFFFFFF;
-                for (int t = l; t < c; t += kWave) {
+                for (int t = gl; t < c; t += kGroupLanes) {
                     const int x = mem[t];
                     cand = (x > last && x < cand) ? x : cand;
                 }
-                last = wave_min(cand);
-                add_row(last);
+#pragma unroll
+                for (int off = kGroupLanes / 2; off >= 1; off >>= 1) {
+                    const int o = __shfl_xor(cand, off);
+                    cand = o < cand ? o : cand;
+                }
+                last = cand;
+                R x;
+                x.load(vcur_h + static_cast<size_t>(last) * D, gl);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[e] += x.get(e);
             }
         }
         const float tot = static_cast<float>(m + c);
+        R out;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) cv[si * D + col + e] = f32_elem<T>(acc[e] / tot);
-        if (l == 0) ccount[si] = m + c;
+        for (int e = 0; e < EPL; ++e) out.set(e, acc[e] / tot);
+        out.store(cv + si * D, gl);
+        if (gl == 0) ccount[si] = m + c;
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
-    if (l == 0) {
+    for (int off = kGroupLanes / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+    if (gl == 0) {
         cids[si] = kids[ti];
         cts[si] = step;
         cnorm[si] = __builtin_sqrtf(sq);
@@ -623,10 +648,10 @@ hipError_t launch_tc_merge_scatter(bool bf16, int d, int H, int N, int cap, cons
                                    uint16_t* cids, int32_t* cts, float* cnorm, int32_t* ccount,
                                    hipStream_t s) {
     if (H == 0 || N == 0) return hipSuccess;
-    dim3 grid((N + kMergeTokensPerBlock - 1) / kMergeTokensPerBlock, H);
+    dim3 grid((N + kScatterTokensPerBlock - 1) / kScatterTokensPerBlock, H);
     timer_begin("tempcache_merge_scatter", s);
 #define FASTAR_MSCATTER(T, DD)                                                                     \
-    hipLaunchKernelGGL((tc_merge_scatter_kernel<T, DD>), grid, dim3(64 * kMergeTokensPerBlock), 0, s, \
+    hipLaunchKernelGGL((tc_merge_scatter_kernel<T, DD>), grid, dim3(256), 0, s,                   \
                        dest, grp_cnt, grp_off, grp_mem, static_cast<const T*>(k_cur),                 \
                        static_cast<const T*>(v_cur), kcur_ids, step, static_cast<T*>(ck),             \
                        static_cast<T*>(cv), cids, cts, cnorm, ccount, N, cap)
