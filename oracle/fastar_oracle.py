@@ -66,6 +66,17 @@ R11 Every matched token joins the group of its top-1 slot (none is dropped):
 R12 Appended and replacing tokens start groups of size 1; an evicted slot's
     group leaves the cache with it.  Selection of the evicted slots is R7's.
 
+Multi-table variant (blog, "3. AnnSA": a token may fall in several buckets;
+summary, Core Components C):
+
+R16 T hash tables, each with its own P planes; a token's id holds T fields of
+    P bits, table t in bits t*P .. t*P+P-1 (so one hash over the T*P planes of
+    all tables gives every field at once; T*P <= 16).
+R17 A query attends to the union over tables of the keys that share its
+    bucket in that table; a key matching in several tables is counted once
+    (a set union, not a sum of per-table attentions).
+R18 The TempCache top-1 searches the same union of buckets.
+
 Tie flags (the decision is numerically fragile; a parallel fp32 result may
 legitimately differ there): a hash bit whose |<x, r>| / (|x| |r|) < 1e-5; an
 argmax whose runner-up cosine is within 1e-5; a threshold test with
@@ -182,6 +193,44 @@ def annsa(q, q_ids, k, v, k_ids, scale: float, k_counts=None) -> Tuple[np.ndarra
     return O, lse
 
 
+def bucket_fields(ids, P: int, T: int) -> np.ndarray:
+    """The T per-table bucket ids held in each id (R16): [N, T] int64,
+    column t = bits t*P .. t*P+P-1."""
+    ids = np.asarray(ids).astype(np.int64)
+    return np.stack([(ids >> (t * P)) & ((1 << P) - 1) for t in range(T)], axis=1)
+
+
+def annsa_multi(q, q_ids, k, v, k_ids, scale: float, P: int, T: int, k_counts=None,
+                block: int = 512) -> Tuple[np.ndarray, np.ndarray]:
+    """Multi-table AnnSA (R16, R17): query i attends to every key that shares
+    its bucket in at least one of the T tables, each such key once:
+    O_i = sum_{j in U_i} softmax_j(l_ij) v_j with U_i = {j : some t has
+    field_t(q_i) = field_t(k_j)} and l_ij as in ``annsa`` (group-size shift
+    included).  Empty U_i gives O = 0, lse = -inf.  Written as a masked dense
+    attention over ``block`` queries at a time."""
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    fq, fk = bucket_fields(q_ids, P, T), bucket_fields(k_ids, P, T)
+    bias = np.zeros(K.shape[0]) if k_counts is None else np.log(_f64(k_counts))
+    O = np.zeros((Q.shape[0], V.shape[1]))
+    lse = np.full(Q.shape[0], -np.inf)
+    for s0 in range(0, Q.shape[0], block):
+        rows = slice(s0, min(Q.shape[0], s0 + block))
+        member = np.zeros((fq[rows].shape[0], K.shape[0]), bool)
+        for t in range(T):
+            member |= fq[rows, t][:, None] == fk[None, :, t]
+        S = np.where(member, (Q[rows] @ K.T) * scale + bias[None, :], -np.inf)
+        has = member.any(axis=1)
+        if not has.any():
+            continue
+        m = np.where(has, S.max(axis=1), 0.0)
+        E = np.where(member, np.exp(S - m[:, None]), 0.0)
+        l = E.sum(axis=1)
+        idx = np.arange(rows.start, rows.stop)[has]
+        O[idx] = (E[has] @ V) / l[has][:, None]
+        lse[idx] = m[has] + np.log(l[has])
+    return O, lse
+
+
 # ---------------------------------------------------------------------------
 # AnnCA  (blog, "2. AnnCA"; summary, Core Components B; R4)
 # ---------------------------------------------------------------------------
@@ -218,13 +267,16 @@ def annca(q, q_ids, frame_len: int, kp, vp, kp_ids, scale: float):
 # TempCache  (blog, "1. TempCache"; summary, Core Components A; R5-R9)
 # ---------------------------------------------------------------------------
 
-def tempcache_top1(q, q_ids, cache_k, cache_ids, n: int):
+def tempcache_top1(q, q_ids, cache_k, cache_ids, n: int, P: Optional[int] = None, T: int = 1):
     """For each current query, its most similar previous-frame key within the
-    query's bucket (R5).
+    query's bucket (R5); with ``T`` > 1 tables of ``P`` bits, within the union
+    of its buckets (R16-R18).
 
     Returns ``(best [N] int64 (-1: no candidate), cos [N] (-inf: none),
     argmax_tie [N] bool, near: list of the candidate slots whose cosine is
     within 1e-5 of the maximum)``."""
+    if T > 1:
+        return _top1_union(q, q_ids, cache_k, cache_ids, n, P, T)
     Q = _f64(q)
     K = _f64(cache_k[:n])
     kid = np.asarray(cache_ids[:n]).astype(np.int64)
@@ -252,6 +304,33 @@ def tempcache_top1(q, q_ids, cache_k, cache_ids, n: int):
             close = kj[c[r] >= s[r] - TIE_EPS]
             near[i] = close
             tie[i] = close.size > 1
+    return best, cos, tie, near
+
+
+def _top1_union(q, q_ids, cache_k, cache_ids, n: int, P: int, T: int):
+    """tempcache_top1 over the union of a query's T buckets (R18): the same
+    cosine, ties and flags, candidates from any table."""
+    Q = _f64(q)
+    K = _f64(cache_k[:n])
+    fq, fk = bucket_fields(q_ids, P, T), bucket_fields(np.asarray(cache_ids)[:n], P, T)
+    N = Q.shape[0]
+    best = np.full(N, -1, np.int64)
+    cos = np.full(N, -np.inf)
+    tie = np.zeros(N, bool)
+    near: List[np.ndarray] = [np.zeros(0, np.int64) for _ in range(N)]
+    qn = np.linalg.norm(Q, axis=1)
+    kn = np.linalg.norm(K, axis=1)
+    for i in range(N):
+        kj = np.nonzero((fk == fq[i][None, :]).any(axis=1))[0]
+        if kj.size == 0:
+            continue
+        den = qn[i] * kn[kj]
+        dots = K[kj] @ Q[i]
+        c = np.where(den > 0, dots / np.where(den > 0, den, 1.0), 0.0)
+        a = int(np.argmax(c))
+        best[i], cos[i] = kj[a], c[a]
+        near[i] = kj[c >= c[a] - TIE_EPS]
+        tie[i] = near[i].size > 1
     return best, cos, tie, near
 
 
