@@ -50,6 +50,7 @@ extern "C" {
 #define FASTAR_ABI_VERSION 2
 #define FASTAR_MAX_PLANES 10      /* bucketed calls: at most 1024 buckets per head */
 #define FASTAR_MAX_HASH_PLANES 16 /* ids are uint16 */
+#define FASTAR_MAX_TABLES 8        /* multi-table AnnSA: tables * P <= 16 */
 
 typedef enum {
     FASTAR_OK = 0,
@@ -170,6 +171,33 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
                                    int32_t Ncur, int32_t P, float scale, void* out,
                                    int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Multi-table AnnSA (blog, "3. AnnSA": a token may fall in several buckets;
+ * summary, Core Components C).  The ids hold ``tables`` fields of P bits:
+ * the bucket of a token in table t is (id >> (t*P)) & (2^P - 1) -- what
+ * fastar_ann_hash returns for planes [H][tables*P][d] holding each table's P
+ * planes in turn.  Query i attends to the union over tables of the context
+ * keys sharing its bucket in that table, each key once:
+ *   out[h][i] = sum_{j in U_i} softmax_j(l_ij) v_j,
+ *   U_i = { j : some t has field_t(k_j) == field_t(q_i) },
+ * l_ij, lse, the empty case, the mean-merge shift and the fused search
+ * (now over U_i) as in fastar_annsa_forward, which is the case tables = 1.
+ * 1 <= tables <= FASTAR_MAX_TABLES, P <= FASTAR_MAX_PLANES and
+ * tables * P <= 16 (FASTAR_ESHAPE otherwise).  The cache's ids must hold the
+ * same fields (fastar_tempcache_update copies a written token's id whole).
+ * ws: fastar_annsa_multi_workspace(H, Nq, cap, Ncur, d, P, tables) bytes; it
+ * also holds each query's running state between the per-table passes.
+ * ------------------------------------------------------------------------ */
+size_t fastar_annsa_multi_workspace(int32_t H, int32_t Nq, int32_t cap, int32_t Ncur, int32_t d,
+                                    int32_t P, int32_t tables);
+fastar_status fastar_annsa_multi_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                         int32_t d, int32_t dtype, const fastar_cache* cache,
+                                         const void* k_cur, const void* v_cur,
+                                         const uint16_t* kcur_ids, int32_t Ncur, int32_t P,
+                                         int32_t tables, float scale, void* out, int32_t out_dtype,
+                                         float* lse, int32_t* best, float* best_cos, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * AnnCA: frame-relevant prompt pruning + cross-attention (blog, "2. AnnCA";

@@ -170,9 +170,13 @@ def annsa_forward(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor, v_c
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                   want_lse: bool = True, ws: Optional[torch.Tensor] = None,
                   search: bool = False, best: Optional[torch.Tensor] = None,
-                  best_cos: Optional[torch.Tensor] = None):
+                  best_cos: Optional[torch.Tensor] = None, tables: int = 1):
     """Bucket-restricted self-attention over [cache ; current chunk]: (out, lse), or
-    (out, lse, best, best_cos) with ``search`` (TempCache's top-1 from the same pass)."""
+    (out, lse, best, best_cos) with ``search`` (TempCache's top-1 from the same pass).
+
+    With ``tables`` > 1 the ids hold one ``P``-bit field per table (hash with
+    planes [H, tables*P, d]) and each query attends to the union of its
+    buckets' keys, each key once."""
     H, Nq, d = q.shape
     Ncur = k_cur.shape[1]
     _ids_check(q_ids, (H, Nq))
@@ -192,12 +196,21 @@ def annsa_forward(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor, v_c
             best_cos = torch.empty(H, Nq, dtype=torch.float32, device=q.device)
     cs = cache.struct() if cache is not None else None
     cap = cache.cap if cache is not None else 0
-    wsp, wsn = _workspace(lib.fastar_annsa_workspace(H, Nq, cap, Ncur, P), q.device, ws)
-    check("fastar_annsa_forward", lib.fastar_annsa_forward(
-        _ptr(q), _ptr(q_ids), H, Nq, d, _dtype_code(q), ctypes.byref(cs) if cs else None,
-        _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), Ncur, P, scale, _ptr(out), _dtype_code(out),
-        _ptr(lse), _ptr(best) if search else None, _ptr(best_cos) if search else None,
-        wsp, wsn, _stream(q.device)))
+    if tables == 1:
+        wsp, wsn = _workspace(lib.fastar_annsa_workspace(H, Nq, cap, Ncur, P), q.device, ws)
+        check("fastar_annsa_forward", lib.fastar_annsa_forward(
+            _ptr(q), _ptr(q_ids), H, Nq, d, _dtype_code(q), ctypes.byref(cs) if cs else None,
+            _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), Ncur, P, scale, _ptr(out), _dtype_code(out),
+            _ptr(lse), _ptr(best) if search else None, _ptr(best_cos) if search else None,
+            wsp, wsn, _stream(q.device)))
+    else:
+        wsp, wsn = _workspace(lib.fastar_annsa_multi_workspace(H, Nq, cap, Ncur, d, P, tables),
+                              q.device, ws)
+        check("fastar_annsa_multi_forward", lib.fastar_annsa_multi_forward(
+            _ptr(q), _ptr(q_ids), H, Nq, d, _dtype_code(q), ctypes.byref(cs) if cs else None,
+            _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), Ncur, P, tables, scale, _ptr(out),
+            _dtype_code(out), _ptr(lse), _ptr(best) if search else None,
+            _ptr(best_cos) if search else None, wsp, wsn, _stream(q.device)))
     return (out, lse, best, best_cos) if search else (out, lse)
 
 

@@ -22,6 +22,7 @@ FASTAR_F32 = 0
 FASTAR_BF16 = 1
 FASTAR_MAX_PLANES = 10
 FASTAR_MAX_HASH_PLANES = 16
+FASTAR_MAX_TABLES = 8
 FASTAR_TIMER_MAX = 8192
 FASTAR_ABI_VERSION = 2
 
@@ -50,6 +51,10 @@ SIGNATURES = {
     "fastar_annsa_forward": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(FastarCache),
                                     _vp, _vp, _vp, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _vp,
                                     _vp, _sz, _vp]),
+    "fastar_annsa_multi_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "fastar_annsa_multi_forward": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32,
+                                          ctypes.POINTER(FastarCache), _vp, _vp, _vp, _i32, _i32,
+                                          _i32, _f32, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fastar_annca_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "fastar_annca_forward": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                     _i32, _f32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),

@@ -36,6 +36,14 @@
 //    stages, so two tiles are in flight while a third is computed on.
 //  * The search uses the cached keys' norms kept in the cache, so a cosine is
 //    one product per (query, key): dot * (1/|k|), times 1/|q| at the end.
+//  * MULTI (multi-table AnnSA; blog, "3. AnnSA": a token may fall in several
+//    buckets): ids hold one P-bit field per table and the host launches the
+//    kernel once per table over that table's items.  A pair whose ids agree
+//    in an earlier table's field was counted there and is masked here, so each
+//    key of a query's union of buckets counts once; each query's online
+//    softmax (unnormalised O, running max and sum) and search state carry over
+//    between the launches through the workspace, and the last launch
+//    normalises.  Each key's id travels with its tile like the norms.
 //  * BIAS (AnnSA over a mean-merged cache; summary, "2. Core Components" A,
 //    Lemma 5.1): a cached slot that stands for m tokens adds ln m to its
 //    logits.  The group sizes travel with the tile like the norms, one load
@@ -90,9 +98,10 @@ struct Tile {
 };
 
 // The pieces every kernel below is built from.
-template <typename T, int D, int MODE, bool SEARCH, int NT, bool BIAS = false>
+template <typename T, int D, int MODE, bool SEARCH, int NT, bool BIAS = false, bool MULTI = false>
 struct Blk {
     static_assert(!BIAS || MODE == MODE_SA, "group-size offsets are AnnSA's");
+    static_assert(!MULTI || MODE == MODE_SA, "tables are AnnSA's");
     static constexpr bool SLOTS = SEARCH || BIAS;     // the tile's key indices go to LDS
     using TL = Tile<T, D, MODE, NT>;
     static constexpr bool BF = TL::BF, HAS_V = TL::HAS_V;
@@ -113,6 +122,7 @@ struct Blk {
         u32x4 v[HAS_V ? E : 1];
         float kn;                   // search: the norm of row (u / CPR) * E + u % CPR (u % CPR < E)
         int kc;                     // bias: that row's group size
+        int kq;                     // multi-table: that row's id
         int* slots;
     };
     // Running state of one query (per lane; the four lane groups of a query
@@ -137,6 +147,7 @@ struct Blk {
         int* kslot;
         float* kinv;
         float* kbias;
+        int* kid;
     };
     // Where one head's keys live: index j < na is row j of (ka, va), else row
     // j - na of (kb, vb).  kn holds the cached keys' norms.
@@ -147,6 +158,8 @@ struct Blk {
         const T* vb;
         const float* kn;
         const int32_t* kcnt;
+        const uint16_t* ida;
+        const uint16_t* idb;
         int na;
     };
 
@@ -243,6 +256,11 @@ struct Blk {
             if constexpr (BIAS) S.kc = sr.na > 0 ? sr.kcnt[jc] : 1;
             S.slots[row] = j;
         }
+        if constexpr (MULTI) {
+            const int row = rb * E + (chunk < E ? chunk : E - 1);
+            const int j = kidx[(tile * KT + row) % KCH];
+            S.kq = *(j < sr.na ? sr.ida + j : sr.idb + (j - sr.na));
+        }
     }
 
     // ``inv_c`` = 1 / (scale * log2 e): a group size m becomes the raw-score
@@ -270,12 +288,20 @@ struct Blk {
                                         : 0.f;
             }
         }
+        if constexpr (MULTI)
+            if (chunk < E) sm.kid[rb * E + chunk] = S.kq;
     }
 
     // One 64-key tile (keys kbase.. of an item with nk keys, the first na of
     // the head's index space cached) against the wave's 16 queries.
+    // ``seen``: for multi-table launches, (query id, table, field bits); a pair
+    // whose ids agree in a field below ``table`` is masked.
+    struct Seen {
+        int qid, table, fbits;
+    };
     static __device__ __forceinline__ void compute_tile(Acc& a, const QF& q, const Smem& sm, int kbase,
-                                                        int nk, int na, float scale_log2, int g, int c16) {
+                                                        int nk, int na, float scale_log2, int g, int c16,
+                                                        const Seen& seen = Seen{0, 0, 0}) {
         // ---- S^T = K Q^T for the 4 key blocks of the tile
         f32x4 s[4];
 #pragma unroll
@@ -333,6 +359,26 @@ struct Blk {
         }
 
         if constexpr (HAS_V) {
+            // ---- multi-table: keys that share the query's bucket in an
+            // earlier table were counted by that table's launch (after the
+            // search: a repeated key gives the same cosine)
+            if constexpr (MULTI) {
+                if (seen.table > 0) {                              // uniform
+                    const uint32_t fm = (1u << seen.fbits) - 1u;
+#pragma unroll
+                    for (int kb4 = 0; kb4 < 4; ++kb4) {
+                        const int4 kk = *reinterpret_cast<const int4*>(&sm.kid[kb4 * 16 + 4 * g]);
+                        const int kv[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const uint32_t x = static_cast<uint32_t>(seen.qid ^ kv[r]);
+                            bool dup = false;
+                            for (int t = 0; t < seen.table; ++t) dup |= ((x >> (t * seen.fbits)) & fm) == 0u;
+                            s[kb4][r] = dup ? kNegInf : s[kb4][r];
+                        }
+                    }
+                }
+            }
             // ---- group-size offsets of a mean-merged cache (after the search,
             // which compares plain cosines)
             if constexpr (BIAS) {
@@ -465,6 +511,46 @@ struct Blk {
         }
     }
 
+    // Multi-table, every launch but the last: the query's state goes to the
+    // workspace instead of the output (the search and sum merged over the four
+    // lane groups as in ``finish``; O stays unnormalised).
+    static __device__ __forceinline__ void store_state(Acc& a, bool qvalid, int g, size_t qi,
+                                                       const AttnParams& p) {
+        if constexpr (SEARCH) {
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float oc = __shfl_xor(a.bc, off);
+                const int os = __shfl_xor(a.bs, off);
+                if (oc > a.bc || (oc == a.bc && os < a.bs)) { a.bc = oc; a.bs = os; }
+            }
+        }
+        float l_tot = a.l + __shfl_xor(a.l, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (!qvalid) return;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(p.st_o + qi * D + db * 16 + 4 * g) = a.o[db];
+        if (g == 0) {
+            p.st_m[qi] = a.m;
+            p.st_l[qi] = l_tot;
+            if constexpr (SEARCH) {
+                p.st_bc[qi] = a.bc;
+                p.st_bs[qi] = a.bs;
+            }
+        }
+    }
+    // Multi-table, every launch but the first: resume the query's state (the
+    // sum enters through lane group 0 only, as ``finish`` adds the groups).
+    static __device__ __forceinline__ void load_state(Acc& a, int g, size_t qi, const AttnParams& p) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) a.o[db] = *reinterpret_cast<const f32x4*>(p.st_o + qi * D + db * 16 + 4 * g);
+        a.m = p.st_m[qi];
+        a.l = g == 0 ? p.st_l[qi] : 0.f;
+        if constexpr (SEARCH) {
+            a.bc = p.st_bc[qi];
+            a.bs = p.st_bs[qi];
+        }
+    }
+
     static __device__ __forceinline__ Src src_of(const AttnParams& p, int h) {
         Src s;
         s.ka = static_cast<const T*>(p.ka) + static_cast<size_t>(h) * p.a_rows * D;
@@ -473,6 +559,8 @@ struct Blk {
         s.vb = (HAS_V && p.vb) ? static_cast<const T*>(p.vb) + static_cast<size_t>(h) * p.b_rows * D : nullptr;
         s.kn = SEARCH ? p.knorm + static_cast<size_t>(h) * p.a_rows : nullptr;
         s.kcnt = BIAS ? p.kcount + static_cast<size_t>(h) * p.a_rows : nullptr;
+        s.ida = MULTI && p.ida ? p.ida + static_cast<size_t>(h) * p.a_rows : nullptr;
+        s.idb = MULTI && p.idb ? p.idb + static_cast<size_t>(h) * p.b_rows : nullptr;
         s.na = 0;
         return s;
     }
@@ -482,19 +570,21 @@ struct Blk {
 
 // NW waves per block; the item is 16*NW queries (SA / TOP1: the 64-query
 // slices of the bucket sort, NW = 4).
-template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false>
+template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false,
+          bool MULTI = false>
 __device__ __forceinline__ void attn_body(const AttnParams& p) {
     constexpr int NT = 64 * NW, QT = 16 * NW;
     static_assert(MODE == MODE_CA || QT == kQTile, "SA / TOP1 items are kQTile queries");
-    using B = Blk<T, D, MODE, SEARCH, NT, BIAS>;
+    using B = Blk<T, D, MODE, SEARCH, NT, BIAS, MULTI>;
     __shared__ __align__(16) T Ks[KT * B::STRK];
     __shared__ __align__(16) T Vs[B::HAS_V ? KT * B::STRV : 1];
     __shared__ __align__(16) int kslot[SEARCH ? KT : 4];
     __shared__ __align__(16) float kinv[SEARCH ? KT : 4];
     __shared__ __align__(16) float kbias[BIAS ? KT : 4];
+    __shared__ __align__(16) int kid[MULTI ? KT : 4];
     __shared__ int sslot[2][B::SLOTS ? KT : 1];
     __shared__ int kidx[KCH];
-    const typename B::Smem sm{Ks, Vs, kslot, kinv, kbias};
+    const typename B::Smem sm{Ks, Vs, kslot, kinv, kbias, kid};
     const float inv_c = BIAS ? 1.f / p.scale_log2 : 0.f;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -547,6 +637,12 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 
     typename B::Acc acc;
     acc.reset();
+    const size_t qi = static_cast<size_t>(h) * p.Nq + qrow;
+    typename B::Seen seen{0, 0, 0};
+    if constexpr (MULTI) {
+        seen = typename B::Seen{qvalid ? static_cast<int>(p.q_ids[qi]) : 0, p.table, p.fbits};
+        if (p.table > 0 && qvalid) B::load_state(acc, g, qi, p);
+    }
     const int nt = (nk + KT - 1) / KT;
 
     // One pipeline step on tile t held in stage S: store it, refill S with
@@ -563,7 +659,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
             }
             B::load_tile(S, kidx, t + 2, sr, tid);
         }
-        if (wave_active) B::compute_tile(acc, qf, sm, t * KT, nk, sr.na, p.scale_log2, g, c16);
+        if (wave_active) B::compute_tile(acc, qf, sm, t * KT, nk, sr.na, p.scale_log2, g, c16, seen);
     };
 
     typename B::Stage A, Bs;
@@ -581,17 +677,21 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
         step(Bs, t + 1);
     }
 
-    const size_t qi = static_cast<size_t>(h) * p.Nq + qrow;
+    if (MULTI && p.table + 1 < p.tables) {
+        B::store_state(acc, qvalid, g, qi, p);
+        return;
+    }
     B::template finish<OT>(acc, qf, qvalid, g, static_cast<OT*>(p.out) + qi * D, p.lse ? p.lse + qi : nullptr,
                            p.best ? p.best + qi : nullptr, p.bcos ? p.bcos + qi : nullptr, p.scale_log2);
 }
 
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
 // registers per lane, i.e. 2 waves per SIMD.
-template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false>
+template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false,
+          bool MULTI = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_kv_kernel(const AttnParams p) {
-    attn_body<T, D, MODE, SEARCH, OT, NW, BIAS>(p);
+    attn_body<T, D, MODE, SEARCH, OT, NW, BIAS, MULTI>(p);
 }
 
 // The search alone stages K only and runs at the occupancy its registers allow.
@@ -618,14 +718,17 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
         hipLaunchKernelGGL((attn_top1_kernel<T, D>), grid, dim3(256), 0, s, p);
     } else if constexpr (MODE == MODE_SA) {
         const bool bias = p.kcount != nullptr && p.a_rows > 0;
-        if (p.best && bias)
-            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, true, OT, 4, true>), grid, dim3(256), 0, s, p);
-        else if (p.best)
-            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, true, OT, 4>), grid, dim3(256), 0, s, p);
-        else if (bias)
-            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, false, OT, 4, true>), grid, dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, false, OT, 4>), grid, dim3(256), 0, s, p);
+        const bool search = p.best != nullptr;
+#define FASTAR_SA(S_, B_, M_) \
+    hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, S_, OT, 4, B_, M_>), grid, dim3(256), 0, s, p)
+        if (p.tables > 1) {
+            if (search) { if (bias) FASTAR_SA(true, true, true); else FASTAR_SA(true, false, true); }
+            else { if (bias) FASTAR_SA(false, true, true); else FASTAR_SA(false, false, true); }
+        } else {
+            if (search) { if (bias) FASTAR_SA(true, true, false); else FASTAR_SA(true, false, false); }
+            else { if (bias) FASTAR_SA(false, true, false); else FASTAR_SA(false, false, false); }
+        }
+#undef FASTAR_SA
     } else {
         hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_CA, false, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0,
                            s, p);

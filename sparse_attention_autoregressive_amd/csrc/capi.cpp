@@ -103,6 +103,24 @@ AnnsaWs carve_annsa(Carver& c, int H, int Nq, int cap, int Ncur, int P) {
     return w;
 }
 
+// Multi-table AnnSA: each query's online-softmax and search state between
+// the per-table launches.
+struct StateWs {
+    float *o = nullptr, *m = nullptr, *l = nullptr, *bc = nullptr;
+    int32_t* bs = nullptr;
+};
+StateWs carve_state(Carver& c, int H, int Nq, int d, int tables) {
+    StateWs w;
+    if (tables <= 1) return w;
+    const long long HQ = static_cast<long long>(H) * Nq;
+    w.o = c.take<float>(HQ * d);
+    w.m = c.take<float>(HQ);
+    w.l = c.take<float>(HQ);
+    w.bc = c.take<float>(HQ);
+    w.bs = c.take<int32_t>(HQ);
+    return w;
+}
+
 struct AnncaWs {
     int32_t* idx;
     int32_t* cnt;
@@ -146,6 +164,10 @@ bool dtype_ok(int dt) { return dt == FASTAR_F32 || dt == FASTAR_BF16; }
 bool d_ok(int d) { return d == 64 || d == 128; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool planes_ok(int P) { return P >= 0 && P <= FASTAR_MAX_PLANES; }
+// Tables of P bits each share one 16-bit id.
+bool tables_ok(int P, int tables) {
+    return tables >= 1 && tables <= FASTAR_MAX_TABLES && P * tables <= FASTAR_MAX_HASH_PLANES;
+}
 
 // Tensor pointer rule: required when the tensor is non-empty, 16-byte aligned when given.
 bool tensor_ok(const void* p, long long elems) {
@@ -243,15 +265,27 @@ size_t fastar_annsa_workspace(int32_t H, int32_t Nq, int32_t cap, int32_t Ncur, 
     return c.off;
 }
 
-fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
-                                   int32_t d, int32_t dtype, const fastar_cache* cache,
-                                   const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
-                                   int32_t Ncur, int32_t P, float scale, void* out,
-                                   int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
-                                   void* ws, size_t ws_bytes, void* stream) {
+size_t fastar_annsa_multi_workspace(int32_t H, int32_t Nq, int32_t cap, int32_t Ncur, int32_t d,
+                                    int32_t P, int32_t tables) {
+    if (H < 0 || Nq < 0 || cap < 0 || Ncur < 0 || !d_ok(d) || !tables_ok(P, tables)) return 0;
+    Carver c(nullptr);
+    carve_annsa(c, H, Nq, cap, Ncur, P);
+    carve_state(c, H, Nq, d, tables);
+    return c.off;
+}
+
+}  // extern "C"
+
+namespace {
+
+fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq, int32_t d,
+                         int32_t dtype, const fastar_cache* cache, const void* k_cur, const void* v_cur,
+                         const uint16_t* kcur_ids, int32_t Ncur, int32_t P, int32_t tables, float scale,
+                         void* out, int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
+                         void* ws, size_t ws_bytes, void* stream) {
     if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return FASTAR_EDTYPE;
     if (H < 0 || Nq < 0 || Ncur < 0 || !std::isfinite(scale) || !(scale > 0.f)) return FASTAR_EINVAL;
-    if (!d_ok(d) || !planes_ok(P)) return FASTAR_ESHAPE;
+    if (!d_ok(d) || !planes_ok(P) || !tables_ok(P, tables)) return FASTAR_ESHAPE;
     if (cache && (cache->H != H || cache->d != d)) return FASTAR_ESHAPE;
     if (cache && cache->dtype != dtype) return FASTAR_EDTYPE;
     if (!cache_ok(cache, H, d, dtype)) return FASTAR_EINVAL;
@@ -265,30 +299,16 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
         return FASTAR_EINVAL;
     if ((best == nullptr) != (best_cos == nullptr)) return FASTAR_EINVAL;
     if (best && cache && H > 0 && cap > 0 && !cache->knorm) return FASTAR_EINVAL;
-    const size_t need = fastar_annsa_workspace(H, Nq, cap, Ncur, P);
+    if (tables > 1 && cache && H > 0 && cap > 0 && !cache->ids) return FASTAR_EINVAL;
+    const size_t need = tables > 1 ? fastar_annsa_multi_workspace(H, Nq, cap, Ncur, d, P, tables)
+                                   : fastar_annsa_workspace(H, Nq, cap, Ncur, P);
     if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
     if (HQ == 0) return FASTAR_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     Carver c(ws);
     AnnsaWs w = carve_annsa(c, H, Nq, cap, Ncur, P);
-    IdSet sets[2];
-    sets[0].a = q_ids;
-    sets[0].a_stride = Nq;
-    sets[0].a_fixed = Nq;
-    if (cache) {
-        sets[1].a = cache->ids;
-        sets[1].a_stride = cap;
-        sets[1].a_nvalid = cache->n_valid;
-        sets[1].a_cap = cap;
-    }
-    sets[1].b = kcur_ids;
-    sets[1].b_stride = Ncur;
-    sets[1].nb = Ncur;
-    SortBufs bufs[2] = {w.q, w.k};
-    hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, s);
-    if (e != hipSuccess) return FASTAR_EHIP;
-
+    StateWs st = carve_state(c, H, Nq, d, tables);
     AttnParams p;
     p.q = q;
     p.Nq = Nq;
@@ -313,7 +333,66 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
     p.knorm = cache ? cache->knorm : nullptr;
     p.kcount = cache ? cache->count : nullptr;
     p.scale_log2 = scale * 1.4426950408889634f;
-    return hip_status(launch_attn(MODE_SA, dtype == FASTAR_BF16, d, out_dtype == FASTAR_BF16, H, p, s));
+    p.tables = tables;
+    p.fbits = P;
+    p.q_ids = q_ids;
+    p.ida = cache ? cache->ids : nullptr;
+    p.idb = kcur_ids;
+    p.st_o = st.o;
+    p.st_m = st.m;
+    p.st_l = st.l;
+    p.st_bc = st.bc;
+    p.st_bs = st.bs;
+    // one sort + attention pass per table (the sort buffers are reused)
+    for (int t = 0; t < tables; ++t) {
+        IdSet sets[2];
+        sets[0].shift = t * P;
+        sets[0].a = q_ids;
+        sets[0].a_stride = Nq;
+        sets[0].a_fixed = Nq;
+        if (cache) {
+            sets[1].a = cache->ids;
+            sets[1].a_stride = cap;
+            sets[1].a_nvalid = cache->n_valid;
+            sets[1].a_cap = cap;
+        }
+        sets[1].shift = t * P;
+        sets[1].b = kcur_ids;
+        sets[1].b_stride = Ncur;
+        sets[1].nb = Ncur;
+        SortBufs bufs[2] = {w.q, w.k};
+        hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, s);
+        if (e != hipSuccess) return FASTAR_EHIP;
+        p.table = t;
+        e = launch_attn(MODE_SA, dtype == FASTAR_BF16, d, out_dtype == FASTAR_BF16, H, p, s);
+        if (e != hipSuccess) return FASTAR_EHIP;
+    }
+    return FASTAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                   int32_t d, int32_t dtype, const fastar_cache* cache,
+                                   const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
+                                   int32_t Ncur, int32_t P, float scale, void* out,
+                                   int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
+                                   void* ws, size_t ws_bytes, void* stream) {
+    return annsa_impl(q, q_ids, H, Nq, d, dtype, cache, k_cur, v_cur, kcur_ids, Ncur, P, 1, scale, out,
+                      out_dtype, lse, best, best_cos, ws, ws_bytes, stream);
+}
+
+fastar_status fastar_annsa_multi_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                         int32_t d, int32_t dtype, const fastar_cache* cache,
+                                         const void* k_cur, const void* v_cur,
+                                         const uint16_t* kcur_ids, int32_t Ncur, int32_t P,
+                                         int32_t tables, float scale, void* out, int32_t out_dtype,
+                                         float* lse, int32_t* best, float* best_cos, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    return annsa_impl(q, q_ids, H, Nq, d, dtype, cache, k_cur, v_cur, kcur_ids, Ncur, P, tables, scale,
+                      out, out_dtype, lse, best, best_cos, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ AnnCA

@@ -21,6 +21,7 @@ hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const floa
 // second part (source b) holds ``nb`` ids.  Element e of the set is a[e] for
 // e < na, b[e - na] otherwise.
 struct IdSet {
+    int shift = 0;             // bucket id = (id >> shift) & (2^P - 1): table field of a multi-table id
     const uint16_t* a = nullptr;
     int a_stride = 0;          // ids per head in a's array
     int a_fixed = 0;
@@ -81,6 +82,18 @@ struct AttnParams {
     int cap = 0;
     const float* knorm = nullptr;   // [H][a_rows] key norms of source a (search)
     const int32_t* kcount = nullptr; // [H][a_rows] group sizes of source a (mean-merged cache)
+    // multi-table AnnSA (tables > 1): one launch per table; ids hold a P-bit
+    // field per table; pairs already matched by an earlier table are masked,
+    // and the online-softmax / search state carries over between launches
+    int table = 0, tables = 1, fbits = 0;
+    const uint16_t* q_ids = nullptr;  // [H][Nq]
+    const uint16_t* ida = nullptr;    // [H][a_rows] ids of source a
+    const uint16_t* idb = nullptr;    // [H][b_rows] ids of source b
+    float* st_o = nullptr;            // [H][Nq][D] unnormalised output
+    float* st_m = nullptr;            // [H][Nq] running max (raw score units)
+    float* st_l = nullptr;            // [H][Nq] running sum
+    float* st_bc = nullptr;           // [H][Nq] search: best dot/|k|
+    int32_t* st_bs = nullptr;         // [H][Nq] search: its slot
     // bucket groupings and work items (SA, TOP1)
     const int32_t* qperm = nullptr;
     int qperm_stride = 0;

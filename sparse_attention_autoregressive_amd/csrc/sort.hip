@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
 #pragma unroll
     for (int r = 0; r < kSortTile / 256; ++r) {
         const int e = t * kSortTile + r * 256 + threadIdx.x;
-        if (e < n) atomicAdd(&cnt[set_id(S, h, na, e) & (B - 1)], 1);
+        if (e < n) atomicAdd(&cnt[(set_id(S, h, na, e) >> S.shift) & (B - 1)], 1);
     }
     __syncthreads();
     int* dst = O.hist + (static_cast<size_t>(h) * O.max_tiles + t) * B;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     for (int r = 0; r < kSortTile / 256; ++r) {
         const int e = t * kSortTile + r * 256 + threadIdx.x;
         const bool valid = e < n;
-        const int id = valid ? (set_id(S, h, na, e) & (B - 1)) : 0;
+        const int id = valid ? ((set_id(S, h, na, e) >> S.shift) & (B - 1)) : 0;
         uint64_t mask = __ballot(valid);
         for (int p = 0; p < P; ++p) {
             const bool bit = (id >> p) & 1;

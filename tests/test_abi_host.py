@@ -99,6 +99,27 @@ def test_annsa_validation(lib):
     assert f(*args(best=FAKE, bcos=FAKE, cache=ctypes.byref(c3))) == _lib.FASTAR_EINVAL
 
 
+def test_annsa_multi_validation(lib):
+    f = lib.fastar_annsa_multi_forward
+    wq = lib.fastar_annsa_multi_workspace
+    assert wq(1, 32, 64, 16, 64, 4, 2) > lib.fastar_annsa_workspace(1, 32, 64, 16, 4)
+    assert wq(1, 32, 64, 16, 64, 4, 1) == lib.fastar_annsa_workspace(1, 32, 64, 16, 4)
+    assert wq(1, 32, 64, 16, 64, 6, 3) == 0               # 18 id bits
+    assert wq(1, 32, 64, 16, 64, 2, 9) == 0               # above FASTAR_MAX_TABLES
+    assert wq(1, 32, 64, 16, 64, 4, 0) == 0
+    assert wq(1, 32, 64, 16, 80, 4, 2) == 0               # d
+    need = wq(1, 32, 64, 16, 64, 4, 2)
+    c = _cache()
+    args = lambda **kw: [FAKE, FAKE, 1, 32, 64, 0, ctypes.byref(c), FAKE, FAKE, FAKE, 16,
+                         kw.get("P", 4), kw.get("T", 2), 0.125, FAKE, 0, None, None, None, FAKE,
+                         kw.get("ws", need), None]
+    assert f(*args(ws=need - 1)) == _lib.FASTAR_EWORKSPACE
+    assert f(*args(T=0)) == _lib.FASTAR_ESHAPE
+    assert f(*args(P=6, T=3)) == _lib.FASTAR_ESHAPE
+    assert f(*args(P=11, T=1)) == _lib.FASTAR_ESHAPE
+    assert _lib.FASTAR_MAX_TABLES == 8
+
+
 def test_annca_validation(lib):
     f = lib.fastar_annca_forward
     need = lib.fastar_annca_workspace(1, 30, 10, 8, 4)

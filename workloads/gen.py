@@ -335,3 +335,11 @@ def group_sizes(seed: int, H: int, cap: int, max_m: int = 32) -> np.ndarray:
     if cap:
         m[:, 0] = max_m
     return m
+
+
+def table_planes(seed: int, H: int, tables: int, P: int, d: int) -> np.ndarray:
+    """Hyperplanes of ``tables`` independent hash tables: ``[H, tables*P, d]``
+    float32 ~ N(0, 1), table t in rows t*P .. t*P+P-1
+    (``PCG64(SeedSequence([seed, 130363]))``)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 130363])))
+    return rng.standard_normal((H, tables * P, d)).astype(np.float32)
