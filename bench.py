@@ -17,7 +17,9 @@ step captured as a HIP graph (one graph per cache copy) and
 ``ms_per_step_eager_one_stream`` issues the calls on one stream.
 ``mean_merge`` times the same step on a mean-merged cache (Lemma 5.1 of the
 FAST-AR summary: slots carry group sizes, AnnSA adds ln m to their logits and
-the commit folds matched tokens into their slot's group).
+the commit folds matched tokens into their slot's group).  ``multi_table``
+times AnnSA (with the search) over two hash tables of P planes each -- the
+union of a query's two buckets -- against one table on the same chunk.
 
 Inputs are seeded synthetic tensors, resident in HBM before the timed region.
 Every timed step starts from its own pristine copy of the cache (the commit
@@ -68,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true",
                     help="skip the mean-merged-cache variant of the step")
+    ap.add_argument("--no-multi", action="store_true",
+                    help="skip the two-table AnnSA measurement")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="only time the bucket-attention kernel at P = 0, 1, 2, 3 and the "
                          "config's P (one JSON line: TFLOP/s on kept pairs vs the bf16 MFMA peak)")
@@ -300,6 +304,70 @@ def main():
                  "annsa_attn_GB/s": sa_bytes / (mk_ms["annsa_attn"] * 1e-3) / 1e9
                  if mk_ms.get("annsa_attn") else None}
 
+    # ---- multi-table AnnSA (blog, "3. AnnSA": several buckets per token): the
+    # same chunk and cache hashed into two tables of P planes each; AnnSA with
+    # the fused search over the union of buckets, timed alone (the cache is
+    # only read), against the one-table call on the same ids' first field
+    multi = None
+    if not args.no_multi:
+        from workloads import table_planes
+        T = 2
+        mpl = torch.from_numpy(table_planes(args.seed, H, T, P, d)).to(dev)
+        mq, mk = fa.ann_hash(q, mpl), fa.ann_hash(kc, mpl)
+        mc = base.clone()
+        fa.ann_hash(mc.k, mpl, ids=mc.ids, norms=mc.knorm)
+        lib = fa.load()
+        mws = torch.empty(lib.fastar_annsa_multi_workspace(H, Nq, cap, Nq, d, P, T), dtype=torch.uint8,
+                          device=dev)
+        mo = torch.empty(H, Nq, d, dtype=out_dt, device=dev)
+        ml = torch.empty(H, Nq, dtype=torch.float32, device=dev)
+        mb = torch.empty(H, Nq, dtype=torch.int32, device=dev)
+        mcos = torch.empty(H, Nq, dtype=torch.float32, device=dev)
+        one_mask = (1 << P) - 1
+        mq1, mk1 = (mq.int() & one_mask).short(), (mk.int() & one_mask).short()
+        mc1 = mc.clone()
+        mc1.ids.copy_((mc.ids.int() & one_mask).short())
+        call = lambda tb, qq, kk, cc: fa.annsa_forward(q, qq, kc, vc, kk, P, cache=cc, out=mo, lse=ml,
+                                                       ws=mws, search=True, best=mb, best_cos=mcos,
+                                                       tables=tb)
+        for _ in range(args.warmup):
+            call(T, mq, mk, mc)
+            call(1, mq1, mk1, mc1)
+        ms_multi = timed(lambda i: call(T, mq, mk, mc))
+        ms_single = timed(lambda i: call(1, mq1, mk1, mc1))
+        with fa.kernel_timer() as kt3:
+            for _ in range(args.steps):
+                call(T, mq, mk, mc)
+        torch.cuda.synchronize()
+        k3 = {k: (v[0] // args.steps, v[1] / args.steps) for k, v in kt3.times.items()}
+        # kept pairs: the union over tables by inclusion-exclusion over table subsets
+        qid = mq.long() & 0xFFFF
+        kid = torch.cat([mc.ids.long() & 0xFFFF, mk.long() & 0xFFFF], dim=1)
+        union = 0.0
+        per_table_keys = 0.0
+        for sub in range(1, 1 << T):
+            fmask = sum(one_mask << (t * P) for t in range(T) if (sub >> t) & 1)
+            sgn = 1.0 if bin(sub).count("1") % 2 else -1.0
+            for h in range(H):
+                nq = torch.bincount(qid[h] & fmask, minlength=1 << 16).double()
+                nk = torch.bincount(kid[h] & fmask, minlength=1 << 16).double()
+                union += sgn * float((nq * nk).sum())
+                if bin(sub).count("1") == 1:
+                    per_table_keys += float((nk * (nq > 0)).sum())
+        attn_ms_total = k3.get("annsa_attn", (0, 0.0))[1]
+        # per table: Q, each kept key row (K, V, id, norm); state out/in between
+        # tables; the last table writes O, lse, best and cosine
+        mbytes = (T * H * Nq * (2 * d + 2) + per_table_keys * (4 * d + 6)
+                  + (T - 1) * 2 * H * Nq * (4 * d + 16) + H * Nq * (d * osz + 12))
+        multi = {"tables": T, "planes_per_table": P, "ms_annsa": ms_multi,
+                 "ms_annsa_one_table": ms_single,
+                 "kept_pairs_union": union, "kept_pairs_one_table_equiv": sa_pairs,
+                 "tflops_union_pairs": 4.0 * d * union / (ms_multi * 1e-3) / 1e12,
+                 "kernel_ms_per_call": {k: v[1] for k, v in k3.items()},
+                 "launches_per_call": {k: v[0] for k, v in k3.items()},
+                 "attn": {"bytes": mbytes, "ms": attn_ms_total,
+                          "GB/s": mbytes / (attn_ms_total * 1e-3) / 1e9 if attn_ms_total else None}}
+
     line = {
         "metric": "attention step latency (ms) + achieved bf16 TFLOP/s on kept pairs, Wan-1.3B chunk",
         "value": value_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -318,6 +386,7 @@ def main():
         "kept_pairs": {"annsa": sa_pairs, "annca": ca_pairs,
                        "annsa_frac_of_dense": sa_pairs / (H * Nq * (cap + Nq))},
         "mean_merge": merge,
+        "multi_table": multi,
     }
 
     if not args.no_cpu_baseline:
