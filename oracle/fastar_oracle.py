@@ -77,6 +77,15 @@ R17 A query attends to the union over tables of the keys that share its
     (a set union, not a sum of per-table attentions).
 R18 The TempCache top-1 searches the same union of buckets.
 
+Quantization variant (summary, Core Components A and B name quantization as
+the alternative ANN):
+
+R19 A head's codebook holds B codewords; a token's bucket is its nearest
+    codeword in Euclidean distance, argmin_c |x - c|^2, i.e. argmax_c
+    <x, c> - |c|^2 / 2; ties go to the lowest index.  The codebook is an
+    input (how it is learned is not described).  Its tie flag: the runner-up
+    score within 1e-5 * (|x| max_c |c| + max_c |c|^2) of the best.
+
 Tie flags (the decision is numerically fragile; a parallel fp32 result may
 legitimately differ there): a hash bit whose |<x, r>| / (|x| |r|) < 1e-5; an
 argmax whose runner-up cosine is within 1e-5; a threshold test with
@@ -124,6 +133,29 @@ def ann_hash(x, planes) -> Tuple[np.ndarray, np.ndarray]:
         ids |= (proj[:, p] >= 0).astype(np.int64) << p
         tie |= (rel[:, p] < TIE_EPS).astype(np.int64) << p
     return ids.astype(np.uint16), tie.astype(np.uint16)
+
+
+def ann_quantize(x, codebook) -> Tuple[np.ndarray, np.ndarray]:
+    """Bucket id of every row of ``x`` [N, d]: the index of its nearest
+    codeword in ``codebook`` [B, d] (R19), as argmax_c <x, c> - |c|^2 / 2
+    (lowest index on ties).
+
+    Returns ``(ids uint16 [N], tie bool [N])``: ``tie`` marks rows whose
+    runner-up is within the R19 margin."""
+    X = _f64(x)
+    C = _f64(codebook).reshape(-1, X.shape[1])
+    N, B = X.shape[0], C.shape[0]
+    if B == 1:
+        return np.zeros(N, np.uint16), np.zeros(N, bool)
+    score = X @ C.T - 0.5 * np.sum(C * C, axis=1)[None, :]
+    ids = np.argmax(score, axis=1)
+    top = score[np.arange(N), ids]
+    masked = score.copy()
+    masked[np.arange(N), ids] = -np.inf
+    second = masked.max(axis=1)
+    cn = np.linalg.norm(C, axis=1)
+    margin = TIE_EPS * (np.linalg.norm(X, axis=1) * cn.max() + (cn ** 2).max())
+    return ids.astype(np.uint16), (top - second) < margin
 
 
 # ---------------------------------------------------------------------------
