@@ -51,6 +51,7 @@ extern "C" {
 #define FASTAR_MAX_PLANES 10      /* bucketed calls: at most 1024 buckets per head */
 #define FASTAR_MAX_HASH_PLANES 16 /* ids are uint16 */
 #define FASTAR_MAX_TABLES 8        /* multi-table AnnSA: tables * P <= 16 */
+#define FASTAR_MAX_CODEWORDS 65536 /* quantization ids are uint16 */
 
 typedef enum {
     FASTAR_OK = 0,
@@ -117,6 +118,26 @@ int32_t fastar_abi_version(void);
 fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
                               const float* planes, int32_t P, uint16_t* ids, float* norms,
                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quantization bucket ids (summary, Core Components A and B name quantization
+ * as the alternative ANN to LSH): each vector's bucket is its nearest codeword
+ * of its head's codebook,
+ *
+ *   ids[h][i] = argmin_c |x[h][i] - codebook[h][c]|^2
+ *             = argmax_c <x[h][i], codebook[h][c]> - |codebook[h][c]|^2 / 2
+ *
+ * with the lowest c on ties.
+ * x        [H][N][d] of ``dtype``      codebook  [H][B][d] fp32
+ * ids      [H][N] uint16 (output)      norms     [H][N] fp32 (output, may be NULL): |x|
+ * 1 <= B <= FASTAR_MAX_CODEWORDS.  The inner products are fp32 sums on the
+ * matrix cores; a runner-up within fp32 rounding of the best may be chosen.
+ * The ids feed every bucketed call with P = ceil(log2 B) (B <= 2^FASTAR_MAX_PLANES
+ * there).  How the codebook is obtained is the caller's choice.
+ * ------------------------------------------------------------------------ */
+fastar_status fastar_ann_quantize(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
+                                  const float* codebook, int32_t B, uint16_t* ids, float* norms,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------
  * Stable grouping of tokens by bucket -- the block-sparse layout AnnSA runs

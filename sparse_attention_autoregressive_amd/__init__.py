@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import FASTAR_BF16, FASTAR_F32, FastarError, check, load
 
-__all__ = ["ann_hash", "bucket_sort", "annsa_forward", "annca_forward", "tempcache_update",
+__all__ = ["ann_hash", "ann_quantize", "bucket_sort", "annsa_forward", "annca_forward", "tempcache_update",
            "KVCache", "kernel_timer", "load", "FastarError"]
 
 _DT = {torch.float32: FASTAR_F32, torch.bfloat16: FASTAR_BF16}
@@ -148,6 +148,26 @@ def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] 
         raise ValueError("norms must be float32 [H, N]")
     check("fastar_ann_hash", load().fastar_ann_hash(_ptr(x), _dtype_code(x), H, N, d, _ptr(planes),
                                                     P, _ptr(ids), _ptr(norms), _stream(x.device)))
+    return ids
+
+
+def ann_quantize(x: torch.Tensor, codebook: torch.Tensor, ids: Optional[torch.Tensor] = None,
+                 norms: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Nearest-codeword bucket ids [H, N] (int16 holding uint16 bits) of x
+    [H, N, d] under codebook [H, B, d] float32; with ``norms`` ([H, N]
+    float32) also writes |x|.  Bucketed calls take P = ceil(log2 B)."""
+    H, N, d = x.shape
+    B = codebook.shape[1]
+    if codebook.dtype != torch.float32 or tuple(codebook.shape) != (H, B, d):
+        raise ValueError("codebook must be float32 [H, B, d]")
+    if ids is None:
+        ids = torch.empty(H, N, dtype=torch.int16, device=x.device)
+    _ids_check(ids, (H, N))
+    if norms is not None and (norms.dtype != torch.float32 or tuple(norms.shape) != (H, N)):
+        raise ValueError("norms must be float32 [H, N]")
+    check("fastar_ann_quantize", load().fastar_ann_quantize(
+        _ptr(x), _dtype_code(x), H, N, d, _ptr(codebook), B, _ptr(ids), _ptr(norms),
+        _stream(x.device)))
     return ids
 
 

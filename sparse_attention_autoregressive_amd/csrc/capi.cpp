@@ -227,6 +227,21 @@ fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N
                                   static_cast<hipStream_t>(stream)));
 }
 
+fastar_status fastar_ann_quantize(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
+                                  const float* codebook, int32_t B, uint16_t* ids, float* norms,
+                                  void* stream) {
+    if (!dtype_ok(dtype)) return FASTAR_EDTYPE;
+    if (H < 0 || N < 0) return FASTAR_EINVAL;
+    if (!d_ok(d) || B < 1 || B > FASTAR_MAX_CODEWORDS) return FASTAR_ESHAPE;
+    const long long HN = static_cast<long long>(H) * N;
+    if (!fits_i32(HN * d) || !fits_i32(static_cast<long long>(H) * B * d)) return FASTAR_EINVAL;
+    if (!tensor_ok(x, HN * d) || !small_ok(ids, HN)) return FASTAR_EINVAL;
+    if (!tensor_ok(codebook, (HN > 0 ? static_cast<long long>(H) * B * d : 0))) return FASTAR_EINVAL;
+    if (HN == 0) return FASTAR_OK;
+    return hip_status(launch_quantize(x, dtype == FASTAR_BF16, H, N, d, codebook, B, ids, norms,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------------------ bucket sort
 size_t fastar_bucket_sort_workspace(int32_t H, int32_t N, int32_t P) {
     if (H < 0 || N < 0 || !planes_ok(P)) return 0;

@@ -15,6 +15,10 @@ void timer_end(hipStream_t s);
 hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const float* planes, int P,
                        uint16_t* ids, float* norms, hipStream_t s);
 
+// ------------------------------------------------------------------ quantization ids
+hipError_t launch_quantize(const void* x, bool bf16, int H, int N, int d, const float* codebook, int B,
+                           uint16_t* ids, float* norms, hipStream_t s);
+
 // ------------------------------------------------------------------ sort
 // A set of ids per head: the first part (source a) holds either ``a_fixed``
 // ids or, when ``a_nvalid`` is set, clamp(a_nvalid[h], 0, a_cap) ids; the

@@ -1,0 +1,147 @@
+// Quantization bucket ids: each vector goes to its nearest codeword of its
+// head's codebook (FAST-AR summary, "2. Core Components", parts A and B name
+// quantization as the alternative to LSH for the shared bucket space).
+//
+//   id(x) = argmin_c |x - c|^2 = argmax_c <x, c> - |c|^2 / 2   (lowest c on ties)
+//
+// The inner products X C^T are a dense contraction, so they run on the matrix
+// cores: fp32 v_mfma_f32_16x16x4f32 (bf16 inputs are widened exactly; the
+// codebook keeps its fp32 values).  Scores are formed transposed, S^T = C X^T,
+// so that each lane holds one vector (column) and four codewords (rows) of
+// every 16 x 16 block and keeps a running best over its codewords; the four
+// lane groups of a vector merge at the end.  The contraction index is
+// permuted consistently on both operands -- lane group g sums dimensions
+// g*D/4 .. (g+1)*D/4-1 -- so every lane reads contiguous runs of both.
+//
+// A block of 4 waves takes 64 vectors (16 per wave, held in registers) and
+// streams the codebook through LDS 64 codewords at a time, with each
+// codeword's |c|^2 / 2 (padding codewords past B get +inf).  LDS rows are
+// padded by 4 floats so the 16 rows one quarter-wave reads fall on distinct
+// banks.  The same pass can write |x|.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fastar {
+
+namespace {
+constexpr int QZ_CW = 64;        // codewords per LDS chunk
+constexpr int QZ_TOK = 64;       // vectors per block
+}  // namespace
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ x, const float* __restrict__ cb,
+                                                       int N, int B, uint16_t* __restrict__ ids,
+                                                       float* __restrict__ norms) {
+    constexpr int DG = D / 4;                  // dimensions per lane group
+    constexpr int STR = D + 4;                 // LDS row stride (floats)
+    __shared__ __align__(16) float cs[QZ_CW * STR];
+    __shared__ float hn[QZ_CW];
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int tok = blockIdx.x * QZ_TOK + w * 16 + c16;
+    const bool valid = tok < N;
+
+    // this lane's slice of its vector: dimensions g*DG .. g*DG + DG-1
+    float xv[DG];
+    {
+        const T* row = x + (static_cast<size_t>(h) * N + (valid ? tok : 0)) * D + g * DG;
+#pragma unroll
+        for (int e = 0; e < DG; e += 8) {
+            float v[8];
+            load8_f32(row + e, v);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) xv[e + k] = valid ? v[k] : 0.f;
+        }
+    }
+
+    const float* cbh = cb + static_cast<size_t>(h) * B * D;
+    float best = -__builtin_huge_valf();
+    int bidx = 0x7FFFFFFF;
+    for (int c0 = 0; c0 < B; c0 += QZ_CW) {
+        __syncthreads();                       // the previous chunk is consumed
+        // stage 64 codewords (16-byte pieces; rows past B are zero)
+        for (int pidx = tid; pidx < QZ_CW * (D / 4); pidx += 256) {
+            const int r = pidx / (D / 4), q = pidx % (D / 4);
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c0 + r < B) v = *reinterpret_cast<const float4*>(cbh + static_cast<size_t>(c0 + r) * D + 4 * q);
+            *reinterpret_cast<float4*>(&cs[r * STR + 4 * q]) = v;
+        }
+        __syncthreads();
+        // |c|^2 / 2 of each staged codeword (+inf past B): 4 lanes per row
+        {
+            const int r = tid >> 2, part = tid & 3;
+            float sq = 0.f;
+#pragma unroll 8
+            for (int k = part * DG; k < (part + 1) * DG; ++k) sq = __builtin_fmaf(cs[r * STR + k], cs[r * STR + k], sq);
+            sq += __shfl_xor(sq, 1);
+            sq += __shfl_xor(sq, 2);
+            if (part == 0) hn[r] = c0 + r < B ? 0.5f * sq : __builtin_huge_valf();
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int blk = 0; blk < QZ_CW / 16; ++blk) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const float* crow = &cs[(blk * 16 + c16) * STR + g * DG];
+#pragma unroll
+            for (int e = 0; e < DG; e += 4) {
+                const float4 a = *reinterpret_cast<const float4*>(crow + e);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, xv[e], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, xv[e + 1], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, xv[e + 2], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, xv[e + 3], acc, 0, 0, 0);
+            }
+            // lane holds codewords blk*16 + 4g + r (ascending) of its vector
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int cl = blk * 16 + 4 * g + r;
+                const float sc = acc[r] - hn[cl];
+                if (sc > best) {
+                    best = sc;
+                    bidx = c0 + cl;
+                }
+            }
+        }
+    }
+    // merge the four lane groups (each saw a disjoint quarter of the codewords)
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+        const float ob = __shfl_xor(best, off);
+        const int oi = __shfl_xor(bidx, off);
+        if (ob > best || (ob == best && oi < bidx)) {
+            best = ob;
+            bidx = oi;
+        }
+    }
+    float sq = 0.f;
+    if (norms) {
+#pragma unroll
+        for (int e = 0; e < DG; ++e) sq = __builtin_fmaf(xv[e], xv[e], sq);
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+    }
+    if (valid && g == 0) {
+        ids[static_cast<size_t>(h) * N + tok] = static_cast<uint16_t>(bidx);
+        if (norms) norms[static_cast<size_t>(h) * N + tok] = __builtin_sqrtf(sq);
+    }
+}
+
+hipError_t launch_quantize(const void* x, bool bf16, int H, int N, int d, const float* codebook, int B,
+                           uint16_t* ids, float* norms, hipStream_t s) {
+    if (N == 0 || H == 0) return hipSuccess;
+    dim3 grid((N + QZ_TOK - 1) / QZ_TOK, H);
+    timer_begin("ann_quantize", s);
+#define FASTAR_QZ(T, DD)                                                                     \
+    hipLaunchKernelGGL((quantize_kernel<T, DD>), grid, dim3(256), 0, s, static_cast<const T*>(x), \
+                       codebook, N, B, ids, norms)
+    if (bf16) {
+        if (d == 64) FASTAR_QZ(uint16_t, 64); else FASTAR_QZ(uint16_t, 128);
+    } else {
+        if (d == 64) FASTAR_QZ(float, 64); else FASTAR_QZ(float, 128);
+    }
+#undef FASTAR_QZ
+    timer_end(s);
+    return hipGetLastError();
+}
+
+}  // namespace fastar

@@ -3,7 +3,7 @@ two HIP streams, eagerly or as a captured HIP graph.
 
 The step (FAST-AR summary, "2. Core Components"; blog, sections 1-3):
 
-    ids of Q, K_cur and the prompt keys      (ann_hash)
+    ids of Q, K_cur and the prompt keys      (ann_hash, or ann_quantize)
     AnnSA over [cache ; chunk] + TempCache top-1 in the same pass
     AnnCA over each frame's kept prompt tokens
     TempCache commit of the chunk into the cache
@@ -29,7 +29,7 @@ from typing import Optional
 
 import torch
 
-from . import KVCache, ann_hash, annca_forward, annsa_forward, load, tempcache_update
+from . import KVCache, ann_hash, ann_quantize, annca_forward, annsa_forward, load, tempcache_update
 
 
 class AttentionStep:
@@ -42,9 +42,15 @@ class AttentionStep:
 
     def __init__(self, H: int, Nq: int, d: int, cap: int, P: int, frame_len: int, L: int,
                  tau: float, out_dtype=torch.float32, device="cuda", overlap: bool = True,
-                 scale: Optional[float] = None):
+                 scale: Optional[float] = None, ann: str = "lsh"):
+        """``ann``: "lsh" (the step's ``planes`` are [H, P, d] hyperplanes) or
+        "quantize" (they are an [H, B, d] codebook, B <= 2^P: nearest-codeword
+        buckets)."""
         if frame_len <= 0 or Nq % frame_len:
             raise ValueError("frame_len must divide Nq")
+        if ann not in ("lsh", "quantize"):
+            raise ValueError("ann must be 'lsh' or 'quantize'")
+        self.ann = ann
         dev = torch.device(device)
         lib = load()
         self.H, self.Nq, self.d, self.cap, self.P = H, Nq, d, cap, P
@@ -71,6 +77,12 @@ class AttentionStep:
         self._ev_k, self._ev_sa, self._ev_side = (torch.cuda.Event() for _ in range(3))
 
     # ------------------------------------------------------------------ pieces
+    def _ids(self, x, planes, out):
+        if self.ann == "lsh":
+            ann_hash(x, planes, ids=out)
+        else:
+            ann_quantize(x, planes, ids=out)
+
     def _annsa(self, cache, q, k_cur, v_cur):
         annsa_forward(q, self.ids["q"], k_cur, v_cur, self.ids["k"], self.P, cache=cache,
                       scale=self.scale, out=self.o_sa, lse=self.lse, ws=self.ws_sa, search=True,
@@ -91,9 +103,9 @@ class AttentionStep:
         """Enqueues one step on the current stream (and the side stream)."""
         main = torch.cuda.current_stream(q.device)
         if not self.overlap:
-            ann_hash(q, planes, ids=self.ids["q"])
-            ann_hash(k_cur, planes, ids=self.ids["k"])
-            ann_hash(kp, planes, ids=self.ids["p"])
+            self._ids(q, planes, self.ids["q"])
+            self._ids(k_cur, planes, self.ids["k"])
+            self._ids(kp, planes, self.ids["p"])
             self._annsa(cache, q, k_cur, v_cur)
             self._annca(q, kp, vp)
             self._commit(cache, q, k_cur, v_cur, step)
@@ -101,10 +113,10 @@ class AttentionStep:
         side = self.side
         side.wait_stream(main)
         with torch.cuda.stream(side):
-            ann_hash(k_cur, planes, ids=self.ids["k"])
+            self._ids(k_cur, planes, self.ids["k"])
             self._ev_k.record(side)
-            ann_hash(kp, planes, ids=self.ids["p"])
-        ann_hash(q, planes, ids=self.ids["q"])
+            self._ids(kp, planes, self.ids["p"])
+        self._ids(q, planes, self.ids["q"])
         main.wait_event(self._ev_k)
         self._annsa(cache, q, k_cur, v_cur)
         self._ev_sa.record(main)

@@ -120,6 +120,20 @@ def test_annsa_multi_validation(lib):
     assert _lib.FASTAR_MAX_TABLES == 8
 
 
+def test_quantize_validation(lib):
+    f = lib.fastar_ann_quantize
+    base = lambda **kw: [FAKE, kw.get("dt", 0), 2, 10, kw.get("d", 64), FAKE, kw.get("B", 16), FAKE,
+                         None, None]
+    assert f(*base(B=0)) == _lib.FASTAR_ESHAPE
+    assert f(*base(B=65537)) == _lib.FASTAR_ESHAPE
+    assert f(*base(d=96)) == _lib.FASTAR_ESHAPE
+    assert f(*base(dt=7)) == _lib.FASTAR_EDTYPE
+    args = base()
+    args[5] = MISALIGNED
+    assert f(*args) == _lib.FASTAR_EINVAL
+    assert _lib.FASTAR_MAX_CODEWORDS == 65536
+
+
 def test_annca_validation(lib):
     f = lib.fastar_annca_forward
     need = lib.fastar_annca_workspace(1, 30, 10, 8, 4)

@@ -7,9 +7,9 @@ no attention, no cache policy. Both the CPU oracle and the HIP path consume the
 exact same bytes produced here.
 """
 from .gen import (CONFIGS, WorkloadConfig, Step, make_step, rollout_chunks, commit_case, group_sizes,
-                  table_planes,
+                  table_planes, codebook_from_keys,
                   bf16_round, bf16_bits_to_f32, f32_to_bf16_bits)
 
 __all__ = ["CONFIGS", "WorkloadConfig", "Step", "make_step", "rollout_chunks", "commit_case", "group_sizes",
-           "table_planes",
+           "table_planes", "codebook_from_keys",
            "bf16_round", "bf16_bits_to_f32", "f32_to_bf16_bits"]

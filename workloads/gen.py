@@ -343,3 +343,17 @@ def table_planes(seed: int, H: int, tables: int, P: int, d: int) -> np.ndarray:
     (``PCG64(SeedSequence([seed, 130363]))``)."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 130363])))
     return rng.standard_normal((H, tables * P, d)).astype(np.float32)
+
+
+def codebook_from_keys(cache_k: np.ndarray, n_valid, B: int, seed: int, noise: float = 0.1) -> np.ndarray:
+    """A codebook per head standing in for one fitted to the keys: ``B``
+    distinct valid cached keys (``PCG64(SeedSequence([seed, 155921]))``
+    chooses them) plus ``noise`` * N(0, 1); ``[H, B, d]`` float32."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 155921])))
+    H, _, d = cache_k.shape
+    out = np.empty((H, B, d), np.float32)
+    for h in range(H):
+        n = int(np.asarray(n_valid).reshape(-1)[h if np.size(n_valid) > 1 else 0])
+        pick = rng.choice(n, size=B, replace=False)
+        out[h] = cache_k[h][pick] + noise * rng.standard_normal((B, d))
+    return out
