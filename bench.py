@@ -20,6 +20,8 @@ FAST-AR summary: slots carry group sizes, AnnSA adds ln m to their logits and
 the commit folds matched tokens into their slot's group).  ``multi_table``
 times AnnSA (with the search) over two hash tables of P planes each -- the
 union of a query's two buckets -- against one table on the same chunk.
+``quantize`` times the step with nearest-codeword buckets (a 2^P-codeword
+codebook per head) in place of the hyperplanes.
 
 Inputs are seeded synthetic tensors, resident in HBM before the timed region.
 Every timed step starts from its own pristine copy of the cache (the commit
@@ -72,6 +74,8 @@ def parse():
                     help="skip the mean-merged-cache variant of the step")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the two-table AnnSA measurement")
+    ap.add_argument("--no-quantize", action="store_true",
+                    help="skip the quantization-bucket step")
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="only time the bucket-attention kernel at P = 0, 1, 2, 3 and the "
                          "config's P (one JSON line: TFLOP/s on kept pairs vs the bf16 MFMA peak)")
@@ -368,6 +372,42 @@ def main():
                  "attn": {"bytes": mbytes, "ms": attn_ms_total,
                           "GB/s": mbytes / (attn_ms_total * 1e-3) / 1e9 if attn_ms_total else None}}
 
+    # ---- quantization buckets (summary, Core Components A/B): the same step
+    # with nearest-codeword ids from a 2^P-codeword codebook per head (drawn from
+    # the cached keys) instead of the hyperplanes
+    quant = None
+    if not args.no_quantize:
+        from workloads import codebook_from_keys
+        Bq = 1 << P
+        cbk = torch.from_numpy(codebook_from_keys(st.cache_k, st.n_valid, Bq, args.seed)).to(dev)
+        qbase = base.clone()
+        fa.ann_quantize(qbase.k, cbk, ids=qbase.ids, norms=qbase.knorm)
+        qs = AttentionStep(H, Nq, d, cap, P, cfg.frame_len, cfg.L, cfg.tau, out_dtype=out_dt,
+                           device=dev, overlap=True, ann="quantize")
+        qs1 = AttentionStep(H, Nq, d, cap, P, cfg.frame_len, cfg.L, cfg.tau, out_dtype=out_dt,
+                            device=dev, overlap=False, ann="quantize")
+        qit = iter([qbase.clone() for _ in range(args.warmup + 2 * args.steps)])
+        qrun = lambda s_, c_: s_(c_, q, kc, vc, kp, vp, cbk, st.step)
+        for _ in range(args.warmup):
+            qrun(qs, next(qit))
+        ms_quant = timed(lambda i: qrun(qs, next(qit)))
+        with fa.kernel_timer() as kt4:
+            for _ in range(args.steps):
+                qrun(qs1, next(qit))
+        torch.cuda.synchronize()
+        q_ms = {k: v[1] / max(1, v[0]) for k, v in kt4.times.items()}
+        q_launch = {k: v[0] // args.steps for k, v in kt4.times.items()}
+        # the three quantize launches: 2 N B d flops each (N = Nq, Nq, L per head)
+        qz_flops = 2.0 * H * (2 * Nq + cfg.L) * Bq * d / 3
+        qz_bytes = H * (2 * Nq + cfg.L) * (d * esz + 2) / 3
+        qz_ms = q_ms.get("ann_quantize")
+        quant = {"codewords": Bq, "ms_per_step": ms_quant, "kernel_ms": q_ms,
+                 "kernel_launches_per_step": q_launch,
+                 "ann_quantize": {"flops_per_launch": qz_flops, "bytes_per_launch": qz_bytes,
+                                  "TFLOP/s": qz_flops / (qz_ms * 1e-3) / 1e12 if qz_ms else None,
+                                  "GB/s": qz_bytes / (qz_ms * 1e-3) / 1e9 if qz_ms else None,
+                                  "fp32_mfma_peak_TFLOP/s": 157.3}}
+
     line = {
         "metric": "attention step latency (ms) + achieved bf16 TFLOP/s on kept pairs, Wan-1.3B chunk",
         "value": value_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -387,6 +427,7 @@ def main():
                        "annsa_frac_of_dense": sa_pairs / (H * Nq * (cap + Nq))},
         "mean_merge": merge,
         "multi_table": multi,
+        "quantize": quant,
     }
 
     if not args.no_cpu_baseline:

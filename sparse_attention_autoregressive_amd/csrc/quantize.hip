@@ -26,6 +26,7 @@ namespace fastar {
 namespace {
 constexpr int QZ_CW = 64;        // codewords per LDS chunk
 constexpr int QZ_TOK = 64;       // vectors per block
+constexpr int QZ_NB = 4;         // 16-codeword blocks whose MFMA chains interleave
 }  // namespace
 
 template <typename T, int D>
@@ -69,8 +70,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ x, 
         }
         __syncthreads();
         // |c|^2 / 2 of each staged codeword (+inf past B): 4 lanes per row
-        {
-            const int r = tid >> 2, part = tid & 3;
+        for (int r = tid >> 2; r < QZ_CW; r += 64) {
+            const int part = tid & 3;
             float sq = 0.f;
 #pragma unroll 8
             for (int k = part * DG; k < (part + 1) * DG; ++k) sq = __builtin_fmaf(cs[r * STR + k], cs[r * STR + k], sq);
@@ -79,26 +80,41 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ x, 
             if (part == 0) hn[r] = c0 + r < B ? 0.5f * sq : __builtin_huge_valf();
         }
         __syncthreads();
+        // four 16-codeword blocks at a time: four independent MFMA chains
 #pragma unroll 1
-        for (int blk = 0; blk < QZ_CW / 16; ++blk) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const float* crow = &cs[(blk * 16 + c16) * STR + g * DG];
+        for (int blk0 = 0; blk0 < QZ_CW / 16; blk0 += QZ_NB) {
+            f32x4 acc[QZ_NB];
+            const float* crow[QZ_NB];
+#pragma unroll
+            for (int b = 0; b < QZ_NB; ++b) {
+                acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+                crow[b] = &cs[((blk0 + b) * 16 + c16) * STR + g * DG];
+            }
 #pragma unroll
             for (int e = 0; e < DG; e += 4) {
-                const float4 a = *reinterpret_cast<const float4*>(crow + e);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, xv[e], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, xv[e + 1], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, xv[e + 2], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, xv[e + 3], acc, 0, 0, 0);
-            }
-            // lane holds codewords blk*16 + 4g + r (ascending) of its vector
+                float4 a[QZ_NB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int cl = blk * 16 + 4 * g + r;
-                const float sc = acc[r] - hn[cl];
-                if (sc > best) {
-                    best = sc;
-                    bidx = c0 + cl;
+                for (int b = 0; b < QZ_NB; ++b) a[b] = *reinterpret_cast<const float4*>(crow[b] + e);
+#pragma unroll
+                for (int b = 0; b < QZ_NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[b].x, xv[e], acc[b], 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < QZ_NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[b].y, xv[e + 1], acc[b], 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < QZ_NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[b].z, xv[e + 2], acc[b], 0, 0, 0);
+#pragma unroll
+                for (int b = 0; b < QZ_NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[b].w, xv[e + 3], acc[b], 0, 0, 0);
+            }
+            // lane holds codewords (blk0+b)*16 + 4g + r (ascending in b, r) of its vector
+#pragma unroll
+            for (int b = 0; b < QZ_NB; ++b) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int cl = (blk0 + b) * 16 + 4 * g + r;
+                    const float sc = acc[b][r] - hn[cl];
+                    if (sc > best) {
+                        best = sc;
+                        bidx = c0 + cl;
+                    }
                 }
             }
         }
