@@ -58,27 +58,55 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
 }
 
 // One block per head.  Thread (part, b) owns bucket b over a contiguous range
-// of tiles (1024 / B parts), so every tile count is read by one thread and the
-// loads of a part are independent.
+// of tiles (1024 / B parts), so every tile count is read by one thread.  When
+// a part spans at most kScanRegs tiles (the usual case) the counts of both sets
+// are loaded into registers up front -- one round trip for the whole kernel --
+// and the running offsets are written back from them; longer parts loop.
+constexpr int kScanRegs = 8;
+
 __global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
     __shared__ int part_sum[1024];
     __shared__ int smem[16];
     __shared__ int offs[2][1025];
+    __shared__ int rank_acc[1024];
     const int h = blockIdx.x, B = a.B, tid = threadIdx.x;
     const int parts = 1024 / B;
     const int b = tid % B, part = tid / B;
-    for (int si = 0; si < a.nsets; ++si) {
-        const IdSet& S = a.set[si];
-        const SortBufs& O = a.buf[si];
+    rank_acc[tid] = 0;                    // ordered before its use by the scans' barriers
+    int cnt[2][kScanRegs];
+    int t0s[2], t1s[2];
+    bool regs[2];
+#pragma unroll
+    for (int si = 0; si < 2; ++si) {
+        t0s[si] = t1s[si] = 0;
+        regs[si] = true;
+        if (si >= a.nsets) continue;
         int na;
-        const int n = set_count(S, h, na);
+        const int n = set_count(a.set[si], h, na);
         const int ntiles = sort_tiles(n);
         const int tpp = (ntiles + parts - 1) / parts;
-        const int t0 = min(ntiles, part * tpp), t1 = min(ntiles, t0 + tpp);
+        t0s[si] = min(ntiles, part * tpp);
+        t1s[si] = min(ntiles, t0s[si] + tpp);
+        regs[si] = tpp <= kScanRegs;                               // block uniform
+        const int* hist = a.buf[si].hist + static_cast<size_t>(h) * a.buf[si].max_tiles * B + b;
+#pragma unroll
+        for (int k = 0; k < kScanRegs; ++k)
+            cnt[si][k] = (regs[si] && t0s[si] + k < t1s[si]) ? hist[static_cast<size_t>(t0s[si] + k) * B] : 0;
+    }
+#pragma unroll
+    for (int si = 0; si < 2; ++si) {
+        if (si >= a.nsets) break;
+        const SortBufs& O = a.buf[si];
+        const int t0 = t0s[si], t1 = t1s[si];
         int* hist = O.hist + static_cast<size_t>(h) * O.max_tiles * B + b;
         int sum = 0;
+        if (regs[si]) {
+#pragma unroll
+            for (int k = 0; k < kScanRegs; ++k) sum += cnt[si][k];
+        } else {
 #pragma unroll 4
-        for (int t = t0; t < t1; ++t) sum += hist[static_cast<size_t>(t) * B];
+            for (int t = t0; t < t1; ++t) sum += hist[static_cast<size_t>(t) * B];
+        }
         part_sum[part * B + b] = sum;
         __syncthreads();
         int pre = 0, tot = 0;
@@ -93,10 +121,18 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
         if (tid == 0) offs[si][B] = total;
         __syncthreads();
         int run = offs[si][b] + pre;
-        for (int t = t0; t < t1; ++t) {
-            const int c = hist[static_cast<size_t>(t) * B];
-            hist[static_cast<size_t>(t) * B] = run;
-            run += c;
+        if (regs[si]) {
+#pragma unroll
+            for (int k = 0; k < kScanRegs; ++k) {
+                if (t0 + k < t1) hist[static_cast<size_t>(t0 + k) * B] = run;
+                run += cnt[si][k];
+            }
+        } else {
+            for (int t = t0; t < t1; ++t) {
+                const int c = hist[static_cast<size_t>(t) * B];
+                hist[static_cast<size_t>(t) * B] = run;
+                run += c;
+            }
         }
         if (part == 0) O.off[static_cast<size_t>(h) * (B + 1) + b] = offs[si][b];
         if (tid == 0) O.off[static_cast<size_t>(h) * (B + 1) + B] = total;
@@ -104,18 +140,21 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
     if (a.items.items && a.nsets == 2) {
         // Items in decreasing order of key count (ties: lower bucket first), so
         // the longest items start first.  rank[b] = position of bucket b.
+        // every part counts the buckets of its share of c that rank before b
         __shared__ int slot_tiles[1024];
         const int qc = (part == 0) ? offs[0][b + 1] - offs[0][b] : 0;
-        const int kn = (part == 0) ? offs[1][b + 1] - offs[1][b] : 0;
+        const int kn = offs[1][b + 1] - offs[1][b];
         const int tiles = (qc + kQTile - 1) / kQTile;
-        int rank = 0;
-        if (part == 0) {
-            for (int c = 0; c < B; ++c) {
-                const int kc = offs[1][c + 1] - offs[1][c];
-                rank += (kc > kn) || (kc == kn && c < b);
-            }
-            slot_tiles[rank] = tiles;
+        const int per = (B + parts - 1) / parts;
+        int r = 0;
+        for (int c = part * per; c < min(B, (part + 1) * per); ++c) {
+            const int kc = offs[1][c + 1] - offs[1][c];
+            r += (kc > kn) || (kc == kn && c < b);
         }
+        atomicAdd(&rank_acc[b], r);
+        __syncthreads();
+        const int rank = rank_acc[b];
+        if (part == 0) slot_tiles[rank] = tiles;
         __syncthreads();
         int ntot;
         const int first_by_rank = block_exclusive_scan<1024>(part == 0 ? slot_tiles[b] : 0, smem, ntot);
