@@ -119,6 +119,18 @@ fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N
                               const float* planes, int32_t P, uint16_t* ids, float* norms,
                               void* stream);
 
+/* Several token sets hashed with the same planes in one launch (a step's
+ * queries and current keys, say): the same result as one fastar_ann_hash per
+ * set.  ``x``, ``N``, ``ids`` and ``norms`` are HOST arrays of ``count``
+ * entries holding device pointers and sizes; ``norms`` may be NULL or hold
+ * NULL entries.  1 <= count <= FASTAR_HASH_BATCH; the sets share H, d, dtype
+ * and the planes. */
+#define FASTAR_HASH_BATCH 4
+fastar_status fastar_ann_hash_batch(int32_t count, const void* const* x, const int32_t* N,
+                                    uint16_t* const* ids, float* const* norms, int32_t dtype,
+                                    int32_t H, int32_t d, const float* planes, int32_t P,
+                                    void* stream);
+
 /* ------------------------------------------------------------------------
  * Quantization bucket ids (summary, Core Components A and B name quantization
  * as the alternative ANN to LSH): each vector's bucket is its nearest codeword

@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import FASTAR_BF16, FASTAR_F32, FastarError, check, load
 
-__all__ = ["ann_hash", "ann_quantize", "bucket_sort", "annsa_forward", "annca_forward", "tempcache_update",
+__all__ = ["ann_hash", "ann_hash_batch", "ann_quantize", "bucket_sort", "annsa_forward", "annca_forward", "tempcache_update",
            "KVCache", "kernel_timer", "load", "FastarError"]
 
 _DT = {torch.float32: FASTAR_F32, torch.bfloat16: FASTAR_BF16}
@@ -148,6 +148,39 @@ def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] 
         raise ValueError("norms must be float32 [H, N]")
     check("fastar_ann_hash", load().fastar_ann_hash(_ptr(x), _dtype_code(x), H, N, d, _ptr(planes),
                                                     P, _ptr(ids), _ptr(norms), _stream(x.device)))
+    return ids
+
+
+def ann_hash_batch(xs, planes: torch.Tensor, ids=None, norms=None):
+    """Bucket ids of several [H, N_i, d] tensors under the same planes in one
+    launch (at most ``FASTAR_HASH_BATCH`` tensors); returns the list of id
+    tensors.  ``ids`` / ``norms``: optional lists of outputs (entries may be
+    None)."""
+    xs = list(xs)
+    count = len(xs)
+    if not 1 <= count <= _lib.FASTAR_HASH_BATCH:
+        raise ValueError(f"between 1 and {_lib.FASTAR_HASH_BATCH} tensors")
+    H, _, d = xs[0].shape
+    P = planes.shape[1]
+    if planes.dtype != torch.float32 or tuple(planes.shape) != (H, P, d):
+        raise ValueError("planes must be float32 [H, P, d]")
+    dt = _dtype_code(xs[0])
+    ids = list(ids) if ids is not None else [None] * count
+    norms = list(norms) if norms is not None else [None] * count
+    for i, x in enumerate(xs):
+        if x.shape[0] != H or x.shape[2] != d or _dtype_code(x) != dt:
+            raise ValueError("all tensors must share H, d and dtype")
+        if ids[i] is None:
+            ids[i] = torch.empty(H, x.shape[1], dtype=torch.int16, device=x.device)
+        _ids_check(ids[i], (H, x.shape[1]))
+        if norms[i] is not None and (norms[i].dtype != torch.float32
+                                     or tuple(norms[i].shape) != (H, x.shape[1])):
+            raise ValueError("norms must be float32 [H, N]")
+    arr = lambda vals: (ctypes.c_void_p * count)(*vals)
+    check("fastar_ann_hash_batch", load().fastar_ann_hash_batch(
+        count, arr([_ptr(x) for x in xs]), (ctypes.c_int32 * count)(*[x.shape[1] for x in xs]),
+        arr([_ptr(t) for t in ids]), arr([_ptr(t) for t in norms]), dt, H, d, _ptr(planes), P,
+        _stream(xs[0].device)))
     return ids
 
 

@@ -24,6 +24,7 @@ FASTAR_MAX_PLANES = 10
 FASTAR_MAX_HASH_PLANES = 16
 FASTAR_MAX_TABLES = 8
 FASTAR_MAX_CODEWORDS = 65536
+FASTAR_HASH_BATCH = 4
 FASTAR_TIMER_MAX = 8192
 FASTAR_ABI_VERSION = 2
 
@@ -46,6 +47,7 @@ SIGNATURES = {
     "fastar_status_string": (ctypes.c_char_p, [_i32]),
     "fastar_abi_version": (_i32, []),
     "fastar_ann_hash": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "fastar_ann_hash_batch": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp]),
     "fastar_ann_quantize": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "fastar_bucket_sort_workspace": (_sz, [_i32, _i32, _i32]),
     "fastar_bucket_sort": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),

@@ -227,6 +227,30 @@ fastar_status fastar_ann_hash(const void* x, int32_t dtype, int32_t H, int32_t N
                                   static_cast<hipStream_t>(stream)));
 }
 
+fastar_status fastar_ann_hash_batch(int32_t count, const void* const* x, const int32_t* N,
+                                    uint16_t* const* ids, float* const* norms, int32_t dtype,
+                                    int32_t H, int32_t d, const float* planes, int32_t P,
+                                    void* stream) {
+    static_assert(FASTAR_HASH_BATCH == kHashBatch, "batch size");
+    if (!dtype_ok(dtype)) return FASTAR_EDTYPE;
+    if (count < 1 || count > FASTAR_HASH_BATCH || !x || !N || !ids || H < 0) return FASTAR_EINVAL;
+    if (!d_ok(d) || P < 0 || P > FASTAR_MAX_HASH_PLANES) return FASTAR_ESHAPE;
+    int n[FASTAR_HASH_BATCH];
+    long long total = 0;
+    for (int i = 0; i < count; ++i) {
+        if (N[i] < 0) return FASTAR_EINVAL;
+        const long long HN = static_cast<long long>(H) * N[i];
+        if (!fits_i32(HN * d)) return FASTAR_EINVAL;
+        if (!tensor_ok(x[i], HN * d) || !small_ok(ids[i], HN)) return FASTAR_EINVAL;
+        n[i] = N[i];
+        total += HN;
+    }
+    if (!tensor_ok(planes, total > 0 ? static_cast<long long>(H) * P * d : 0)) return FASTAR_EINVAL;
+    if (total == 0) return FASTAR_OK;
+    return hip_status(launch_hash_batch(count, x, n, ids, norms, dtype == FASTAR_BF16, H, d, planes, P,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 fastar_status fastar_ann_quantize(const void* x, int32_t dtype, int32_t H, int32_t N, int32_t d,
                                   const float* codebook, int32_t B, uint16_t* ids, float* norms,
                                   void* stream) {

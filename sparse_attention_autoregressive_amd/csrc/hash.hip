@@ -8,17 +8,29 @@
 // element).  Partial projections are summed across the group with DPP row
 // butterflies, which leave the same fp32 sum in every lane of the group.  The
 // same pass can also return each vector's norm (a cache keeps its keys'
-// norms for the TempCache cosine search).
+// norms for the TempCache cosine search).  Several token sets (e.g. a step's
+// queries and current keys) can share one launch.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace fastar {
 
+// Up to kHashBatch token sets hashed with the same planes in one launch
+// (grid z = set): one launch instead of one per set.
+struct HashSets {
+    const void* x[kHashBatch];
+    int N[kHashBatch];
+    uint16_t* ids[kHashBatch];
+    float* norms[kHashBatch];
+};
+
 template <typename T, int D, int MAXP>
-__global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x,
-                                                   const float* __restrict__ planes, int N, int P,
-                                                   uint16_t* __restrict__ ids,
-                                                   float* __restrict__ norms) {
+__global__ __launch_bounds__(256) void hash_kernel(const HashSets sets,
+                                                   const float* __restrict__ planes, int P) {
+    const T* __restrict__ x = static_cast<const T*>(sets.x[blockIdx.z]);
+    const int N = sets.N[blockIdx.z];
+    uint16_t* __restrict__ ids = sets.ids[blockIdx.z];
+    float* __restrict__ norms = sets.norms[blockIdx.z];
     constexpr int LPV = D / 8;         // lanes per vector
     constexpr int VPB = 256 / LPV;     // vectors per block per step
     constexpr int UNROLL = 4;
@@ -82,31 +94,53 @@ __global__ __launch_bounds__(256) void hash_kernel(const T* __restrict__ x,
 }
 
 template <typename T, int D>
-static hipError_t hash_dispatch_p(const void* x, int H, int N, const float* planes, int P,
-                                  uint16_t* ids, float* norms, hipStream_t s) {
+static hipError_t hash_dispatch_p(const HashSets& sets, int count, int H, const float* planes, int P,
+                                  hipStream_t s) {
     constexpr int VPB = 256 / (D / 8);
-    int blocks = (N + VPB * 4 - 1) / (VPB * 4);
+    int nmax = 0;
+    for (int i = 0; i < count; ++i) nmax = sets.N[i] > nmax ? sets.N[i] : nmax;
+    int blocks = (nmax + VPB * 4 - 1) / (VPB * 4);
     if (blocks < 1) blocks = 1;
-    dim3 grid(blocks, H);
+    dim3 grid(blocks, H, count);
     timer_begin("ann_hash", s);
     if (P <= 8)
-        hipLaunchKernelGGL((hash_kernel<T, D, 8>), grid, dim3(256), 0, s,
-                           static_cast<const T*>(x), planes, N, P, ids, norms);
+        hipLaunchKernelGGL((hash_kernel<T, D, 8>), grid, dim3(256), 0, s, sets, planes, P);
     else
-        hipLaunchKernelGGL((hash_kernel<T, D, 16>), grid, dim3(256), 0, s,
-                           static_cast<const T*>(x), planes, N, P, ids, norms);
+        hipLaunchKernelGGL((hash_kernel<T, D, 16>), grid, dim3(256), 0, s, sets, planes, P);
     timer_end(s);
     return hipGetLastError();
 }
 
+hipError_t launch_hash_batch(int count, const void* const* x, const int* N, uint16_t* const* ids,
+                             float* const* norms, bool bf16, int H, int d, const float* planes, int P,
+                             hipStream_t s) {
+    HashSets sets;
+    int used = 0;
+    for (int i = 0; i < count && i < kHashBatch; ++i) {
+        if (N[i] == 0) continue;
+        sets.x[used] = x[i];
+        sets.N[used] = N[i];
+        sets.ids[used] = ids[i];
+        sets.norms[used] = norms ? norms[i] : nullptr;
+        ++used;
+    }
+    if (used == 0 || H == 0) return hipSuccess;
+    for (int i = used; i < kHashBatch; ++i) {
+        sets.x[i] = nullptr;
+        sets.N[i] = 0;
+        sets.ids[i] = nullptr;
+        sets.norms[i] = nullptr;
+    }
+    if (bf16)
+        return d == 64 ? hash_dispatch_p<uint16_t, 64>(sets, used, H, planes, P, s)
+                       : hash_dispatch_p<uint16_t, 128>(sets, used, H, planes, P, s);
+    return d == 64 ? hash_dispatch_p<float, 64>(sets, used, H, planes, P, s)
+                   : hash_dispatch_p<float, 128>(sets, used, H, planes, P, s);
+}
+
 hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const float* planes, int P,
                        uint16_t* ids, float* norms, hipStream_t s) {
-    if (N == 0 || H == 0) return hipSuccess;
-    if (bf16)
-        return d == 64 ? hash_dispatch_p<uint16_t, 64>(x, H, N, planes, P, ids, norms, s)
-                       : hash_dispatch_p<uint16_t, 128>(x, H, N, planes, P, ids, norms, s);
-    return d == 64 ? hash_dispatch_p<float, 64>(x, H, N, planes, P, ids, norms, s)
-                   : hash_dispatch_p<float, 128>(x, H, N, planes, P, ids, norms, s);
+    return launch_hash_batch(1, &x, &N, &ids, &norms, bf16, H, d, planes, P, s);
 }
 
 }  // namespace fastar

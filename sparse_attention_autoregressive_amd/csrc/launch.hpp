@@ -12,8 +12,14 @@ void timer_begin(const char* name, hipStream_t s);
 void timer_end(hipStream_t s);
 
 // ------------------------------------------------------------------ hash
+constexpr int kHashBatch = 4;          // token sets per batched launch
 hipError_t launch_hash(const void* x, bool bf16, int H, int N, int d, const float* planes, int P,
                        uint16_t* ids, float* norms, hipStream_t s);
+// ``count`` <= kHashBatch sets (host arrays); ``norms`` may be null, or hold
+// null entries.
+hipError_t launch_hash_batch(int count, const void* const* x, const int* N, uint16_t* const* ids,
+                             float* const* norms, bool bf16, int H, int d, const float* planes, int P,
+                             hipStream_t s);
 
 // ------------------------------------------------------------------ quantization ids
 hipError_t launch_quantize(const void* x, bool bf16, int H, int N, int d, const float* codebook, int B,

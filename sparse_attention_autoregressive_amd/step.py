@@ -9,9 +9,9 @@ The step (FAST-AR summary, "2. Core Components"; blog, sections 1-3):
     TempCache commit of the chunk into the cache
 
 Stream layout (both at the default priority).  The caller's stream carries
-the critical path: hash(Q) -> AnnSA (bucket sort + attention) -> commit.  A
-side stream hashes K_cur (AnnSA waits for it) and the prompt keys, then runs
-AnnCA once AnnSA is done: AnnCA needs only Q, the prompt and the ids, so it
+the critical path: hash(Q, K_cur) in one launch -> AnnSA (bucket sort +
+attention) -> commit.  A side stream hashes the prompt keys, then runs AnnCA
+once AnnSA is done: AnnCA needs only Q, the prompt and the ids, so it
 overlaps the commit, whose select kernel occupies one CU per head.  The step
 ends by joining the side stream into the caller's stream, so consecutive steps
 never overlap (they share the id buffers, workspaces and outputs).
@@ -29,7 +29,8 @@ from typing import Optional
 
 import torch
 
-from . import KVCache, ann_hash, ann_quantize, annca_forward, annsa_forward, load, tempcache_update
+from . import (KVCache, ann_hash, ann_hash_batch, ann_quantize, annca_forward, annsa_forward, load,
+               tempcache_update)
 
 
 class AttentionStep:
@@ -74,7 +75,7 @@ class AttentionStep:
         self.keep = torch.empty(H, F, L, dtype=u8, device=dev)
         self.keep_count = torch.empty(H, F, dtype=torch.int32, device=dev)
         self.side = torch.cuda.Stream(dev)
-        self._ev_k, self._ev_sa, self._ev_side = (torch.cuda.Event() for _ in range(3))
+        self._ev_sa, self._ev_side = (torch.cuda.Event() for _ in range(2))
 
     # ------------------------------------------------------------------ pieces
     def _ids(self, x, planes, out):
@@ -103,9 +104,12 @@ class AttentionStep:
         """Enqueues one step on the current stream (and the side stream)."""
         main = torch.cuda.current_stream(q.device)
         if not self.overlap:
-            self._ids(q, planes, self.ids["q"])
-            self._ids(k_cur, planes, self.ids["k"])
-            self._ids(kp, planes, self.ids["p"])
+            if self.ann == "lsh":
+                ann_hash_batch([q, k_cur, kp], planes, ids=[self.ids["q"], self.ids["k"], self.ids["p"]])
+            else:
+                self._ids(q, planes, self.ids["q"])
+                self._ids(k_cur, planes, self.ids["k"])
+                self._ids(kp, planes, self.ids["p"])
             self._annsa(cache, q, k_cur, v_cur)
             self._annca(q, kp, vp)
             self._commit(cache, q, k_cur, v_cur, step)
@@ -113,11 +117,12 @@ class AttentionStep:
         side = self.side
         side.wait_stream(main)
         with torch.cuda.stream(side):
-            self._ids(k_cur, planes, self.ids["k"])
-            self._ev_k.record(side)
             self._ids(kp, planes, self.ids["p"])
-        self._ids(q, planes, self.ids["q"])
-        main.wait_event(self._ev_k)
+        if self.ann == "lsh":
+            ann_hash_batch([q, k_cur], planes, ids=[self.ids["q"], self.ids["k"]])
+        else:
+            self._ids(q, planes, self.ids["q"])
+            self._ids(k_cur, planes, self.ids["k"])
         self._annsa(cache, q, k_cur, v_cur)
         self._ev_sa.record(main)
         side.wait_event(self._ev_sa)

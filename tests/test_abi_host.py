@@ -120,6 +120,24 @@ def test_annsa_multi_validation(lib):
     assert _lib.FASTAR_MAX_TABLES == 8
 
 
+def test_hash_batch_validation(lib):
+    f = lib.fastar_ann_hash_batch
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    ns = lambda *v: (ctypes.c_int32 * len(v))(*v)
+    ok = lambda c, **kw: f(c, arr(*([FAKE] * c)), ns(*([10] * c)), arr(*([FAKE] * c)), None,
+                           kw.get("dt", 0), 2, kw.get("d", 64), FAKE, kw.get("P", 4), None)
+    assert ok(0) == _lib.FASTAR_EINVAL
+    assert ok(5) == _lib.FASTAR_EINVAL
+    assert ok(2, d=96) == _lib.FASTAR_ESHAPE
+    assert ok(2, P=17) == _lib.FASTAR_ESHAPE
+    assert ok(2, dt=3) == _lib.FASTAR_EDTYPE
+    assert f(2, arr(FAKE, MISALIGNED), ns(10, 10), arr(FAKE, FAKE), None, 0, 2, 64, FAKE, 4,
+             None) == _lib.FASTAR_EINVAL
+    assert f(2, arr(FAKE, FAKE), ns(10, -1), arr(FAKE, FAKE), None, 0, 2, 64, FAKE, 4,
+             None) == _lib.FASTAR_EINVAL
+    assert _lib.FASTAR_HASH_BATCH == 4
+
+
 def test_quantize_validation(lib):
     f = lib.fastar_ann_quantize
     base = lambda **kw: [FAKE, kw.get("dt", 0), 2, 10, kw.get("d", 64), FAKE, kw.get("B", 16), FAKE,

@@ -85,3 +85,20 @@ def test_bucket_sort_ignores_high_bits():
     off, perm = fa.bucket_sort(dev_ids(ids), 3)
     ro, rp = o_sort(ids[0] & 7, 3)
     assert np.array_equal(off.cpu().numpy()[0], ro) and np.array_equal(perm.cpu().numpy()[0], rp)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "wan13_bf16"])
+def test_hash_batch_equals_single_calls(name):
+    """One launch over the step's queries, current keys and prompt keys (three
+    sizes) gives the ids and norms of three separate calls, bit for bit."""
+    require_gpu()
+    prep = prepared(name)
+    st, cfg = prep["step"], prep["cfg"]
+    planes = torch.from_numpy(st.planes).cuda()
+    xs = [dev(a, cfg.dtype) for a in (st.q, st.k_cur, st.kp)]
+    norms = [torch.empty(cfg.H, x.shape[1], dtype=torch.float32, device="cuda") for x in xs]
+    got = fa.ann_hash_batch(xs, planes, norms=norms)
+    for x, g, nb in zip(xs, got, norms):
+        n1 = torch.empty_like(nb)
+        one = fa.ann_hash(x, planes, norms=n1)
+        assert torch.equal(one, g) and torch.equal(n1, nb)
