@@ -4,8 +4,8 @@
 //
 // HBM-bound: every element of x is read once.  Each group of d/8 lanes owns one
 // vector; lane ``seg`` always handles the same 8 coordinates, so its slice of
-// every hyperplane lives in registers for the whole kernel (no LDS traffic per
-// element).  Partial projections are summed across the group with DPP row
+// every hyperplane lives in registers for the whole kernel (staged once per
+// block through LDS; no LDS traffic per element).  Partial projections are summed across the group with DPP row
 // butterflies, which leave the same fp32 sum in every lane of the group.  The
 // same pass can also return each vector's norm (a cache keeps its keys'
 // norms for the TempCache cosine search).  Several token sets (e.g. a step's
@@ -38,13 +38,19 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashSets sets,
     const int seg = threadIdx.x % LPV;
     const int vslot = threadIdx.x / LPV;
 
+    // the head's planes go through LDS once per block (each block would
+    // otherwise read them from L2 once per vector slot)
+    __shared__ __align__(16) float spl[MAXP * D];
+    for (int i = threadIdx.x; i < P * D / 4; i += 256)
+        *reinterpret_cast<float4*>(&spl[4 * i]) =
+            *reinterpret_cast<const float4*>(planes + static_cast<size_t>(h) * P * D + 4 * i);
+    __syncthreads();
     float pl[MAXP][8];
 #pragma unroll
     for (int p = 0; p < MAXP; ++p) {
         if (p < P) {
-            const float* src = planes + (static_cast<size_t>(h) * P + p) * D + seg * 8;
-            float4 a = *reinterpret_cast<const float4*>(src);
-            float4 b = *reinterpret_cast<const float4*>(src + 4);
+            const float4 a = *reinterpret_cast<const float4*>(&spl[p * D + seg * 8]);
+            const float4 b = *reinterpret_cast<const float4*>(&spl[p * D + seg * 8 + 4]);
             pl[p][0] = a.x; pl[p][1] = a.y; pl[p][2] = a.z; pl[p][3] = a.w;
             pl[p][4] = b.x; pl[p][5] = b.y; pl[p][6] = b.z; pl[p][7] = b.w;
         } else {
