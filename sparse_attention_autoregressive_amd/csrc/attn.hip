@@ -60,6 +60,9 @@
 #ifndef CA_WAVES
 #define CA_WAVES 8
 #endif
+#ifndef CA_GROUPS
+#define CA_GROUPS 2              // 16-query groups per AnnCA wave
+#endif
 
 namespace fastar {
 
@@ -292,6 +295,49 @@ struct Blk {
             if (chunk < E) sm.kid[rb * E + chunk] = S.kq;
     }
 
+    // Online softmax of one 16-query group over a 64-key tile (one query per
+    // lane): masks the keys past nk, updates the running max, sum and output
+    // scale, and leaves the probabilities in ``s``.  The running max is kept in
+    // raw score units; the scale folds into the exponent:
+    // p = 2^(s*c - m*c), c = scale * log2(e) > 0.
+    static __device__ __forceinline__ void softmax_update(Acc& a, f32x4 (&s)[4], bool full, int kbase, int nk,
+                                                          float scale_log2, int g) {
+        if (!full) {
+#pragma unroll
+            for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (kbase + kb4 * 16 + 4 * g + r >= nk) s[kb4][r] = kNegInf;
+        }
+        float tmax = kNegInf;
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4)
+            tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb4][0], s[kb4][1]), fmaxf(s[kb4][2], s[kb4][3])));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(a.m, tmax);
+        const float c = scale_log2;
+        const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb4][r], c, -mc));
+                s[kb4][r] = e;
+                psum += e;
+            }
+        }
+        if (__ballot(m_new > a.m) != 0) {                   // some lane's max grew
+            const float alpha = (a.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(a.m, c, -mc));
+            a.l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) a.o[db] *= alpha;
+        }
+        a.l += psum;
+        a.m = m_new;
+    }
+
     // One 64-key tile (keys kbase.. of an item with nk keys, the first na of
     // the head's index space cached) against the wave's 16 queries.
     // ``seen``: for multi-table launches, (query id, table, field bits); a pair
@@ -391,43 +437,7 @@ struct Blk {
                     s[kb4][3] += b.w;
                 }
             }
-            // ---- online softmax, one query per lane.  The running max is kept
-            // in raw score units; the scale folds into the exponent:
-            // p = 2^(s*c - m*c), c = scale * log2(e) > 0.
-            if (!full) {
-#pragma unroll
-                for (int kb4 = 0; kb4 < 4; ++kb4)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (kbase + kb4 * 16 + 4 * g + r >= nk) s[kb4][r] = kNegInf;
-            }
-            float tmax = kNegInf;
-#pragma unroll
-            for (int kb4 = 0; kb4 < 4; ++kb4)
-                tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb4][0], s[kb4][1]), fmaxf(s[kb4][2], s[kb4][3])));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-            const float m_new = fmaxf(a.m, tmax);
-            const float c = scale_log2;
-            const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
-            float psum = 0.f;
-#pragma unroll
-            for (int kb4 = 0; kb4 < 4; ++kb4) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb4][r], c, -mc));
-                    s[kb4][r] = e;
-                    psum += e;
-                }
-            }
-            if (__ballot(m_new > a.m) != 0) {                   // some lane's max grew
-                const float alpha = (a.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(a.m, c, -mc));
-                a.l *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) a.o[db] *= alpha;
-            }
-            a.l += psum;
-            a.m = m_new;
+            softmax_update(a, s, full, kbase, nk, scale_log2, g);
 
             // ---- O^T += V^T P^T
             if constexpr (BF) {
@@ -463,6 +473,85 @@ struct Blk {
 #pragma unroll
                         for (int db = 0; db < NDB; ++db)
                             a.o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[db * 16 + c16], s[kb4][st], a.o[db], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    // AnnCA with two 16-query groups per wave: each K and V fragment read from
+    // LDS feeds the MFMAs of both groups, halving LDS reads per product.
+    static __device__ __forceinline__ void compute_tile2(Acc (&a)[2], const QF (&q)[2], const Smem& sm,
+                                                         int kbase, int nk, float scale_log2, int g,
+                                                         int c16) {
+        static_assert(MODE == MODE_CA && !SEARCH && !BIAS && !MULTI, "two query groups: AnnCA only");
+        f32x4 s[2][4];
+#pragma unroll
+        for (int kb4 = 0; kb4 < 4; ++kb4) {
+            s[0][kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s[1][kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const T* krow = &sm.Ks[(kb4 * 16 + c16) * STRK];
+            if constexpr (BF) {
+                bf16x8_t af[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    af[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 32 + 8 * g);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    s[0][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], q[0].b[ks], s[0][kb4], 0, 0, 0);
+                    s[1][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], q[1].b[ks], s[1][kb4], 0, 0, 0);
+                }
+            } else {
+                float af[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) af[ks] = reinterpret_cast<const float*>(krow)[ks * 4 + g];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    s[0][kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ks], q[0].f[ks], s[0][kb4], 0, 0, 0);
+                    s[1][kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ks], q[1].f[ks], s[1][kb4], 0, 0, 0);
+                }
+            }
+        }
+        const bool full = kbase + KT <= nk;                    // uniform
+        softmax_update(a[0], s[0], full, kbase, nk, scale_log2, g);
+        softmax_update(a[1], s[1], full, kbase, nk, scale_log2, g);
+        if constexpr (BF) {
+#pragma unroll
+            for (int kg = 0; kg < 2; ++kg) {
+                bf16x8_t pb[2];
+#pragma unroll
+                for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pb[qg][r] = static_cast<__bf16>(s[qg][2 * kg][r]);
+                        pb[qg][4 + r] = static_cast<__bf16>(s[qg][2 * kg + 1][r]);
+                    }
+                const T* vb0 = &sm.Vs[(kg * 32 + 4 * g + (c16 >> 2)) * STRV + 4 * (c16 & 3)];
+                v4i16 lo[NDB], hi[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    lo[db] = lds_read_tr(vb0 + db * 16);
+                    hi[db] = lds_read_tr(vb0 + 16 * STRV + db * 16);
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x8_t av = __builtin_bit_cast(
+                        bf16x8_t, __builtin_shufflevector(lo[db], hi[db], 0, 1, 2, 3, 4, 5, 6, 7));
+                    a[0].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[0], a[0].o[db], 0, 0, 0);
+                    a[1].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[1], a[1].o[db], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kb4 = 0; kb4 < 4; ++kb4) {
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const float* vrow = reinterpret_cast<const float*>(&sm.Vs[(kb4 * 16 + 4 * g + st) * STRV]);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const float vv = vrow[db * 16 + c16];
+                        a[0].o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, s[0][kb4][st], a[0].o[db], 0, 0, 0);
+                        a[1].o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, s[1][kb4][st], a[1].o[db], 0, 0, 0);
                     }
                 }
             }
@@ -685,6 +774,90 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
                            p.best ? p.best + qi : nullptr, p.bcos ? p.bcos + qi : nullptr, p.scale_log2);
 }
 
+// AnnCA with two 16-query groups per wave (32 queries per wave, 32*NW per
+// block): the same gather pipeline as attn_body, with every K/V fragment read
+// from LDS used by both groups.
+template <typename T, int D, typename OT, int NW>
+__device__ __forceinline__ void attn_ca2_body(const AttnParams& p) {
+    constexpr int NT = 64 * NW, QT = 32 * NW;
+    using B = Blk<T, D, MODE_CA, false, NT>;
+    __shared__ __align__(16) T Ks[KT * B::STRK];
+    __shared__ __align__(16) T Vs[KT * B::STRV];
+    __shared__ int sslot[2][1];
+    __shared__ int kidx[KCH];
+    const typename B::Smem sm{Ks, Vs, nullptr, nullptr, nullptr, nullptr};
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int h = blockIdx.z, f = blockIdx.y, c = blockIdx.x;
+    const int qbase = f * p.frame_len + c * QT;
+    const int q_count = min(QT, p.frame_len - c * QT);
+    const int nk = p.ca_cnt[h * p.F + f];
+    const int32_t* klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
+    const typename B::Src sr = B::src_of(p, h);
+
+    const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
+    typename B::QF qf[2];
+    typename B::Acc acc[2];
+    bool qvalid[2];
+    int qrow[2];
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const int ql = w * 32 + qg * 16 + c16;
+        qvalid[qg] = ql < q_count;
+        qrow[qg] = qbase + (qvalid[qg] ? ql : 0);
+        B::load_q(qf[qg], qvalid[qg] ? qh + static_cast<size_t>(qrow[qg]) * D : nullptr, g);
+        acc[qg].reset();
+    }
+    const bool wave_active = w * 32 < q_count;
+
+    auto stage_idx = [&](int first) __attribute__((always_inline)) {
+        for (int i = tid; i < KCH; i += NT) {
+            const int r = first + i;
+            kidx[i] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+        }
+    };
+    const int nt = (nk + KT - 1) / KT;
+    auto step = [&](typename B::Stage& S, int t) __attribute__((always_inline)) {
+        if (t >= nt) return;                              // block-uniform
+        __syncthreads();
+        B::store_tile(S, sm, 0, tid, 0.f);
+        __syncthreads();
+        if (t + 2 < nt) {
+            if (((t + 2) * KT) % KCH == 0) {
+                stage_idx((t + 2) * KT);
+                __syncthreads();
+            }
+            B::load_tile(S, kidx, t + 2, sr, tid);
+        }
+        if (wave_active) B::compute_tile2(acc, qf, sm, t * KT, nk, p.scale_log2, g, c16);
+    };
+    typename B::Stage A, Bs;
+    A.slots = sslot[0];
+    Bs.slots = sslot[1];
+    stage_idx(0);
+    __syncthreads();
+    if (nt > 0) B::load_tile(A, kidx, 0, sr, tid);
+    if (nt > 1) B::load_tile(Bs, kidx, 1, sr, tid);
+#pragma unroll 1
+    for (int t = 0; t < nt; t += 2) {
+        step(A, t);
+        step(Bs, t + 1);
+    }
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+        const size_t qi = static_cast<size_t>(h) * p.Nq + qrow[qg];
+        B::template finish<OT>(acc[qg], qf[qg], qvalid[qg], g, static_cast<OT*>(p.out) + qi * D, nullptr,
+                               nullptr, nullptr, p.scale_log2);
+    }
+}
+
+template <typename T, int D, typename OT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_ca2_kernel(const AttnParams p) {
+    attn_ca2_body<T, D, OT, NW>(p);
+}
+
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
 // registers per lane, i.e. 2 waves per SIMD.
 template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false,
@@ -702,15 +875,16 @@ __global__ __launch_bounds__(256) void attn_top1_kernel(const AttnParams p) {
 
 namespace {
 
-// AnnCA blocks take 16*kCaWaves consecutive queries of a frame: every K/V
-// tile gathered into LDS serves that many queries.
+// AnnCA blocks take 16*kCaGroups*kCaWaves consecutive queries of a frame:
+// every K/V tile gathered into LDS serves that many queries.
 constexpr int kCaWaves = CA_WAVES;
+constexpr int kCaGroups = CA_GROUPS;
 
 template <typename T, int D, int MODE, typename OT>
 void attn_go(int H, const AttnParams& p, hipStream_t s) {
     dim3 grid;
     if constexpr (MODE == MODE_CA)
-        grid = dim3((p.frame_len + 16 * kCaWaves - 1) / (16 * kCaWaves), p.F, H);
+        grid = dim3((p.frame_len + 16 * kCaGroups * kCaWaves - 1) / (16 * kCaGroups * kCaWaves), p.F, H);
     else
         grid = dim3(H, p.max_items);
     if (grid.x == 0 || grid.y == 0 || grid.z == 0) return;
@@ -729,6 +903,9 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
             else { if (bias) FASTAR_SA(false, true, false); else FASTAR_SA(false, false, false); }
         }
 #undef FASTAR_SA
+    } else if constexpr (kCaGroups == 2 && (sizeof(T) == 2 || D == 64)) {
+        // (fp32 with d = 128 keeps one group per wave: two would spill)
+        hipLaunchKernelGGL((attn_ca2_kernel<T, D, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0, s, p);
     } else {
         hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_CA, false, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0,
                            s, p);
