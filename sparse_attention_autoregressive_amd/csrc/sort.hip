@@ -1,18 +1,22 @@
 // Stable counting sort of token indices by bucket id: the block-sparse layout
 // that bucket attention gathers from (FAST-AR summary, "2. Core Components",
-// part C).  Three launches, every count stays on the device:
+// part C).  Two launches, every count stays on the device:
 //
 //   sort_hist    one block per 1024-id tile: LDS histogram -> hist[h][tile][b]
-//   sort_scan    one block per head: per-bucket exclusive prefix over tiles (in
-//                place) plus a block scan over buckets -> off[h][b], for each
-//                set; optionally the attention work list (one item per bucket
-//                and 64-query slice, longest key lists first)
-//   sort_scatter one block per tile: stable rank of every id inside its tile
-//                (wave ballots on the P id bits give the rank among equal ids of
-//                the wave; LDS counters tagged by round carry it across waves
-//                and rounds), then perm[off + tile base + rank] = index.
+//   sort_scatter one block per tile: first the tile's base offsets, from the
+//                histograms of all tiles of its head (ids below b anywhere,
+//                plus ids equal to b in earlier tiles); block 0 of each head
+//                also writes off[h][b] and, for a (queries, keys) pair of
+//                sets, the attention work list (one item per bucket and
+//                64-query slice, longest key lists first).  Then the stable
+//                rank of every id inside its tile (wave ballots on the P id
+//                bits give the rank among equal ids of the wave; LDS counters
+//                tagged by round carry it across waves and rounds), and
+//                perm[base + rank] = index.
 //
-// The result is unique (a stable sort), so it is bit-identical run to run.
+// Every block re-reads its head's tile histograms (a few KB, from L2) instead
+// of waiting for a separate scan launch.  The result is unique (a stable sort),
+// so it is bit-identical run to run.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -57,134 +61,218 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
     for (int b = threadIdx.x; b < B; b += 256) dst[b] = cnt[b];
 }
 
-// One block per head.  Thread (part, b) owns bucket b over a contiguous range
-// of tiles (1024 / B parts), so every tile count is read by one thread.  When
-// a part spans at most kScanRegs tiles (the usual case) the counts of both sets
-// are loaded into registers up front -- one round trip for the whole kernel --
-// and the running offsets are written back from them; longer parts loop.
-constexpr int kScanRegs = 8;
+// Per-bucket sums of one set's tile counts -- over the tiles before ``t`` and
+// over all tiles -- for the buckets of this thread.  With B <= 256 every
+// bucket b is summed by 256 / B threads (part p, b), each over a contiguous
+// range of tiles whose counts it loads in one go (up to kTileLoads at once);
+// the parts meet in LDS and thread b keeps bucket b (k = 1).  With B > 256
+// thread i keeps buckets i*k .. i*k+k-1 (k = B / 256) and sums all tiles.
+constexpr int kTileLoads = 32;
 
-__global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
-    __shared__ int part_sum[1024];
-    __shared__ int smem[16];
-    __shared__ int offs[2][1025];
-    __shared__ int rank_acc[1024];
-    const int h = blockIdx.x, B = a.B, tid = threadIdx.x;
-    const int parts = 1024 / B;
-    const int b = tid % B, part = tid / B;
-    rank_acc[tid] = 0;                    // ordered before its use by the scans' barriers
-    int cnt[2][kScanRegs];
-    int t0s[2], t1s[2];
-    bool regs[2];
+struct BucketSums {
+    int before[4], total[4];
+};
+
+__device__ __forceinline__ void bucket_sums(const SortBufs& O, int h, int t, int ntiles, int B, int k,
+                                            BucketSums& s, int* pt, int* pb) {
+    const int tid = threadIdx.x;
+    const int* hh = O.hist + static_cast<size_t>(h) * O.max_tiles * B;
 #pragma unroll
-    for (int si = 0; si < 2; ++si) {
-        t0s[si] = t1s[si] = 0;
-        regs[si] = true;
-        if (si >= a.nsets) continue;
-        int na;
-        const int n = set_count(a.set[si], h, na);
-        const int ntiles = sort_tiles(n);
-        const int tpp = (ntiles + parts - 1) / parts;
-        t0s[si] = min(ntiles, part * tpp);
-        t1s[si] = min(ntiles, t0s[si] + tpp);
-        regs[si] = tpp <= kScanRegs;                               // block uniform
-        const int* hist = a.buf[si].hist + static_cast<size_t>(h) * a.buf[si].max_tiles * B + b;
+    for (int j = 0; j < 4; ++j) s.before[j] = s.total[j] = 0;
+    if (k == 1) {
+        const int parts = 256 / B, part = tid / B, b = tid % B;
+        int sum = 0, bef = 0;
+        if (part < parts) {
+            const int tpp = (ntiles + parts - 1) / parts;
+            const int t0 = min(ntiles, part * tpp), t1 = min(ntiles, t0 + tpp);
+            for (int c0 = t0; c0 < t1; c0 += kTileLoads) {
+                int c[kTileLoads];
 #pragma unroll
-        for (int k = 0; k < kScanRegs; ++k)
-            cnt[si][k] = (regs[si] && t0s[si] + k < t1s[si]) ? hist[static_cast<size_t>(t0s[si] + k) * B] : 0;
-    }
+                for (int i = 0; i < kTileLoads; ++i) c[i] = c0 + i < t1 ? hh[static_cast<size_t>(c0 + i) * B + b] : 0;
 #pragma unroll
-    for (int si = 0; si < 2; ++si) {
-        if (si >= a.nsets) break;
-        const SortBufs& O = a.buf[si];
-        const int t0 = t0s[si], t1 = t1s[si];
-        int* hist = O.hist + static_cast<size_t>(h) * O.max_tiles * B + b;
-        int sum = 0;
-        if (regs[si]) {
-#pragma unroll
-            for (int k = 0; k < kScanRegs; ++k) sum += cnt[si][k];
-        } else {
+                for (int i = 0; i < kTileLoads; ++i) {
+                    sum += c[i];
+                    bef += c0 + i < t ? c[i] : 0;
+                }
+            }
+            pt[part * B + b] = sum;
+            pb[part * B + b] = bef;
+        }
+        __syncthreads();
+        if (tid < B) {
+            for (int q = 0; q < parts; ++q) {
+                s.total[0] += pt[q * B + tid];
+                s.before[0] += pb[q * B + tid];
+            }
+        }
+        __syncthreads();                          // pt / pb may be reused
+    } else {
+        const int b0 = tid * k;
 #pragma unroll 4
-            for (int t = t0; t < t1; ++t) sum += hist[static_cast<size_t>(t) * B];
-        }
-        part_sum[part * B + b] = sum;
-        __syncthreads();
-        int pre = 0, tot = 0;
-        for (int q = 0; q < parts; ++q) {
-            const int v = part_sum[q * B + b];
-            pre += (q < part) ? v : 0;
-            tot += v;
-        }
-        int total;
-        const int excl = block_exclusive_scan<1024>(part == 0 ? tot : 0, smem, total);
-        if (part == 0) offs[si][b] = excl;
-        if (tid == 0) offs[si][B] = total;
-        __syncthreads();
-        int run = offs[si][b] + pre;
-        if (regs[si]) {
+        for (int tt = 0; tt < ntiles; ++tt) {
 #pragma unroll
-            for (int k = 0; k < kScanRegs; ++k) {
-                if (t0 + k < t1) hist[static_cast<size_t>(t0 + k) * B] = run;
-                run += cnt[si][k];
-            }
-        } else {
-            for (int t = t0; t < t1; ++t) {
-                const int c = hist[static_cast<size_t>(t) * B];
-                hist[static_cast<size_t>(t) * B] = run;
-                run += c;
+            for (int j = 0; j < 4; ++j) {
+                if (j < k) {
+                    const int c = hh[static_cast<size_t>(tt) * B + b0 + j];
+                    s.total[j] += c;
+                    s.before[j] += tt < t ? c : 0;
+                }
             }
         }
-        if (part == 0) O.off[static_cast<size_t>(h) * (B + 1) + b] = offs[si][b];
-        if (tid == 0) O.off[static_cast<size_t>(h) * (B + 1) + B] = total;
     }
-    if (a.items.items && a.nsets == 2) {
-        // Items in decreasing order of key count (ties: lower bucket first), so
-        // the longest items start first.  rank[b] = position of bucket b.
-        // every part counts the buckets of its share of c that rank before b
-        __shared__ int slot_tiles[1024];
-        const int qc = (part == 0) ? offs[0][b + 1] - offs[0][b] : 0;
-        const int kn = offs[1][b + 1] - offs[1][b];
-        const int tiles = (qc + kQTile - 1) / kQTile;
-        const int per = (B + parts - 1) / parts;
-        int r = 0;
-        for (int c = part * per; c < min(B, (part + 1) * per); ++c) {
-            const int kc = offs[1][c + 1] - offs[1][c];
-            r += (kc > kn) || (kc == kn && c < b);
-        }
-        atomicAdd(&rank_acc[b], r);
-        __syncthreads();
-        const int rank = rank_acc[b];
-        if (part == 0) slot_tiles[rank] = tiles;
-        __syncthreads();
-        int ntot;
-        const int first_by_rank = block_exclusive_scan<1024>(part == 0 ? slot_tiles[b] : 0, smem, ntot);
-        if (part == 0) slot_tiles[b] = first_by_rank;          // start of rank b
-        __syncthreads();
-        int4* it = a.items.items + static_cast<size_t>(h) * a.items.max_items;
-        if (part == 0) {
-            const int first = slot_tiles[rank];
-            const int ks = offs[1][b];
-            for (int c = 0; c < tiles; ++c)
-                it[first + c] = make_int4(offs[0][b] + c * kQTile, min(kQTile, qc - c * kQTile), ks, kn);
-        }
-        for (int i = ntot + tid; i < a.items.max_items; i += 1024) it[i] = make_int4(0, 0, 0, 0);
+}
+
+// Exclusive prefix over buckets (in bucket order) of the totals: ``start[j]``
+// for the thread's buckets; returns the grand total.
+__device__ __forceinline__ int bucket_starts(const BucketSums& s, int B, int k, int (&start)[4], int* smem) {
+    const int b0 = threadIdx.x * k;
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine += (j < k && b0 + j < B) ? s.total[j] : 0;
+    int total;
+    int run = block_exclusive_scan<256>(mine, smem, total);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        start[j] = run;
+        run += (j < k && b0 + j < B) ? s.total[j] : 0;
     }
+    return total;
 }
 
 __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     __shared__ int run[1024];
     __shared__ int base[1024];
     __shared__ uint32_t wcnt[4][1024];
-    const IdSet& S = a.set[blockIdx.z];
-    const SortBufs& O = a.buf[blockIdx.z];
-    const int h = blockIdx.y, t = blockIdx.x, B = a.B, P = a.P;
+    __shared__ int smem[8];
+    __shared__ int racc[256];
+    const int si = blockIdx.z;
+    const IdSet& S = a.set[si];
+    const SortBufs& O = a.buf[si];
+    const int h = blockIdx.y, t = blockIdx.x, B = a.B, P = a.P, tid = threadIdx.x;
     int na;
     const int n = set_count(S, h, na);
-    if (t * kSortTile >= n) return;
-    const int* tb = O.hist + (static_cast<size_t>(h) * O.max_tiles + t) * B;
-    for (int b = threadIdx.x; b < B; b += 256) {
+    const int ntiles = sort_tiles(n);
+    const bool lead = t == 0;                     // writes off (and the work list)
+    if (t >= ntiles && !lead) return;             // block uniform
+    const int k = (B + 255) / 256, b0 = tid * k;
+
+    // ---- the tile's base offsets (and, for the lead block, off); the part
+    // sums borrow the rank step's LDS
+    int* pt = reinterpret_cast<int*>(wcnt[0]);
+    int* pb = reinterpret_cast<int*>(wcnt[1]);
+    BucketSums bs;
+    bucket_sums(O, h, t, ntiles, B, k, bs, pt, pb);
+    int start[4];
+    const int total = bucket_starts(bs, B, k, start, smem);
+    int32_t* offp = O.off ? O.off + static_cast<size_t>(h) * (B + 1) : nullptr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < k && b0 + j < B) {
+            base[b0 + j] = start[j] + bs.before[j];
+            if (lead && offp) offp[b0 + j] = start[j];
+        }
+    }
+    if (lead && offp && tid == 0) offp[B] = total;
+
+    // ---- the attention work list: items in decreasing order of key count
+    // (ties: lower bucket first), so the longest items start first.  Built by
+    // the lead block of the query set from both sets' histograms; the LDS of
+    // the rank step below is borrowed until the ranking starts.
+    if (lead && si == 0 && a.items.items && a.nsets == 2) {
+        int* qoff = reinterpret_cast<int*>(wcnt[0]);
+        int* qcnt = reinterpret_cast<int*>(wcnt[1]);
+        int* koff = reinterpret_cast<int*>(wcnt[2]);
+        int* kcnt = reinterpret_cast<int*>(wcnt[3]);
+        int* slot = run;
+        int nak;
+        const int nkeys = set_count(a.set[1], h, nak);
+        BucketSums ks;
+        bucket_sums(a.buf[1], h, 0, sort_tiles(nkeys), B, k, ks, pt, pb);
+        int kstart[4];
+        bucket_starts(ks, B, k, kstart, smem);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < k && b0 + j < B) {
+                qoff[b0 + j] = start[j];
+                qcnt[b0 + j] = bs.total[j];
+                koff[b0 + j] = kstart[j];
+                kcnt[b0 + j] = ks.total[j];
+            }
+        }
+        __syncthreads();
+        // rank of bucket b = buckets with more keys, or as many and a lower
+        // index; with B <= 256 the 256 / B threads of a bucket split the count
+        int rank[4], tiles[4];
+        if (k == 1) {
+            const int parts = 256 / B, part = tid / B, b = tid % B;
+            if (tid < B) racc[tid] = 0;
+            __syncthreads();
+            if (part < parts) {
+                const int per = (B + parts - 1) / parts, kn = kcnt[b];
+                int r = 0;
+                for (int c = part * per; c < min(B, (part + 1) * per); ++c) {
+                    const int kc = kcnt[c];
+                    r += (kc > kn) || (kc == kn && c < b);
+                }
+                atomicAdd(&racc[b], r);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            rank[j] = 0;
+            tiles[j] = 0;
+            const int b = b0 + j;
+            if (j < k && b < B) {
+                if (k == 1) {
+                    rank[j] = racc[b];
+                } else {
+                    const int kn = kcnt[b];
+                    for (int c = 0; c < B; ++c) {
+                        const int kc = kcnt[c];
+                        rank[j] += (kc > kn) || (kc == kn && c < b);
+                    }
+                }
+                tiles[j] = (qcnt[b] + kQTile - 1) / kQTile;
+                slot[rank[j]] = tiles[j];
+            }
+        }
+        __syncthreads();
+        // exclusive prefix of the slice counts in rank order: first item of each rank
+        int rs = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rs += (j < k && b0 + j < B) ? slot[b0 + j] : 0;
+        int ntot;
+        int first = block_exclusive_scan<256>(rs, smem, ntot);
+        int firsts[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            firsts[j] = first;
+            first += (j < k && b0 + j < B) ? slot[b0 + j] : 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (j < k && b0 + j < B) slot[b0 + j] = firsts[j];     // start of rank b0 + j
+        __syncthreads();
+        int4* it = a.items.items + static_cast<size_t>(h) * a.items.max_items;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = b0 + j;
+            if (j < k && b < B) {
+                const int f0 = slot[rank[j]], qc = qcnt[b];
+                for (int c = 0; c < tiles[j]; ++c)
+                    it[f0 + c] = make_int4(qoff[b] + c * kQTile, min(kQTile, qc - c * kQTile), koff[b],
+                                           kcnt[b]);
+            }
+        }
+        for (int i = ntot + tid; i < a.items.max_items; i += 256) it[i] = make_int4(0, 0, 0, 0);
+        __syncthreads();                          // the borrowed LDS is free again
+    }
+    if (t >= ntiles) return;                      // block uniform
+
+    for (int b = tid; b < B; b += 256) {
         run[b] = 0;
-        base[b] = tb[b];
         wcnt[0][b] = wcnt[1][b] = wcnt[2][b] = wcnt[3][b] = 0;
     }
     __syncthreads();
@@ -250,14 +338,9 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
         hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
         timer_end(s);
     }
-    timer_begin("sort_scan", s);
-    hipLaunchKernelGGL(sort_scan_kernel, dim3(H), dim3(1024), 0, s, a);
+    timer_begin("sort_scatter", s);
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(max_tiles > 0 ? max_tiles : 1, H, nsets), dim3(256), 0, s, a);
     timer_end(s);
-    if (max_tiles > 0) {
-        timer_begin("sort_scatter", s);
-        hipLaunchKernelGGL(sort_scatter_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
-        timer_end(s);
-    }
     return hipGetLastError();
 }
 
