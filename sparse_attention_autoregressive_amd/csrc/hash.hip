@@ -1,15 +1,14 @@
 // Random-hyperplane bucket ids (the LSH that places queries, cache keys,
 // current keys and prompt keys in one shared bucket space; FAST-AR summary,
-// "2. Core Components", parts A and B).
+// "2. Core Components", parts A and B):
 //
-// HBM-bound: every element of x is read once.  Each group of d/8 lanes owns one
-// vector; lane ``seg`` always handles the same 8 coordinates, so its slice of
-// every hyperplane lives in registers for the whole kernel (staged once per
-// block through LDS; no LDS traffic per element).  Partial projections are summed across the group with DPP row
-// butterflies, which leave the same fp32 sum in every lane of the group.  The
-// same pass can also return each vector's norm (a cache keeps its keys'
-// norms for the TempCache cosine search).  Several token sets (e.g. a step's
-// queries and current keys) can share one launch.
+//   id(x) = sum_p [<x, r_p> >= 0] << p
+//
+// The projections onto the P <= 16 planes are one 16-row matrix-core block per
+// 16 vectors (see hash_kernel).  The same pass can also return each vector's
+// norm (a cache keeps its keys' norms for the TempCache cosine search).
+// Several token sets (e.g. a step's queries and current keys) can share one
+// launch.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,95 +23,97 @@ struct HashSets {
     float* norms[kHashBatch];
 };
 
-template <typename T, int D, int MAXP>
-__global__ __launch_bounds__(256) void hash_kernel(const HashSets sets,
-                                                   const float* __restrict__ planes, int P) {
+// One block of 4 waves hashes 64 vectors of one head and one token set.  The
+// projections X R^T run on the matrix cores (fp32 v_mfma_f32_16x16x4f32; bf16
+// inputs widen exactly, the planes stay fp32): the P <= 16 planes are the 16
+// rows of one MFMA block (rows past P are zero and their bits dropped), the
+// wave's 16 vectors its columns, and lane group g sums dimensions g*D/4 ..
+// (g+1)*D/4-1 of both operands, so each lane reads contiguous runs.  A lane
+// then holds the projections of planes 4g..4g+3 onto its vector and turns
+// their signs into id bits; the four groups OR their bits together.  Two
+// accumulator chains (the two halves of each group's dimensions) overlap.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void hash_kernel(const HashSets sets, const float* __restrict__ planes,
+                                                   int P) {
+    constexpr int DG = D / 4;                  // dimensions per lane group
+    constexpr int STR = D + 4;                 // LDS row stride (floats): distinct banks per quarter-wave
+    __shared__ __align__(16) float pl[16 * STR];
     const T* __restrict__ x = static_cast<const T*>(sets.x[blockIdx.z]);
     const int N = sets.N[blockIdx.z];
     uint16_t* __restrict__ ids = sets.ids[blockIdx.z];
     float* __restrict__ norms = sets.norms[blockIdx.z];
-    constexpr int LPV = D / 8;         // lanes per vector
-    constexpr int VPB = 256 / LPV;     // vectors per block per step
-    constexpr int UNROLL = 4;
     const int h = blockIdx.y;
-    const int seg = threadIdx.x % LPV;
-    const int vslot = threadIdx.x / LPV;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int i = blockIdx.x * 64 + w * 16 + c16;
+    if (blockIdx.x * 64 >= N) return;          // block uniform
 
-    // the head's planes go through LDS once per block (each block would
-    // otherwise read them from L2 once per vector slot)
-    __shared__ __align__(16) float spl[MAXP * D];
-    for (int i = threadIdx.x; i < P * D / 4; i += 256)
-        *reinterpret_cast<float4*>(&spl[4 * i]) =
-            *reinterpret_cast<const float4*>(planes + static_cast<size_t>(h) * P * D + 4 * i);
-    __syncthreads();
-    float pl[MAXP][8];
+    // the head's planes, rows past P zero
+    for (int k = tid; k < 16 * (D / 4); k += 256) {
+        const int r = k / (D / 4), q = k % (D / 4);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < P) v = *reinterpret_cast<const float4*>(planes + (static_cast<size_t>(h) * P + r) * D + 4 * q);
+        *reinterpret_cast<float4*>(&pl[r * STR + 4 * q]) = v;
+    }
+    // this lane's slice of its vector
+    const bool valid = i < N;
+    float xv[DG];
+    {
+        const T* row = x + (static_cast<size_t>(h) * N + (valid ? i : 0)) * D + g * DG;
 #pragma unroll
-    for (int p = 0; p < MAXP; ++p) {
-        if (p < P) {
-            const float4 a = *reinterpret_cast<const float4*>(&spl[p * D + seg * 8]);
-            const float4 b = *reinterpret_cast<const float4*>(&spl[p * D + seg * 8 + 4]);
-            pl[p][0] = a.x; pl[p][1] = a.y; pl[p][2] = a.z; pl[p][3] = a.w;
-            pl[p][4] = b.x; pl[p][5] = b.y; pl[p][6] = b.z; pl[p][7] = b.w;
-        } else {
+        for (int e = 0; e < DG; e += 8) {
+            float v[8];
+            load8_f32(row + e, v);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pl[p][e] = 0.f;
+            for (int k = 0; k < 8; ++k) xv[e + k] = valid ? v[k] : 0.f;
         }
     }
+    __syncthreads();
 
-    const T* xh = x + static_cast<size_t>(h) * N * D;
-    uint16_t* idh = ids + static_cast<size_t>(h) * N;
-    for (int base = blockIdx.x * VPB * UNROLL; base < N; base += gridDim.x * VPB * UNROLL) {
-        float v[UNROLL][8];
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const float* prow = &pl[c16 * STR + g * DG];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int i = base + u * VPB + vslot;
-            if (i < N) {
-                load8_f32(xh + static_cast<size_t>(i) * D + seg * 8, v[u]);
-            } else {
+    for (int e = 0; e < DG / 2; e += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(prow + e);
+        const float4 b = *reinterpret_cast<const float4*>(prow + DG / 2 + e);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, xv[e], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b.x, xv[DG / 2 + e], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, xv[e + 1], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b.y, xv[DG / 2 + e + 1], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, xv[e + 2], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b.z, xv[DG / 2 + e + 2], acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, xv[e + 3], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b.w, xv[DG / 2 + e + 3], acc1, 0, 0, 0);
+    }
+    uint32_t bits = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
-            }
-        }
+    for (int r = 0; r < 4; ++r) {
+        const int pidx = 4 * g + r;
+        if (pidx < P && acc0[r] + acc1[r] >= 0.f) bits |= 1u << pidx;
+    }
+    bits |= __shfl_xor(bits, 16);
+    bits |= __shfl_xor(bits, 32);
+    float sq = 0.f;
+    if (norms) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int i = base + u * VPB + vslot;
-            uint32_t id = 0;
-#pragma unroll
-            for (int p = 0; p < MAXP; ++p) {
-                if (p < P) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s = __builtin_fmaf(v[u][e], pl[p][e], s);
-                    s = group_sum<(LPV < 16 ? LPV : 16)>(s);
-                    id |= static_cast<uint32_t>(s >= 0.f) << p;
-                }
-            }
-            if (seg == 0 && i < N) idh[i] = static_cast<uint16_t>(id);
-            if (norms) {                                   // |x|, the cache keeps it per slot
-                float sq = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sq = __builtin_fmaf(v[u][e], v[u][e], sq);
-                sq = group_sum<(LPV < 16 ? LPV : 16)>(sq);
-                if (seg == 0 && i < N) norms[static_cast<size_t>(h) * N + i] = __builtin_sqrtf(sq);
-            }
-        }
+        for (int e = 0; e < DG; ++e) sq = __builtin_fmaf(xv[e], xv[e], sq);
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+    }
+    if (valid && g == 0) {
+        ids[static_cast<size_t>(h) * N + i] = static_cast<uint16_t>(bits);
+        if (norms) norms[static_cast<size_t>(h) * N + i] = __builtin_sqrtf(sq);
     }
 }
 
 template <typename T, int D>
 static hipError_t hash_dispatch_p(const HashSets& sets, int count, int H, const float* planes, int P,
                                   hipStream_t s) {
-    constexpr int VPB = 256 / (D / 8);
     int nmax = 0;
     for (int i = 0; i < count; ++i) nmax = sets.N[i] > nmax ? sets.N[i] : nmax;
-    int blocks = (nmax + VPB * 4 - 1) / (VPB * 4);
-    if (blocks < 1) blocks = 1;
-    dim3 grid(blocks, H, count);
+    dim3 grid((nmax + 63) / 64, H, count);
     timer_begin("ann_hash", s);
-    if (P <= 8)
-        hipLaunchKernelGGL((hash_kernel<T, D, 8>), grid, dim3(256), 0, s, sets, planes, P);
-    else
-        hipLaunchKernelGGL((hash_kernel<T, D, 16>), grid, dim3(256), 0, s, sets, planes, P);
+    hipLaunchKernelGGL((hash_kernel<T, D>), grid, dim3(256), 0, s, sets, planes, P);
     timer_end(s);
     return hipGetLastError();
 }
