@@ -11,10 +11,13 @@ cache; 7 hyperplanes = 128 buckets; 512 prompt tokens):
     tempcache_update(claims from that top-1 + select + row scatter)
 
 The step runs on two streams: AnnCA (independent of the cache) overlaps the
-TempCache commit, whose select phase keeps only one CU per head busy.  The
-headline issues the calls one by one; ``ms_per_step_graph`` replays the same
-step captured as a HIP graph (one graph per cache copy) and
-``ms_per_step_eager_one_stream`` issues the calls on one stream.
+TempCache commit, whose select phase keeps only one CU per head busy, and
+the side stream lists the commit's eviction candidates while AnnSA runs.  The
+headline (``ms_per_step`` = ``ms_per_step_graph``) replays the step captured
+as a HIP graph -- how a serving loop runs a fixed-shape step, without the
+host's per-launch cost -- one graph per cache copy, each replayed once in the
+timed region; ``ms_per_step_eager_two_stream`` issues the same calls one by
+one and ``ms_per_step_eager_one_stream`` issues them on one stream.
 ``mean_merge`` times the same step on a mean-merged cache (Lemma 5.1 of the
 FAST-AR summary: slots carry group sizes, AnnSA adds ln m to their logits and
 the commit folds matched tokens into their slot's group).  ``multi_table``
@@ -149,7 +152,7 @@ def main():
     two, one = mk(True), mk(False)
     ids = two.ids
     # every step commits into its own pristine copy of the cache
-    n_copies = 3 * args.warmup + 6 * args.steps
+    n_copies = 3 * args.warmup + 7 * args.steps
     caches = [base.clone() for _ in range(n_copies)]
     it = iter(caches)
     run = lambda s, c: s(c, q, kc, vc, kp, vp, planes, st.step)
@@ -176,10 +179,10 @@ def main():
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / args.steps
 
-    # ---- timed regions: K two-stream steps issued call by call (the headline);
-    # the same step as K graph replays, and issued on one stream
+    # ---- timed regions: the step as K graph replays (the headline); K
+    # two-stream steps issued call by call, and K issued on one stream
     ms_graph = timed(lambda i: graphs[args.warmup + i].replay())
-    ms_per_step = timed(lambda i: run(two, next(it)))
+    ms_eager_two = timed(lambda i: run(two, next(it)))
     ms_one_stream = timed(lambda i: run(one, next(it)))
     cnt = two.keep_count
 
@@ -213,6 +216,23 @@ def main():
     kernel_ms = {k: v[1] / max(1, v[0]) for k, v in kt.times.items()}
     kernel_launches = {k: v[0] // args.steps for k, v in kt.times.items()}
 
+    # ---- the commit's select with the eviction candidates listed on the side
+    # stream beforehand (what a captured step does): K eager two-stream steps
+    # with the list, per-kernel HIP events on each kernel's own stream (the
+    # list overlaps AnnSA, so its duration includes that sharing)
+    listed = AttentionStep(H, Nq, d, cap, P, cfg.frame_len, cfg.L, cfg.tau, out_dtype=out_dt,
+                           device=dev, overlap=True, order_list=True)
+    run(listed, next(it))
+    torch.cuda.synchronize()
+    with fa.kernel_timer() as kt_l:
+        for _ in range(args.steps - 1):
+            run(listed, next(it))
+    torch.cuda.synchronize()
+    kl = {k: v[1] / max(1, v[0]) for k, v in kt_l.times.items()}
+    eviction_list = {"tempcache_order_ms": kl.get("tempcache_order"),
+                     "tempcache_select_ms_listed": kl.get("tempcache_select"),
+                     "tempcache_select_ms_full_scan": kernel_ms.get("tempcache_select")}
+
     # ---- work accounting (not timed): kept pairs and algorithmic bytes
     B = 1 << P
     qi = ids["q"].long() & 0xFFFF
@@ -222,6 +242,7 @@ def main():
     sa_pairs = float((nqb * nkb).sum())
     ca_pairs = float(cnt.double().sum() * cfg.frame_len)
     flops = 4.0 * d * (sa_pairs + ca_pairs)
+    ms_per_step = ms_graph
     value_tflops = flops / (ms_per_step * 1e-3) / 1e12
 
     esz = 2 if cfg.dtype == "bf16" else 4
@@ -299,7 +320,9 @@ def main():
                   + matched * (d * esz + 4) + (mwritten - groups) * (2 * d * esz + 4)
                   + H * Nq * 12.0)
         ms_ms = mk_ms.get("tempcache_merge_scatter")
-        merge = {"ms_per_step": ms_merge, "value_tflops": flops / (ms_merge * 1e-3) / 1e12,
+        merge = {"ms_per_step": ms_merge, "launch": "eager, two streams",
+                 "ms_per_step_replacement_same_launch": ms_eager_two,
+                 "value_tflops": flops / (ms_merge * 1e-3) / 1e12,
                  "group_sizes": "uniform 1..32 per slot",
                  "kernel_ms": mk_ms,
                  "merge_scatter": {"bytes": mbytes,
@@ -401,7 +424,8 @@ def main():
         qz_flops = 2.0 * H * (2 * Nq + cfg.L) * Bq * d / 3
         qz_bytes = H * (2 * Nq + cfg.L) * (d * esz + 2) / 3
         qz_ms = q_ms.get("ann_quantize")
-        quant = {"codewords": Bq, "ms_per_step": ms_quant, "kernel_ms": q_ms,
+        quant = {"codewords": Bq, "ms_per_step": ms_quant, "launch": "eager, two streams",
+                 "ms_per_step_hyperplanes_same_launch": ms_eager_two, "kernel_ms": q_ms,
                  "kernel_launches_per_step": q_launch,
                  "ann_quantize": {"flops_per_launch": qz_flops, "bytes_per_launch": qz_bytes,
                                   "TFLOP/s": qz_flops / (qz_ms * 1e-3) / 1e12 if qz_ms else None,
@@ -412,17 +436,18 @@ def main():
         "metric": "attention step latency (ms) + achieved bf16 TFLOP/s on kept pairs, Wan-1.3B chunk",
         "value": value_tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "ms_per_step_graph": ms_graph,
-        "ms_per_step_eager_one_stream": ms_one_stream,
+        "ms_per_step_eager_two_stream": ms_eager_two, "ms_per_step_eager_one_stream": ms_one_stream,
         "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {H} heads x d={d}, chunk {cfg.Fq} frames x "
                                f"{cfg.frame_len} = {Nq} tokens, cache {cap} slots (full), "
                                f"P={P} ({B} buckets), prompt {cfg.L}, tau={cfg.tau}",
-                   "out_dtype": args.out_dtype, "seed": args.seed, "streams": 2},
+                   "out_dtype": args.out_dtype, "seed": args.seed, "streams": 2,
+                   "launch": "hip graph replay"},
         "roofline": roofline,
         "latency_ms": latency,
         "kernel_ms": kernel_ms, "kernel_launches_per_step": kernel_launches,
-        "kernel_gbs": kernel_gbs,
+        "kernel_gbs": kernel_gbs, "eviction_list": eviction_list,
         "kept_pairs": {"annsa": sa_pairs, "annca": ca_pairs,
                        "annsa_frac_of_dense": sa_pairs / (H * Nq * (cap + Nq))},
         "mean_merge": merge,

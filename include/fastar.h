@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FASTAR_ABI_VERSION 2
+#define FASTAR_ABI_VERSION 3
 #define FASTAR_MAX_PLANES 10      /* bucketed calls: at most 1024 buckets per head */
 #define FASTAR_MAX_HASH_PLANES 16 /* ids are uint16 */
 #define FASTAR_MAX_TABLES 8        /* multi-table AnnSA: tables * P <= 16 */
@@ -278,6 +278,11 @@ fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t
  *     cap, then the e = max(0, n + u - cap) non-refreshed slots with the
  *     smallest (ts, slot), taken in ascending slot order.
  *     n_valid[h] <- min(cap, n + u), so it never exceeds cap.
+ *     order_in (may be NULL): fastar_tempcache_order's list for this cache
+ *     and this N, made after the cache's last change; the evicted slots are
+ *     then searched among those candidates only (same result, less work).
+ *     A list from another cache state gives undefined slot choices (never
+ *     an access outside the cache).
  * Outputs (each may be NULL):
  *   best [H][N] int32, best_cos [H][N] fp32 (step 1's result, or the inputs),
  *   dest [H][N] int32 (slot written by each token, -1 if dropped; in a
@@ -295,9 +300,24 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
                                       const uint16_t* q_ids, const void* k_cur, const void* v_cur,
                                       const uint16_t* kcur_ids, int32_t N, int32_t P, float tau,
                                       int32_t step, const int32_t* best_in, const float* cos_in,
-                                      int32_t* best, float* best_cos, int32_t* dest,
-                                      int32_t* evicted, int32_t* counts, void* ws,
+                                      const int32_t* order_in, int32_t* best, float* best_cos,
+                                      int32_t* dest, int32_t* evicted, int32_t* counts, void* ws,
                                       size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Eviction candidates of the next commit (blog, "1. TempCache": the least
+ * recently refreshed entries leave a full cache first).  Per head, with
+ * n = n_valid[h]: order[h][0 .. min(n, N)) = the min(n, N) slots of smallest
+ * (ts, slot), in ascending slot order; order[h][min(n, N) .. N) = -1.
+ * A commit of N tokens evicts only among these slots: each of its e evicted
+ * slots is preceded in (ts, slot) order by fewer than e non-refreshed slots
+ * and by at most r refreshed ones, and e + r <= N.  The list reads only ts
+ * and n_valid, so it can be made on another stream while the step's
+ * attention runs, then passed to fastar_tempcache_update as order_in.
+ * order [H][N] int32 device buffer, written on ``stream``.  Requires
+ * N <= cache->cap (else FASTAR_ECAPACITY).
+ * ------------------------------------------------------------------------ */
+fastar_status fastar_tempcache_order(const fastar_cache* cache, int32_t N, int32_t* order, void* stream);
 
 /* ------------------------------------------------------------------------
  * Optional per-kernel timing, for measurement only.  While enabled, every

@@ -12,5 +12,5 @@ Parity status of each function is listed in ``fastar_oracle``'s header.
 """
 from .fastar_oracle import (  # noqa: F401
     TIE_EPS, ann_hash, ann_quantize, bucket_sort, key_context, key_counts, annsa, annsa_multi, bucket_fields, annca,
-    tempcache_top1, tempcache_commit, tempcache_update, attention_step,
+    tempcache_top1, tempcache_commit, tempcache_update, eviction_candidates, attention_step,
 )

@@ -448,6 +448,23 @@ def tempcache_commit(cache: Dict[str, np.ndarray], n: int, k_cur, v_cur, kcur_id
             "matched": matched, "thr_tie": thr_tie}
 
 
+def eviction_candidates(ts, n: int, N: int) -> np.ndarray:
+    """The slots an update of N tokens may evict (R7): the min(n, N) valid
+    slots that come first in (timestamp, slot) order, listed by slot,
+    padded with -1 to length N.  R7 evicts the e oldest non-refreshed slots;
+    with r refreshed slots and u unmatched tokens, e <= u and r + u <= N, so
+    each evicted slot has at most e - 1 + r <= N - 1 slots before it in that
+    order and always lies in this list."""
+    ts = np.asarray(ts)
+    if not 0 <= n <= ts.shape[0] or N < 0:
+        raise ValueError("need 0 <= n <= cap and N >= 0")
+    m = min(n, N)
+    first = sorted(range(n), key=lambda j: (int(ts[j]), j))[:m]
+    out = np.full(N, -1, np.int64)
+    out[:m] = sorted(first)
+    return out
+
+
 def tempcache_update(cache: Dict[str, np.ndarray], n: int, q, q_ids, k_cur, v_cur, kcur_ids,
                      tau: float, step: int, merge: bool = False):
     """Top-1 search, then commit (blog, "1. TempCache"; ``merge``: R10-R12)."""

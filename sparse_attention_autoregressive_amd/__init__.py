@@ -19,6 +19,7 @@ from . import _lib
 from ._lib import FASTAR_BF16, FASTAR_F32, FastarError, check, load
 
 __all__ = ["ann_hash", "ann_hash_batch", "ann_quantize", "bucket_sort", "annsa_forward", "annca_forward", "tempcache_update",
+           "tempcache_order",
            "KVCache", "kernel_timer", "load", "FastarError"]
 
 _DT = {torch.float32: FASTAR_F32, torch.bfloat16: FASTAR_BF16}
@@ -131,6 +132,11 @@ class KVCache:
 def _ids_check(ids: torch.Tensor, shape) -> None:
     if ids.dtype != torch.int16 or tuple(ids.shape) != tuple(shape):
         raise ValueError(f"ids must be int16 of shape {tuple(shape)}, got {ids.dtype} {tuple(ids.shape)}")
+
+
+def _int32_check(t: torch.Tensor, shape, what: str) -> None:
+    if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must be int32 of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
 
 
 def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] = None,
@@ -302,8 +308,10 @@ def annca_forward(q: torch.Tensor, q_ids: torch.Tensor, frame_len: int, kp: torc
 def tempcache_update(cache: KVCache, q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor,
                      v_cur: torch.Tensor, kcur_ids: torch.Tensor, P: int, tau: float, step: int,
                      best_in: Optional[torch.Tensor] = None, cos_in: Optional[torch.Tensor] = None,
-                     outputs: bool = True, ws: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
-    """Commits one chunk to ``cache`` in place; returns best, cos, dest, evicted, counts."""
+                     outputs: bool = True, ws: Optional[torch.Tensor] = None,
+                     order_in: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Commits one chunk to ``cache`` in place; returns best, cos, dest, evicted, counts.
+    ``order_in``: ``tempcache_order(cache, N)`` made since the cache last changed."""
     H, N, d = q.shape
     _ids_check(q_ids, (H, N))
     _ids_check(kcur_ids, (H, N))
@@ -317,13 +325,31 @@ def tempcache_update(cache: KVCache, q: torch.Tensor, q_ids: torch.Tensor, k_cur
                "evicted": torch.empty(H, N, dtype=torch.int32, device=dev),
                "counts": torch.empty(H, 5, dtype=torch.int32, device=dev)}
     cs = cache.struct()
+    if order_in is not None:
+        _int32_check(order_in, (H, N), "order_in")
     wsp, wsn = _workspace(lib.fastar_tempcache_workspace(H, N, cache.cap, P), dev, ws)
     check("fastar_tempcache_update", lib.fastar_tempcache_update(
         ctypes.byref(cs), _ptr(q), _ptr(q_ids), _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), N, P,
-        tau, step, _ptr(best_in), _ptr(cos_in), _ptr(res.get("best")), _ptr(res.get("cos")),
+        tau, step, _ptr(best_in), _ptr(cos_in), _ptr(order_in), _ptr(res.get("best")), _ptr(res.get("cos")),
         _ptr(res.get("dest")), _ptr(res.get("evicted")), _ptr(res.get("counts")), wsp, wsn,
         _stream(dev)))
     return res
+
+
+def tempcache_order(cache: KVCache, N: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The eviction candidates of a commit of ``N`` tokens: per head the
+    min(n_valid, N) slots of smallest (ts, slot), ascending, -1 padded ([H, N]
+    int32); pass it to ``tempcache_update(order_in=...)`` before the cache
+    changes."""
+    H = cache.k.shape[0]
+    if out is None:
+        out = torch.empty(H, N, dtype=torch.int32, device=cache.k.device)
+    else:
+        _int32_check(out, (H, N), "out")
+    cs = cache.struct()
+    check("fastar_tempcache_order", load().fastar_tempcache_order(ctypes.byref(cs), N, _ptr(out),
+                                                                   _stream(cache.k.device)))
+    return out
 
 
 class kernel_timer:

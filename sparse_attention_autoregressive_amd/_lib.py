@@ -26,7 +26,7 @@ FASTAR_MAX_TABLES = 8
 FASTAR_MAX_CODEWORDS = 65536
 FASTAR_HASH_BATCH = 4
 FASTAR_TIMER_MAX = 8192
-FASTAR_ABI_VERSION = 2
+FASTAR_ABI_VERSION = 3
 
 
 class FastarCache(ctypes.Structure):
@@ -64,8 +64,9 @@ SIGNATURES = {
                                     _i32, _f32, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "fastar_tempcache_workspace": (_sz, [_i32, _i32, _i32, _i32]),
     "fastar_tempcache_update": (_i32, [ctypes.POINTER(FastarCache), _vp, _vp, _vp, _vp, _vp, _i32,
-                                       _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i32, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _sz, _vp]),
+    "fastar_tempcache_order": (_i32, [ctypes.POINTER(FastarCache), _i32, _vp, _vp]),
     "fastar_timer_start": (_i32, []),
     "fastar_timer_stop": (_i32, [ctypes.POINTER(FastarKernelTime), _i32]),
 }

@@ -491,12 +491,27 @@ size_t fastar_tempcache_workspace(int32_t H, int32_t N, int32_t cap, int32_t P) 
     return c.off;
 }
 
+fastar_status fastar_tempcache_order(const fastar_cache* cache, int32_t N, int32_t* order, void* stream) {
+    if (!cache) return FASTAR_EINVAL;
+    const int H = cache->H, cap = cache->cap;
+    if (H < 0 || N < 0 || cap < 0) return FASTAR_EINVAL;
+    if (N > cap) return FASTAR_ECAPACITY;
+    const long long HN = static_cast<long long>(H) * N;
+    if (H > 0 && (!cache->n_valid || (cap > 0 && !cache->ts))) return FASTAR_EINVAL;
+    if (!fits_i32(HN) || !small_ok(order, HN)) return FASTAR_EINVAL;
+    if (HN == 0) return FASTAR_OK;
+    return launch_tc_order(cache->ts, cache->n_valid, H, cap, N, order, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? FASTAR_OK
+               : FASTAR_EHIP;
+}
+
 fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
                                       const uint16_t* q_ids, const void* k_cur, const void* v_cur,
                                       const uint16_t* kcur_ids, int32_t N, int32_t P, float tau,
                                       int32_t step, const int32_t* best_in, const float* cos_in,
-                                      int32_t* best, float* best_cos, int32_t* dest,
-                                      int32_t* evicted, int32_t* counts, void* ws,
+                                      const int32_t* order_in, int32_t* best, float* best_cos,
+                                      int32_t* dest, int32_t* evicted, int32_t* counts, void* ws,
                                       size_t ws_bytes, void* stream) {
     if (!cache) return FASTAR_EINVAL;
     const int H = cache->H, d = cache->d, dtype = cache->dtype, cap = cache->cap;
@@ -582,6 +597,7 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
     sp.dest = dest ? dest : w.dest;
     sp.evicted = evicted;
     sp.counts = counts;
+    sp.order = order_in;
     const bool merge = cache->count != nullptr && cap > 0;
     sp.grp_cnt = merge ? w.grp_cnt : nullptr;
     sp.grp_off = merge ? w.grp_off : nullptr;

@@ -146,6 +146,7 @@ struct TcSelectParams {
     int32_t* dest;           // [H][N] output (scratch or caller's)
     int32_t* evicted;        // [H][N] caller output or null
     int32_t* counts;         // [H][5] caller output or null
+    const int32_t* order;    // [H][N] eviction candidates (launch_tc_order) or null
     // mean merge only (null otherwise): the matched tokens grouped by the
     // token that represents their slot
     int32_t* grp_cnt;        // [H][N] scratch: group size of each representative, else 0
@@ -156,6 +157,10 @@ struct TcSelectParams {
     float tau;
 };
 hipError_t launch_tc_select(const TcSelectParams& p, hipStream_t s);
+// The min(n_valid, N) slots of smallest (ts, slot) per head, ascending, -1
+// padded to N: the candidates of the next commit's eviction search.
+hipError_t launch_tc_order(const int32_t* ts, const int32_t* n_valid, int H, int cap, int N, int32_t* order,
+                           hipStream_t s);
 
 hipError_t launch_tc_scatter(bool bf16, int d, int H, int N, int cap, const int32_t* dest,
                              const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,

@@ -11,9 +11,10 @@
 //   3. if the cache overflows, selects the e non-refreshed slots with the
 //      smallest (timestamp, slot) by a radix select on the timestamps
 //      (8-bit digits of ts - min(ts); one pass when timestamps span < 256)
-//      and lists them in slot order (two block scans); slot data are loaded
-//      once per 32768-slot chunk, 32 consecutive slots (one bitmap word) per
-//      thread,
+//      and lists them in slot order (two block scans); the search runs over
+//      the N oldest slots when an order kernel has listed them beforehand
+//      (they always hold the answer, see tc_order_kernel), else over every
+//      slot, 32 consecutive slots (one bitmap word) per thread,
 //   4. writes the unmatched tokens' destinations, the eviction list, the counts
 //      and the new valid-slot count;
 // then a copy kernel moves the written tokens' rows into place (16 lanes per
@@ -75,6 +76,223 @@ __device__ __forceinline__ bool is_matched(int b, float c, int n, float tau) {
     return b >= 0 && b < n && c >= tau;
 }
 }  // namespace
+
+// ------------------------------------------------------------ eviction search
+// Sources of the eviction search: a sequence of positions, ITEMS consecutive
+// ones per thread, each standing for a cache slot with a key (its timestamp,
+// order-preserving as unsigned) and a candidate bit.
+namespace {
+// Every slot 0..n-1, 32 per thread (one refreshed-bitmap word).  refr null:
+// every valid slot is a candidate.
+struct SlotRange {
+    static constexpr int ITEMS = SLOT_ITEMS;
+    const int32_t* ts;
+    const uint32_t* refr;
+    int n;
+    uint32_t key[ITEMS];
+    uint32_t cand = 0;
+    int base = 0, cached = -1;
+    __device__ SlotRange(const int32_t* t, const uint32_t* r, int n_) : ts(t), refr(r), n(n_) {}
+    __device__ __forceinline__ void load(int c0) {
+        if (cached == c0) return;
+        cached = c0;
+        base = c0 + static_cast<int>(threadIdx.x) * ITEMS;
+        const bool vec = base + ITEMS <= n && (reinterpret_cast<uintptr_t>(ts + base) & 15) == 0;
+        if (vec) {
+#pragma unroll
+            for (int k = 0; k < ITEMS; k += 4) {
+                const int4 t = *reinterpret_cast<const int4*>(ts + base + k);
+                key[k] = ts_key(t.x); key[k + 1] = ts_key(t.y);
+                key[k + 2] = ts_key(t.z); key[k + 3] = ts_key(t.w);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < ITEMS; ++k) key[k] = (base + k < n) ? ts_key(ts[base + k]) : 0u;
+        }
+        const int left = n - base;
+        const uint32_t valid = left >= ITEMS ? 0xFFFFFFFFu : (left > 0 ? (1u << left) - 1u : 0u);
+        cand = (valid && refr) ? (~refr[base >> 5] & valid) : valid;
+    }
+    __device__ __forceinline__ int slot(int k) const { return base + k; }
+};
+
+// The slots of a list (ascending), 8 per thread; entries outside [0, n) are
+// no candidates (a list from another cache state gives wrong evictions, never
+// an access outside the cache).
+struct SlotList {
+    static constexpr int ITEMS = 8;
+    const int32_t* list;
+    const int32_t* ts;
+    const uint32_t* refr;
+    int m, n;
+    uint32_t key[ITEMS];
+    int sl[ITEMS];
+    uint32_t cand = 0;
+    int cached = -1;
+    __device__ SlotList(const int32_t* l, const int32_t* t, const uint32_t* r, int m_, int n_)
+        : list(l), ts(t), refr(r), m(m_), n(n_) {}
+    __device__ __forceinline__ void load(int c0) {
+        if (cached == c0) return;
+        cached = c0;
+        const int base = c0 + static_cast<int>(threadIdx.x) * ITEMS;
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) sl[k] = base + k < m ? list[base + k] : -1;
+        cand = 0;
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            const bool in = static_cast<unsigned>(sl[k]) < static_cast<unsigned>(n);
+            if (!in) sl[k] = 0;
+            key[k] = ts_key(ts[sl[k]]);
+            if (in && !((refr[sl[k] >> 5] >> (sl[k] & 31)) & 1u)) cand |= 1u << k;
+        }
+    }
+    __device__ __forceinline__ int slot(int k) const { return sl[k]; }
+};
+}  // namespace
+
+// The e candidates of smallest (key, position) among positions 0..n_items-1
+// of ``src``, written to out[0..e) in position order (as slots).  A radix
+// select on 8-bit digits of key - min(key) (one pass when the keys span
+// < 256) finds the e-th key tstar and how many of the candidates equal to it
+// are taken; one packed block scan then gives every thread the list position
+// of its first selected item.  Needs at least e candidates; block-wide (every
+// thread of the SEL_NT-thread block calls it).
+template <class Src>
+__device__ __forceinline__ void select_smallest(Src& src, int n_items, int e, int32_t* out, int* smem,
+                                                uint32_t* red, int* hist, int* bcast) {
+    constexpr int ITEMS = Src::ITEMS;
+    constexpr int CHUNK = SEL_NT * ITEMS;
+    const int tid = threadIdx.x;
+    uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
+    for (int c0 = 0; c0 < n_items; c0 += CHUNK) {
+        src.load(c0);
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k)
+            if ((src.cand >> k) & 1) {
+                lmin = src.key[k] < lmin ? src.key[k] : lmin;
+                lmax = src.key[k] > lmax ? src.key[k] : lmax;
+            }
+    }
+    uint32_t kmin = lmin, kmax = lmax;
+    block_min_max(kmin, kmax, red);
+    uint32_t prefix = 0;
+    int need = e;
+    if (kmax != kmin) {
+        const uint32_t range = kmax - kmin;
+        const int nbits = 32 - __clz(static_cast<int>(range));
+        for (int shift = ((nbits - 1) / 8) * 8; shift >= 0; shift -= 8) {
+            if (tid < 256) hist[tid] = 0;
+            __syncthreads();
+            for (int c0 = 0; c0 < n_items; c0 += CHUNK) {
+                src.load(c0);
+                // neighbouring items usually share a timestamp: add runs of
+                // equal digits with one atomic each
+                int rd = -1, rc = 0;
+#pragma unroll
+                for (int k = 0; k < ITEMS; ++k) {
+                    if ((src.cand >> k) & 1) {
+                        const uint32_t rel = src.key[k] - kmin;
+                        const uint32_t hi = (shift + 8 >= 32) ? 0u : (rel >> (shift + 8));
+                        if (hi == prefix) {
+                            const int dg = static_cast<int>((rel >> shift) & 255u);
+                            if (dg != rd) {
+                                if (rc) atomicAdd(&hist[rd], rc);
+                                rd = dg;
+                                rc = 0;
+                            }
+                            ++rc;
+                        }
+                    }
+                }
+                if (rc) atomicAdd(&hist[rd], rc);
+            }
+            __syncthreads();
+            // the digit holding the need-th candidate: a scan over the 256
+            // bins, owned by the one thread whose bin straddles it
+            const int v = tid < 256 ? hist[tid] : 0;
+            int tot;
+            const int ex = block_exclusive_scan<SEL_NT>(v, smem, tot);
+            if (tid < 256 && ex < need && need <= ex + v) {
+                bcast[0] = tid;
+                bcast[1] = need - ex;
+            }
+            __syncthreads();
+            prefix = (prefix << 8) | static_cast<uint32_t>(bcast[0]);
+            need = bcast[1];
+            __syncthreads();
+        }
+    }
+    // The e selected items are every candidate below tstar plus the first
+    // ``need`` equal to it, in position order; one packed scan (below | equal
+    // << 16, unsigned: a field's chunk total reaches at most 32768) gives
+    // every thread its first list position: (# below before it) + min(# equal
+    // before it, need).
+    const uint32_t tstar = kmin + prefix;
+    int carry_lt = 0, carry_eq = 0;
+    for (int c0 = 0; c0 < n_items; c0 += CHUNK) {
+        src.load(c0);
+        uint32_t ltf = 0, eqf = 0;
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            if ((src.cand >> k) & 1) {
+                if (src.key[k] < tstar) ltf |= 1u << k;
+                else if (src.key[k] == tstar) eqf |= 1u << k;
+            }
+        }
+        const uint32_t ltc = __popc(ltf), eqc = __popc(eqf);
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan<SEL_NT, uint32_t>(
+            ltc | (eqc << 16), reinterpret_cast<uint32_t*>(smem), tot);
+        int er = carry_eq + static_cast<int>(ex >> 16);
+        int pos = carry_lt + static_cast<int>(ex & 0xFFFFu) + min(er, need);
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            bool sel = (ltf >> k) & 1;
+            if ((eqf >> k) & 1) sel = er++ < need;
+            if (sel) {
+                if (pos < e) out[pos] = src.slot(k);
+                ++pos;
+            }
+        }
+        carry_lt += static_cast<int>(tot & 0xFFFFu);
+        carry_eq += static_cast<int>(tot >> 16);
+    }
+}
+
+// The min(n, N) slots of smallest (ts, slot) of each head, ascending, then -1
+// up to N.  A commit of N tokens evicts only from these: with r refreshed
+// slots and u unmatched tokens (r + u <= N), each of the e <= u evicted slots
+// has fewer than e non-refreshed and at most r refreshed slots before it in
+// (ts, slot) order.  The list depends on nothing but the timestamps and
+// n_valid, so it can be found while the step's attention runs.
+__global__ __launch_bounds__(SEL_NT) void tc_order_kernel(const int32_t* __restrict__ ts_all,
+                                                          const int32_t* __restrict__ n_valid, int cap,
+                                                          int N, int32_t* __restrict__ order) {
+    __shared__ int smem[SEL_NT / kWave];
+    __shared__ uint32_t red[2 * (SEL_NT / kWave)];
+    __shared__ int hist[256];
+    __shared__ int bcast[2];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const int n = clamp_n(n_valid, h, cap);
+    const int m = min(n, N);
+    int32_t* out = order + static_cast<size_t>(h) * N;
+    if (m < n) {
+        SlotRange src(ts_all + static_cast<size_t>(h) * cap, nullptr, n);
+        select_smallest(src, n, m, out, smem, red, hist, bcast);
+    } else {
+        for (int i = tid; i < m; i += SEL_NT) out[i] = i;
+    }
+    for (int i = m + tid; i < N; i += SEL_NT) out[i] = -1;
+}
+
+hipError_t launch_tc_order(const int32_t* ts, const int32_t* n_valid, int H, int cap, int N, int32_t* order,
+                           hipStream_t s) {
+    if (H == 0 || N == 0) return hipSuccess;
+    timer_begin("tempcache_order", s);
+    hipLaunchKernelGGL(tc_order_kernel, dim3(H), dim3(SEL_NT), 0, s, ts, n_valid, cap, N, order);
+    timer_end(s);
+    return hipGetLastError();
+}
 
 // LDSC: the claim table (one int per slot) and the refreshed bitmap live in
 // LDS (dynamic, cap <= kLdsClaimSlots); otherwise in the workspace.
@@ -249,125 +467,15 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     const int e = max(0, n + u - cap);
     const int appended = u - e;
 
-    // 3. the e oldest non-refreshed slots (ties: lower slot), ascending
+    // 3. the e oldest non-refreshed slots (ties: lower slot), ascending:
+    //    among the precomputed candidates when given, else among all slots
     if (e > 0) {
-        uint32_t key[SLOT_ITEMS];
-        uint32_t cand = 0;
-        int sbase = 0, cached = -1;
-        auto load = [&](int c0) __attribute__((always_inline)) {
-            if (cached == c0) return;
-            cached = c0;
-            sbase = c0 + tid * SLOT_ITEMS;
-            const bool vec = sbase + SLOT_ITEMS <= n &&
-                             (reinterpret_cast<uintptr_t>(ts + sbase) & 15) == 0;
-            if (vec) {
-#pragma unroll
-                for (int k = 0; k < SLOT_ITEMS; k += 4) {
-                    const int4 t = *reinterpret_cast<const int4*>(ts + sbase + k);
-                    key[k] = ts_key(t.x); key[k + 1] = ts_key(t.y);
-                    key[k + 2] = ts_key(t.z); key[k + 3] = ts_key(t.w);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < SLOT_ITEMS; ++k) key[k] = (sbase + k < n) ? ts_key(ts[sbase + k]) : 0u;
-            }
-            const int left = n - sbase;
-            const uint32_t valid = left >= SLOT_ITEMS ? 0xFFFFFFFFu : (left > 0 ? (1u << left) - 1u : 0u);
-            cand = valid ? (~refr[sbase >> 5] & valid) : 0u;
-        };
-        uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
-        for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
-            load(c0);
-#pragma unroll
-            for (int k = 0; k < SLOT_ITEMS; ++k)
-                if ((cand >> k) & 1) {
-                    lmin = key[k] < lmin ? key[k] : lmin;
-                    lmax = key[k] > lmax ? key[k] : lmax;
-                }
-        }
-        uint32_t kmin = lmin, kmax = lmax;
-        block_min_max(kmin, kmax, red);
-        uint32_t prefix = 0;
-        int need = e;
-        if (kmax != kmin) {
-            const uint32_t range = kmax - kmin;
-            const int nbits = 32 - __clz(static_cast<int>(range));
-            for (int shift = ((nbits - 1) / 8) * 8; shift >= 0; shift -= 8) {
-                if (tid < 256) hist[tid] = 0;
-                __syncthreads();
-                for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
-                    load(c0);
-                    // neighbouring slots usually share a timestamp: add runs of
-                    // equal digits with one atomic each
-                    int rd = -1, rc = 0;
-#pragma unroll
-                    for (int k = 0; k < SLOT_ITEMS; ++k) {
-                        if ((cand >> k) & 1) {
-                            const uint32_t rel = key[k] - kmin;
-                            const uint32_t hi = (shift + 8 >= 32) ? 0u : (rel >> (shift + 8));
-                            if (hi == prefix) {
-                                const int dg = static_cast<int>((rel >> shift) & 255u);
-                                if (dg != rd) {
-                                    if (rc) atomicAdd(&hist[rd], rc);
-                                    rd = dg;
-                                    rc = 0;
-                                }
-                                ++rc;
-                            }
-                        }
-                    }
-                    if (rc) atomicAdd(&hist[rd], rc);
-                }
-                __syncthreads();
-                // the digit holding the need-th candidate: a scan over the 256
-                // bins, owned by the one thread whose bin straddles it
-                const int v = tid < 256 ? hist[tid] : 0;
-                int tot;
-                const int ex = block_exclusive_scan<SEL_NT>(v, smem, tot);
-                if (tid < 256 && ex < need && need <= ex + v) {
-                    bcast[0] = tid;
-                    bcast[1] = need - ex;
-                }
-                __syncthreads();
-                prefix = (prefix << 8) | static_cast<uint32_t>(bcast[0]);
-                need = bcast[1];
-                __syncthreads();
-            }
-        }
-        // The e selected slots are every candidate below tstar plus the first
-        // ``need`` equal to it, in slot order; one packed scan (below | equal
-        // << 16, unsigned: a field's chunk total reaches at most 32768) gives
-        // every thread its first
-        // list position: (# below before it) + min(# equal before it, need).
-        const uint32_t tstar = kmin + prefix;
-        int carry_lt = 0, carry_eq = 0;
-        for (int c0 = 0; c0 < n; c0 += SLOT_CHUNK) {
-            load(c0);
-            uint32_t ltf = 0, eqf = 0;
-#pragma unroll
-            for (int k = 0; k < SLOT_ITEMS; ++k) {
-                if ((cand >> k) & 1) {
-                    if (key[k] < tstar) ltf |= 1u << k;
-                    else if (key[k] == tstar) eqf |= 1u << k;
-                }
-            }
-            const uint32_t ltc = __popc(ltf), eqc = __popc(eqf);
-            uint32_t tot;
-            const uint32_t ex = block_exclusive_scan<SEL_NT, uint32_t>(
-                ltc | (eqc << 16), reinterpret_cast<uint32_t*>(smem), tot);
-            int er = carry_eq + static_cast<int>(ex >> 16);
-            int pos = carry_lt + static_cast<int>(ex & 0xFFFFu) + min(er, need);
-#pragma unroll
-            for (int k = 0; k < SLOT_ITEMS; ++k) {
-                bool sel = (ltf >> k) & 1;
-                if ((eqf >> k) & 1) sel = er++ < need;
-                if (sel) {
-                    if (pos < e) ev[pos] = sbase + k;     // e <= N: never past the row
-                    ++pos;
-                }
-            }
-            carry_lt += static_cast<int>(tot & 0xFFFFu);
-            carry_eq += static_cast<int>(tot >> 16);
+        if (p.order) {
+            SlotList src(p.order + static_cast<size_t>(h) * N, ts, refr, min(n, N), n);
+            select_smallest(src, min(n, N), e, ev, smem, red, hist, bcast);
+        } else {
+            SlotRange src(ts, refr, n);
+            select_smallest(src, n, e, ev, smem, red, hist, bcast);
         }
     }
     __syncthreads();

@@ -16,6 +16,14 @@ overlaps the commit, whose select kernel occupies one CU per head.  The step
 ends by joining the side stream into the caller's stream, so consecutive steps
 never overlap (they share the id buffers, workspaces and outputs).
 
+Optionally the side stream also lists the commit's eviction candidates (the N
+oldest slots; they depend only on the cache as it was before the step) while
+AnnSA runs, so the commit's select searches N slots instead of the whole
+cache.  That costs the caller's stream one more cross-stream wait: inside a
+captured graph the wait is a plain dependency and the step is shorter with
+the list; issued eagerly the wait costs about what the list saves.  By
+default the list is used only while a graph is being captured.
+
 ``graph()`` captures the same step into a HIP graph bound to one cache and one
 set of input tensors (their addresses are baked in): replaying it removes the
 host's per-launch cost, which otherwise exceeds the GPU time of the small
@@ -30,7 +38,7 @@ from typing import Optional
 import torch
 
 from . import (KVCache, ann_hash, ann_hash_batch, ann_quantize, annca_forward, annsa_forward, load,
-               tempcache_update)
+               tempcache_order, tempcache_update)
 
 
 class AttentionStep:
@@ -43,10 +51,11 @@ class AttentionStep:
 
     def __init__(self, H: int, Nq: int, d: int, cap: int, P: int, frame_len: int, L: int,
                  tau: float, out_dtype=torch.float32, device="cuda", overlap: bool = True,
-                 scale: Optional[float] = None, ann: str = "lsh"):
+                 scale: Optional[float] = None, ann: str = "lsh", order_list: Optional[bool] = None):
         """``ann``: "lsh" (the step's ``planes`` are [H, P, d] hyperplanes) or
         "quantize" (they are an [H, B, d] codebook, B <= 2^P: nearest-codeword
-        buckets)."""
+        buckets).  ``order_list``: list the eviction candidates on the side
+        stream (True), never (False), or only under graph capture (None)."""
         if frame_len <= 0 or Nq % frame_len:
             raise ValueError("frame_len must divide Nq")
         if ann not in ("lsh", "quantize"):
@@ -58,6 +67,7 @@ class AttentionStep:
         self.frame_len, self.L, self.tau = frame_len, L, tau
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
         self.overlap = overlap
+        self.order_list = order_list
         F = Nq // frame_len
         u8 = torch.uint8
         self.ws_sa = torch.empty(lib.fastar_annsa_workspace(H, Nq, cap, Nq, P), dtype=u8, device=dev)
@@ -74,8 +84,9 @@ class AttentionStep:
         self.best_cos = torch.empty(H, Nq, dtype=torch.float32, device=dev)
         self.keep = torch.empty(H, F, L, dtype=u8, device=dev)
         self.keep_count = torch.empty(H, F, dtype=torch.int32, device=dev)
+        self.order = torch.empty(H, Nq, dtype=torch.int32, device=dev)
         self.side = torch.cuda.Stream(dev)
-        self._ev_sa, self._ev_side = (torch.cuda.Event() for _ in range(2))
+        self._ev_sa, self._ev_side, self._ev_order = (torch.cuda.Event() for _ in range(3))
 
     # ------------------------------------------------------------------ pieces
     def _ids(self, x, planes, out):
@@ -94,10 +105,10 @@ class AttentionStep:
                       scale=self.scale, out=self.o_ca, ws=self.ws_ca, keep=self.keep,
                       keep_count=self.keep_count)
 
-    def _commit(self, cache, q, k_cur, v_cur, step):
+    def _commit(self, cache, q, k_cur, v_cur, step, order=None):
         tempcache_update(cache, q, self.ids["q"], k_cur, v_cur, self.ids["k"], self.P, self.tau,
                          step, best_in=self.best, cos_in=self.best_cos, outputs=False,
-                         ws=self.ws_tc)
+                         ws=self.ws_tc, order_in=order)
 
     # ------------------------------------------------------------------ step
     def __call__(self, cache: KVCache, q, k_cur, v_cur, kp, vp, planes, step: int) -> None:
@@ -114,10 +125,13 @@ class AttentionStep:
             self._annca(q, kp, vp)
             self._commit(cache, q, k_cur, v_cur, step)
             return
+        use_order = (torch.cuda.is_current_stream_capturing() if self.order_list is None
+                     else self.order_list)
         side = self.side
         side.wait_stream(main)
-        with torch.cuda.stream(side):
-            self._ids(kp, planes, self.ids["p"])
+        if not use_order:
+            with torch.cuda.stream(side):
+                self._ids(kp, planes, self.ids["p"])
         if self.ann == "lsh":
             ann_hash_batch([q, k_cur], planes, ids=[self.ids["q"], self.ids["k"]])
         else:
@@ -125,11 +139,19 @@ class AttentionStep:
             self._ids(k_cur, planes, self.ids["k"])
         self._annsa(cache, q, k_cur, v_cur)
         self._ev_sa.record(main)
+        if use_order:
+            # enqueued after AnnSA so the critical path starts first
+            with torch.cuda.stream(side):
+                tempcache_order(cache, self.Nq, out=self.order)
+                self._ev_order.record(side)
+                self._ids(kp, planes, self.ids["p"])
         side.wait_event(self._ev_sa)
         with torch.cuda.stream(side):
             self._annca(q, kp, vp)
             self._ev_side.record(side)
-        self._commit(cache, q, k_cur, v_cur, step)
+        if use_order:
+            main.wait_event(self._ev_order)
+        self._commit(cache, q, k_cur, v_cur, step, self.order if use_order else None)
         main.wait_event(self._ev_side)
 
     def graph(self, cache: KVCache, q, k_cur, v_cur, kp, vp, planes, step: int) -> torch.cuda.CUDAGraph:

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.fastar_abi_version() == _lib.FASTAR_ABI_VERSION == 2
+    assert lib.fastar_abi_version() == _lib.FASTAR_ABI_VERSION == 3
     for code, name in [(0, "FASTAR_OK"), (-1, "FASTAR_EINVAL"), (-2, "FASTAR_EDTYPE"),
                        (-3, "FASTAR_ESHAPE"), (-4, "FASTAR_EWORKSPACE"), (-5, "FASTAR_ECAPACITY"),
                        (-6, "FASTAR_EHIP")]:
@@ -171,7 +171,7 @@ def test_tempcache_validation(lib):
     need = lib.fastar_tempcache_workspace(1, 32, 64, 4)
     def call(N=32, cache=c, tau=0.9, best_in=None, cos_in=None, ws=need, P=4):
         return f(ctypes.byref(cache) if cache is not None else None, FAKE, FAKE, FAKE, FAKE, FAKE,
-                 N, P, tau, 3, best_in, cos_in, None, None, None, None, None, FAKE, ws, None)
+                 N, P, tau, 3, best_in, cos_in, None, None, None, None, None, None, FAKE, ws, None)
     assert call(ws=need - 1) == _lib.FASTAR_EWORKSPACE
     assert call(N=65) == _lib.FASTAR_ECAPACITY
     assert call(tau=float("nan")) == _lib.FASTAR_EINVAL
@@ -181,6 +181,19 @@ def test_tempcache_validation(lib):
     bad = _cache(cap=64, dtype=3)
     assert call(cache=bad) == _lib.FASTAR_EDTYPE
     assert call(cache=_cache(cap=64, knorm=None)) == _lib.FASTAR_EINVAL   # norms are needed
+
+
+def test_tempcache_order_validation(lib):
+    f = lib.fastar_tempcache_order
+    c = _cache(cap=64)
+    assert f(None, 32, FAKE, None) == _lib.FASTAR_EINVAL
+    assert f(ctypes.byref(c), 65, FAKE, None) == _lib.FASTAR_ECAPACITY
+    assert f(ctypes.byref(c), -1, FAKE, None) == _lib.FASTAR_EINVAL
+    assert f(ctypes.byref(c), 32, None, None) == _lib.FASTAR_EINVAL      # no output buffer
+    assert f(ctypes.byref(c), 0, None, None) == _lib.FASTAR_OK           # nothing to list
+    no_ts = _cache(cap=64)
+    no_ts.ts = None
+    assert f(ctypes.byref(no_ts), 32, FAKE, None) == _lib.FASTAR_EINVAL
 
 
 def test_bucket_sort_validation(lib):

@@ -3,7 +3,8 @@
 * the two-stream step on the tiny workload agrees with the oracle's end-to-end
   step exactly as the one-stream calls do (integers exact, floats within the
   attention tolerances);
-* one-stream and two-stream eager steps give bit-identical results;
+* one-stream and two-stream eager steps give bit-identical results, with and
+  without the eviction candidates listed on the side stream;
 * a captured step, replayed several times with eager work (cache restore,
   output poisoning) and synchronisation between the replays, reproduces the
   eager step bit for bit on every replay.
@@ -32,9 +33,9 @@ def _inputs(cfg, seed):
     return st, t, base
 
 
-def _stepper(cfg, overlap):
+def _stepper(cfg, overlap, order_list=None):
     return AttentionStep(cfg.H, cfg.Nq, cfg.d, cfg.cap, cfg.P, cfg.frame_len, cfg.L, cfg.tau,
-                         overlap=overlap)
+                         overlap=overlap, order_list=order_list)
 
 
 def _run(stepper, cache, t, step):
@@ -96,6 +97,12 @@ def test_graph_replays_match_eager(name):
     c1 = base.clone()
     _run(one, c1, t, st.step)
     ref = _snapshot(one, c1)
+
+    listed = _stepper(cfg, overlap=True, order_list=True)
+    c3 = base.clone()
+    _run(listed, c3, t, st.step)
+    _assert_same(ref, _snapshot(listed, c3), "two streams with the order list vs one")
+    del c3
 
     two = _stepper(cfg, overlap=True)
     c2 = base.clone()

@@ -8,6 +8,9 @@
   precision), dest, evicted, counts, n_valid and every cache array must be
   bit-exact -- full cache, partial cache, nothing matched (FIFO), everything
   matched, and scattered timestamps (multi-pass radix select);
+* the same commits with the eviction candidates listed beforehand
+  (fastar_tempcache_order, checked against the oracle's
+  ``eviction_candidates``) and passed as order_in: the same bit-exact results;
 * the full GPU path's commit must satisfy the cache invariants;
 * a multi-chunk rollout stays bit-identical to the oracle's.
 """
@@ -16,7 +19,7 @@ import pytest
 import torch
 
 import sparse_attention_autoregressive_amd as fa
-from oracle import tempcache_commit, tempcache_top1
+from oracle import eviction_candidates, tempcache_commit, tempcache_top1
 from tests.gpu_util import COS_ABS, dev, dev_ids, device_cache, host_ids, prepared, require_gpu
 from workloads import rollout_chunks
 
@@ -30,13 +33,22 @@ def oracle_top1(prep, n):
     return res
 
 
-def call(prep, cache, tau, best_in=None, cos_in=None, step=None):
+def call(prep, cache, tau, best_in=None, cos_in=None, step=None, order_in=None):
     st, cfg = prep["step"], prep["cfg"]
     return fa.tempcache_update(cache, dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]),
                                dev(st.k_cur, cfg.dtype), dev(st.v_cur, cfg.dtype),
                                dev_ids(prep["k_cur_ids"]), cfg.P, tau,
                                st.step if step is None else step,
-                               best_in=best_in, cos_in=cos_in)
+                               best_in=best_in, cos_in=cos_in, order_in=order_in)
+
+
+def checked_order(cache, N, ts, n_valid):
+    """fastar_tempcache_order on ``cache``, compared with the oracle."""
+    order = fa.tempcache_order(cache, N)
+    got = order.cpu().numpy()
+    for h in range(got.shape[0]):
+        assert np.array_equal(got[h], eviction_candidates(ts[h], int(n_valid[h]), N)), f"order head {h}"
+    return order
 
 
 def cache_host(cache, dtype):
@@ -108,16 +120,17 @@ def test_commit_keeps_key_norms():
                                rtol=2e-6, atol=0)
 
 
-def _commit_case(prep, cache_dev, n, tau, ts=None, step=None):
+def _commit_case(prep, cache_dev, n, tau, ts=None, step=None, ordered=False):
     st, cfg = prep["step"], prep["cfg"]
     step = st.step if step is None else step
     tops = oracle_top1(prep, n)
     best = np.stack([t[0] for t in tops]).astype(np.int32)
     cos32 = np.stack([t[1] for t in tops]).astype(np.float32)
-    res = call(prep, cache_dev, tau, best_in=torch.from_numpy(best).cuda(),
-               cos_in=torch.from_numpy(cos32).cuda(), step=step)
-    got = cache_host(cache_dev, cfg.dtype)
     ts0 = st.cache_ts if ts is None else ts
+    order = checked_order(cache_dev, cfg.Nq, ts0, [n] * cfg.H) if ordered else None
+    res = call(prep, cache_dev, tau, best_in=torch.from_numpy(best).cuda(),
+               cos_in=torch.from_numpy(cos32).cuda(), step=step, order_in=order)
+    got = cache_host(cache_dev, cfg.dtype)
     tau32 = float(np.float32(tau))
     for h in range(cfg.H):
         ref = tempcache_commit({"k": st.cache_k[h], "v": st.cache_v[h], "ids": prep["cache_ids"][h],
@@ -134,24 +147,27 @@ def _commit_case(prep, cache_dev, n, tau, ts=None, step=None):
     return res
 
 
+@pytest.mark.parametrize("ordered", [False, True])
 @pytest.mark.parametrize("name", ["tiny_f32", "single_bf16", "wan13_bf16"])
-def test_commit_bit_exact_full_cache(name):
+def test_commit_bit_exact_full_cache(name, ordered):
     require_gpu()
     prep = prepared(name)
     cfg = prep["cfg"]
-    res = _commit_case(prep, device_cache(prep), cfg.n0, cfg.tau)
+    res = _commit_case(prep, device_cache(prep), cfg.n0, cfg.tau, ordered=ordered)
     assert (res["counts"][:, 4] > 0).all()          # the full cache evicted
 
 
+@pytest.mark.parametrize("ordered", [False, True])
 @pytest.mark.parametrize("tau", [2.0, -2.0, 0.97])
-def test_commit_bit_exact_partial_cache(tau):
+def test_commit_bit_exact_partial_cache(tau, ordered):
     require_gpu()
     prep = prepared("single_bf16")
     n = prep["cfg"].cap - 1000
-    _commit_case(prep, device_cache(prep, n=n), n, tau)
+    _commit_case(prep, device_cache(prep, n=n), n, tau, ordered=ordered)
 
 
-def test_commit_scattered_timestamps():
+@pytest.mark.parametrize("ordered", [False, True])
+def test_commit_scattered_timestamps(ordered):
     require_gpu()
     prep = prepared("single_bf16")
     cfg = prep["cfg"]
@@ -160,7 +176,19 @@ def test_commit_scattered_timestamps():
     ts[:, ::7] = ts[:, 5:6]                      # many equal timestamps
     cache = device_cache(prep)
     cache.ts.copy_(torch.from_numpy(ts).cuda())
-    _commit_case(prep, cache, cfg.n0, 2.0, ts=ts, step=100000)
+    _commit_case(prep, cache, cfg.n0, 2.0, ts=ts, step=100000, ordered=ordered)
+
+
+def test_order_of_small_caches():
+    """n below N (every valid slot listed, then -1) and an empty cache."""
+    require_gpu()
+    prep = prepared("tiny_f32")
+    cfg = prep["cfg"]
+    for n in (0, 5, cfg.Nq - 1, cfg.Nq):
+        if n > cfg.cap:
+            continue
+        cache = device_cache(prep, n=n)
+        checked_order(cache, cfg.Nq, prep["step"].cache_ts, [n] * cfg.H)
 
 
 def _check_invariants(old, new, res, N, cap):
@@ -237,8 +265,9 @@ def test_rollout_stays_bit_identical():
         assert np.array_equal(got["ids"][0], state["ids"]), f"chunk {c}"
 
 
+@pytest.mark.parametrize("ordered", [False, True])
 @pytest.mark.parametrize("pool", [0, 50])
-def test_commit_bit_exact_multi_chunk(pool):
+def test_commit_bit_exact_multi_chunk(pool, ordered):
     """N above one block pass of tokens (8192) and a cache above one pass of
     slots (32768), full and partial heads; with ``pool`` = 50 thousands of
     tokens claim the same few slots."""
@@ -252,10 +281,11 @@ def test_commit_bit_exact_multi_chunk(pool):
                        n_valid=torch.from_numpy(n_valid).cuda(),
                        knorm=torch.zeros(H, cap, dtype=torch.float32, device="cuda"))
     kc = torch.from_numpy(c["k_cur"]).cuda()
+    order = checked_order(cache, N, c["cache_ts"], n_valid) if ordered else None
     res = fa.tempcache_update(cache, kc, dev_ids(c["kcur_ids"]), kc,
                               torch.from_numpy(c["v_cur"]).cuda(), dev_ids(c["kcur_ids"]), P, tau,
                               step, best_in=torch.from_numpy(c["best"]).cuda(),
-                              cos_in=torch.from_numpy(c["cos"]).cuda())
+                              cos_in=torch.from_numpy(c["cos"]).cuda(), order_in=order)
     got = cache_host(cache, "f32")
     for h in range(H):
         ref = tempcache_commit({"k": c["cache_k"][h], "v": c["cache_v"][h], "ids": c["cache_ids"][h],

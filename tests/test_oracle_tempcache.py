@@ -9,7 +9,11 @@
   slot, cosine = 1 (closed form);
 * invariants on the tiny workload: the cache never exceeds its cap, dest is
   injective, refreshed slots are never evicted, evicted slots are the oldest,
-  written rows are the current tokens and nothing else changed.
+  written rows are the current tokens and nothing else changed;
+* eviction candidates: a hand-worked fixture, numpy's lexsort (a library
+  routine) on tied timestamps, and the evicted slots of random updates always
+  among them -- including the tight case where refreshed slots are the oldest
+  and the last evicted slot is the N-th in (timestamp, slot) order.
 """
 import json
 import os
@@ -18,7 +22,7 @@ import numpy as np
 import pytest
 from scipy.spatial.distance import cdist
 
-from oracle import ann_hash, tempcache_commit, tempcache_top1, tempcache_update
+from oracle import ann_hash, eviction_candidates, tempcache_commit, tempcache_top1, tempcache_update
 from tests.conftest import GOLDEN
 from workloads import CONFIGS, make_step
 
@@ -174,3 +178,64 @@ def test_invariants_on_tiny_workload(tau, cap_extra):
     out = tempcache_update(cache, n, st.q[0], qi, st.k_cur[0], st.v_cur[0], ki, tau, st.step)
     _check_invariants(cache, n, out, st.k_cur[0], st.v_cur[0], ki, st.step)
     assert 0 < out["counts"][0] < cfg.Nq
+
+
+def test_eviction_candidates_hand_fixture():
+    ts = [5, 3, 3, 9, 1, 3]
+    # (ts, slot) order: 4, 1, 2, 5, 0, 3
+    assert eviction_candidates(ts, 6, 3).tolist() == [1, 2, 4]
+    assert eviction_candidates(ts, 4, 3).tolist() == [0, 1, 2]          # slots 4, 5 not valid
+    assert eviction_candidates(ts, 6, 8).tolist() == [0, 1, 2, 3, 4, 5, -1, -1]
+    assert eviction_candidates(ts, 0, 2).tolist() == [-1, -1]
+    assert eviction_candidates(ts, 6, 0).tolist() == []
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_eviction_candidates_by_lexsort(seed):
+    rng = np.random.default_rng(seed)
+    cap = 500
+    ts = rng.integers(0, 20, cap)                     # many equal timestamps
+    for n, N in ((cap, 37), (cap, cap), (300, 120), (300, 400)):
+        order = np.lexsort((np.arange(n), ts[:n]))    # by ts, then slot
+        m = min(n, N)
+        got = eviction_candidates(ts, n, N)
+        assert got[:m].tolist() == sorted(order[:m].tolist())
+        assert (got[m:] == -1).all()
+
+
+def _random_commit(rng, cap, n, N, match_frac):
+    d = 4
+    cache = _cache(rng.standard_normal((cap, d)), rng.standard_normal((cap, d)),
+                   rng.integers(0, 4, cap), rng.integers(0, 6, cap))
+    best = rng.integers(0, max(n, 1), N)
+    cos = np.where(rng.random(N) < match_frac, 1.0, 0.0)
+    kc, vc = rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    out = tempcache_commit(cache, n, kc, vc, rng.integers(0, 4, N), best, cos, 0.5, 99)
+    return cache, out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_evictions_lie_in_candidates(seed):
+    rng = np.random.default_rng(seed)
+    cap = 60
+    for n, N, frac in ((60, 20, 0.3), (60, 60, 0.5), (55, 12, 0.0), (50, 30, 0.9), (60, 1, 0.0)):
+        cache, out = _random_commit(rng, cap, n, N, frac)
+        cand = set(eviction_candidates(cache["ts"], n, N).tolist()) - {-1}
+        ev = out["evicted"][out["evicted"] >= 0]
+        assert set(ev.tolist()) <= cand
+
+
+def test_eviction_candidates_bound_is_tight():
+    # the 3 oldest slots are refreshed and 5 tokens are unmatched: the evicted
+    # slots are the 4th..8th oldest, the last of them the N-th (N = 8)
+    cap, N = 20, 8
+    ts = np.arange(cap)[::-1].copy()                  # slot 19 oldest, then 18, ...
+    cache = _cache(np.eye(cap, 4), np.zeros((cap, 4)), np.zeros(cap), ts)
+    best = np.array([19, 18, 17, 0, 0, 0, 0, 0])
+    cos = np.array([1.0, 1.0, 1.0, 0, 0, 0, 0, 0])
+    out = tempcache_commit(cache, cap, np.ones((N, 4)), np.ones((N, 4)), np.zeros(N), best, cos, 0.5, 50)
+    assert out["counts"][1] == 3 and out["counts"][4] == 5
+    assert out["evicted"][:5].tolist() == [12, 13, 14, 15, 16]
+    cand = eviction_candidates(ts, cap, N)
+    assert cand.tolist() == list(range(12, 20))
+    assert 12 in cand and 12 not in eviction_candidates(ts, cap, N - 1)
