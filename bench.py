@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--mfma-sweep", action="store_true",
                     help="only time the bucket-attention kernel at P = 0, 1, 2, 3 and the "
                          "config's P (one JSON line: TFLOP/s on kept pairs vs the bf16 MFMA peak)")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="only run hash, bucket sort and AnnCA selection at batched sizes "
+                         "(the step's heads x 1..64) and report their GB/s")
     ap.add_argument("--rollout", type=int, default=0, metavar="CHUNKS",
                     help="only run a rollout of CHUNKS chunks: per-chunk step latency and cache "
                          "size, next to a dense uncapped-cache baseline (one JSON line)")
@@ -115,6 +118,9 @@ def main():
         return
     if args.rollout > 0:
         rollout(args)
+        return
+    if args.size_sweep:
+        size_sweep(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -272,7 +278,7 @@ def main():
     ca_keys = float(cnt.double().sum())
     step_bytes = {
         "ann_hash": (2 * Nq + cfg.L) * H * (d * esz + 2),
-        "sort": 8.0 * H * (2 * Nq + cap),                       # ids read twice, perm written
+        "sort": 6.0 * H * (2 * Nq + cap),                       # id read, perm written
         "annca_select": H * (Nq + F * cfg.L) * 2.0 + H * F * cfg.L * 5.0,
         "annca_attn": Nq * H * (d * esz + d * osz) + ca_keys * 2 * d * esz,
         "tempcache_select": H * Nq * 12.0 + H * cap * 4.0,      # best, cos in, dest out; ts
@@ -527,6 +533,81 @@ def mfma_sweep(args):
         torch.cuda.empty_cache()
     print(json.dumps({"mfma_sweep": rows, "kernel": "annsa_attn (no search)", "peak_tflops": BF16_PEAK_TFLOPS,
                       "config": cfg0.name, "dtype": cfg0.dtype, "out_dtype": "f32"}), flush=True)
+
+
+def size_sweep(args):
+    """The step's small kernels at batched sizes: the hash over H x (k x Nq)
+    bf16 vectors, the bucket sort over as many ids, and AnnCA's prompt
+    selection over k x H heads (k chunks' worth of heads, the real 4680
+    queries and 512 prompt tokens each).  At the step's own size these
+    kernels move a few MB and are bound by launch latency; the sweep shows
+    the bandwidth each reaches once the work is large enough.  Algorithmic
+    bytes: hash 2d + 2 per vector (row in, id out); sort 2 + 4 per id (id in,
+    perm out); selection 2 per query id and per prompt id read, 1 + 4 per
+    (frame, prompt token) written (keep byte, index) plus the frame's count."""
+    import numpy as np
+    import torch
+    import sparse_attention_autoregressive_amd as fa
+    from workloads import CONFIGS
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H, Nq, d, P, L, fl = cfg.H, cfg.Nq, cfg.d, cfg.P, cfg.L, cfg.frame_len
+    B = 1 << P
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    esz = 2 if cfg.dtype == "bf16" else 4
+    planes = torch.randn(H, P, d, generator=gen, device=dev)
+    reps = 10
+    rows = []
+
+    def kernel_ms(call, names):
+        call()
+        torch.cuda.synchronize()
+        with fa.kernel_timer() as kt:
+            for _ in range(reps):
+                call()
+        torch.cuda.synchronize()
+        return sum(kt.times[n][1] for n in names if n in kt.times) / reps
+
+    for k in (1, 4, 16, 64):
+        N = k * Nq
+        x = torch.randn(H, N, d, generator=gen, device=dev).to(dt)
+        ids = torch.empty(H, N, dtype=torch.int16, device=dev)
+        ms = kernel_ms(lambda: fa.ann_hash(x, planes, ids=ids), ["ann_hash"])
+        nbytes = H * N * (d * esz + 2.0)
+        rows.append({"kernel": "ann_hash", "vectors": H * N, "bytes": nbytes, "ms": ms,
+                     "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del x
+        sid = torch.randint(0, B, (H, N), generator=gen, device=dev, dtype=torch.int32).to(torch.int16)
+        ws = torch.empty(fa.load().fastar_bucket_sort_workspace(H, N, P), dtype=torch.uint8, device=dev)
+        ms = kernel_ms(lambda: fa.bucket_sort(sid, P, ws=ws), ["sort_hist", "sort_scatter"])
+        nbytes = H * N * 6.0
+        rows.append({"kernel": "bucket_sort", "ids": H * N, "bytes": nbytes, "ms": ms,
+                     "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del sid, ws
+        print(json.dumps({"progress": "size_sweep", "k": k}), file=sys.stderr, flush=True)
+    F = Nq // fl
+    for k in (1, 16, 64):
+        Hk = k * H
+        qi = torch.randint(0, B, (Hk, Nq), generator=gen, device=dev, dtype=torch.int32).to(torch.int16)
+        pi = torch.randint(0, B, (Hk, L), generator=gen, device=dev, dtype=torch.int32).to(torch.int16)
+        q = torch.randn(Hk, Nq, d, generator=gen, device=dev).to(dt)
+        kp = torch.randn(Hk, L, d, generator=gen, device=dev).to(dt)
+        vp = torch.randn(Hk, L, d, generator=gen, device=dev).to(dt)
+        out = torch.empty(Hk, Nq, d, dtype=torch.float32, device=dev)
+        keep = torch.empty(Hk, F, L, dtype=torch.uint8, device=dev)
+        ws = torch.empty(fa.load().fastar_annca_workspace(Hk, Nq, fl, L, P), dtype=torch.uint8, device=dev)
+        ms = kernel_ms(lambda: fa.annca_forward(q, qi, fl, kp, vp, pi, P, out=out, keep=keep, ws=ws),
+                       ["annca_select"])
+        nbytes = Hk * (Nq + F * L) * 2.0 + Hk * F * (L * 5.0 + 4.0)
+        rows.append({"kernel": "annca_select", "heads": Hk, "bytes": nbytes, "ms": ms,
+                     "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del q, kp, vp, out, ws
+        print(json.dumps({"progress": "size_sweep annca", "k": k}), file=sys.stderr, flush=True)
+    print(json.dumps({"size_sweep": rows, "config": cfg.name, "dtype": cfg.dtype, "P": P,
+                      "peak_GB/s": HBM_PEAK_GBS, "inputs": "uniform random ids, N(0,1) vectors"}),
+          flush=True)
 
 
 def rollout(args):

@@ -6,13 +6,15 @@
 //   sort_scatter one block per tile: first the tile's base offsets, from the
 //                histograms of all tiles of its head (ids below b anywhere,
 //                plus ids equal to b in earlier tiles); block 0 of each head
-//                also writes off[h][b] and, for a (queries, keys) pair of
-//                sets, the attention work list (one item per bucket and
-//                64-query slice, longest key lists first).  Then the stable
-//                rank of every id inside its tile (wave ballots on the P id
-//                bits give the rank among equal ids of the wave; LDS counters
-//                tagged by round carry it across waves and rounds), and
-//                perm[base + rank] = index.
+//                also writes off[h][b].  Then the stable rank of every id
+//                inside its tile (wave ballots on the P id bits give the rank
+//                among equal ids of the wave; LDS counters tagged by round
+//                carry it across waves and rounds), and perm[base + rank] =
+//                index.  For a (queries, keys) pair of sets one more block
+//                per head builds the attention work list (one item per bucket
+//                and 64-query slice, longest key lists first) beside the
+//                tiles.  The tile's ids are loaded before the histograms, so
+//                both loads are in flight together.
 //
 // Every block re-reads its head's tile histograms (a few KB, from L2) instead
 // of waiting for a separate scan launch.  The result is unique (a stable sort),
@@ -28,6 +30,7 @@ struct SortArgs {
     int nsets;
     int B;
     int P;
+    int builder_block;            // grid x index of the work-list block, or -1
     ItemTable items;
 };
 
@@ -152,9 +155,20 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     int na;
     const int n = set_count(S, h, na);
     const int ntiles = sort_tiles(n);
-    const bool lead = t == 0;                     // writes off (and the work list)
-    if (t >= ntiles && !lead) return;             // block uniform
+    const bool lead = t == 0;                     // writes off
+    // the work-list builder: the extra last block of the query set's grid row
+    const bool builder = a.items.items && a.nsets == 2 && t == a.builder_block;
+    if (builder && si != 0) return;               // block uniform
+    if (t >= ntiles && !lead && !builder) return; // block uniform
     const int k = (B + 255) / 256, b0 = tid * k;
+    // the tile's ids, loaded first so their latency overlaps the histogram reads
+    constexpr int R = kSortTile / 256;
+    int idr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = t * kSortTile + r * 256 + tid;
+        idr[r] = (!builder && e < n) ? ((set_id(S, h, na, e) >> S.shift) & (B - 1)) : 0;
+    }
 
     // ---- the tile's base offsets (and, for the lead block, off); the part
     // sums borrow the rank step's LDS
@@ -176,9 +190,9 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
 
     // ---- the attention work list: items in decreasing order of key count
     // (ties: lower bucket first), so the longest items start first.  Built by
-    // the lead block of the query set from both sets' histograms; the LDS of
-    // the rank step below is borrowed until the ranking starts.
-    if (lead && si == 0 && a.items.items && a.nsets == 2) {
+    // the builder block from both sets' histograms (its ``start`` and
+    // ``bs.total`` above are the query set's).
+    if (builder) {
         int* qoff = reinterpret_cast<int*>(wcnt[0]);
         int* qcnt = reinterpret_cast<int*>(wcnt[1]);
         int* koff = reinterpret_cast<int*>(wcnt[2]);
@@ -267,7 +281,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
             }
         }
         for (int i = ntot + tid; i < a.items.max_items; i += 256) it[i] = make_int4(0, 0, 0, 0);
-        __syncthreads();                          // the borrowed LDS is free again
+        return;                                   // block uniform
     }
     if (t >= ntiles) return;                      // block uniform
 
@@ -279,11 +293,11 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     const int lane = lane_id();
     const int w = threadIdx.x / kWave;
     int32_t* perm = O.perm + static_cast<size_t>(h) * O.perm_stride;
-#pragma unroll 1
-    for (int r = 0; r < kSortTile / 256; ++r) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
         const int e = t * kSortTile + r * 256 + threadIdx.x;
         const bool valid = e < n;
-        const int id = valid ? ((set_id(S, h, na, e) >> S.shift) & (B - 1)) : 0;
+        const int id = idr[r];
         uint64_t mask = __ballot(valid);
         for (int p = 0; p < P; ++p) {
             const bool bit = (id >> p) & 1;
@@ -319,6 +333,7 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
                               const ItemTable* items, hipStream_t s) {
     SortArgs a;
     a.nsets = nsets;
+    a.builder_block = -1;
     a.B = 1 << P;
     a.P = P;
     a.items = items ? *items : ItemTable();
@@ -338,8 +353,10 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
         hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
         timer_end(s);
     }
+    int gx = max_tiles > 0 ? max_tiles : 1;
+    if (a.items.items && nsets == 2) a.builder_block = gx++;
     timer_begin("sort_scatter", s);
-    hipLaunchKernelGGL(sort_scatter_kernel, dim3(max_tiles > 0 ? max_tiles : 1, H, nsets), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(sort_scatter_kernel, dim3(gx, H, nsets), dim3(256), 0, s, a);
     timer_end(s);
     return hipGetLastError();
 }

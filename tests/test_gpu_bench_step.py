@@ -1,6 +1,7 @@
 """The step exactly as bench.py times it -- the two-stream ``AttentionStep`` on
 the Wan-1.3B-like chunk (12 heads, 4680 queries, full 32760-slot cache, 128
-buckets, 512 prompt tokens) -- against the oracle on sampled heads.
+buckets, 512 prompt tokens) -- against the oracle on sampled heads; the same
+for the Wan-14B-like layer (40 heads, 256 buckets, 128 centroids per head).
 
 Tie protocol (the oracle's flags): bucket ids must agree outside flagged hash
 bits, and the oracle's later stages then run on the GPU's ids; the TempCache
@@ -25,9 +26,10 @@ from workloads import CONFIGS, make_step
 pytestmark = pytest.mark.gpu
 
 
-def test_bench_step_matches_oracle_on_sampled_heads():
+@pytest.mark.parametrize("name,heads", [("wan13_bf16", (0, 6, 11)), ("wan14_bf16", (0, 19, 39))])
+def test_bench_step_matches_oracle_on_sampled_heads(name, heads):
     require_gpu()
-    cfg = CONFIGS["wan13_bf16"]
+    cfg = CONFIGS[name]
     st = make_step(cfg, 0)
     planes = torch.from_numpy(st.planes).cuda()
     t = {k: dev(getattr(st, k), cfg.dtype) for k in ("q", "k_cur", "v_cur", "kp", "vp")}
@@ -42,7 +44,7 @@ def test_bench_step_matches_oracle_on_sampled_heads():
     best, bcos = s.best.cpu().numpy(), s.best_cos.cpu().numpy()
     lse = s.lse.cpu().numpy()
     scale = 1.0 / math.sqrt(cfg.d)
-    for h in (0, 6, 11):
+    for h in heads:
         for key, arr, g in (("q", st.q, ids["q"]), ("k", st.k_cur, ids["k"]), ("p", st.kp, ids["p"]),
                             ("c", st.cache_k, cache_ids)):
             ref, tie = ann_hash(arr[h], st.planes[h])
