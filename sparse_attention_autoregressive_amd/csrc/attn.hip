@@ -479,12 +479,14 @@ struct Blk {
         }
     }
 
-    // AnnCA with two 16-query groups per wave: each K and V fragment read from
-    // LDS feeds the MFMAs of both groups, halving LDS reads per product.
+    // Two 16-query groups per wave (AnnCA, wide AnnSA): each K and V fragment
+    // read from LDS feeds the MFMAs of both groups, halving LDS reads per
+    // product.
     static __device__ __forceinline__ void compute_tile2(Acc (&a)[2], const QF (&q)[2], const Smem& sm,
                                                          int kbase, int nk, float scale_log2, int g,
                                                          int c16) {
-        static_assert(MODE == MODE_CA && !SEARCH && !BIAS && !MULTI, "two query groups: AnnCA only");
+        static_assert(MODE != MODE_TOP1 && !SEARCH && !BIAS && !MULTI,
+                      "two query groups: AnnCA and plain AnnSA only");
         f32x4 s[2][4];
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
@@ -705,24 +707,32 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     const int ql = w * 16 + c16;
     const bool qvalid = ql < q_count;
     const bool wave_active = w * 16 < q_count;
-    int qrow = 0;
-    if (qvalid) qrow = (MODE == MODE_CA) ? qbase + ql : qlist[ql];
-    const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
-
-    typename B::QF qf;
-    B::load_q(qf, qvalid ? qh + static_cast<size_t>(qrow) * D : nullptr, g);
-    B::finish_q(qf);
 
     // The key list is staged in LDS (KCH entries at a time, coalesced), so the
     // gathers never wait on a dependent index load.  Entries past the end
     // repeat the last key, so every lane of a partial tile still gathers a
-    // valid row (its score is masked).
+    // valid row (its score is masked).  The first chunk is loaded before the
+    // query rows' indices, so the two index loads are in flight together and
+    // the first K/V gathers start while the query rows are still on their way.
     auto stage_idx = [&](int first) __attribute__((always_inline)) {
         for (int i = tid; i < KCH; i += NT) {
             const int r = first + i;
             kidx[i] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
         }
     };
+    static_assert(KCH % NT == 0, "key chunk split");
+    int kfirst[KCH / NT];
+#pragma unroll
+    for (int u = 0; u < KCH / NT; ++u) {
+        const int r = tid + u * NT;
+        kfirst[u] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+    }
+    int qrow = 0;
+    if (qvalid) qrow = (MODE == MODE_CA) ? qbase + ql : qlist[ql];
+    const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
+
+    typename B::QF qf;
+    B::load_q(qf, qvalid ? qh + static_cast<size_t>(qrow) * D : nullptr, g);
 
     typename B::Acc acc;
     acc.reset();
@@ -754,7 +764,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     typename B::Stage A, Bs;
     A.slots = sslot[0];
     Bs.slots = sslot[1];
-    stage_idx(0);
+#pragma unroll
+    for (int u = 0; u < KCH / NT; ++u) kidx[tid + u * NT] = kfirst[u];
     __syncthreads();
     if (nt > 0) B::load_tile(A, kidx, 0, sr, tid);
     if (nt > 1) B::load_tile(Bs, kidx, 1, sr, tid);
@@ -770,17 +781,24 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
         B::store_state(acc, qvalid, g, qi, p);
         return;
     }
+    B::finish_q(qf);                          // 1/|q|, needed by the search's cosine only
     B::template finish<OT>(acc, qf, qvalid, g, static_cast<OT*>(p.out) + qi * D, p.lse ? p.lse + qi : nullptr,
                            p.best ? p.best + qi : nullptr, p.bcos ? p.bcos + qi : nullptr, p.scale_log2);
 }
 
-// AnnCA with two 16-query groups per wave (32 queries per wave, 32*NW per
-// block): the same gather pipeline as attn_body, with every K/V fragment read
-// from LDS used by both groups.
-template <typename T, int D, typename OT, int NW>
-__device__ __forceinline__ void attn_ca2_body(const AttnParams& p) {
+// Two 16-query groups per wave (32 queries per wave, 32*NW per block): the
+// same gather pipeline as attn_body, with every K/V fragment read from LDS
+// used by both groups.  MODE_CA: AnnCA, one block per (head, frame, 32*NW
+// consecutive queries).  MODE_SA: AnnSA over items of kQTileWide queries (the
+// bucket sort's slices when buckets average that many queries), for large
+// buckets: each gathered K/V tile then serves four times the queries of a
+// 64-query item, so the head's keys are re-read a quarter as often.  No
+// search, group-size shift or tables in this form.
+template <typename T, int D, int MODE, typename OT, int NW>
+__device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
     constexpr int NT = 64 * NW, QT = 32 * NW;
-    using B = Blk<T, D, MODE_CA, false, NT>;
+    static_assert(MODE == MODE_CA || QT == kQTileWide, "wide AnnSA items are kQTileWide queries");
+    using B = Blk<T, D, MODE, false, NT>;
     __shared__ __align__(16) T Ks[KT * B::STRK];
     __shared__ __align__(16) T Vs[KT * B::STRV];
     __shared__ int sslot[2][1];
@@ -789,13 +807,37 @@ __device__ __forceinline__ void attn_ca2_body(const AttnParams& p) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int h = blockIdx.z, f = blockIdx.y, c = blockIdx.x;
-    const int qbase = f * p.frame_len + c * QT;
-    const int q_count = min(QT, p.frame_len - c * QT);
-    const int nk = p.ca_cnt[h * p.F + f];
-    const int32_t* klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
-    const typename B::Src sr = B::src_of(p, h);
+    int h, q_count, nk, qbase = 0;
+    const int32_t* qlist = nullptr;
+    const int32_t* klist;
+    if constexpr (MODE == MODE_CA) {
+        h = blockIdx.z;
+        const int f = blockIdx.y, c = blockIdx.x;
+        qbase = f * p.frame_len + c * QT;
+        q_count = min(QT, p.frame_len - c * QT);
+        nk = p.ca_cnt[h * p.F + f];
+        klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
+    } else {
+        h = blockIdx.x;                          // heads fastest, as in attn_body
+        const int4 it = p.items[static_cast<size_t>(h) * p.max_items + blockIdx.y];
+        if (it.y <= 0) return;
+        q_count = it.y;
+        qlist = p.qperm + static_cast<size_t>(h) * p.qperm_stride + it.x;
+        nk = it.w;
+        klist = p.kperm + static_cast<size_t>(h) * p.kperm_stride + it.z;
+    }
+    typename B::Src sr = B::src_of(p, h);
+    if constexpr (MODE == MODE_SA) sr.na = clamp_n(p.n_valid, h, p.cap);
 
+    // the first chunk of the key list is loaded before the query rows, so the
+    // first K/V gathers need not wait for them
+    static_assert(KCH % NT == 0, "key chunk split");
+    int kfirst[KCH / NT];
+#pragma unroll
+    for (int u = 0; u < KCH / NT; ++u) {
+        const int r = tid + u * NT;
+        kfirst[u] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+    }
     const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
     typename B::QF qf[2];
     typename B::Acc acc[2];
@@ -805,7 +847,8 @@ __device__ __forceinline__ void attn_ca2_body(const AttnParams& p) {
     for (int qg = 0; qg < 2; ++qg) {
         const int ql = w * 32 + qg * 16 + c16;
         qvalid[qg] = ql < q_count;
-        qrow[qg] = qbase + (qvalid[qg] ? ql : 0);
+        if constexpr (MODE == MODE_CA) qrow[qg] = qbase + (qvalid[qg] ? ql : 0);
+        else qrow[qg] = qvalid[qg] ? qlist[ql] : 0;
         B::load_q(qf[qg], qvalid[qg] ? qh + static_cast<size_t>(qrow[qg]) * D : nullptr, g);
         acc[qg].reset();
     }
@@ -821,7 +864,7 @@ __device__ __forceinline__ void attn_ca2_body(const AttnParams& p) {
     auto step = [&](typename B::Stage& S, int t) __attribute__((always_inline)) {
         if (t >= nt) return;                              // block-uniform
         __syncthreads();
-        B::store_tile(S, sm, 0, tid, 0.f);
+        B::store_tile(S, sm, sr.na, tid, 0.f);
         __syncthreads();
         if (t + 2 < nt) {
             if (((t + 2) * KT) % KCH == 0) {
@@ -835,7 +878,8 @@ __device__ __forceinline__ void attn_ca2_body(const AttnParams& p) {
     typename B::Stage A, Bs;
     A.slots = sslot[0];
     Bs.slots = sslot[1];
-    stage_idx(0);
+#pragma unroll
+    for (int u = 0; u < KCH / NT; ++u) kidx[tid + u * NT] = kfirst[u];
     __syncthreads();
     if (nt > 0) B::load_tile(A, kidx, 0, sr, tid);
     if (nt > 1) B::load_tile(Bs, kidx, 1, sr, tid);
@@ -847,15 +891,16 @@ __device__ __forceinline__ void attn_ca2_body(const AttnParams& p) {
 #pragma unroll
     for (int qg = 0; qg < 2; ++qg) {
         const size_t qi = static_cast<size_t>(h) * p.Nq + qrow[qg];
-        B::template finish<OT>(acc[qg], qf[qg], qvalid[qg], g, static_cast<OT*>(p.out) + qi * D, nullptr,
-                               nullptr, nullptr, p.scale_log2);
+        B::template finish<OT>(acc[qg], qf[qg], qvalid[qg], g, static_cast<OT*>(p.out) + qi * D,
+                               (MODE == MODE_SA && p.lse) ? p.lse + qi : nullptr, nullptr, nullptr,
+                               p.scale_log2);
     }
 }
 
-template <typename T, int D, typename OT, int NW>
+template <typename T, int D, int MODE, typename OT, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_ca2_kernel(const AttnParams p) {
-    attn_ca2_body<T, D, OT, NW>(p);
+void attn_wide_kernel(const AttnParams p) {
+    attn_wide_body<T, D, MODE, OT, NW>(p);
 }
 
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
@@ -895,6 +940,14 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
         const bool search = p.best != nullptr;
 #define FASTAR_SA(S_, B_, M_) \
     hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_SA, S_, OT, 4, B_, M_>), grid, dim3(256), 0, s, p)
+        if constexpr (sizeof(T) == 2 || D == 64) {
+            if (p.wide) {
+                // the host asks for it only without search, group sizes or tables
+                hipLaunchKernelGGL((attn_wide_kernel<T, D, MODE_SA, OT, kQTileWide / 32>), grid,
+                                   dim3(2 * kQTileWide), 0, s, p);
+                return;
+            }
+        }
         if (p.tables > 1) {
             if (search) { if (bias) FASTAR_SA(true, true, true); else FASTAR_SA(true, false, true); }
             else { if (bias) FASTAR_SA(false, true, true); else FASTAR_SA(false, false, true); }
@@ -905,7 +958,7 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
 #undef FASTAR_SA
     } else if constexpr (kCaGroups == 2 && (sizeof(T) == 2 || D == 64)) {
         // (fp32 with d = 128 keeps one group per wave: two would spill)
-        hipLaunchKernelGGL((attn_ca2_kernel<T, D, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0, s, p);
+        hipLaunchKernelGGL((attn_wide_kernel<T, D, MODE_CA, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0, s, p);
     } else {
         hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_CA, false, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0,
                            s, p);

@@ -348,6 +348,13 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
     Carver c(ws);
     AnnsaWs w = carve_annsa(c, H, Nq, cap, Ncur, P);
     StateWs st = carve_state(c, H, Nq, d, tables);
+    // Buckets averaging kQTileWide queries or more take the wide kernel
+    // (256-query items), when no search, group sizes or tables are asked for;
+    // the item table, sized for 64-query items, holds the fewer wide ones.
+    const bool bias = cache && cache->count && cap > 0;
+    const bool wide = tables == 1 && !best && !bias && (dtype == FASTAR_BF16 || d == 64) &&
+                      (static_cast<long long>(kQTileWide) << P) <= Nq;
+    w.it.qtile = wide ? kQTileWide : kQTile;
     AttnParams p;
     p.q = q;
     p.Nq = Nq;
@@ -373,6 +380,7 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
     p.kcount = cache ? cache->count : nullptr;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.tables = tables;
+    p.wide = wide ? 1 : 0;
     p.fbits = P;
     p.q_ids = q_ids;
     p.ida = cache ? cache->ids : nullptr;

@@ -52,15 +52,19 @@ struct SortBufs {
 
 constexpr int kSortTile = 1024;
 constexpr int kQTile = 64;   // queries per attention block
+// queries per block of the wide AnnSA kernel (8 waves x 2 groups of 16),
+// used when buckets average at least this many queries
+constexpr int kQTileWide = 256;
 __host__ __device__ inline int sort_tiles(long long n) { return static_cast<int>((n + kSortTile - 1) / kSortTile); }
 
 // Attention work items built from a (query set, key set) pair of groupings:
-// one item per (bucket, 64-query slice) with at least one query, in bucket
+// one item per (bucket, qtile-query slice) with at least one query, in bucket
 // order: x = first query position in the query permutation, y = number of
 // queries (0 marks padding), z = first key position, w = number of keys.
 struct ItemTable {
     int4* items = nullptr;      // [H][max_items]
     int max_items = 0;
+    int qtile = kQTile;         // queries per item: kQTile or kQTileWide
 };
 // Upper bound on the number of items of one head (a multiple of 8).
 inline int max_attn_items(long long nq, int B) {
@@ -96,6 +100,7 @@ struct AttnParams {
     // field per table; pairs already matched by an earlier table are masked,
     // and the online-softmax / search state carries over between launches
     int table = 0, tables = 1, fbits = 0;
+    int wide = 0;               // AnnSA items of kQTileWide queries (the wide kernel)
     const uint16_t* q_ids = nullptr;  // [H][Nq]
     const uint16_t* ida = nullptr;    // [H][a_rows] ids of source a
     const uint16_t* idb = nullptr;    // [H][b_rows] ids of source b

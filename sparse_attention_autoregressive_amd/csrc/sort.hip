@@ -12,7 +12,7 @@
 //                carry it across waves and rounds), and perm[base + rank] =
 //                index.  For a (queries, keys) pair of sets one more block
 //                per head builds the attention work list (one item per bucket
-//                and 64-query slice, longest key lists first) beside the
+//                and 64- or 256-query slice, longest key lists first) beside the
 //                tiles.  The tile's ids are loaded before the histograms, so
 //                both loads are in flight together.
 //
@@ -214,6 +214,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
             }
         }
         __syncthreads();
+        const int qt = a.items.qtile;
         // rank of bucket b = buckets with more keys, or as many and a lower
         // index; with B <= 256 the 256 / B threads of a bucket split the count
         int rank[4], tiles[4];
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
                         rank[j] += (kc > kn) || (kc == kn && c < b);
                     }
                 }
-                tiles[j] = (qcnt[b] + kQTile - 1) / kQTile;
+                tiles[j] = (qcnt[b] + qt - 1) / qt;
                 slot[rank[j]] = tiles[j];
             }
         }
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
             if (j < k && b < B) {
                 const int f0 = slot[rank[j]], qc = qcnt[b];
                 for (int c = 0; c < tiles[j]; ++c)
-                    it[f0 + c] = make_int4(qoff[b] + c * kQTile, min(kQTile, qc - c * kQTile), koff[b],
+                    it[f0 + c] = make_int4(qoff[b] + c * qt, min(qt, qc - c * qt), koff[b],
                                            kcnt[b]);
             }
         }

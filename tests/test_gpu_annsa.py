@@ -1,7 +1,10 @@
 """GPU parity of fastar_annsa_forward against the oracle (same inputs, the
 oracle's bucket ids), at the tiny fp32, single-head bf16 and full Wan-1.3B-like
 shapes, plus one bucket (dense attention), a partly filled cache, no cache,
-empty buckets, bf16 outputs and run-to-run determinism."""
+empty buckets, bf16 outputs and run-to-run determinism.  Few buckets (at least
+256 queries per bucket on average) take the wide kernel's 256-query items:
+checked at 2, 4 and 8 buckets, with a partly filled cache and with buckets
+that hold queries but no keys."""
 import numpy as np
 import pytest
 import torch
@@ -119,3 +122,43 @@ def test_annsa_bf16_output_and_determinism():
     a, la = run(prep, cache=cache)
     b, lb = run(prep, cache=cache)
     assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("name,P,heads", [("single_bf16", 1, None), ("single_bf16", 2, None),
+                                          ("tiny_f32", 0, None), ("wan13_bf16", 3, (0, 7))])
+@pytest.mark.parametrize("partial", [False, True])
+def test_annsa_wide_items(name, P, heads, partial):
+    """Buckets from the low P bits of the step's ids (a P-plane hash): every
+    bucket averages >= 256 queries, so the call runs 256-query items."""
+    require_gpu()
+    prep = prepared(name)
+    st, cfg = prep["step"], prep["cfg"]
+    assert (256 << P) <= cfg.Nq
+    m = (1 << P) - 1
+    q_ids, k_ids, c_ids = (prep[k] & m for k in ("q_ids", "k_cur_ids", "cache_ids"))
+    n = cfg.cap // 2 + 37 if partial else cfg.n0
+    cache = device_cache(prep, n=n)
+    cache.ids.copy_(dev_ids(c_ids))
+    out, lse = run(prep, cache=cache, q_ids=q_ids, kcur_ids=k_ids, P=P)
+    hs = list(range(cfg.H)) if heads is None else list(heads)
+    O, L = oracle_annsa(prep, n, q_ids=q_ids, kcur_ids=k_ids, cache_ids=c_ids, heads=hs)
+    assert_attention_close(out[hs], O, cfg.dtype, f"wide {name} P={P}")
+    check_lse(lse[hs], L)
+
+
+def test_annsa_wide_items_empty_bucket():
+    """Wide items for a bucket whose queries have no keys: O = 0, lse = -inf."""
+    require_gpu()
+    prep = prepared("single_bf16")
+    st, cfg = prep["step"], prep["cfg"]
+    P = 2
+    q_ids = prep["q_ids"] & 3
+    k_ids = np.minimum(prep["k_cur_ids"] & 3, 2).astype(np.uint16)
+    c_ids = np.minimum(prep["cache_ids"] & 3, 2).astype(np.uint16)
+    cache = device_cache(prep)
+    cache.ids.copy_(dev_ids(c_ids))
+    out, lse = run(prep, cache=cache, q_ids=q_ids, kcur_ids=k_ids, P=P)
+    O, L = oracle_annsa(prep, cfg.n0, q_ids=q_ids, kcur_ids=k_ids, cache_ids=c_ids)
+    assert np.isneginf(L).sum() == int((q_ids == 3).sum()) > 0
+    assert_attention_close(out, O, cfg.dtype, "wide, empty bucket")
+    check_lse(lse, L)
