@@ -154,11 +154,25 @@ class AttentionStep:
         self._commit(cache, q, k_cur, v_cur, step, self.order if use_order else None)
         main.wait_event(self._ev_side)
 
-    def graph(self, cache: KVCache, q, k_cur, v_cur, kp, vp, planes, step: int) -> torch.cuda.CUDAGraph:
+    def graph(self, cache: KVCache, q, k_cur, v_cur, kp, vp, planes, step: int) -> "StepGraph":
         """The step captured into a graph; ``replay()`` runs it on the current
         stream against exactly these tensors (contents may change, addresses
-        may not)."""
+        may not).  The returned object keeps the tensors alive."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             self(cache, q, k_cur, v_cur, kp, vp, planes, step)
-        return g
+        return StepGraph(g, (self, cache, q, k_cur, v_cur, kp, vp, planes))
+
+
+class StepGraph:
+    """A captured step and every tensor its kernels address: the cache, the
+    inputs and the step's own buffers stay allocated as long as the graph
+    does, so a replay never writes into memory that was freed and handed to
+    another tensor."""
+
+    def __init__(self, graph: torch.cuda.CUDAGraph, bound):
+        self.graph = graph
+        self._bound = bound
+
+    def replay(self) -> None:
+        self.graph.replay()
