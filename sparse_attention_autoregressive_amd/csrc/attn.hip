@@ -8,7 +8,7 @@
 //            key (TempCache's top-1, blog "1. TempCache"; summary A): those
 //            keys are exactly the cached members of the query's bucket, whose
 //            dot products the attention computes anyway.
-//  MODE_CA   AnnCA: one block per (head, frame, 64 consecutive queries); keys
+//  MODE_CA   AnnCA: one block per (head, frame, 64 or 128 consecutive queries); keys
 //            are the frame's kept prompt tokens (blog, "2. AnnCA"; summary B).
 //  MODE_TOP1 TempCache search alone: the SA items over cached keys only, no
 //            softmax; each query keeps its best cosine and slot.
@@ -58,7 +58,7 @@
 #include "launch.hpp"
 
 #ifndef CA_WAVES
-#define CA_WAVES 8
+#define CA_WAVES 4
 #endif
 #ifndef CA_GROUPS
 #define CA_GROUPS 2              // 16-query groups per AnnCA wave
@@ -920,18 +920,27 @@ __global__ __launch_bounds__(256) void attn_top1_kernel(const AttnParams p) {
 
 namespace {
 
-// AnnCA blocks take 16*kCaGroups*kCaWaves consecutive queries of a frame:
-// every K/V tile gathered into LDS serves that many queries.
+// AnnCA blocks take 16*kCaGroups*kCaWaves consecutive queries of a frame
+// (16*kCaWaves where a wave keeps one group): every K/V tile gathered into
+// LDS serves that many queries.  Blocks of 128 queries: the 256-query form
+// is faster alone (31.6 vs 33.5 us at the Wan-1.3B chunk) but slower in the
+// step, where AnnCA shares the CUs with the commit's kernels.
 constexpr int kCaWaves = CA_WAVES;
 constexpr int kCaGroups = CA_GROUPS;
+template <typename T, int D>
+constexpr bool ca_grouped() { return kCaGroups == 2 && (sizeof(T) == 2 || D == 64); }
+template <typename T, int D>
+constexpr int ca_block_queries() { return 16 * (ca_grouped<T, D>() ? kCaGroups : 1) * kCaWaves; }
 
 template <typename T, int D, int MODE, typename OT>
 void attn_go(int H, const AttnParams& p, hipStream_t s) {
     dim3 grid;
-    if constexpr (MODE == MODE_CA)
-        grid = dim3((p.frame_len + 16 * kCaGroups * kCaWaves - 1) / (16 * kCaGroups * kCaWaves), p.F, H);
-    else
+    if constexpr (MODE == MODE_CA) {
+        constexpr int QB = ca_block_queries<T, D>();
+        grid = dim3((p.frame_len + QB - 1) / QB, p.F, H);
+    } else {
         grid = dim3(H, p.max_items);
+    }
     if (grid.x == 0 || grid.y == 0 || grid.z == 0) return;
     if constexpr (MODE == MODE_TOP1) {
         hipLaunchKernelGGL((attn_top1_kernel<T, D>), grid, dim3(256), 0, s, p);
@@ -956,7 +965,7 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
             else { if (bias) FASTAR_SA(false, true, false); else FASTAR_SA(false, false, false); }
         }
 #undef FASTAR_SA
-    } else if constexpr (kCaGroups == 2 && (sizeof(T) == 2 || D == 64)) {
+    } else if constexpr (ca_grouped<T, D>()) {
         // (fp32 with d = 128 keeps one group per wave: two would spill)
         hipLaunchKernelGGL((attn_wide_kernel<T, D, MODE_CA, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0, s, p);
     } else {

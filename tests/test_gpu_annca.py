@@ -1,7 +1,8 @@
 """GPU parity of fastar_annca_forward against the oracle: keep masks and counts
 bit-exact, outputs within tolerance; workloads as generated (nearly every
 prompt token kept), constructed ids that prune most of the prompt, frames with
-nothing kept, and an empty prompt."""
+nothing kept, an empty prompt, and fp32 / bf16 at d = 64 and 128 with frames
+that end in a partial block."""
 import numpy as np
 import pytest
 import torch
@@ -71,3 +72,23 @@ def test_annca_nothing_kept_and_empty_prompt():
     empty = np.zeros((cfg.H, 0, cfg.d), np.float32)
     run_and_check(prep, prep["q_ids"], np.zeros((cfg.H, 0), np.uint16), cfg.P, "empty prompt",
                   kp=empty, vp=empty)
+
+
+@pytest.mark.parametrize("name,d", [("tiny_f32", 128), ("tiny_f32", 64), ("single_bf16", 64),
+                                    ("single_bf16", 128)])
+def test_annca_dtypes_widths_ragged_frames(name, d):
+    """Three frames of 200 queries (fp32 d = 128 blocks take 64 queries, the
+    others 128: every frame ends in a partial block), P = 2 so some prompt
+    tokens are pruned per frame."""
+    require_gpu()
+    prep = prepared(name, d=d, frame_len=200, Fq=3, Fc=2)
+    cfg = prep["cfg"]
+    assert cfg.Nq == 600
+    P = 2
+    rng = np.random.default_rng(d)
+    q_ids = np.empty_like(prep["q_ids"])
+    for f in range(3):      # frame f occupies buckets {f, f + 1} only
+        q_ids[:, f * 200:(f + 1) * 200] = rng.integers(f, f + 2, size=(cfg.H, 200))
+    kp_ids = (prep["kp_ids"] & 3).astype(np.uint16)
+    keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, P, f"ragged {name} d={d}")
+    assert 0 < keep.mean() < 1

@@ -162,3 +162,18 @@ def test_annsa_wide_items_empty_bucket():
     assert np.isneginf(L).sum() == int((q_ids == 3).sum()) > 0
     assert_attention_close(out, O, cfg.dtype, "wide, empty bucket")
     check_lse(lse, L)
+
+
+@pytest.mark.parametrize("search", [False, True])
+def test_annsa_f32_d128(search):
+    """fp32 inputs at d = 128 (the register-heavy kernel form) against the oracle."""
+    require_gpu()
+    prep = prepared("tiny_f32", d=128)
+    st, cfg = prep["step"], prep["cfg"]
+    cache = device_cache(prep)
+    out, lse, *_ = fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
+                                    dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), cfg.P, cache=cache,
+                                    search=search)
+    O, L = oracle_annsa(prep, cfg.n0)
+    assert_attention_close(out, O, cfg.dtype, f"f32 d=128 search={search}")
+    check_lse(lse, L)
