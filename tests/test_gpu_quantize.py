@@ -68,8 +68,8 @@ def test_quantize_matches_oracle(name, B, src):
     print(f"quantize {name} B={B} {src}: {ties} flagged near-ties")
 
 
-@pytest.mark.parametrize("N,B", [(100, 1), (100, 65), (257, 1000), (64, 64)])
-@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("N,B", [(100, 1), (100, 65), (257, 1000), (64, 64), (513, 129)])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64), ("f32", 128)])
 def test_quantize_edge_shapes(N, B, dtype, d):
     require_gpu()
     rng = np.random.default_rng(N + B)
