@@ -210,6 +210,7 @@ struct Blk {
     // keys first, so at most one tile per item mixes the two, and every other
     // tile gathers from one base pointer held in scalar registers with a
     // 32-bit byte offset per row.
+    template <bool LK = true, bool LV = true>
     static __device__ __forceinline__ void load_tile(Stage& S, const int* kidx, int tile, const Src& sr,
                                                      int tid) {
         int jf = 0, jl = 0;
@@ -229,18 +230,20 @@ struct Blk {
             const int j = kidx[(tile * KT + row) % KCH];
             if (all_a || all_b) {
                 const uint32_t off = static_cast<uint32_t>(j - sub) * ROWB + chunk * 16;
-                S.k[e] = *reinterpret_cast<const u32x4*>(kbase + off);
-                if constexpr (HAS_V) S.v[e] = *reinterpret_cast<const u32x4*>(vbase + off);
+                if constexpr (LK) S.k[e] = *reinterpret_cast<const u32x4*>(kbase + off);
+                if constexpr (HAS_V && LV) S.v[e] = *reinterpret_cast<const u32x4*>(vbase + off);
             } else {
                 const bool from_a = j < sr.na;
                 const uint32_t off = static_cast<uint32_t>(from_a ? j : j - sr.na) * ROWB + chunk * 16;
-                S.k[e] = *reinterpret_cast<const u32x4*>(
-                    reinterpret_cast<const char*>(from_a ? sr.ka : sr.kb) + off);
-                if constexpr (HAS_V)
+                if constexpr (LK)
+                    S.k[e] = *reinterpret_cast<const u32x4*>(
+                        reinterpret_cast<const char*>(from_a ? sr.ka : sr.kb) + off);
+                if constexpr (HAS_V && LV)
                     S.v[e] = *reinterpret_cast<const u32x4*>(
                         reinterpret_cast<const char*>(from_a ? sr.va : sr.vb) + off);
             }
         }
+        if constexpr (!LK) return;
         if constexpr (SLOTS) {
             // One norm (and group size) per thread: lanes u % CPR = e < E
             // take row rb*E + e (the others repeat row rb*E + E-1), so a tile
@@ -268,14 +271,17 @@ struct Blk {
 
     // ``inv_c`` = 1 / (scale * log2 e): a group size m becomes the raw-score
     // offset log2(m) * inv_c = ln(m) / scale.
+    // ``SV``: the stage whose V part is stored (the K stage itself, or a
+    // separate V stage in the split pipeline).
     static __device__ __forceinline__ void store_tile(const Stage& S, const Smem& sm, int na, int tid,
-                                                      float inv_c) {
+                                                      float inv_c, const Stage* SV = nullptr) {
         const int chunk = tid % CPR, rb = tid / CPR;
+        const Stage& V = SV ? *SV : S;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int row = rb * E + e;
             *reinterpret_cast<u32x4*>(&sm.Ks[row * STRK + chunk * EPC]) = S.k[e];
-            if constexpr (HAS_V) *reinterpret_cast<u32x4*>(&sm.Vs[row * STRV + chunk * EPC]) = S.v[e];
+            if constexpr (HAS_V) *reinterpret_cast<u32x4*>(&sm.Vs[row * STRV + chunk * EPC]) = V.v[e];
         }
         if constexpr (SLOTS) {
             if (chunk < E) {
@@ -383,19 +389,16 @@ struct Blk {
                 auto scan = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
                     for (int kb4 = 0; kb4 < 4; ++kb4) {
-                        const int4 sl = *reinterpret_cast<const int4*>(&sm.kslot[kb4 * 16 + 4 * g]);
-                        const float4 iv = *reinterpret_cast<const float4*>(&sm.kinv[kb4 * 16 + 4 * g]);
-                        const int slv[4] = {sl.x, sl.y, sl.z, sl.w};
-                        const float ivv[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const float cs = s[kb4][r] * ivv[r];
+                            const int sl = sm.kslot[kb4 * 16 + 4 * g + r];
+                            const float cs = s[kb4][r] * sm.kinv[kb4 * 16 + 4 * g + r];
                             bool ok = cs > a.bc;
                             if constexpr (decltype(masked)::value)
-                                ok = ok && (MODE == MODE_TOP1 || slv[r] < na) &&
+                                ok = ok && (MODE == MODE_TOP1 || sl < na) &&
                                      kbase + kb4 * 16 + 4 * g + r < nk;
                             a.bc = ok ? cs : a.bc;
-                            a.bs = ok ? slv[r] : a.bs;
+                            a.bs = ok ? sl : a.bs;
                         }
                     }
                 };
@@ -744,19 +747,26 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     }
     const int nt = (nk + KT - 1) / KT;
 
-    // One pipeline step on tile t held in stage S: store it, refill S with
-    // tile t+2, compute on tile t.  Tile t+1 stays in flight in the other stage.
+    // One pipeline step on tile t: store its K (stage S) and V (stage VS),
+    // refill VS with V of tile t+1 and S with K of tile t+2, compute on tile
+    // t.  K runs two tiles ahead, V one: three tiles' rows in registers
+    // instead of four, so three waves fit on a SIMD.  The V indices of tile
+    // t+1 are read before a new index chunk may overwrite them (the barrier
+    // before the chunk's staging keeps every wave's reads ahead of it).
+    typename B::Stage VS;
     auto step = [&](typename B::Stage& S, int t) __attribute__((always_inline)) {
         if (t >= nt) return;                              // block-uniform
         __syncthreads();
-        B::store_tile(S, sm, sr.na, tid, inv_c);
+        B::store_tile(S, sm, sr.na, tid, inv_c, &VS);
         __syncthreads();
+        if (t + 1 < nt) B::template load_tile<false, true>(VS, kidx, t + 1, sr, tid);
         if (t + 2 < nt) {
             if (((t + 2) * KT) % KCH == 0) {        // next index chunk
+                __syncthreads();
                 stage_idx((t + 2) * KT);
                 __syncthreads();
             }
-            B::load_tile(S, kidx, t + 2, sr, tid);
+            B::template load_tile<true, false>(S, kidx, t + 2, sr, tid);
         }
         if (wave_active) B::compute_tile(acc, qf, sm, t * KT, nk, sr.na, p.scale_log2, g, c16, seen);
     };
@@ -764,11 +774,15 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     typename B::Stage A, Bs;
     A.slots = sslot[0];
     Bs.slots = sslot[1];
+    VS.slots = nullptr;
 #pragma unroll
     for (int u = 0; u < KCH / NT; ++u) kidx[tid + u * NT] = kfirst[u];
     __syncthreads();
-    if (nt > 0) B::load_tile(A, kidx, 0, sr, tid);
-    if (nt > 1) B::load_tile(Bs, kidx, 1, sr, tid);
+    if (nt > 0) {
+        B::template load_tile<true, false>(A, kidx, 0, sr, tid);
+        B::template load_tile<false, true>(VS, kidx, 0, sr, tid);
+    }
+    if (nt > 1) B::template load_tile<true, false>(Bs, kidx, 1, sr, tid);
     // Each stage is named in exactly one place of a fixed pair of steps, so
     // both keep fixed registers.  A step past the last tile does nothing.
 #pragma unroll 1
@@ -905,9 +919,15 @@ void attn_wide_kernel(const AttnParams p) {
 
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
 // registers per lane, i.e. 2 waves per SIMD.
+#ifndef KV_WAVES
+#define KV_WAVES 3
+#endif
+template <typename T, bool BIAS, bool MULTI>
+constexpr int kv_waves() { return (sizeof(T) == 2 && !BIAS && !MULTI) ? KV_WAVES : 2; }
 template <typename T, int D, int MODE, bool SEARCH, typename OT, int NW, bool BIAS = false,
           bool MULTI = false>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(kv_waves<T, BIAS, MULTI>(), kv_waves<T, BIAS, MULTI>())))
 void attn_kv_kernel(const AttnParams p) {
     attn_body<T, D, MODE, SEARCH, OT, NW, BIAS, MULTI>(p);
 }
