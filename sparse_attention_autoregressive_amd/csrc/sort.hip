@@ -17,7 +17,9 @@
 //                both loads are in flight together.
 //
 // Every block re-reads its head's tile histograms (a few KB, from L2) instead
-// of waiting for a separate scan launch.  The result is unique (a stable sort),
+// of waiting for a separate scan launch -- up to kSortScanTiles tiles per head;
+// beyond that a scan launch (one block per head and set) turns the
+// histograms into per-tile prefixes first.  The result is unique (a stable sort),
 // so it is bit-identical run to run.
 #include "common.hpp"
 #include "launch.hpp"
@@ -31,6 +33,7 @@ struct SortArgs {
     int B;
     int P;
     int builder_block;            // grid x index of the work-list block, or -1
+    int scanned;                  // hist holds per-tile prefixes and off is written (scan launch)
     ItemTable items;
 };
 
@@ -71,6 +74,10 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
 // the parts meet in LDS and thread b keeps bucket b (k = 1).  With B > 256
 // thread i keeps buckets i*k .. i*k+k-1 (k = B / 256) and sums all tiles.
 constexpr int kTileLoads = 32;
+// Tiles per head above which the histograms are scanned in a launch of their
+// own (the step's 37 tiles keep the two-launch form: one more launch on the
+// critical path costs more than the re-reads).
+constexpr int kSortScanTiles = 64;
 
 struct BucketSums {
     int before[4], total[4];
@@ -142,6 +149,51 @@ __device__ __forceinline__ int bucket_starts(const BucketSums& s, int B, int k, 
     return total;
 }
 
+// With many tiles per head (long key sets) the scatter blocks would each
+// re-read every tile histogram of their head; one block per (head, set)
+// instead turns the histograms into per-tile prefixes in place (thread b
+// walks bucket b's column, loads in runs of kTileLoads) and writes off.
+__global__ __launch_bounds__(256) void sort_scan_kernel(SortArgs a) {
+    __shared__ int smem[8];
+    const int h = blockIdx.x, si = blockIdx.y, B = a.B, tid = threadIdx.x;
+    const IdSet& S = a.set[si];
+    const SortBufs& O = a.buf[si];
+    int na;
+    const int ntiles = sort_tiles(set_count(S, h, na));
+    const int k = (B + 255) / 256, b0 = tid * k;
+    int* hh = O.hist + static_cast<size_t>(h) * O.max_tiles * B;
+    int tot[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int b = b0 + j;
+        if (j >= k || b >= B) continue;
+        int running = 0;
+        for (int t0 = 0; t0 < ntiles; t0 += kTileLoads) {
+            int c[kTileLoads];
+#pragma unroll
+            for (int i = 0; i < kTileLoads; ++i) c[i] = t0 + i < ntiles ? hh[static_cast<size_t>(t0 + i) * B + b] : 0;
+#pragma unroll
+            for (int i = 0; i < kTileLoads; ++i) {
+                if (t0 + i < ntiles) hh[static_cast<size_t>(t0 + i) * B + b] = running;
+                running += c[i];
+            }
+        }
+        tot[j] = running;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine += tot[j];
+    int total;
+    int run = block_exclusive_scan<256>(mine, smem, total);
+    int32_t* offp = O.off + static_cast<size_t>(h) * (B + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < k && b0 + j < B) offp[b0 + j] = run;
+        run += tot[j];
+    }
+    if (tid == 0) offp[B] = total;
+}
+
 __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     __shared__ int run[1024];
     __shared__ int base[1024];
@@ -171,46 +223,77 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     }
 
     // ---- the tile's base offsets (and, for the lead block, off); the part
-    // sums borrow the rank step's LDS
+    // sums borrow the rank step's LDS.  After a scan launch: off (bucket
+    // starts) plus the tile's prefix, and the bucket totals from off.
     int* pt = reinterpret_cast<int*>(wcnt[0]);
     int* pb = reinterpret_cast<int*>(wcnt[1]);
-    BucketSums bs;
-    bucket_sums(O, h, t, ntiles, B, k, bs, pt, pb);
-    int start[4];
-    const int total = bucket_starts(bs, B, k, start, smem);
     int32_t* offp = O.off ? O.off + static_cast<size_t>(h) * (B + 1) : nullptr;
+    int start[4], tot[4];
+    if (a.scanned) {
+        const int* hh = O.hist + static_cast<size_t>(h) * O.max_tiles * B;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < k && b0 + j < B) {
-            base[b0 + j] = start[j] + bs.before[j];
-            if (lead && offp) offp[b0 + j] = start[j];
+        for (int j = 0; j < 4; ++j) {
+            const int b = b0 + j;
+            start[j] = tot[j] = 0;
+            if (j < k && b < B) {
+                start[j] = offp[b];
+                tot[j] = offp[b + 1] - offp[b];
+                if (t < ntiles) base[b] = start[j] + hh[static_cast<size_t>(t) * B + b];
+            }
         }
+    } else {
+        BucketSums bs;
+        bucket_sums(O, h, t, ntiles, B, k, bs, pt, pb);
+        const int total = bucket_starts(bs, B, k, start, smem);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            tot[j] = bs.total[j];
+            if (j < k && b0 + j < B) {
+                base[b0 + j] = start[j] + bs.before[j];
+                if (lead && offp) offp[b0 + j] = start[j];
+            }
+        }
+        if (lead && offp && tid == 0) offp[B] = total;
     }
-    if (lead && offp && tid == 0) offp[B] = total;
 
     // ---- the attention work list: items in decreasing order of key count
     // (ties: lower bucket first), so the longest items start first.  Built by
     // the builder block from both sets' histograms (its ``start`` and
-    // ``bs.total`` above are the query set's).
+    // ``tot`` above are the query set's; after a scan, both sets' off).
     if (builder) {
         int* qoff = reinterpret_cast<int*>(wcnt[0]);
         int* qcnt = reinterpret_cast<int*>(wcnt[1]);
         int* koff = reinterpret_cast<int*>(wcnt[2]);
         int* kcnt = reinterpret_cast<int*>(wcnt[3]);
         int* slot = run;
-        int nak;
-        const int nkeys = set_count(a.set[1], h, nak);
-        BucketSums ks;
-        bucket_sums(a.buf[1], h, 0, sort_tiles(nkeys), B, k, ks, pt, pb);
-        int kstart[4];
-        bucket_starts(ks, B, k, kstart, smem);
+        int kstart[4], ktot[4];
+        if (a.scanned) {
+            const int32_t* ko = a.buf[1].off + static_cast<size_t>(h) * (B + 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int b = b0 + j;
+                kstart[j] = ktot[j] = 0;
+                if (j < k && b < B) {
+                    kstart[j] = ko[b];
+                    ktot[j] = ko[b + 1] - ko[b];
+                }
+            }
+        } else {
+            int nak;
+            const int nkeys = set_count(a.set[1], h, nak);
+            BucketSums ks;
+            bucket_sums(a.buf[1], h, 0, sort_tiles(nkeys), B, k, ks, pt, pb);
+            bucket_starts(ks, B, k, kstart, smem);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ktot[j] = ks.total[j];
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j < k && b0 + j < B) {
                 qoff[b0 + j] = start[j];
-                qcnt[b0 + j] = bs.total[j];
+                qcnt[b0 + j] = tot[j];
                 koff[b0 + j] = kstart[j];
-                kcnt[b0 + j] = ks.total[j];
+                kcnt[b0 + j] = ktot[j];
             }
         }
         __syncthreads();
@@ -349,9 +432,18 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
         a.buf[1] = a.buf[0];
     }
     if (H == 0) return hipSuccess;
+    // a scan launch once the tiles are many (every set must then have off)
+    bool offs = true;
+    for (int i = 0; i < nsets; ++i) offs = offs && bufs[i].off != nullptr;
+    a.scanned = (max_tiles > kSortScanTiles && offs) ? 1 : 0;
     if (max_tiles > 0) {
         timer_begin("sort_hist", s);
         hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
+        timer_end(s);
+    }
+    if (a.scanned) {
+        timer_begin("sort_scan", s);
+        hipLaunchKernelGGL(sort_scan_kernel, dim3(H, nsets), dim3(256), 0, s, a);
         timer_end(s);
     }
     int gx = max_tiles > 0 ? max_tiles : 1;

@@ -177,3 +177,19 @@ def test_annsa_f32_d128(search):
     O, L = oracle_annsa(prep, cfg.n0)
     assert_attention_close(out, O, cfg.dtype, f"f32 d=128 search={search}")
     check_lse(lse, L)
+
+
+def test_annsa_long_key_set():
+    """A cache of 76 800 keys (75 sort tiles per head with the chunk: the sort
+    takes its scan-launch form) with the fused search, against the oracle."""
+    require_gpu()
+    prep = prepared("tiny_f32", Fc=300, cap=80000)
+    st, cfg = prep["step"], prep["cfg"]
+    assert cfg.n0 == 76800
+    cache = device_cache(prep)
+    out, lse, best, bcos = fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
+                                            dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), cfg.P,
+                                            cache=cache, search=True)
+    O, L = oracle_annsa(prep, cfg.n0)
+    assert_attention_close(out, O, cfg.dtype, "long key set")
+    check_lse(lse, L)
