@@ -581,7 +581,7 @@ def size_sweep(args):
         del x
         sid = torch.randint(0, B, (H, N), generator=gen, device=dev, dtype=torch.int32).to(torch.int16)
         ws = torch.empty(fa.load().fastar_bucket_sort_workspace(H, N, P), dtype=torch.uint8, device=dev)
-        ms = kernel_ms(lambda: fa.bucket_sort(sid, P, ws=ws), ["sort_hist", "sort_scatter"])
+        ms = kernel_ms(lambda: fa.bucket_sort(sid, P, ws=ws), ["sort_hist", "sort_scan", "sort_scatter"])
         nbytes = H * N * 6.0
         rows.append({"kernel": "bucket_sort", "ids": H * N, "bytes": nbytes, "ms": ms,
                      "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})

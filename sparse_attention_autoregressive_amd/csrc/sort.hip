@@ -75,9 +75,10 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
 // thread i keeps buckets i*k .. i*k+k-1 (k = B / 256) and sums all tiles.
 constexpr int kTileLoads = 32;
 // Tiles per head above which the histograms are scanned in a launch of their
-// own (the step's 37 tiles keep the two-launch form: one more launch on the
-// critical path costs more than the re-reads).
-constexpr int kSortScanTiles = 64;
+// own.  Measured over 12 heads of 128 buckets: at 75 tiles the two-launch
+// form takes 21.9 us and the three-launch form 27.8; at 293 tiles 77 and
+// 57.8.  (The step's 37 tiles keep the two-launch form.)
+constexpr int kSortScanTiles = 128;
 
 struct BucketSums {
     int before[4], total[4];
@@ -151,47 +152,94 @@ __device__ __forceinline__ int bucket_starts(const BucketSums& s, int B, int k, 
 
 // With many tiles per head (long key sets) the scatter blocks would each
 // re-read every tile histogram of their head; one block per (head, set)
-// instead turns the histograms into per-tile prefixes in place (thread b
-// walks bucket b's column, loads in runs of kTileLoads) and writes off.
-__global__ __launch_bounds__(256) void sort_scan_kernel(SortArgs a) {
-    __shared__ int smem[8];
+// instead turns the histograms into per-tile prefixes in place and writes
+// off.  kScanNT threads: with B <= kScanNT each bucket's column is split into
+// kScanNT / B contiguous tile ranges (parts); a part sums its range (loads in
+// runs of kTileLoads), the parts' sums meet in LDS, and each part rewrites
+// its range starting from the sum of the parts before it.  With B >
+// kScanNT each thread walks whole columns.
+constexpr int kScanNT = 1024;
+
+__global__ __launch_bounds__(kScanNT) void sort_scan_kernel(SortArgs a) {
+    __shared__ int smem[kScanNT / kWave];
+    __shared__ int psum[kScanNT];
     const int h = blockIdx.x, si = blockIdx.y, B = a.B, tid = threadIdx.x;
     const IdSet& S = a.set[si];
     const SortBufs& O = a.buf[si];
     int na;
     const int ntiles = sort_tiles(set_count(S, h, na));
-    const int k = (B + 255) / 256, b0 = tid * k;
     int* hh = O.hist + static_cast<size_t>(h) * O.max_tiles * B;
-    int tot[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int b = b0 + j;
-        if (j >= k || b >= B) continue;
-        int running = 0;
-        for (int t0 = 0; t0 < ntiles; t0 += kTileLoads) {
+    // thread -> (bucket, part): buckets fastest, so a load of one tile row is
+    // coalesced over the buckets
+    const int parts = B <= kScanNT ? kScanNT / B : 1;
+    const int cols = B <= kScanNT ? 1 : B / kScanNT;        // columns per thread
+    const int part = B <= kScanNT ? tid / B : 0;
+    const int tpp = (ntiles + parts - 1) / parts;
+    const int t0 = min(ntiles, part * tpp), t1 = min(ntiles, t0 + tpp);
+    auto col_sum = [&](int b) {
+        int sum = 0;
+        for (int c0 = t0; c0 < t1; c0 += kTileLoads) {
             int c[kTileLoads];
 #pragma unroll
-            for (int i = 0; i < kTileLoads; ++i) c[i] = t0 + i < ntiles ? hh[static_cast<size_t>(t0 + i) * B + b] : 0;
+            for (int i = 0; i < kTileLoads; ++i) c[i] = c0 + i < t1 ? hh[static_cast<size_t>(c0 + i) * B + b] : 0;
+#pragma unroll
+            for (int i = 0; i < kTileLoads; ++i) sum += c[i];
+        }
+        return sum;
+    };
+    auto col_rewrite = [&](int b, int running) {
+        for (int c0 = t0; c0 < t1; c0 += kTileLoads) {
+            int c[kTileLoads];
+#pragma unroll
+            for (int i = 0; i < kTileLoads; ++i) c[i] = c0 + i < t1 ? hh[static_cast<size_t>(c0 + i) * B + b] : 0;
 #pragma unroll
             for (int i = 0; i < kTileLoads; ++i) {
-                if (t0 + i < ntiles) hh[static_cast<size_t>(t0 + i) * B + b] = running;
+                if (c0 + i < t1) hh[static_cast<size_t>(c0 + i) * B + b] = running;
                 running += c[i];
             }
         }
-        tot[j] = running;
-    }
-    int mine = 0;
+        return running;
+    };
+    int mine = 0;                        // this thread's share of the bucket totals
+    if (B <= kScanNT) {
+        const int b = tid % B;
+        const bool act = part < parts;
+        const int sum = act ? col_sum(b) : 0;
+        psum[tid] = sum;
+        __syncthreads();
+        int before = 0, total = 0;
+        if (act) {
+            for (int q = 0; q < parts; ++q) {
+                const int v = psum[q * B + b];
+                before += q < part ? v : 0;
+                total += v;
+            }
+            col_rewrite(b, before);
+        }
+        mine = (act && part == 0) ? total : 0;
+        __syncthreads();                 // psum is reused below only through smem
+        int tot;
+        const int run = block_exclusive_scan<kScanNT>(mine, smem, tot);
+        int32_t* offp = O.off + static_cast<size_t>(h) * (B + 1);
+        if (act && part == 0) offp[b] = run;
+        if (tid == 0) offp[B] = tot;
+    } else {
+        int tots[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mine += tot[j];
-    int total;
-    int run = block_exclusive_scan<256>(mine, smem, total);
-    int32_t* offp = O.off + static_cast<size_t>(h) * (B + 1);
+        for (int j = 0; j < 4; ++j)
+            if (j < cols) tots[j] = col_rewrite(tid * cols + j, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < k && b0 + j < B) offp[b0 + j] = run;
-        run += tot[j];
+        for (int j = 0; j < 4; ++j) mine += tots[j];
+        int tot;
+        int run = block_exclusive_scan<kScanNT>(mine, smem, tot);
+        int32_t* offp = O.off + static_cast<size_t>(h) * (B + 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < cols) offp[tid * cols + j] = run;
+            run += tots[j];
+        }
+        if (tid == 0) offp[B] = tot;
     }
-    if (tid == 0) offp[B] = total;
 }
 
 __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
@@ -443,7 +491,7 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
     }
     if (a.scanned) {
         timer_begin("sort_scan", s);
-        hipLaunchKernelGGL(sort_scan_kernel, dim3(H, nsets), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(sort_scan_kernel, dim3(H, nsets), dim3(kScanNT), 0, s, a);
         timer_end(s);
     }
     int gx = max_tiles > 0 ? max_tiles : 1;

@@ -179,13 +179,15 @@ def test_annsa_f32_d128(search):
     check_lse(lse, L)
 
 
-def test_annsa_long_key_set():
-    """A cache of 76 800 keys (75 sort tiles per head with the chunk: the sort
-    takes its scan-launch form) with the fused search, against the oracle."""
+@pytest.mark.parametrize("Fc,cap", [(300, 80000), (550, 150000)])
+def test_annsa_long_key_set(Fc, cap):
+    """Caches of 76 800 and 140 800 keys (75 and 138 sort tiles per head with
+    the chunk: the second takes the sort's scan-launch form) with the fused
+    search, against the oracle."""
     require_gpu()
-    prep = prepared("tiny_f32", Fc=300, cap=80000)
+    prep = prepared("tiny_f32", Fc=Fc, cap=cap)
     st, cfg = prep["step"], prep["cfg"]
-    assert cfg.n0 == 76800
+    assert cfg.n0 == Fc * 256
     cache = device_cache(prep)
     out, lse, best, bcos = fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
                                             dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), cfg.P,

@@ -62,8 +62,8 @@ def test_hash_norms(dtype, d):
 
 @pytest.mark.parametrize("P,N", [(0, 17), (3, 0), (5, 1), (7, 1023), (7, 1025), (7, 37440),
                                  (10, 5000), (8, 4096),
-                                 # more than 64 tiles per head: the scan-launch form
-                                 (7, 65537), (10, 100000), (0, 70000), (9, 299520)])
+                                 # past 128 tiles per head the sort adds a scan launch
+                                 (7, 65537), (10, 100000), (0, 140000), (9, 299520), (7, 131073)])
 def test_bucket_sort_bit_exact(P, N):
     require_gpu()
     rng = np.random.default_rng(10 * P + N)
