@@ -92,3 +92,12 @@ def test_annca_dtypes_widths_ragged_frames(name, d):
     kp_ids = (prep["kp_ids"] & 3).astype(np.uint16)
     keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, P, f"ragged {name} d={d}")
     assert 0 < keep.mean() < 1
+
+
+@pytest.mark.parametrize("P", [9, 10])
+def test_annca_many_buckets(P):
+    """512 and 1024 buckets: the selection's bucket bitmap at its largest."""
+    require_gpu()
+    prep = prepared("single_bf16", P=P)
+    keep = run_and_check(prep, prep["q_ids"], prep["kp_ids"], P, f"annca P={P}")
+    assert 0 < keep.mean() < 1

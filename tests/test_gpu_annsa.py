@@ -195,3 +195,19 @@ def test_annsa_long_key_set(Fc, cap):
     O, L = oracle_annsa(prep, cfg.n0)
     assert_attention_close(out, O, cfg.dtype, "long key set")
     check_lse(lse, L)
+
+
+@pytest.mark.parametrize("P", [9, 10])
+def test_annsa_many_buckets(P):
+    """512 and 1024 buckets (the most the bucketed calls take): the sort's
+    several-buckets-per-thread paths, with the fused search, against the oracle."""
+    require_gpu()
+    prep = prepared("single_bf16", P=P)
+    st, cfg = prep["step"], prep["cfg"]
+    cache = device_cache(prep)
+    out, lse, best, bcos = fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
+                                            dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), P, cache=cache,
+                                            search=True)
+    O, L = oracle_annsa(prep, cfg.n0)
+    assert_attention_close(out, O, cfg.dtype, f"P={P}")
+    check_lse(lse, L)
