@@ -25,8 +25,8 @@ struct HashSets {
 };
 
 // One block of 4 waves hashes 64 * GPW vectors of one head and one token set
-// (GPW 16-vector groups per wave; bf16 blocks take GPW = 4, so the planes are
-// staged once per 256 vectors and every wave has four groups' loads in
+// (GPW 16-vector groups per wave; bf16 blocks take GPW = 2, so the planes are
+// staged once per 128 vectors and every wave has two groups' loads in
 // flight).  The projections X R^T run on the matrix cores: the P <= 16
 // planes are the 16 rows of one MFMA block (rows past P are zero and their
 // bits dropped) and 16 vectors its columns.  A lane ends with the projections
@@ -214,13 +214,13 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashSets sets, const fl
     }
 }
 
-// bf16 blocks take four 16-vector groups per wave (256 vectors per block;
-// measured faster than 64-vector blocks from the step's 112 k vectors up),
-// fp32 blocks one.
+// bf16 blocks take two 16-vector groups per wave (128 vectors per block;
+// the step's three-set launch: 9.7 us against 12.0 with four groups and 12.6
+// with one), fp32 blocks one.
 template <typename T, int D>
 static hipError_t hash_dispatch_p(const HashSets& sets, int count, int H, const float* planes, int P,
                                   hipStream_t s) {
-    constexpr int GPW = sizeof(T) == 2 ? 4 : 1;
+    constexpr int GPW = sizeof(T) == 2 ? 2 : 1;
     int nmax = 0;
     for (int i = 0; i < count; ++i) nmax = sets.N[i] > nmax ? sets.N[i] : nmax;
     timer_begin("ann_hash", s);
