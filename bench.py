@@ -59,7 +59,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 # factors being what a 512 MiB device copy reads on the same counters
 # (profiles/step_wan13_hbm_traffic.md).  Valid for the kernel build the
 # counters were taken on; None for other workloads.
-ANNSA_TRAFFIC_BYTES = {"wan13_bf16": 333.2e6}
+ANNSA_TRAFFIC_BYTES = {"wan13_bf16": 333.3e6}
 
 
 def parse():
