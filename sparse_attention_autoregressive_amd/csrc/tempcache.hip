@@ -83,24 +83,21 @@ __device__ __forceinline__ bool is_matched(int b, float c, int n, float tau) {
 // order-preserving as unsigned) and a candidate bit.
 namespace {
 // Every slot 0..n-1, 32 per thread (one refreshed-bitmap word).  refr null:
-// every valid slot is a candidate.  The timestamps are read by fetch(),
-// which needs only the cache capacity, so a caller can issue it before n and
-// the refreshed bitmap are known; load() adds the candidate bits.
+// every valid slot is a candidate.
 struct SlotRange {
     static constexpr int ITEMS = SLOT_ITEMS;
     const int32_t* ts;
     const uint32_t* refr;
-    int n, cap;
+    int n;
     uint32_t key[ITEMS];
     uint32_t cand = 0;
-    int base = 0, cached = -1, fetched = -1;
-    __device__ SlotRange(const int32_t* t, const uint32_t* r, int n_, int cap_)
-        : ts(t), refr(r), n(n_), cap(cap_) {}
-    __device__ __forceinline__ void fetch(int c0) {
-        if (fetched == c0) return;
-        fetched = c0;
+    int base = 0, cached = -1;
+    __device__ SlotRange(const int32_t* t, const uint32_t* r, int n_) : ts(t), refr(r), n(n_) {}
+    __device__ __forceinline__ void load(int c0) {
+        if (cached == c0) return;
+        cached = c0;
         base = c0 + static_cast<int>(threadIdx.x) * ITEMS;
-        const bool vec = base + ITEMS <= cap && (reinterpret_cast<uintptr_t>(ts + base) & 15) == 0;
+        const bool vec = base + ITEMS <= n && (reinterpret_cast<uintptr_t>(ts + base) & 15) == 0;
         if (vec) {
 #pragma unroll
             for (int k = 0; k < ITEMS; k += 4) {
@@ -110,13 +107,8 @@ struct SlotRange {
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < ITEMS; ++k) key[k] = (base + k < cap) ? ts_key(ts[base + k]) : 0u;
+            for (int k = 0; k < ITEMS; ++k) key[k] = (base + k < n) ? ts_key(ts[base + k]) : 0u;
         }
-    }
-    __device__ __forceinline__ void load(int c0) {
-        if (cached == c0) return;
-        cached = c0;
-        fetch(c0);
         const int left = n - base;
         const uint32_t valid = left >= ITEMS ? 0xFFFFFFFFu : (left > 0 ? (1u << left) - 1u : 0u);
         cand = (valid && refr) ? (~refr[base >> 5] & valid) : valid;
@@ -124,55 +116,33 @@ struct SlotRange {
     __device__ __forceinline__ int slot(int k) const { return base + k; }
 };
 
-// The slots of a list (ascending), 8 per thread; positions at or past m and
-// entries outside [0, n) are no candidates (a list from another cache state
-// gives wrong evictions, never an access outside the cache).  fetch() reads
-// the entries up to the list's length and their timestamps (entries outside
-// [0, cap) read slot 0's), so it can run before m, n and the refreshed bitmap
-// are known; set_bounds() then gives m and n.
+// The slots of a list (ascending), 8 per thread; entries outside [0, n) are
+// no candidates (a list from another cache state gives wrong evictions, never
+// an access outside the cache).
 struct SlotList {
     static constexpr int ITEMS = 8;
     const int32_t* list;
     const int32_t* ts;
     const uint32_t* refr;
-    int len, cap, m = 0, n = 0;
+    int m, n;
     uint32_t key[ITEMS];
     int sl[ITEMS];
     uint32_t cand = 0;
-    int cached = -1, fetched = -1;
-    __device__ SlotList(const int32_t* l, const int32_t* t, const uint32_t* r, int len_, int cap_)
-        : list(l), ts(t), refr(r), len(len_), cap(cap_) {}
-    __device__ __forceinline__ void set_bounds(int m_, int n_) {
-        m = m_;
-        n = n_;
-        cached = -1;
-    }
-    // the list entries (issued first: the timestamp reads depend on them)
-    __device__ __forceinline__ void fetch_list(int c0) {
-        const int base = c0 + static_cast<int>(threadIdx.x) * ITEMS;
-#pragma unroll
-        for (int k = 0; k < ITEMS; ++k) sl[k] = base + k < len ? list[base + k] : -1;
-    }
-    __device__ __forceinline__ void fetch_keys() {
-#pragma unroll
-        for (int k = 0; k < ITEMS; ++k)
-            key[k] = ts_key(ts[static_cast<unsigned>(sl[k]) < static_cast<unsigned>(cap) ? sl[k] : 0]);
-    }
-    __device__ __forceinline__ void fetch(int c0) {
-        if (fetched == c0) return;
-        fetched = c0;
-        fetch_list(c0);
-        fetch_keys();
-    }
+    int cached = -1;
+    __device__ SlotList(const int32_t* l, const int32_t* t, const uint32_t* r, int m_, int n_)
+        : list(l), ts(t), refr(r), m(m_), n(n_) {}
     __device__ __forceinline__ void load(int c0) {
         if (cached == c0) return;
         cached = c0;
-        fetch(c0);
         const int base = c0 + static_cast<int>(threadIdx.x) * ITEMS;
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) sl[k] = base + k < m ? list[base + k] : -1;
         cand = 0;
 #pragma unroll
         for (int k = 0; k < ITEMS; ++k) {
-            const bool in = base + k < m && static_cast<unsigned>(sl[k]) < static_cast<unsigned>(n);
+            const bool in = static_cast<unsigned>(sl[k]) < static_cast<unsigned>(n);
+            if (!in) sl[k] = 0;
+            key[k] = ts_key(ts[sl[k]]);
             if (in && !((refr[sl[k] >> 5] >> (sl[k] & 31)) & 1u)) cand |= 1u << k;
         }
     }
@@ -307,7 +277,7 @@ __global__ __launch_bounds__(SEL_NT) void tc_order_kernel(const int32_t* __restr
     const int m = min(n, N);
     int32_t* out = order + static_cast<size_t>(h) * N;
     if (m < n) {
-        SlotRange src(ts_all + static_cast<size_t>(h) * cap, nullptr, n, cap);
+        SlotRange src(ts_all + static_cast<size_t>(h) * cap, nullptr, n);
         select_smallest(src, n, m, out, smem, red, hist, bcast);
     } else {
         for (int i = tid; i < m; i += SEL_NT) out[i] = i;
@@ -371,20 +341,6 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
 #pragma unroll
         for (int k = 0; k < TOK_ITEMS; ++k) ci[k] = (base + k < N) ? cosv[base + k] : 0.f;
     };
-
-    // The eviction search's global reads over a candidate list (its entries,
-    // then their timestamps) depend on nothing the claim phases compute: with
-    // one chunk they are issued here, beside the token loads, and arrive
-    // while the claims are resolved.  (A full scan's 32 timestamps per thread
-    // would not stay in registers through those phases.)
-    SlotList olist(p.order ? p.order + static_cast<size_t>(h) * N : nullptr, ts, refr, N, cap);
-    const bool pre_list = p.order != nullptr && N <= SlotList::ITEMS * SEL_NT;
-    if (pre_list) olist.fetch_list(0);
-    load_tok(0);
-    if (pre_list) {
-        olist.fetched = 0;
-        olist.fetch_keys();
-    }
 
     const bool merge = p.grp_cnt != nullptr;                  // uniform
     int32_t* gcnt_out = merge ? p.grp_cnt + static_cast<size_t>(h) * N : nullptr;
@@ -515,11 +471,11 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     //    among the precomputed candidates when given, else among all slots
     if (e > 0) {
         if (p.order) {
-            olist.set_bounds(min(n, N), n);
-            select_smallest(olist, min(n, N), e, ev, smem, red, hist, bcast);
+            SlotList src(p.order + static_cast<size_t>(h) * N, ts, refr, min(n, N), n);
+            select_smallest(src, min(n, N), e, ev, smem, red, hist, bcast);
         } else {
-            SlotRange srange(ts, refr, n, cap);
-            select_smallest(srange, n, e, ev, smem, red, hist, bcast);
+            SlotRange src(ts, refr, n);
+            select_smallest(src, n, e, ev, smem, red, hist, bcast);
         }
     }
     __syncthreads();
