@@ -124,7 +124,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(every head is independent; see the sharding note in DESIGN.md)", file=sys.stderr)
+              "(every head is independent, so several GPUs would each take a share of the heads "
+              "with no exchange inside the step)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
