@@ -325,7 +325,10 @@ fastar_status fastar_tempcache_order(const fastar_cache* cache, int32_t N, int32
  * (at most FASTAR_TIMER_MAX launches are recorded).  fastar_timer_stop waits
  * for those events, fills up to ``max`` entries (one per kernel name: the
  * number of launches and their summed duration in ms), returns the number of
- * distinct kernels, and disables timing.  Process-wide, not thread-safe.
+ * distinct kernels, and disables timing.  The timer's state is per host
+ * thread (it times the launches the calling thread enqueues); launches on a
+ * stream that is being captured into a graph are not timed.  This is the
+ * library's only state; every other call keeps none between calls.
  * ------------------------------------------------------------------------ */
 #define FASTAR_TIMER_MAX 8192
 typedef struct {

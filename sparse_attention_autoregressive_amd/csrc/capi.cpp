@@ -14,16 +14,19 @@
 namespace fastar {
 
 // ------------------------------------------------------------------ timer
+// The measurement timer's state is per host thread: a thread's
+// fastar_timer_start / fastar_timer_stop see only the launches that thread
+// enqueued, and threads never share it.  Every other call keeps no state.
 namespace {
 struct TimerRec {
     const char* name;
     hipEvent_t a, b;
 };
-bool g_timer_on = false;
-bool g_pending = false;
-std::vector<TimerRec> g_recs;
-std::vector<hipEvent_t> g_pool;
-size_t g_pool_used = 0;
+thread_local bool g_timer_on = false;
+thread_local bool g_pending = false;
+thread_local std::vector<TimerRec> g_recs;
+thread_local std::vector<hipEvent_t> g_pool;
+thread_local size_t g_pool_used = 0;
 
 hipEvent_t pool_get() {
     if (g_pool_used < g_pool.size()) return g_pool[g_pool_used++];
@@ -38,6 +41,9 @@ hipEvent_t pool_get() {
 void timer_begin(const char* name, hipStream_t s) {
     g_pending = false;
     if (!g_timer_on || g_recs.size() >= FASTAR_TIMER_MAX) return;
+    // a stream being captured into a graph gets no event nodes
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return;
     hipEvent_t a = pool_get(), b = pool_get();
     if (!a || !b || hipEventRecord(a, s) != hipSuccess) return;
     g_recs.push_back({name, a, b});

@@ -72,9 +72,10 @@ inline int max_attn_items(long long nq, int B) {
     return static_cast<int>((m + 7) / 8 * 8);
 }
 
-// Sorts one or two sets (nsets = 1 or 2) per head, in three launches.  With
-// ``items`` set (two sets: queries, keys) the scan also writes the attention
-// work list.
+// Sorts one or two sets (nsets = 1 or 2) per head: a tile-histogram launch
+// and a scatter launch (plus a scan launch between them when a set spans
+// more than kSortScanTiles tiles).  With ``items`` set (two sets: queries,
+// keys) one more scatter block per head writes the attention work list.
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
                               const ItemTable* items, hipStream_t s);
 

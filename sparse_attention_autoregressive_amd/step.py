@@ -157,7 +157,12 @@ class AttentionStep:
     def graph(self, cache: KVCache, q, k_cur, v_cur, kp, vp, planes, step: int) -> "StepGraph":
         """The step captured into a graph; ``replay()`` runs it on the current
         stream against exactly these tensors (contents may change, addresses
-        may not).  The returned object keeps the tensors alive."""
+        may not).  The returned object keeps the tensors alive.
+
+        Scalars are fixed at capture too: every replay stamps the slots it
+        writes with this ``step`` (the TempCache timestamp that orders
+        eviction).  A graph is therefore one step's work; a rollout replays a
+        graph captured for each chunk's step (or steps eagerly)."""
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             self(cache, q, k_cur, v_cur, kp, vp, planes, step)
@@ -168,7 +173,8 @@ class StepGraph:
     """A captured step and every tensor its kernels address: the cache, the
     inputs and the step's own buffers stay allocated as long as the graph
     does, so a replay never writes into memory that was freed and handed to
-    another tensor."""
+    another tensor.  The step's scalars (the timestamp ``step``, tau, scale)
+    are the ones given at capture: every replay writes the same timestamp."""
 
     def __init__(self, graph: torch.cuda.CUDAGraph, bound):
         self.graph = graph

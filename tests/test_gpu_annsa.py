@@ -4,17 +4,33 @@ shapes, plus one bucket (dense attention), a partly filled cache, no cache,
 empty buckets, bf16 outputs and run-to-run determinism.  Few buckets (at least
 256 queries per bucket on average) take the wide kernel's 256-query items:
 checked at 2, 4 and 8 buckets, with a partly filled cache and with buckets
-that hold queries but no keys."""
+that hold queries but no keys.  Calls that ask for the fused TempCache search
+also have its (slot, cosine) checked against the oracle's top-1 under the
+tie protocol (``assert_top1_matches``)."""
+
 import numpy as np
 import pytest
 import torch
 
 import sparse_attention_autoregressive_amd as fa
 from oracle import annsa as o_annsa, key_context
-from tests.gpu_util import (LSE_ABS, assert_attention_close, dev, dev_ids, device_cache,
-                            prepared, require_gpu)
+from tests.gpu_util import (LSE_ABS, assert_attention_close, assert_top1_matches, dev, dev_ids,
+                            device_cache, prepared, require_gpu)
 
 pytestmark = pytest.mark.gpu
+
+
+def check_search(prep, best, bcos, n, P=None, what=""):
+    """The fused search's result on every head against the oracle's top-1."""
+    st, cfg = prep["step"], prep["cfg"]
+    b, c = best.cpu().numpy(), bcos.cpu().numpy()
+    mask = (1 << (cfg.P if P is None else P)) - 1
+    worst, ties = 0.0, 0
+    for h in range(cfg.H):
+        err, t, _ = assert_top1_matches(b[h], c[h], st.q[h], prep["q_ids"][h] & mask, st.cache_k[h],
+                                        prep["cache_ids"][h] & mask, n, cfg.tau, f"{what} head {h}")
+        worst, ties = max(worst, err), ties + t
+    print(f"search {what}: max cos err {worst:.2e}, {ties} argmax near-ties")
 
 
 def oracle_annsa(prep, n, q_ids=None, kcur_ids=None, cache_ids=None, heads=None, use_cache=True):
@@ -171,12 +187,14 @@ def test_annsa_f32_d128(search):
     prep = prepared("tiny_f32", d=128)
     st, cfg = prep["step"], prep["cfg"]
     cache = device_cache(prep)
-    out, lse, *_ = fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
-                                    dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), cfg.P, cache=cache,
-                                    search=search)
+    res = fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
+                           dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), cfg.P, cache=cache,
+                           search=search)
     O, L = oracle_annsa(prep, cfg.n0)
-    assert_attention_close(out, O, cfg.dtype, f"f32 d=128 search={search}")
-    check_lse(lse, L)
+    assert_attention_close(res[0], O, cfg.dtype, f"f32 d=128 search={search}")
+    check_lse(res[1], L)
+    if search:
+        check_search(prep, res[2], res[3], cfg.n0, what="f32 d=128")
 
 
 @pytest.mark.parametrize("Fc,cap", [(300, 80000), (550, 150000)])
@@ -195,6 +213,7 @@ def test_annsa_long_key_set(Fc, cap):
     O, L = oracle_annsa(prep, cfg.n0)
     assert_attention_close(out, O, cfg.dtype, "long key set")
     check_lse(lse, L)
+    check_search(prep, best, bcos, cfg.n0, what=f"cache {cfg.n0}")
 
 
 @pytest.mark.parametrize("P", [9, 10])
@@ -211,3 +230,4 @@ def test_annsa_many_buckets(P):
     O, L = oracle_annsa(prep, cfg.n0)
     assert_attention_close(out, O, cfg.dtype, f"P={P}")
     check_lse(lse, L)
+    check_search(prep, best, bcos, cfg.n0, P=P, what=f"P={P}")
