@@ -54,12 +54,84 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 
-# HBM bytes per launch of the AnnSA attention kernel at the wan13_bf16 workload:
-# rocprofv3 FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (KiB per dispatch), the
-# factors being what a 512 MiB device copy reads on the same counters
-# (profiles/step_wan13_hbm_traffic.md).  Valid for the kernel build the
-# counters were taken on; None for other workloads.
-ANNSA_TRAFFIC_BYTES = {"wan13_bf16": 333.3e6}
+# HBM bytes per launch of the AnnSA attention kernel, from rocprofv3's
+# FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) scaled by what the same
+# counters read for a device copy of known size.  ``--ingest-counters`` writes
+# them to TRAFFIC_FILE together with the SHA-256 of the kernel's sources; the
+# bench line reports them only while those sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "annsa_traffic_wan13.json")
+KERNEL_SOURCES = ["sparse_attention_autoregressive_amd/csrc/attn.hip",
+                  "sparse_attention_autoregressive_amd/csrc/common.hpp",
+                  "sparse_attention_autoregressive_amd/csrc/launch.hpp",
+                  "sparse_attention_autoregressive_amd/build.py"]
+ANNSA_KERNEL = "attn_kv_kernel<unsigned short, 128, 0, true, float, 4, false, false>"
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str, out_dtype: str):
+    """(bytes per launch, note) for the AnnSA kernel of this build, or (None, why not)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter record"
+    if rec.get("config") != config or rec.get("out_dtype") != out_dtype:
+        return None, f"counters taken on {rec.get('config')} / {rec.get('out_dtype')}"
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None, "kernel sources changed since the counters were taken"
+    return rec["traffic_bytes"], f"{os.path.relpath(TRAFFIC_FILE, ROOT)} (sources sha256 {rec['sources_sha256'][:12]})"
+
+
+def ingest_counters(paths):
+    """Writes TRAFFIC_FILE from four rocprofv3 counter CSVs: FETCH_SIZE and
+    WRITE_SIZE of a bench run, then of ``--copy-calibration`` (a device copy of
+    known size, whose counters give the scale factors)."""
+    import csv
+    fetch, write, cfetch, cwrite = paths
+
+    def per_kernel(path):
+        acc = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                v = acc.setdefault(row["Kernel_Name"], [0, 0.0])
+                v[0] += 1
+                v[1] += float(row["Counter_Value"])
+        return {k: (n, tot / n) for k, (n, tot) in acc.items()}
+
+    def copy_kib(path):
+        rows = [v for k, v in per_kernel(path).items() if "copyBuffer" in k]
+        if not rows:
+            raise SystemExit(f"{path}: no device-copy dispatch")
+        return max(r[1] for r in rows)
+
+    def annsa(path):
+        rows = [v for k, v in per_kernel(path).items() if ANNSA_KERNEL in k]
+        if len(rows) != 1:
+            raise SystemExit(f"{path}: expected one {ANNSA_KERNEL} kernel, found {len(rows)}")
+        return rows[0]
+
+    copy_bytes = 512 * (1 << 20)
+    f_scale = copy_bytes / 1024 / copy_kib(cfetch)
+    w_scale = copy_bytes / 1024 / copy_kib(cwrite)
+    nf, fk = annsa(fetch)
+    nw, wk = annsa(write)
+    rec = {"kernel": ANNSA_KERNEL, "config": "wan13_bf16", "out_dtype": "f32",
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": [nf, nw],
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "traffic_bytes": (f_scale * fk + w_scale * wk) * 1024,
+           "sources": KERNEL_SOURCES, "sources_sha256": kernel_sources_sha256(),
+           "counter_files": [os.path.relpath(p, ROOT) for p in paths]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec), flush=True)
 
 
 def parse():
@@ -88,6 +160,9 @@ def parse():
     ap.add_argument("--rollout", type=int, default=0, metavar="CHUNKS",
                     help="only run a rollout of CHUNKS chunks: per-chunk step latency and cache "
                          "size, next to a dense uncapped-cache baseline (one JSON line)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only write the AnnSA traffic record from rocprofv3 counter CSVs "
+                         "(FETCH_SIZE and WRITE_SIZE of a bench run, then of --copy-calibration 512)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (the plain copy whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the traffic figures), then exit")
@@ -110,6 +185,9 @@ def copy_calibration(mib):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(args.ingest_counters)
+        return
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
         return
@@ -263,10 +341,11 @@ def main():
                 + cached_read * 4)
     attn_ms = kernel_ms.get("annsa_attn")
     achieved = sa_bytes / (attn_ms * 1e-3) / 1e9 if attn_ms else None
+    traffic, traffic_note = measured_traffic(args.config, args.out_dtype)
     roofline = {"kernel": "annsa_attn", "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                "traffic": ANNSA_TRAFFIC_BYTES.get(args.config) if args.out_dtype == "f32" else None,
+                "traffic": traffic, "traffic_source": traffic_note,
                 "algorithmic_bytes": sa_bytes,
                 "mean_ms": attn_ms}
 
