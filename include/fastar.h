@@ -60,7 +60,8 @@ typedef enum {
     FASTAR_ESHAPE = -3,      /* d not 64/128, P out of range, frame_len not dividing Nq, H mismatch */
     FASTAR_EWORKSPACE = -4,  /* workspace smaller than the query returned (or NULL with size > 0) */
     FASTAR_ECAPACITY = -5,   /* a chunk larger than the cache capacity */
-    FASTAR_EHIP = -6         /* HIP error while enqueueing */
+    FASTAR_EHIP = -6,        /* HIP error while enqueueing */
+    FASTAR_ESCRATCH = -7     /* the call needs more than the static scratch array holds */
 } fastar_status;
 
 typedef enum { FASTAR_F32 = 0, FASTAR_BF16 = 1 } fastar_dtype;
@@ -204,6 +205,34 @@ fastar_status fastar_annsa_forward(const void* q, const uint16_t* q_ids, int32_t
                                    int32_t Ncur, int32_t P, float scale, void* out,
                                    int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * AnnSA for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The same
+ * computation, arguments and results as fastar_annsa_forward, without the
+ * workspace arguments: the library's own static device array of
+ * FASTAR_STATIC_SCRATCH_BYTES serves as the workspace.  Each device the
+ * library runs on holds its own copy of that array (reserved when the
+ * library's code is loaded on the device, kept until the process ends); its
+ * device address is resolved once per device, on the first call with that
+ * device current, and the calling thread's current device must be the
+ * stream's device.
+ * Every call on one device uses the same array and leaves its contents there;
+ * nothing in it needs to start at zero (a call writes every entry it reads
+ * before reading it).  Two calls that overlap on one device -- on different
+ * streams, or from different host threads -- race on the array: their
+ * results are undefined.  Calls on one stream are ordered and safe.
+ * Returns FASTAR_ESCRATCH, with nothing enqueued, when
+ * fastar_annsa_workspace(H, Nq, cap, Ncur, P) exceeds the array; every other
+ * status as fastar_annsa_forward.  Calls no allocating routine.
+ * ------------------------------------------------------------------------ */
+#define FASTAR_STATIC_SCRATCH_BYTES (16u << 20)
+fastar_status fastar_annsa_forward_static(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,
+                                          int32_t d, int32_t dtype, const fastar_cache* cache,
+                                          const void* k_cur, const void* v_cur, const uint16_t* kcur_ids,
+                                          int32_t Ncur, int32_t P, float scale, void* out,
+                                          int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
+                                          void* stream);
 
 /* ------------------------------------------------------------------------
  * Multi-table AnnSA (blog, "3. AnnSA": a token may fall in several buckets;

@@ -18,7 +18,8 @@ import torch
 from . import _lib
 from ._lib import FASTAR_BF16, FASTAR_F32, FastarError, check, load
 
-__all__ = ["ann_hash", "ann_hash_batch", "ann_quantize", "bucket_sort", "annsa_forward", "annca_forward", "tempcache_update",
+__all__ = ["ann_hash", "ann_hash_batch", "ann_quantize", "bucket_sort", "annsa_forward",
+           "annsa_forward_static", "annca_forward", "tempcache_update",
            "tempcache_order",
            "KVCache", "kernel_timer", "load", "FastarError"]
 
@@ -270,6 +271,42 @@ def annsa_forward(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor, v_c
             _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), Ncur, P, tables, scale, _ptr(out),
             _dtype_code(out), _ptr(lse), _ptr(best) if search else None,
             _ptr(best_cos) if search else None, wsp, wsn, _stream(q.device)))
+    return (out, lse, best, best_cos) if search else (out, lse)
+
+
+def annsa_forward_static(q: torch.Tensor, q_ids: torch.Tensor, k_cur: torch.Tensor,
+                         v_cur: torch.Tensor, kcur_ids: torch.Tensor, P: int,
+                         cache: Optional[KVCache] = None, scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         best: Optional[torch.Tensor] = None, best_cos: Optional[torch.Tensor] = None,
+                         search: bool = False, out_dtype=torch.float32):
+    """``annsa_forward`` through fastar_annsa_forward_static: the library's
+    static per-device scratch array is the workspace, so the call itself
+    allocates nothing (pass ``out``, ``lse`` and, with ``search``, ``best`` /
+    ``best_cos`` to allocate nothing here either).  Overlapping calls on one
+    device race on that array."""
+    H, Nq, d = q.shape
+    Ncur = k_cur.shape[1]
+    _ids_check(q_ids, (H, Nq))
+    _ids_check(kcur_ids, (H, Ncur))
+    if k_cur.shape != (H, Ncur, d) or v_cur.shape != (H, Ncur, d):
+        raise ValueError("k_cur / v_cur must be [H, Ncur, d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty(H, Nq, d, dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(H, Nq, dtype=torch.float32, device=q.device)
+    if search:
+        if best is None:
+            best = torch.empty(H, Nq, dtype=torch.int32, device=q.device)
+        if best_cos is None:
+            best_cos = torch.empty(H, Nq, dtype=torch.float32, device=q.device)
+    cs = cache.struct() if cache is not None else None
+    check("fastar_annsa_forward_static", load().fastar_annsa_forward_static(
+        _ptr(q), _ptr(q_ids), H, Nq, d, _dtype_code(q), ctypes.byref(cs) if cs else None,
+        _ptr(k_cur), _ptr(v_cur), _ptr(kcur_ids), Ncur, P, scale, _ptr(out), _dtype_code(out),
+        _ptr(lse), _ptr(best) if search else None, _ptr(best_cos) if search else None,
+        _stream(q.device)))
     return (out, lse, best, best_cos) if search else (out, lse)
 
 

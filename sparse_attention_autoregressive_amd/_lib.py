@@ -17,6 +17,7 @@ FASTAR_ESHAPE = -3
 FASTAR_EWORKSPACE = -4
 FASTAR_ECAPACITY = -5
 FASTAR_EHIP = -6
+FASTAR_ESCRATCH = -7
 
 FASTAR_F32 = 0
 FASTAR_BF16 = 1
@@ -27,6 +28,7 @@ FASTAR_MAX_CODEWORDS = 65536
 FASTAR_HASH_BATCH = 4
 FASTAR_TIMER_MAX = 8192
 FASTAR_ABI_VERSION = 3
+FASTAR_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class FastarCache(ctypes.Structure):
@@ -55,6 +57,8 @@ SIGNATURES = {
     "fastar_annsa_forward": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(FastarCache),
                                     _vp, _vp, _vp, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _vp,
                                     _vp, _sz, _vp]),
+    "fastar_annsa_forward_static": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, ctypes.POINTER(FastarCache),
+                                           _vp, _vp, _vp, _i32, _i32, _f32, _vp, _i32, _vp, _vp, _vp, _vp]),
     "fastar_annsa_multi_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "fastar_annsa_multi_forward": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32,
                                           ctypes.POINTER(FastarCache), _vp, _vp, _vp, _i32, _i32,

@@ -19,7 +19,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfastar.so")
 ARCH = "gfx950"
 
-SOURCES = ["hash.hip", "quantize.hip", "sort.hip", "attn.hip", "annca.hip", "tempcache.hip", "capi.cpp"]
+SOURCES = ["hash.hip", "quantize.hip", "sort.hip", "attn.hip", "annca.hip", "tempcache.hip", "scratch.hip",
+           "capi.cpp"]
 
 # Packed-fp32 VALU forms are kept out of every HIP object (see DESIGN notes on
 # the packed-fp32 issue); the host pass ignores the flag with a warning.

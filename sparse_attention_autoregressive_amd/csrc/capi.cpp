@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "fastar.h"
+#include "annsa_entry.hpp"
 #include "launch.hpp"
 
 namespace fastar {
@@ -211,6 +212,7 @@ const char* fastar_status_string(int32_t status) {
         case FASTAR_EWORKSPACE: return "FASTAR_EWORKSPACE";
         case FASTAR_ECAPACITY: return "FASTAR_ECAPACITY";
         case FASTAR_EHIP: return "FASTAR_EHIP";
+        case FASTAR_ESCRATCH: return "FASTAR_ESCRATCH";
         default: return "FASTAR_UNKNOWN";
     }
 }
@@ -321,13 +323,13 @@ size_t fastar_annsa_multi_workspace(int32_t H, int32_t Nq, int32_t cap, int32_t 
 
 }  // extern "C"
 
-namespace {
+namespace fastar {
 
-fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq, int32_t d,
-                         int32_t dtype, const fastar_cache* cache, const void* k_cur, const void* v_cur,
-                         const uint16_t* kcur_ids, int32_t Ncur, int32_t P, int32_t tables, float scale,
-                         void* out, int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
-                         void* ws, size_t ws_bytes, void* stream) {
+fastar_status annsa_validate(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq, int32_t d,
+                             int32_t dtype, const fastar_cache* cache, const void* k_cur,
+                             const void* v_cur, const uint16_t* kcur_ids, int32_t Ncur, int32_t P,
+                             int32_t tables, float scale, const void* out, int32_t out_dtype,
+                             const int32_t* best, const float* best_cos, size_t* need) {
     if (!dtype_ok(dtype) || !dtype_ok(out_dtype)) return FASTAR_EDTYPE;
     if (H < 0 || Nq < 0 || Ncur < 0 || !std::isfinite(scale) || !(scale > 0.f)) return FASTAR_EINVAL;
     if (!d_ok(d) || !planes_ok(P) || !tables_ok(P, tables)) return FASTAR_ESHAPE;
@@ -345,10 +347,23 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
     if ((best == nullptr) != (best_cos == nullptr)) return FASTAR_EINVAL;
     if (best && cache && H > 0 && cap > 0 && !cache->knorm) return FASTAR_EINVAL;
     if (tables > 1 && cache && H > 0 && cap > 0 && !cache->ids) return FASTAR_EINVAL;
-    const size_t need = tables > 1 ? fastar_annsa_multi_workspace(H, Nq, cap, Ncur, d, P, tables)
-                                   : fastar_annsa_workspace(H, Nq, cap, Ncur, P);
+    *need = tables > 1 ? fastar_annsa_multi_workspace(H, Nq, cap, Ncur, d, P, tables)
+                       : fastar_annsa_workspace(H, Nq, cap, Ncur, P);
+    return FASTAR_OK;
+}
+
+fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq, int32_t d,
+                         int32_t dtype, const fastar_cache* cache, const void* k_cur, const void* v_cur,
+                         const uint16_t* kcur_ids, int32_t Ncur, int32_t P, int32_t tables, float scale,
+                         void* out, int32_t out_dtype, float* lse, int32_t* best, float* best_cos,
+                         void* ws, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    const fastar_status vs = annsa_validate(q, q_ids, H, Nq, d, dtype, cache, k_cur, v_cur, kcur_ids,
+                                            Ncur, P, tables, scale, out, out_dtype, best, best_cos, &need);
+    if (vs != FASTAR_OK) return vs;
     if (ws_bytes < need || (need > 0 && !ws)) return FASTAR_EWORKSPACE;
-    if (HQ == 0) return FASTAR_OK;
+    if (static_cast<long long>(H) * Nq == 0) return FASTAR_OK;
+    const int cap = cache ? cache->cap : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     Carver c(ws);
@@ -423,7 +438,7 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
     return FASTAR_OK;
 }
 
-}  // namespace
+}  // namespace fastar
 
 extern "C" {
 

@@ -39,7 +39,7 @@ def test_status_strings_and_version(lib):
     assert lib.fastar_abi_version() == _lib.FASTAR_ABI_VERSION == 3
     for code, name in [(0, "FASTAR_OK"), (-1, "FASTAR_EINVAL"), (-2, "FASTAR_EDTYPE"),
                        (-3, "FASTAR_ESHAPE"), (-4, "FASTAR_EWORKSPACE"), (-5, "FASTAR_ECAPACITY"),
-                       (-6, "FASTAR_EHIP")]:
+                       (-6, "FASTAR_EHIP"), (-7, "FASTAR_ESCRATCH")]:
         assert lib.fastar_status_string(code).decode() == name
     assert lib.fastar_status_string(99).decode() == "FASTAR_UNKNOWN"
 
@@ -231,3 +231,26 @@ def test_cache_struct_layout_matches_header(tmp_path):
                                           check=True).stdout.split()]
     assert out[0] == ctypes.sizeof(_lib.FastarCache)
     assert out[1:] == [getattr(_lib.FastarCache, n).offset for n in names]
+
+
+def test_static_scratch_entry_validates_before_touching_the_device(lib):
+    """fastar_annsa_forward_static rejects bad arguments like
+    fastar_annsa_forward, and a call whose workspace exceeds the static array
+    with FASTAR_ESCRATCH -- all before resolving the array or launching."""
+    f = lib.fastar_annsa_forward_static
+    c = _cache(H=1, cap=64, d=64)
+    args = lambda **kw: dict(dict(q=FAKE, q_ids=FAKE, H=1, Nq=32, d=64, dt=0, cache=c, kc=FAKE, vc=FAKE,
+                                  kid=FAKE, Ncur=16, P=4, scale=0.125, out=FAKE, odt=0), **kw)
+    call = lambda a: f(a["q"], a["q_ids"], a["H"], a["Nq"], a["d"], a["dt"], ctypes.byref(a["cache"]),
+                       a["kc"], a["vc"], a["kid"], a["Ncur"], a["P"], a["scale"], a["out"], a["odt"],
+                       None, None, None, None)
+    assert call(args(d=96)) == _lib.FASTAR_ESHAPE
+    assert call(args(dt=5)) == _lib.FASTAR_EDTYPE
+    assert call(args(q=None)) == _lib.FASTAR_EINVAL
+    assert call(args(scale=-1.0)) == _lib.FASTAR_EINVAL
+    big = _cache(H=8, cap=1_000_000, d=128, dtype=1)
+    need = lib.fastar_annsa_workspace(8, 4680, 1_000_000, 4680, 10)
+    assert need > _lib.FASTAR_STATIC_SCRATCH_BYTES
+    assert call(args(H=8, Nq=4680, d=128, dt=1, cache=big, Ncur=4680, P=10)) == _lib.FASTAR_ESCRATCH
+    # empty work succeeds without touching the device
+    assert call(args(Nq=0, q=None, out=None, q_ids=None)) == _lib.FASTAR_OK
