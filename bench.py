@@ -128,6 +128,13 @@ def ingest_counters(paths):
            "fetch_scale": f_scale, "write_scale": w_scale,
            "traffic_bytes": (f_scale * fk + w_scale * wk) * 1024,
            "sources": KERNEL_SOURCES, "sources_sha256": kernel_sources_sha256(),
+           "commands": [
+               "cd /tmp && export TMPDIR=/tmp",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/<run>/FETCH_SIZE -o FETCH_SIZE "
+               "-- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-merge --no-multi --no-quantize",
+               "rocprofv3 --pmc WRITE_SIZE (the same bench command)",
+               "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python3 <repo>/bench.py --copy-calibration 512",
+               "python3 bench.py --ingest-counters <the four counter_collection.csv files>"],
            "counter_files": [os.path.relpath(p, ROOT) for p in paths]}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(rec, f, indent=1)
