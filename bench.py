@@ -513,9 +513,11 @@ def main():
         torch.cuda.synchronize()
         q_ms = {k: v[1] / max(1, v[0]) for k, v in kt4.times.items()}
         q_launch = {k: v[0] // args.steps for k, v in kt4.times.items()}
-        # the three quantize launches: 2 N B d flops each (N = Nq, Nq, L per head)
-        qz_flops = 2.0 * H * (2 * Nq + cfg.L) * Bq * d / 3
-        qz_bytes = H * (2 * Nq + cfg.L) * (d * esz + 2) / 3
+        # the quantize launches of a one-stream step (one launch for Q, K_cur and
+        # the prompt): 2 N B d flops per vector set (N = Nq, Nq, L per head)
+        qz_launches = max(1, q_launch.get("ann_quantize", 1))
+        qz_flops = 2.0 * H * (2 * Nq + cfg.L) * Bq * d / qz_launches
+        qz_bytes = H * (2 * Nq + cfg.L) * (d * esz + 2) / qz_launches
         qz_ms = q_ms.get("ann_quantize")
         quant = {"codewords": Bq, "ms_per_step": ms_quant, "launch": "eager, two streams",
                  "ms_per_step_hyperplanes_same_launch": ms_eager_two, "kernel_ms": q_ms,
@@ -701,7 +703,9 @@ def rollout(args):
     """A long rollout on the same layer: every chunk runs the full step on a
     bounded cache (two streams), each between its own events; beside it a
     dense baseline (one bucket, no merging, the cache grows by a chunk per
-    step: the same kernels at P = 0) is timed every 10th chunk."""
+    step: the same kernels at P = 0) is timed every 10th chunk, and so is the
+    CPU oracle (after the GPU loop, on one head per sampled chunk, from a copy
+    of the cache state the GPU step started that chunk from)."""
     import torch
     import sparse_attention_autoregressive_amd as fa
     from sparse_attention_autoregressive_amd.step import AttentionStep
@@ -749,9 +753,14 @@ def rollout(args):
             print(json.dumps({"progress": "rollout inputs", "chunk": c}), file=sys.stderr, flush=True)
     slots_dev = torch.zeros(n_chunks, H, dtype=torch.int32, device=dev)
     fast_ev, dense_ev, dense_slots = [], {}, {}
+    snaps = {}                 # every 10th chunk: one head's cache as the step found it (device copies)
     n_dense = n0
     torch.cuda.synchronize()
     for c, (q, kc, vc, step) in enumerate(chunks):
+        if c % 10 == 0 and not args.no_cpu_baseline:
+            hs = (c // 10) % H
+            snaps[c] = (hs, cache.k[hs].clone(), cache.v[hs].clone(), cache.ids[hs].clone(),
+                        cache.ts[hs].clone(), cache.n_valid[hs:hs + 1].clone())
         a, b = ev(), ev()
         a.record(main)
         stepper(cache, q, kc, vc, kp, vp, planes, step)
@@ -775,11 +784,31 @@ def rollout(args):
     fast_ms = [a.elapsed_time(b) for a, b in fast_ev]
     dense_ms = {c: a.elapsed_time(b) for c, (a, b) in dense_ev.items()}
     row_bytes = d * (2 if cfg.dtype == "bf16" else 4) * 2 * H
+    # the oracle on every 10th chunk, one head each (cycling), from the cache
+    # state the GPU step started that chunk from
+    oracle = None
+    if snaps:
+        import numpy as np
+        from oracle import attention_step
+        host = lambda t: t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+        per_chunk = {}
+        for c, (hs, k_, v_, ids_, ts_, n_) in snaps.items():
+            q, kc, vc, step = chunks[c]
+            sl = slice(hs, hs + 1)
+            t0 = time.perf_counter()
+            attention_step(host(q[sl]), host(kc[sl]), host(vc[sl]), host(k_)[None], host(v_)[None],
+                           ids_.cpu().numpy().view(np.uint16)[None], ts_.cpu().numpy()[None], n_.cpu().numpy(),
+                           st.planes[sl], host(kp[sl]), host(vp[sl]), cfg.frame_len, cfg.tau, step)
+            per_chunk[c] = (time.perf_counter() - t0) * 1e3
+        oracle = {"ms_per_head": per_chunk, "ms_per_step_equiv_median": float(np.median(list(per_chunk.values()))) * H,
+                  "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                  "sample": f"one head per sampled chunk (heads cycled), every 10th chunk, "
+                            f"started from the GPU's cache state of that chunk; step = {H} heads"}
     print(json.dumps({"rollout": {
         "config": cfg.name, "chunks": n_chunks, "fastar_step_ms": fast_ms,
         "fastar_cache_slots": slots, "fastar_cache_kv_bytes": cap * row_bytes,
         "dense_attention_ms": dense_ms, "dense_cache_slots": dense_slots,
-        "dense_cache_kv_bytes_final": n_dense * row_bytes,
+        "dense_cache_kv_bytes_final": n_dense * row_bytes, "cpu_oracle": oracle,
         "note": "FAST-AR: the whole step (hash, AnnSA + search, AnnCA, commit) on a cache capped at "
                 f"{cap} slots; dense: AnnSA + AnnCA at one bucket over the uncapped cache "
                 "(attention only), timed every 10th chunk"}}), flush=True)

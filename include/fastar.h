@@ -152,6 +152,18 @@ fastar_status fastar_ann_quantize(const void* x, int32_t dtype, int32_t H, int32
                                   const float* codebook, int32_t B, uint16_t* ids, float* norms,
                                   void* stream);
 
+/* Several token sets quantized with the same codebook in one launch (a
+ * step's queries, current keys and prompt keys, say): the same result as one
+ * fastar_ann_quantize per set.  Arguments as fastar_ann_hash_batch: ``x``,
+ * ``N``, ``ids`` and ``norms`` are HOST arrays of ``count`` entries
+ * (1 <= count <= FASTAR_HASH_BATCH) holding device pointers and sizes;
+ * ``norms`` may be NULL or hold NULL entries; the sets share H, d, dtype and
+ * the codebook. */
+fastar_status fastar_ann_quantize_batch(int32_t count, const void* const* x, const int32_t* N,
+                                        uint16_t* const* ids, float* const* norms, int32_t dtype,
+                                        int32_t H, int32_t d, const float* codebook, int32_t B,
+                                        void* stream);
+
 /* ------------------------------------------------------------------------
  * Stable grouping of tokens by bucket -- the block-sparse layout AnnSA runs
  * on (summary, Core Components C).  Exposed for callers that reuse one

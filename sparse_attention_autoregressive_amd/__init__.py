@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import FASTAR_BF16, FASTAR_F32, FastarError, check, load
 
-__all__ = ["ann_hash", "ann_hash_batch", "ann_quantize", "bucket_sort", "annsa_forward",
+__all__ = ["ann_hash", "ann_hash_batch", "ann_quantize", "ann_quantize_batch", "bucket_sort", "annsa_forward",
            "annsa_forward_static", "annca_forward", "tempcache_update",
            "tempcache_order",
            "KVCache", "kernel_timer", "load", "FastarError"]
@@ -158,19 +158,16 @@ def ann_hash(x: torch.Tensor, planes: torch.Tensor, ids: Optional[torch.Tensor] 
     return ids
 
 
-def ann_hash_batch(xs, planes: torch.Tensor, ids=None, norms=None):
-    """Bucket ids of several [H, N_i, d] tensors under the same planes in one
-    launch (at most ``FASTAR_HASH_BATCH`` tensors); returns the list of id
-    tensors.  ``ids`` / ``norms``: optional lists of outputs (entries may be
-    None)."""
+def _batch_call(fn: str, xs, table: torch.Tensor, what: str, ids, norms):
+    """Shared marshalling of the batched id calls (hash planes or codebook)."""
     xs = list(xs)
     count = len(xs)
     if not 1 <= count <= _lib.FASTAR_HASH_BATCH:
         raise ValueError(f"between 1 and {_lib.FASTAR_HASH_BATCH} tensors")
     H, _, d = xs[0].shape
-    P = planes.shape[1]
-    if planes.dtype != torch.float32 or tuple(planes.shape) != (H, P, d):
-        raise ValueError("planes must be float32 [H, P, d]")
+    P = table.shape[1]
+    if table.dtype != torch.float32 or tuple(table.shape) != (H, P, d):
+        raise ValueError(f"{what} must be float32 [H, {'P' if what == 'planes' else 'B'}, d]")
     dt = _dtype_code(xs[0])
     ids = list(ids) if ids is not None else [None] * count
     norms = list(norms) if norms is not None else [None] * count
@@ -184,11 +181,26 @@ def ann_hash_batch(xs, planes: torch.Tensor, ids=None, norms=None):
                                      or tuple(norms[i].shape) != (H, x.shape[1])):
             raise ValueError("norms must be float32 [H, N]")
     arr = lambda vals: (ctypes.c_void_p * count)(*vals)
-    check("fastar_ann_hash_batch", load().fastar_ann_hash_batch(
+    check(fn, getattr(load(), fn)(
         count, arr([_ptr(x) for x in xs]), (ctypes.c_int32 * count)(*[x.shape[1] for x in xs]),
-        arr([_ptr(t) for t in ids]), arr([_ptr(t) for t in norms]), dt, H, d, _ptr(planes), P,
+        arr([_ptr(t) for t in ids]), arr([_ptr(t) for t in norms]), dt, H, d, _ptr(table), P,
         _stream(xs[0].device)))
     return ids
+
+
+def ann_hash_batch(xs, planes: torch.Tensor, ids=None, norms=None):
+    """Bucket ids of several [H, N_i, d] tensors under the same planes in one
+    launch (at most ``FASTAR_HASH_BATCH`` tensors); returns the list of id
+    tensors.  ``ids`` / ``norms``: optional lists of outputs (entries may be
+    None)."""
+    return _batch_call("fastar_ann_hash_batch", xs, planes, "planes", ids, norms)
+
+
+def ann_quantize_batch(xs, codebook: torch.Tensor, ids=None, norms=None):
+    """Nearest-codeword ids of several [H, N_i, d] tensors under the same
+    codebook [H, B, d] in one launch (at most ``FASTAR_HASH_BATCH`` tensors);
+    returns the list of id tensors, as ``ann_hash_batch``."""
+    return _batch_call("fastar_ann_quantize_batch", xs, codebook, "codebook", ids, norms)
 
 
 def ann_quantize(x: torch.Tensor, codebook: torch.Tensor, ids: Optional[torch.Tensor] = None,

@@ -51,6 +51,7 @@ SIGNATURES = {
     "fastar_ann_hash": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
     "fastar_ann_hash_batch": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp]),
     "fastar_ann_quantize": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "fastar_ann_quantize_batch": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp]),
     "fastar_bucket_sort_workspace": (_sz, [_i32, _i32, _i32]),
     "fastar_bucket_sort": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "fastar_annsa_workspace": (_sz, [_i32, _i32, _i32, _i32, _i32]),

@@ -98,15 +98,19 @@ ItemTable carve_items(Carver& c, int H, long long nq, int P) {
     return t;
 }
 
+// One (queries, keys) sort and work list per hash table: multi-table calls
+// sort every table's fields in one launch pair.
 struct AnnsaWs {
-    SortBufs q, k;
-    ItemTable it;
+    SortBufs q[FASTAR_MAX_TABLES], k[FASTAR_MAX_TABLES];
+    ItemTable it[FASTAR_MAX_TABLES];
 };
-AnnsaWs carve_annsa(Carver& c, int H, int Nq, int cap, int Ncur, int P) {
+AnnsaWs carve_annsa(Carver& c, int H, int Nq, int cap, int Ncur, int P, int tables = 1) {
     AnnsaWs w;
-    w.q = carve_sort(c, H, Nq, P, true);
-    w.k = carve_sort(c, H, static_cast<long long>(cap) + Ncur, P, true);
-    w.it = carve_items(c, H, Nq, P);
+    for (int t = 0; t < tables; ++t) {
+        w.q[t] = carve_sort(c, H, Nq, P, true);
+        w.k[t] = carve_sort(c, H, static_cast<long long>(cap) + Ncur, P, true);
+        w.it[t] = carve_items(c, H, Nq, P);
+    }
     return w;
 }
 
@@ -274,6 +278,30 @@ fastar_status fastar_ann_quantize(const void* x, int32_t dtype, int32_t H, int32
                                       static_cast<hipStream_t>(stream)));
 }
 
+fastar_status fastar_ann_quantize_batch(int32_t count, const void* const* x, const int32_t* N,
+                                        uint16_t* const* ids, float* const* norms, int32_t dtype,
+                                        int32_t H, int32_t d, const float* codebook, int32_t B,
+                                        void* stream) {
+    if (!dtype_ok(dtype)) return FASTAR_EDTYPE;
+    if (count < 1 || count > FASTAR_HASH_BATCH || !x || !N || !ids || H < 0) return FASTAR_EINVAL;
+    if (!d_ok(d) || B < 1 || B > FASTAR_MAX_CODEWORDS) return FASTAR_ESHAPE;
+    if (!fits_i32(static_cast<long long>(H) * B * d)) return FASTAR_EINVAL;
+    int n[FASTAR_HASH_BATCH];
+    long long total = 0;
+    for (int i = 0; i < count; ++i) {
+        if (N[i] < 0) return FASTAR_EINVAL;
+        const long long HN = static_cast<long long>(H) * N[i];
+        if (!fits_i32(HN * d)) return FASTAR_EINVAL;
+        if (!tensor_ok(x[i], HN * d) || !small_ok(ids[i], HN)) return FASTAR_EINVAL;
+        n[i] = N[i];
+        total += HN;
+    }
+    if (!tensor_ok(codebook, total > 0 ? static_cast<long long>(H) * B * d : 0)) return FASTAR_EINVAL;
+    if (total == 0) return FASTAR_OK;
+    return hip_status(launch_quantize_batch(count, x, n, ids, norms, dtype == FASTAR_BF16, H, d, codebook, B,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------------------ bucket sort
 size_t fastar_bucket_sort_workspace(int32_t H, int32_t N, int32_t P) {
     if (H < 0 || N < 0 || !planes_ok(P)) return 0;
@@ -301,7 +329,7 @@ fastar_status fastar_bucket_sort(const uint16_t* ids, int32_t H, int32_t N, int3
     s.a = ids;
     s.a_stride = N;
     s.a_fixed = N;
-    return hip_status(launch_bucket_sort(H, P, 1, &s, &b, nullptr, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_bucket_sort(H, P, 1, &s, &b, nullptr, 0, static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------ AnnSA
@@ -316,7 +344,7 @@ size_t fastar_annsa_multi_workspace(int32_t H, int32_t Nq, int32_t cap, int32_t 
                                     int32_t P, int32_t tables) {
     if (H < 0 || Nq < 0 || cap < 0 || Ncur < 0 || !d_ok(d) || !tables_ok(P, tables)) return 0;
     Carver c(nullptr);
-    carve_annsa(c, H, Nq, cap, Ncur, P);
+    carve_annsa(c, H, Nq, cap, Ncur, P, tables);
     carve_state(c, H, Nq, d, tables);
     return c.off;
 }
@@ -367,7 +395,7 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     Carver c(ws);
-    AnnsaWs w = carve_annsa(c, H, Nq, cap, Ncur, P);
+    AnnsaWs w = carve_annsa(c, H, Nq, cap, Ncur, P, tables);
     StateWs st = carve_state(c, H, Nq, d, tables);
     // Buckets averaging kQTileWide queries or more take the wide kernel
     // (256-query items), when no search, group sizes or tables are asked for;
@@ -375,7 +403,32 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
     const bool bias = cache && cache->count && cap > 0;
     const bool wide = tables == 1 && !best && !bias && (dtype == FASTAR_BF16 || d == 64) &&
                       (static_cast<long long>(kQTileWide) << P) <= Nq;
-    w.it.qtile = wide ? kQTileWide : kQTile;
+    w.it[0].qtile = wide ? kQTileWide : kQTile;
+    // every table's (queries, keys) pair sorted in one launch pair; table t
+    // groups by id field t (bits tP .. tP+P-1)
+    IdSet sets[2 * FASTAR_MAX_TABLES];
+    SortBufs bufs[2 * FASTAR_MAX_TABLES];
+    for (int t = 0; t < tables; ++t) {
+        IdSet& qs = sets[2 * t];
+        IdSet& ks = sets[2 * t + 1];
+        qs.shift = ks.shift = t * P;
+        qs.a = q_ids;
+        qs.a_stride = Nq;
+        qs.a_fixed = Nq;
+        if (cache) {
+            ks.a = cache->ids;
+            ks.a_stride = cap;
+            ks.a_nvalid = cache->n_valid;
+            ks.a_cap = cap;
+        }
+        ks.b = kcur_ids;
+        ks.b_stride = Ncur;
+        ks.nb = Ncur;
+        bufs[2 * t] = w.q[t];
+        bufs[2 * t + 1] = w.k[t];
+    }
+    hipError_t e = launch_bucket_sort(H, P, 2 * tables, sets, bufs, w.it, tables, s);
+    if (e != hipSuccess) return FASTAR_EHIP;
     AttnParams p;
     p.q = q;
     p.Nq = Nq;
@@ -387,12 +440,6 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
     p.b_rows = Ncur;
     p.n_valid = cache ? cache->n_valid : nullptr;
     p.cap = cap;
-    p.qperm = w.q.perm;
-    p.qperm_stride = w.q.perm_stride;
-    p.kperm = w.k.perm;
-    p.kperm_stride = w.k.perm_stride;
-    p.items = w.it.items;
-    p.max_items = w.it.max_items;
     p.out = out;
     p.lse = lse;
     p.best = best;
@@ -411,26 +458,14 @@ fastar_status annsa_impl(const void* q, const uint16_t* q_ids, int32_t H, int32_
     p.st_l = st.l;
     p.st_bc = st.bc;
     p.st_bs = st.bs;
-    // one sort + attention pass per table (the sort buffers are reused)
+    // one attention launch per table, each resuming the previous one's state
     for (int t = 0; t < tables; ++t) {
-        IdSet sets[2];
-        sets[0].shift = t * P;
-        sets[0].a = q_ids;
-        sets[0].a_stride = Nq;
-        sets[0].a_fixed = Nq;
-        if (cache) {
-            sets[1].a = cache->ids;
-            sets[1].a_stride = cap;
-            sets[1].a_nvalid = cache->n_valid;
-            sets[1].a_cap = cap;
-        }
-        sets[1].shift = t * P;
-        sets[1].b = kcur_ids;
-        sets[1].b_stride = Ncur;
-        sets[1].nb = Ncur;
-        SortBufs bufs[2] = {w.q, w.k};
-        hipError_t e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, s);
-        if (e != hipSuccess) return FASTAR_EHIP;
+        p.qperm = w.q[t].perm;
+        p.qperm_stride = w.q[t].perm_stride;
+        p.kperm = w.k[t].perm;
+        p.kperm_stride = w.k[t].perm_stride;
+        p.items = w.it[t].items;
+        p.max_items = w.it[t].max_items;
         p.table = t;
         e = launch_attn(MODE_SA, dtype == FASTAR_BF16, d, out_dtype == FASTAR_BF16, H, p, s);
         if (e != hipSuccess) return FASTAR_EHIP;
@@ -592,7 +627,7 @@ fastar_status fastar_tempcache_update(const fastar_cache* cache, const void* q,
         sets[1].a_nvalid = cache->n_valid;
         sets[1].a_cap = cap;
         SortBufs bufs[2] = {w.q, w.k};
-        e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, s);
+        e = launch_bucket_sort(H, P, 2, sets, bufs, &w.it, 1, s);
         if (e != hipSuccess) return FASTAR_EHIP;
         AttnParams p;
         p.q = q;

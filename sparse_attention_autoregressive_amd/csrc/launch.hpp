@@ -24,6 +24,10 @@ hipError_t launch_hash_batch(int count, const void* const* x, const int* N, uint
 // ------------------------------------------------------------------ quantization ids
 hipError_t launch_quantize(const void* x, bool bf16, int H, int N, int d, const float* codebook, int B,
                            uint16_t* ids, float* norms, hipStream_t s);
+// ``count`` <= kHashBatch sets (host arrays), as launch_hash_batch.
+hipError_t launch_quantize_batch(int count, const void* const* x, const int* N, uint16_t* const* ids,
+                                 float* const* norms, bool bf16, int H, int d, const float* codebook, int B,
+                                 hipStream_t s);
 
 // ------------------------------------------------------------------ sort
 // A set of ids per head: the first part (source a) holds either ``a_fixed``
@@ -72,12 +76,15 @@ inline int max_attn_items(long long nq, int B) {
     return static_cast<int>((m + 7) / 8 * 8);
 }
 
-// Sorts one or two sets (nsets = 1 or 2) per head: a tile-histogram launch
-// and a scatter launch (plus a scan launch between them when a set spans
-// more than kSortScanTiles tiles).  With ``items`` set (two sets: queries,
-// keys) one more scatter block per head writes the attention work list.
+// Sorts ``nsets`` sets per head (at most kSortMaxSets): a tile-histogram
+// launch and a scatter launch (plus a scan launch between them when a set
+// spans more than kSortScanTiles tiles).  With ``items`` (an array of
+// ``npairs`` tables; the sets then form npairs (queries, keys) pairs) one
+// more scatter block per head and pair writes that pair's attention work list.
+constexpr int kSortMaxPairs = 8;            // FASTAR_MAX_TABLES
+constexpr int kSortMaxSets = 2 * kSortMaxPairs;
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
-                              const ItemTable* items, hipStream_t s);
+                              const ItemTable* items, int npairs, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
 enum AttnMode { MODE_SA = 0, MODE_CA = 1, MODE_TOP1 = 2 };

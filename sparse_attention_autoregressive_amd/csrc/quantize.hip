@@ -24,6 +24,15 @@
 
 namespace fastar {
 
+// Up to kHashBatch token sets quantized with the same codebook in one launch
+// (grid z = set), like the hash's batched form.
+struct QzSets {
+    const void* x[kHashBatch];
+    int N[kHashBatch];
+    uint16_t* ids[kHashBatch];
+    float* norms[kHashBatch];
+};
+
 namespace {
 constexpr int QZ_CW = 64;        // codewords per LDS chunk
 constexpr int QZ_TOK = 64;       // vectors per block
@@ -31,13 +40,16 @@ constexpr int QZ_NB = 4;         // 16-codeword blocks whose MFMA chains interle
 }  // namespace
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ x, const float* __restrict__ cb,
-                                                       int N, int B, uint16_t* __restrict__ ids,
-                                                       float* __restrict__ norms) {
+__global__ __launch_bounds__(256) void quantize_kernel(const QzSets sets, const float* __restrict__ cb, int B) {
     constexpr int DG = D / 4;                  // dimensions per lane group
     constexpr int STR = D + 4;                 // LDS row stride (floats)
     __shared__ __align__(16) float cs[QZ_CW * STR];
     __shared__ float hn[QZ_CW];
+    const T* __restrict__ x = static_cast<const T*>(sets.x[blockIdx.z]);
+    const int N = sets.N[blockIdx.z];
+    uint16_t* __restrict__ ids = sets.ids[blockIdx.z];
+    float* __restrict__ norms = sets.norms[blockIdx.z];
+    if (blockIdx.x * QZ_TOK >= N) return;      // block uniform
     const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -159,15 +171,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* __restrict__ x, 
 constexpr int QZB_GPW = 2;
 
 template <int D>
-__global__ __launch_bounds__(256) void quantize_bf16_kernel(const uint16_t* __restrict__ x,
-                                                            const float* __restrict__ cb, int N, int B,
-                                                            uint16_t* __restrict__ ids,
-                                                            float* __restrict__ norms) {
+__global__ __launch_bounds__(256) void quantize_bf16_kernel(const QzSets sets, const float* __restrict__ cb,
+                                                            int B) {
     constexpr int KS = D / 32;
     constexpr int PSTR = D + 8;                // bf16 LDS row stride (elements): 16-byte pad
     constexpr int EPT = D / 4;                 // codebook elements per staging thread
     __shared__ __align__(16) uint16_t cp[3][QZ_CW * PSTR];
     __shared__ __align__(16) float hn[QZ_CW];
+    const uint16_t* __restrict__ x = static_cast<const uint16_t*>(sets.x[blockIdx.z]);
+    const int N = sets.N[blockIdx.z];
+    uint16_t* __restrict__ ids = sets.ids[blockIdx.z];
+    float* __restrict__ norms = sets.norms[blockIdx.z];
+    if (blockIdx.x * (64 * QZB_GPW) >= N) return;      // block uniform
     const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
@@ -299,28 +314,48 @@ __global__ __launch_bounds__(256) void quantize_bf16_kernel(const uint16_t* __re
     }
 }
 
-hipError_t launch_quantize(const void* x, bool bf16, int H, int N, int d, const float* codebook, int B,
-                           uint16_t* ids, float* norms, hipStream_t s) {
-    if (N == 0 || H == 0) return hipSuccess;
-    dim3 grid((N + QZ_TOK - 1) / QZ_TOK, H);
+hipError_t launch_quantize_batch(int count, const void* const* x, const int* N, uint16_t* const* ids,
+                                 float* const* norms, bool bf16, int H, int d, const float* codebook, int B,
+                                 hipStream_t s) {
+    QzSets sets;
+    int used = 0, nmax = 0;
+    for (int i = 0; i < count && i < kHashBatch; ++i) {
+        if (N[i] == 0) continue;
+        sets.x[used] = x[i];
+        sets.N[used] = N[i];
+        sets.ids[used] = ids[i];
+        sets.norms[used] = norms ? norms[i] : nullptr;
+        nmax = N[i] > nmax ? N[i] : nmax;
+        ++used;
+    }
+    if (used == 0 || H == 0) return hipSuccess;
+    for (int i = used; i < kHashBatch; ++i) {
+        sets.x[i] = nullptr;
+        sets.N[i] = 0;
+        sets.ids[i] = nullptr;
+        sets.norms[i] = nullptr;
+    }
     timer_begin("ann_quantize", s);
     if (bf16) {
-        const dim3 gb((N + 64 * QZB_GPW - 1) / (64 * QZB_GPW), H);
-        const uint16_t* xb = static_cast<const uint16_t*>(x);
+        const dim3 gb((nmax + 64 * QZB_GPW - 1) / (64 * QZB_GPW), H, used);
         if (d == 64)
-            hipLaunchKernelGGL((quantize_bf16_kernel<64>), gb, dim3(256), 0, s, xb, codebook, N, B, ids, norms);
+            hipLaunchKernelGGL((quantize_bf16_kernel<64>), gb, dim3(256), 0, s, sets, codebook, B);
         else
-            hipLaunchKernelGGL((quantize_bf16_kernel<128>), gb, dim3(256), 0, s, xb, codebook, N, B, ids, norms);
-        timer_end(s);
-        return hipGetLastError();
+            hipLaunchKernelGGL((quantize_bf16_kernel<128>), gb, dim3(256), 0, s, sets, codebook, B);
+    } else {
+        const dim3 grid((nmax + QZ_TOK - 1) / QZ_TOK, H, used);
+        if (d == 64)
+            hipLaunchKernelGGL((quantize_kernel<float, 64>), grid, dim3(256), 0, s, sets, codebook, B);
+        else
+            hipLaunchKernelGGL((quantize_kernel<float, 128>), grid, dim3(256), 0, s, sets, codebook, B);
     }
-#define FASTAR_QZ(T, DD)                                                                     \
-    hipLaunchKernelGGL((quantize_kernel<T, DD>), grid, dim3(256), 0, s, static_cast<const T*>(x), \
-                       codebook, N, B, ids, norms)
-    if (d == 64) FASTAR_QZ(float, 64); else FASTAR_QZ(float, 128);
-#undef FASTAR_QZ
     timer_end(s);
     return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, bool bf16, int H, int N, int d, const float* codebook, int B,
+                           uint16_t* ids, float* norms, hipStream_t s) {
+    return launch_quantize_batch(1, &x, &N, &ids, &norms, bf16, H, d, codebook, B, s);
 }
 
 }  // namespace fastar

@@ -26,15 +26,19 @@
 
 namespace fastar {
 
+// Up to kSortMaxSets sets in one launch (grid z / y = set).  With work lists
+// the sets come in (queries, keys) pairs 2p, 2p+1, and pair p's list goes to
+// items[p] (multi-table AnnSA sorts every table's pair at once).
 struct SortArgs {
-    IdSet set[2];
-    SortBufs buf[2];
+    IdSet set[kSortMaxSets];
+    SortBufs buf[kSortMaxSets];
+    ItemTable items[kSortMaxPairs];
     int nsets;
+    int npairs;                   // pairs with a work list (then nsets = 2 * npairs)
     int B;
     int P;
-    int builder_block;            // grid x index of the work-list block, or -1
+    int builder_block;            // grid x index of the work-list blocks, or -1
     int scanned;                  // hist holds per-tile prefixes and off is written (scan launch)
-    ItemTable items;
 };
 
 __device__ __forceinline__ int set_count(const IdSet& s, int h, int& na) {
@@ -256,10 +260,13 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     const int n = set_count(S, h, na);
     const int ntiles = sort_tiles(n);
     const bool lead = t == 0;                     // writes off
-    // the work-list builder: the extra last block of the query set's grid row
-    const bool builder = a.items.items && a.nsets == 2 && t == a.builder_block;
-    if (builder && si != 0) return;               // block uniform
+    // the work-list builder: the extra last block of each query set's grid row
+    const bool builder = a.npairs > 0 && t == a.builder_block;
+    if (builder && (si & 1)) return;              // block uniform: key sets build nothing
     if (t >= ntiles && !lead && !builder) return; // block uniform
+    const ItemTable& IT = a.items[builder ? si / 2 : 0];
+    const IdSet& KSET = a.set[builder ? si + 1 : si];
+    const SortBufs& KBUF = a.buf[builder ? si + 1 : si];
     const int k = (B + 255) / 256, b0 = tid * k;
     // the tile's ids, loaded first so their latency overlaps the histogram reads
     constexpr int R = kSortTile / 256;
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
         int* slot = run;
         int kstart[4], ktot[4];
         if (a.scanned) {
-            const int32_t* ko = a.buf[1].off + static_cast<size_t>(h) * (B + 1);
+            const int32_t* ko = KBUF.off + static_cast<size_t>(h) * (B + 1);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int b = b0 + j;
@@ -328,9 +335,9 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
             }
         } else {
             int nak;
-            const int nkeys = set_count(a.set[1], h, nak);
+            const int nkeys = set_count(KSET, h, nak);
             BucketSums ks;
-            bucket_sums(a.buf[1], h, 0, sort_tiles(nkeys), B, k, ks, pt, pb);
+            bucket_sums(KBUF, h, 0, sort_tiles(nkeys), B, k, ks, pt, pb);
             bucket_starts(ks, B, k, kstart, smem);
 #pragma unroll
             for (int j = 0; j < 4; ++j) ktot[j] = ks.total[j];
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
             }
         }
         __syncthreads();
-        const int qt = a.items.qtile;
+        const int qt = IT.qtile;
         // rank of bucket b = buckets with more keys, or as many and a lower
         // index; with B <= 256 the 256 / B threads of a bucket split the count
         int rank[4], tiles[4];
@@ -401,7 +408,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
         for (int j = 0; j < 4; ++j)
             if (j < k && b0 + j < B) slot[b0 + j] = firsts[j];     // start of rank b0 + j
         __syncthreads();
-        int4* it = a.items.items + static_cast<size_t>(h) * a.items.max_items;
+        int4* it = IT.items + static_cast<size_t>(h) * IT.max_items;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int b = b0 + j;
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
                                            kcnt[b]);
             }
         }
-        for (int i = ntot + tid; i < a.items.max_items; i += 256) it[i] = make_int4(0, 0, 0, 0);
+        for (int i = ntot + tid; i < IT.max_items; i += 256) it[i] = make_int4(0, 0, 0, 0);
         return;                                   // block uniform
     }
     if (t >= ntiles) return;                      // block uniform
@@ -462,22 +469,22 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
 }
 
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
-                              const ItemTable* items, hipStream_t s) {
+                              const ItemTable* items, int npairs, hipStream_t s) {
+    if (nsets < 1 || nsets > kSortMaxSets || npairs < 0 || npairs > kSortMaxPairs ||
+        (npairs > 0 && nsets != 2 * npairs))
+        return hipErrorInvalidValue;
     SortArgs a;
     a.nsets = nsets;
+    a.npairs = items ? npairs : 0;
     a.builder_block = -1;
     a.B = 1 << P;
     a.P = P;
-    a.items = items ? *items : ItemTable();
+    for (int i = 0; i < a.npairs; ++i) a.items[i] = items[i];
     int max_tiles = 0;
     for (int i = 0; i < nsets; ++i) {
         a.set[i] = sets[i];
         a.buf[i] = bufs[i];
         if (bufs[i].max_tiles > max_tiles) max_tiles = bufs[i].max_tiles;
-    }
-    if (nsets == 1) {
-        a.set[1] = a.set[0];
-        a.buf[1] = a.buf[0];
     }
     if (H == 0) return hipSuccess;
     // a scan launch once the tiles are many (every set must then have off)
@@ -495,7 +502,7 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
         timer_end(s);
     }
     int gx = max_tiles > 0 ? max_tiles : 1;
-    if (a.items.items && nsets == 2) a.builder_block = gx++;
+    if (a.npairs > 0) a.builder_block = gx++;
     timer_begin("sort_scatter", s);
     hipLaunchKernelGGL(sort_scatter_kernel, dim3(gx, H, nsets), dim3(256), 0, s, a);
     timer_end(s);

@@ -37,8 +37,8 @@ from typing import Optional
 
 import torch
 
-from . import (KVCache, ann_hash, ann_hash_batch, ann_quantize, annca_forward, annsa_forward, load,
-               tempcache_order, tempcache_update)
+from . import (KVCache, ann_hash, ann_hash_batch, ann_quantize, ann_quantize_batch, annca_forward,
+               annsa_forward, load, tempcache_order, tempcache_update)
 
 
 class AttentionStep:
@@ -115,12 +115,8 @@ class AttentionStep:
         """Enqueues one step on the current stream (and the side stream)."""
         main = torch.cuda.current_stream(q.device)
         if not self.overlap:
-            if self.ann == "lsh":
-                ann_hash_batch([q, k_cur, kp], planes, ids=[self.ids["q"], self.ids["k"], self.ids["p"]])
-            else:
-                self._ids(q, planes, self.ids["q"])
-                self._ids(k_cur, planes, self.ids["k"])
-                self._ids(kp, planes, self.ids["p"])
+            batch = ann_hash_batch if self.ann == "lsh" else ann_quantize_batch
+            batch([q, k_cur, kp], planes, ids=[self.ids["q"], self.ids["k"], self.ids["p"]])
             self._annsa(cache, q, k_cur, v_cur)
             self._annca(q, kp, vp)
             self._commit(cache, q, k_cur, v_cur, step)
@@ -132,11 +128,8 @@ class AttentionStep:
         if not use_order:
             with torch.cuda.stream(side):
                 self._ids(kp, planes, self.ids["p"])
-        if self.ann == "lsh":
-            ann_hash_batch([q, k_cur], planes, ids=[self.ids["q"], self.ids["k"]])
-        else:
-            self._ids(q, planes, self.ids["q"])
-            self._ids(k_cur, planes, self.ids["k"])
+        batch = ann_hash_batch if self.ann == "lsh" else ann_quantize_batch
+        batch([q, k_cur], planes, ids=[self.ids["q"], self.ids["k"]])
         self._annsa(cache, q, k_cur, v_cur)
         self._ev_sa.record(main)
         if use_order:

@@ -136,3 +136,21 @@ def test_quantized_step_matches_oracle(name):
             assert int(cache.n_valid[h]) == tcres["n"]
             assert np.array_equal(host_ids(cache.ids)[h], tcres["cache"]["ids"])
             assert np.array_equal(cache.ts[h].cpu().numpy(), tcres["cache"]["ts"])
+
+
+@pytest.mark.parametrize("name,B", [("tiny_f32", 16), ("wan13_bf16", 128)])
+def test_quantize_batch_equals_separate_calls(name, B):
+    """fastar_ann_quantize_batch (queries, current keys and prompt keys in one
+    launch, sets of different sizes) gives exactly the ids and norms of one
+    fastar_ann_quantize per set."""
+    require_gpu()
+    cfg = CONFIGS[name]
+    st = make_step(cfg, 0)
+    C = torch.from_numpy(codebook_from_keys(st.cache_k, st.n_valid, B, 0)).cuda()
+    xs = [dev(a, cfg.dtype) for a in (st.q, st.k_cur, st.kp)]
+    norms = [torch.empty(cfg.H, x.shape[1], dtype=torch.float32, device="cuda") for x in xs]
+    got = fa.ann_quantize_batch(xs, C, norms=norms)
+    for x, g, nb in zip(xs, got, norms):
+        n1 = torch.empty_like(nb)
+        one = fa.ann_quantize(x, C, norms=n1)
+        assert torch.equal(g, one) and torch.equal(nb, n1)
