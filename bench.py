@@ -363,11 +363,16 @@ def main():
                               best_in=two.best, cos_in=two.best_cos)
     written = float((res["dest"] >= 0).sum())
     ca_keys = float(cnt.double().sum())
+    # AnnCA's prompt selection: ids read, keep mask and counts written (and the
+    # kept index lists when a long prompt takes the separate launch); up to
+    # 1024 prompt tokens the attention launch does it
+    sel_bytes = H * (Nq + F * cfg.L) * 2.0 + H * F * (cfg.L + 4.0)
+    sel_fused = "annca_select" not in kernel_ms
     step_bytes = {
         "ann_hash": (2 * Nq + cfg.L) * H * (d * esz + 2),
         "sort": 6.0 * H * (2 * Nq + cap),                       # id read, perm written
-        "annca_select": H * (Nq + F * cfg.L) * 2.0 + H * F * cfg.L * 5.0,
-        "annca_attn": Nq * H * (d * esz + d * osz) + ca_keys * 2 * d * esz,
+        "annca_select": sel_bytes + H * F * cfg.L * 4.0,
+        "annca_attn": Nq * H * (d * esz + d * osz) + ca_keys * 2 * d * esz + (sel_bytes if sel_fused else 0),
         "tempcache_select": H * Nq * 12.0 + H * cap * 4.0,      # best, cos in, dest out; ts
         "tempcache_scatter": written * (4 * d * esz + 10) + H * Nq * 4.0,
         "annsa_attn": sa_bytes,
@@ -628,7 +633,9 @@ def size_sweep(args):
     """The step's small kernels at batched sizes: the hash over H x (k x Nq)
     bf16 vectors, the bucket sort over as many ids, and AnnCA's prompt
     selection over k x H heads (k chunks' worth of heads, the real 4680
-    queries and 512 prompt tokens each).  At the step's own size these
+    queries each and a 2048-token prompt: the separate selection launch
+    serves prompts longer than 1024 tokens, shorter ones are selected inside
+    the attention launch).  At the step's own size these
     kernels move a few MB and are bound by launch latency; the sweep shows
     the bandwidth each reaches once the work is large enough.  Algorithmic
     bytes: hash 2d + 2 per vector (row in, id out); sort 2 + 4 per id (id in,
@@ -676,7 +683,9 @@ def size_sweep(args):
                      "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
         del sid, ws
         print(json.dumps({"progress": "size_sweep", "k": k}), file=sys.stderr, flush=True)
-    F = Nq // fl
+    # the separate selection launch serves prompts longer than 1024 tokens
+    # (shorter ones are selected inside the attention launch): 2048 here
+    F, L = Nq // fl, 2048
     for k in (1, 16, 64):
         Hk = k * H
         qi = torch.randint(0, B, (Hk, Nq), generator=gen, device=dev, dtype=torch.int32).to(torch.int16)
@@ -690,7 +699,7 @@ def size_sweep(args):
         ms = kernel_ms(lambda: fa.annca_forward(q, qi, fl, kp, vp, pi, P, out=out, keep=keep, ws=ws),
                        ["annca_select"])
         nbytes = Hk * (Nq + F * L) * 2.0 + Hk * F * (L * 5.0 + 4.0)
-        rows.append({"kernel": "annca_select", "heads": Hk, "bytes": nbytes, "ms": ms,
+        rows.append({"kernel": "annca_select", "heads": Hk, "prompt": L, "bytes": nbytes, "ms": ms,
                      "GB/s": nbytes / (ms * 1e-3) / 1e9, "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
         del q, kp, vp, out, ws
         print(json.dumps({"progress": "size_sweep annca", "k": k}), file=sys.stderr, flush=True)

@@ -285,6 +285,9 @@ fastar_status fastar_annsa_multi_forward(const void* q, const uint16_t* q_ids, i
  * keep       [H][F][L] uint8 (0/1), may be NULL
  * keep_count [H][F] int32, may be NULL
  * frame_len must divide Nq.  L may be 0.  scale: finite and > 0.
+ * ws: fastar_annca_workspace(...) bytes -- 0 when L <= 1024, where the
+ * attention launch selects each frame's prompt tokens itself; a longer
+ * prompt takes a separate selection launch and an [H][F][L] index list.
  * ------------------------------------------------------------------------ */
 size_t fastar_annca_workspace(int32_t H, int32_t Nq, int32_t frame_len, int32_t L, int32_t P);
 fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t H, int32_t Nq,

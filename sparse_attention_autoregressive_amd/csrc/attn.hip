@@ -660,6 +660,97 @@ struct Blk {
     }
 };
 
+// AnnCA prompt selection done by the attention block itself (FAST-AR blog,
+// "2. AnnCA"; summary, "2. Core Components" B): the buckets occupied by
+// frame f's queries form a bitmap in LDS, and the prompt tokens whose bucket
+// bit is set become the block's key list in ascending order, written straight
+// into ``kidx``; the rest of the last tile holds row 0 (any valid row: those
+// scores are masked).  Every block of the frame builds the same list (the ids
+// are a few KB, read through L2); the frame's first block also writes the
+// keep mask and count.  Needs L <= KCH, so the list is a single staged chunk.
+// Returns the number of kept tokens.
+template <int NT>
+__device__ __forceinline__ int ca_select_block(const AttnParams& p, int h, int f, int* kidx) {
+    static_assert(kCaFusedMaxL == KCH, "the kept list fills at most one index chunk");
+    constexpr int PU = KCH / NT;                 // consecutive prompt tokens per thread
+    __shared__ uint32_t bits[kCaMaxBuckets / 32];
+    __shared__ int sscan[NT / kWave];
+    const int tid = threadIdx.x, L = p.L;
+    const uint32_t mask = static_cast<uint32_t>(p.ca_buckets - 1);
+    const size_t row = static_cast<size_t>(h) * p.F + f;
+    const bool first = blockIdx.x == 0;
+    // Every id load is issued before the first is used: the prompt ids
+    // (clamped indices, no branch), then the frame's query ids in 16-byte
+    // loads of 8 ids; the ends before and after the aligned part (at most 7
+    // ids each) are read one id per thread.
+    const uint16_t* pi = p.ca_kp_ids + static_cast<size_t>(h) * L;
+    uint32_t pid[PU];
+    if (L > 0) {
+#pragma unroll
+        for (int u = 0; u < PU; ++u) pid[u] = pi[min(tid * PU + u, L - 1)];
+    }
+    const uint16_t* qi = p.q_ids + static_cast<size_t>(h) * p.Nq + static_cast<size_t>(f) * p.frame_len;
+    const int n = p.frame_len;
+    const int pre = min(n, static_cast<int>(((16u - (reinterpret_cast<uintptr_t>(qi) & 15u)) & 15u) >> 1));
+    const int nv = (n - pre) >> 3, tail = pre + nv * 8;
+    const u32x4* qv = reinterpret_cast<const u32x4*>(qi + pre);
+    const uint32_t id_pre = qi[min(tid, n - 1)];
+    const uint32_t id_tail = qi[min(tail + tid, n - 1)];
+    u32x4 r[4];
+    auto load = [&](int v0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = qv[min(v0 + u * NT + tid, nv - 1)];
+    };
+    auto mark = [&](uint32_t id) __attribute__((always_inline)) {
+        id &= mask;
+        atomicOr(&bits[id >> 5], 1u << (id & 31));
+    };
+    auto mark_all = [&](int v0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (v0 + u * NT + tid < nv) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mark(r[u][e] & 0xffffu);
+                    mark(r[u][e] >> 16);
+                }
+            }
+        }
+    };
+    if (nv > 0) load(0);
+    for (int i = tid; i < (p.ca_buckets + 31) / 32; i += NT) bits[i] = 0;
+    __syncthreads();
+    if (nv > 0) mark_all(0);
+    for (int v0 = 4 * NT; v0 < nv; v0 += 4 * NT) {
+        load(v0);
+        mark_all(v0);
+    }
+    if (tid < pre) mark(id_pre);
+    if (tid < n - tail) mark(id_tail);
+    __syncthreads();
+    // one block scan over the threads' counts places each kept token
+    int keep[PU], cnt = 0;
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+        const uint32_t id = pid[u] & mask;
+        keep[u] = tid * PU + u < L ? static_cast<int>((bits[id >> 5] >> (id & 31)) & 1u) : 0;
+        cnt += keep[u];
+    }
+    int total;
+    int pos = block_exclusive_scan<NT>(cnt, sscan, total);
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+        const int t = tid * PU + u;
+        if (keep[u]) kidx[pos++] = t;
+        if (first && p.ca_keep && t < L) p.ca_keep[row * L + t] = static_cast<uint8_t>(keep[u]);
+    }
+    const int end = (total + KT - 1) / KT * KT;
+    for (int i = total + tid; i < end; i += NT) kidx[i] = 0;
+    if (first && p.ca_keep_count && tid == 0) p.ca_keep_count[row] = total;
+    __syncthreads();
+    return total;
+}
+
 }  // namespace
 
 // NW waves per block; the item is 16*NW queries (SA / TOP1: the 64-query
@@ -687,13 +778,21 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     int h, q_count, nk, qbase = 0;
     const int32_t* qlist = nullptr;
     const int32_t* klist;
+    // AnnCA blocks that select their prompt keys themselves hold the whole
+    // key list in ``kidx`` from here on
+    const bool fused = MODE == MODE_CA && p.ca_fused != 0;
     if constexpr (MODE == MODE_CA) {
         h = blockIdx.z;
         const int f = blockIdx.y, c = blockIdx.x;
         qbase = f * p.frame_len + c * QT;
         q_count = min(QT, p.frame_len - c * QT);
-        nk = p.ca_cnt[h * p.F + f];
-        klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
+        if (fused) {
+            nk = ca_select_block<NT>(p, h, f, kidx);
+            klist = nullptr;
+        } else {
+            nk = p.ca_cnt[h * p.F + f];
+            klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
+        }
     } else {
         h = blockIdx.x;                          // heads fastest: the longest items
         const int item = blockIdx.y;            // of every head dispatch first
@@ -725,10 +824,12 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     };
     static_assert(KCH % NT == 0, "key chunk split");
     int kfirst[KCH / NT];
+    if (!fused) {
 #pragma unroll
-    for (int u = 0; u < KCH / NT; ++u) {
-        const int r = tid + u * NT;
-        kfirst[u] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+        for (int u = 0; u < KCH / NT; ++u) {
+            const int r = tid + u * NT;
+            kfirst[u] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+        }
     }
     int qrow = 0;
     if (qvalid) qrow = (MODE == MODE_CA) ? qbase + ql : qlist[ql];
@@ -775,8 +876,10 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     A.slots = sslot[0];
     Bs.slots = sslot[1];
     VS.slots = nullptr;
+    if (!fused) {
 #pragma unroll
-    for (int u = 0; u < KCH / NT; ++u) kidx[tid + u * NT] = kfirst[u];
+        for (int u = 0; u < KCH / NT; ++u) kidx[tid + u * NT] = kfirst[u];
+    }
     __syncthreads();
     if (nt > 0) {
         B::template load_tile<true, false>(A, kidx, 0, sr, tid);
@@ -824,13 +927,21 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
     int h, q_count, nk, qbase = 0;
     const int32_t* qlist = nullptr;
     const int32_t* klist;
+    // as in attn_body; here the selection runs once the query rows are on
+    // their way
+    const bool fused = MODE == MODE_CA && p.ca_fused != 0;
     if constexpr (MODE == MODE_CA) {
         h = blockIdx.z;
         const int f = blockIdx.y, c = blockIdx.x;
         qbase = f * p.frame_len + c * QT;
         q_count = min(QT, p.frame_len - c * QT);
-        nk = p.ca_cnt[h * p.F + f];
-        klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
+        if (fused) {
+            nk = 0;
+            klist = nullptr;
+        } else {
+            nk = p.ca_cnt[h * p.F + f];
+            klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
+        }
     } else {
         h = blockIdx.x;                          // heads fastest, as in attn_body
         const int4 it = p.items[static_cast<size_t>(h) * p.max_items + blockIdx.y];
@@ -847,10 +958,12 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
     // first K/V gathers need not wait for them
     static_assert(KCH % NT == 0, "key chunk split");
     int kfirst[KCH / NT];
+    if (!fused) {
 #pragma unroll
-    for (int u = 0; u < KCH / NT; ++u) {
-        const int r = tid + u * NT;
-        kfirst[u] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+        for (int u = 0; u < KCH / NT; ++u) {
+            const int r = tid + u * NT;
+            kfirst[u] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
+        }
     }
     const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
     typename B::QF qf[2];
@@ -867,6 +980,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
         acc[qg].reset();
     }
     const bool wave_active = w * 32 < q_count;
+    if (fused) nk = ca_select_block<NT>(p, h, blockIdx.y, kidx);
 
     auto stage_idx = [&](int first) __attribute__((always_inline)) {
         for (int i = tid; i < KCH; i += NT) {
@@ -892,8 +1006,10 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
     typename B::Stage A, Bs;
     A.slots = sslot[0];
     Bs.slots = sslot[1];
+    if (!fused) {
 #pragma unroll
-    for (int u = 0; u < KCH / NT; ++u) kidx[tid + u * NT] = kfirst[u];
+        for (int u = 0; u < KCH / NT; ++u) kidx[tid + u * NT] = kfirst[u];
+    }
     __syncthreads();
     if (nt > 0) B::load_tile(A, kidx, 0, sr, tid);
     if (nt > 1) B::load_tile(Bs, kidx, 1, sr, tid);

@@ -501,6 +501,7 @@ fastar_status fastar_annsa_multi_forward(const void* q, const uint16_t* q_ids, i
 // ------------------------------------------------------------------ AnnCA
 size_t fastar_annca_workspace(int32_t H, int32_t Nq, int32_t frame_len, int32_t L, int32_t P) {
     if (H < 0 || Nq < 0 || L < 0 || frame_len <= 0 || !planes_ok(P)) return 0;
+    if (L <= kCaFusedMaxL) return 0;          // the attention blocks select the prompt keys
     Carver c(nullptr);
     carve_annca(c, H, Nq / frame_len, L);
     return c.off;
@@ -526,19 +527,29 @@ fastar_status fastar_annca_forward(const void* q, const uint16_t* q_ids, int32_t
     if (HQ == 0) return FASTAR_OK;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    Carver c(ws);
-    AnncaWs w = carve_annca(c, H, F, L);
-    hipError_t e = launch_annca_select(q_ids, kp_ids, H, Nq, frame_len, L, P, w.idx, w.cnt, keep,
-                                       keep_count, s);
-    if (e != hipSuccess) return FASTAR_EHIP;
     AttnParams p;
+    if (L <= kCaFusedMaxL) {
+        // one launch: each block builds its frame's kept list in LDS
+        p.ca_fused = 1;
+        p.q_ids = q_ids;
+        p.ca_kp_ids = kp_ids;
+        p.ca_buckets = 1 << P;
+        p.ca_keep = keep;
+        p.ca_keep_count = keep_count;
+    } else {
+        Carver c(ws);
+        AnncaWs w = carve_annca(c, H, F, L);
+        hipError_t e = launch_annca_select(q_ids, kp_ids, H, Nq, frame_len, L, P, w.idx, w.cnt, keep,
+                                           keep_count, s);
+        if (e != hipSuccess) return FASTAR_EHIP;
+        p.ca_idx = w.idx;
+        p.ca_cnt = w.cnt;
+    }
     p.q = q;
     p.Nq = Nq;
     p.ka = kp;
     p.va = vp;
     p.a_rows = L;
-    p.ca_idx = w.idx;
-    p.ca_cnt = w.cnt;
     p.frame_len = frame_len;
     p.F = F;
     p.L = L;

@@ -130,6 +130,15 @@ struct AttnParams {
     int frame_len = 0;
     int F = 0;
     int L = 0;
+    // prompt selection fused into the AnnCA blocks (ca_fused = 1, L <=
+    // kCaFusedMaxL): the prompt's bucket ids (null when L = 0), the bucket
+    // count and the keep outputs (either may be null); with ca_fused = 0 the
+    // blocks read ca_idx / ca_cnt instead
+    int ca_fused = 0;
+    const uint16_t* ca_kp_ids = nullptr;
+    int ca_buckets = 0;
+    uint8_t* ca_keep = nullptr;
+    int32_t* ca_keep_count = nullptr;
     // outputs
     void* out = nullptr;
     float* lse = nullptr;
@@ -137,6 +146,11 @@ struct AttnParams {
     float* bcos = nullptr;
     float scale_log2 = 0.f;
 };
+
+// Longest prompt whose kept list an AnnCA block builds in its own LDS, and
+// the most buckets its bitmap holds (2^10, the bucketed calls' plane limit).
+constexpr int kCaFusedMaxL = 1024;
+constexpr int kCaMaxBuckets = 1024;
 
 hipError_t launch_attn(int mode, bool bf16, int d, bool out_bf16, int H, const AttnParams& p,
                        hipStream_t s);

@@ -137,9 +137,13 @@ class AttentionStep:
             with torch.cuda.stream(side):
                 tempcache_order(cache, self.Nq, out=self.order)
                 self._ev_order.record(side)
-                self._ids(kp, planes, self.ids["p"])
         side.wait_event(self._ev_sa)
         with torch.cuda.stream(side):
+            if use_order:
+                # The prompt hash waits for AnnSA too, so the commit's select
+                # (one block per head, each holding most of a CU's LDS) is
+                # dispatched before AnnCA's blocks spread over every CU.
+                self._ids(kp, planes, self.ids["p"])
             self._annca(q, kp, vp)
             self._ev_side.record(side)
         if use_order:

@@ -65,7 +65,9 @@ def test_workspace_queries(lib):
     assert lib.fastar_annsa_workspace(12, 4680, 32760, 4680, 8) > a
     assert lib.fastar_annsa_workspace(1, 10, 0, 0, 11) == 0          # P out of range
     assert lib.fastar_tempcache_workspace(12, 4680, 32760, 7) > 12 * 32760 * 4
-    assert lib.fastar_annca_workspace(12, 4680, 1560, 512, 7) >= 12 * 3 * 512 * 4
+    assert lib.fastar_annca_workspace(12, 4680, 1560, 512, 7) == 0      # selection inside the blocks
+    assert lib.fastar_annca_workspace(12, 4680, 1560, 1024, 7) == 0
+    assert lib.fastar_annca_workspace(12, 4680, 1560, 1025, 7) >= 12 * 3 * 1025 * 4
     assert lib.fastar_bucket_sort_workspace(2, 1000, 5) > 0
     assert lib.fastar_bucket_sort_workspace(2, 0, 5) == 0
 
@@ -154,8 +156,9 @@ def test_quantize_validation(lib):
 
 def test_annca_validation(lib):
     f = lib.fastar_annca_forward
-    need = lib.fastar_annca_workspace(1, 30, 10, 8, 4)
-    base = [FAKE, FAKE, 1, 30, 10, 64, 0, FAKE, FAKE, FAKE, 8, 4, 0.125, FAKE, 0, None, None]
+    need = lib.fastar_annca_workspace(1, 30, 10, 1100, 4)     # a prompt long enough to need it
+    assert need > 0
+    base = [FAKE, FAKE, 1, 30, 10, 64, 0, FAKE, FAKE, FAKE, 1100, 4, 0.125, FAKE, 0, None, None]
     assert f(*(base + [FAKE, need - 1, None])) == _lib.FASTAR_EWORKSPACE
     bad = list(base); bad[4] = 7                         # 7 does not divide 30
     assert f(*(bad + [FAKE, need, None])) == _lib.FASTAR_ESHAPE

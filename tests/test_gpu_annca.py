@@ -1,8 +1,9 @@
 """GPU parity of fastar_annca_forward against the oracle: keep masks and counts
 bit-exact, outputs within tolerance; workloads as generated (nearly every
 prompt token kept), constructed ids that prune most of the prompt, frames with
-nothing kept, an empty prompt, and fp32 / bf16 at d = 64 and 128 with frames
-that end in a partial block."""
+nothing kept, an empty prompt, fp32 / bf16 at d = 64 and 128 with frames
+that end in a partial block, and prompts on either side of the longest one
+whose selection the attention blocks do themselves."""
 import numpy as np
 import pytest
 import torch
@@ -101,3 +102,29 @@ def test_annca_many_buckets(P):
     prep = prepared("single_bf16", P=P)
     keep = run_and_check(prep, prep["q_ids"], prep["kp_ids"], P, f"annca P={P}")
     assert 0 < keep.mean() < 1
+
+
+@pytest.mark.parametrize("L", [1000, 1024, 1025, 2100])
+def test_annca_prompt_lengths_around_the_fused_selection(L):
+    """Up to 1024 prompt tokens every attention block selects its frame's
+    prompt tokens in LDS (no workspace); a longer prompt takes the separate
+    selection launch and its index list, which the blocks then stage in
+    chunks of 1024 (2100 kept tokens: three chunks, the last one ragged).
+    Two frames of 600 queries; as generated (nearly everything kept) and with
+    each frame confined to six buckets (most of the prompt pruned)."""
+    require_gpu()
+    prep = prepared("single_bf16", L=L, frame_len=600, Fq=2, Fc=2)
+    cfg = prep["cfg"]
+    assert prep["kp_ids"].shape == (1, L)
+    need = fa.load().fastar_annca_workspace(cfg.H, cfg.Nq, cfg.frame_len, L, cfg.P)
+    assert (need == 0) == (L <= 1024)
+    keep = run_and_check(prep, prep["q_ids"], prep["kp_ids"], cfg.P, f"annca L={L}")
+    assert keep.mean() > 0.9
+    rng = np.random.default_rng(L)
+    q_ids = np.empty_like(prep["q_ids"])
+    for f in range(2):
+        q_ids[:, f * 600:(f + 1) * 600] = rng.integers(10 * f, 10 * f + 6, size=(cfg.H, 600))
+    kp_ids = rng.integers(0, cfg.B, size=(cfg.H, L)).astype(np.uint16)
+    keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, cfg.P, f"annca pruned L={L}",
+                         out_dtype=torch.bfloat16)
+    assert 0 < keep.mean() < 0.3
