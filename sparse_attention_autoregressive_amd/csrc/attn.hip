@@ -482,19 +482,20 @@ struct Blk {
         }
     }
 
-    // Two 16-query groups per wave (AnnCA, wide AnnSA): each K and V fragment
-    // read from LDS feeds the MFMAs of both groups, halving LDS reads per
-    // product.
-    static __device__ __forceinline__ void compute_tile2(Acc (&a)[2], const QF (&q)[2], const Smem& sm,
+    // NG 16-query groups per wave (AnnCA, wide AnnSA): each K and V fragment
+    // read from LDS feeds the MFMAs of every group, so LDS reads per product
+    // fall as 1/NG.
+    template <int NG>
+    static __device__ __forceinline__ void compute_tileg(Acc (&a)[NG], const QF (&q)[NG], const Smem& sm,
                                                          int kbase, int nk, float scale_log2, int g,
                                                          int c16) {
         static_assert(MODE != MODE_TOP1 && !SEARCH && !BIAS && !MULTI,
-                      "two query groups: AnnCA and plain AnnSA only");
-        f32x4 s[2][4];
+                      "query groups: AnnCA and plain AnnSA only");
+        f32x4 s[NG][4];
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
-            s[0][kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            s[1][kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qg = 0; qg < NG; ++qg) s[qg][kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
             const T* krow = &sm.Ks[(kb4 * 16 + c16) * STRK];
             if constexpr (BF) {
                 bf16x8_t af[NKS];
@@ -502,30 +503,30 @@ struct Blk {
                 for (int ks = 0; ks < NKS; ++ks)
                     af[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 32 + 8 * g);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    s[0][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], q[0].b[ks], s[0][kb4], 0, 0, 0);
-                    s[1][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], q[1].b[ks], s[1][kb4], 0, 0, 0);
-                }
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int qg = 0; qg < NG; ++qg)
+                        s[qg][kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks], q[qg].b[ks], s[qg][kb4], 0, 0, 0);
             } else {
                 float af[NKS];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) af[ks] = reinterpret_cast<const float*>(krow)[ks * 4 + g];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    s[0][kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ks], q[0].f[ks], s[0][kb4], 0, 0, 0);
-                    s[1][kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ks], q[1].f[ks], s[1][kb4], 0, 0, 0);
-                }
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int qg = 0; qg < NG; ++qg)
+                        s[qg][kb4] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[ks], q[qg].f[ks], s[qg][kb4], 0, 0, 0);
             }
         }
         const bool full = kbase + KT <= nk;                    // uniform
-        softmax_update(a[0], s[0], full, kbase, nk, scale_log2, g);
-        softmax_update(a[1], s[1], full, kbase, nk, scale_log2, g);
+#pragma unroll
+        for (int qg = 0; qg < NG; ++qg) softmax_update(a[qg], s[qg], full, kbase, nk, scale_log2, g);
         if constexpr (BF) {
 #pragma unroll
             for (int kg = 0; kg < 2; ++kg) {
-                bf16x8_t pb[2];
+                bf16x8_t pb[NG];
 #pragma unroll
-                for (int qg = 0; qg < 2; ++qg)
+                for (int qg = 0; qg < NG; ++qg)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         pb[qg][r] = static_cast<__bf16>(s[qg][2 * kg][r]);
@@ -542,8 +543,9 @@ struct Blk {
                 for (int db = 0; db < NDB; ++db) {
                     const bf16x8_t av = __builtin_bit_cast(
                         bf16x8_t, __builtin_shufflevector(lo[db], hi[db], 0, 1, 2, 3, 4, 5, 6, 7));
-                    a[0].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[0], a[0].o[db], 0, 0, 0);
-                    a[1].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[1], a[1].o[db], 0, 0, 0);
+#pragma unroll
+                    for (int qg = 0; qg < NG; ++qg)
+                        a[qg].o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[qg], a[qg].o[db], 0, 0, 0);
                 }
             }
         } else {
@@ -555,8 +557,9 @@ struct Blk {
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) {
                         const float vv = vrow[db * 16 + c16];
-                        a[0].o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, s[0][kb4][st], a[0].o[db], 0, 0, 0);
-                        a[1].o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, s[1][kb4][st], a[1].o[db], 0, 0, 0);
+#pragma unroll
+                        for (int qg = 0; qg < NG; ++qg)
+                            a[qg].o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, s[qg][kb4][st], a[qg].o[db], 0, 0, 0);
                     }
                 }
             }
@@ -911,9 +914,9 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
 // buckets: each gathered K/V tile then serves four times the queries of a
 // 64-query item, so the head's keys are re-read a quarter as often.  No
 // search, group-size shift or tables in this form.
-template <typename T, int D, int MODE, typename OT, int NW>
+template <typename T, int D, int MODE, typename OT, int NW, int NG>
 __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
-    constexpr int NT = 64 * NW, QT = 32 * NW;
+    constexpr int NT = 64 * NW, QT = 16 * NG * NW;
     static_assert(MODE == MODE_CA || QT == kQTileWide, "wide AnnSA items are kQTileWide queries");
     using B = Blk<T, D, MODE, false, NT>;
     __shared__ __align__(16) T Ks[KT * B::STRK];
@@ -966,20 +969,20 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
         }
     }
     const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
-    typename B::QF qf[2];
-    typename B::Acc acc[2];
-    bool qvalid[2];
-    int qrow[2];
+    typename B::QF qf[NG];
+    typename B::Acc acc[NG];
+    bool qvalid[NG];
+    int qrow[NG];
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-        const int ql = w * 32 + qg * 16 + c16;
+    for (int qg = 0; qg < NG; ++qg) {
+        const int ql = w * 16 * NG + qg * 16 + c16;
         qvalid[qg] = ql < q_count;
         if constexpr (MODE == MODE_CA) qrow[qg] = qbase + (qvalid[qg] ? ql : 0);
         else qrow[qg] = qvalid[qg] ? qlist[ql] : 0;
         B::load_q(qf[qg], qvalid[qg] ? qh + static_cast<size_t>(qrow[qg]) * D : nullptr, g);
         acc[qg].reset();
     }
-    const bool wave_active = w * 32 < q_count;
+    const bool wave_active = w * 16 * NG < q_count;
     if (fused) nk = ca_select_block<NT>(p, h, blockIdx.y, kidx);
 
     auto stage_idx = [&](int first) __attribute__((always_inline)) {
@@ -1001,7 +1004,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
             }
             B::load_tile(S, kidx, t + 2, sr, tid);
         }
-        if (wave_active) B::compute_tile2(acc, qf, sm, t * KT, nk, p.scale_log2, g, c16);
+        if (wave_active) B::template compute_tileg<NG>(acc, qf, sm, t * KT, nk, p.scale_log2, g, c16);
     };
     typename B::Stage A, Bs;
     A.slots = sslot[0];
@@ -1019,7 +1022,7 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
         step(Bs, t + 1);
     }
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
+    for (int qg = 0; qg < NG; ++qg) {
         const size_t qi = static_cast<size_t>(h) * p.Nq + qrow[qg];
         B::template finish<OT>(acc[qg], qf[qg], qvalid[qg], g, static_cast<OT*>(p.out) + qi * D,
                                (MODE == MODE_SA && p.lse) ? p.lse + qi : nullptr, nullptr, nullptr,
@@ -1027,10 +1030,12 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
     }
 }
 
-template <typename T, int D, int MODE, typename OT, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NG query groups per wave: two at two waves per SIMD; four at one (their
+// accumulators need the whole register file).
+template <typename T, int D, int MODE, typename OT, int NW, int NG = 2>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NG >= 4 ? 1 : 2, NG >= 4 ? 1 : 2)))
 void attn_wide_kernel(const AttnParams p) {
-    attn_wide_body<T, D, MODE, OT, NW>(p);
+    attn_wide_body<T, D, MODE, OT, NW, NG>(p);
 }
 
 // K+V modes keep two prefetched tiles of K and V in registers: up to 256
@@ -1064,7 +1069,7 @@ namespace {
 constexpr int kCaWaves = CA_WAVES;
 constexpr int kCaGroups = CA_GROUPS;
 template <typename T, int D>
-constexpr bool ca_grouped() { return kCaGroups == 2 && (sizeof(T) == 2 || D == 64); }
+constexpr bool ca_grouped() { return kCaGroups >= 2 && (sizeof(T) == 2 || D == 64); }
 template <typename T, int D>
 constexpr int ca_block_queries() { return 16 * (ca_grouped<T, D>() ? kCaGroups : 1) * kCaWaves; }
 
@@ -1103,7 +1108,8 @@ void attn_go(int H, const AttnParams& p, hipStream_t s) {
 #undef FASTAR_SA
     } else if constexpr (ca_grouped<T, D>()) {
         // (fp32 with d = 128 keeps one group per wave: two would spill)
-        hipLaunchKernelGGL((attn_wide_kernel<T, D, MODE_CA, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0, s, p);
+        hipLaunchKernelGGL((attn_wide_kernel<T, D, MODE_CA, OT, kCaWaves, kCaGroups>), grid, dim3(64 * kCaWaves),
+                           0, s, p);
     } else {
         hipLaunchKernelGGL((attn_kv_kernel<T, D, MODE_CA, false, OT, kCaWaves>), grid, dim3(64 * kCaWaves), 0,
                            s, p);

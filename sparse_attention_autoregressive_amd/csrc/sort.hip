@@ -46,9 +46,15 @@ __device__ __forceinline__ int set_count(const IdSet& s, int h, int& na) {
     return na + s.nb;
 }
 
-__device__ __forceinline__ int set_id(const IdSet& s, int h, int na, int e) {
-    return e < na ? s.a[static_cast<size_t>(h) * s.a_stride + e]
-                  : s.b[static_cast<size_t>(h) * s.b_stride + (e - na)];
+// The bucket of element min(e, n - 1) of a set with n >= 1 elements, read
+// with no branch (the row pointer is selected, then loaded): loads under a
+// branch each get their own wait, so a thread's loads would run one after
+// another instead of all in flight together.
+__device__ __forceinline__ int set_bucket(const IdSet& s, int h, int na, int n, int e, int B) {
+    e = min(e, n - 1);
+    const uint16_t* pa = s.a + static_cast<size_t>(h) * s.a_stride + e;
+    const uint16_t* pb = s.b + static_cast<size_t>(h) * s.b_stride + (e - na);
+    return (*(e < na ? pa : pb) >> s.shift) & (B - 1);
 }
 
 __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
@@ -59,13 +65,15 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
     int na;
     const int n = set_count(S, h, na);
     if (t * kSortTile >= n) return;
+    constexpr int R = kSortTile / 256;
+    int id[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) id[r] = set_bucket(S, h, na, n, t * kSortTile + r * 256 + threadIdx.x, B);
     for (int b = threadIdx.x; b < B; b += 256) cnt[b] = 0;
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kSortTile / 256; ++r) {
-        const int e = t * kSortTile + r * 256 + threadIdx.x;
-        if (e < n) atomicAdd(&cnt[(set_id(S, h, na, e) >> S.shift) & (B - 1)], 1);
-    }
+    for (int r = 0; r < R; ++r)
+        if (t * kSortTile + r * 256 + static_cast<int>(threadIdx.x) < n) atomicAdd(&cnt[id[r]], 1);
     __syncthreads();
     int* dst = O.hist + (static_cast<size_t>(h) * O.max_tiles + t) * B;
     for (int b = threadIdx.x; b < B; b += 256) dst[b] = cnt[b];
@@ -125,12 +133,14 @@ __device__ __forceinline__ void bucket_sums(const SortBufs& O, int h, int t, int
         const int b0 = tid * k;
 #pragma unroll 4
         for (int tt = 0; tt < ntiles; ++tt) {
+            int c[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c[j] = hh[static_cast<size_t>(tt) * B + b0 + min(j, k - 1)];   // no branch
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 if (j < k) {
-                    const int c = hh[static_cast<size_t>(tt) * B + b0 + j];
-                    s.total[j] += c;
-                    s.before[j] += tt < t ? c : 0;
+                    s.total[j] += c[j];
+                    s.before[j] += tt < t ? c[j] : 0;
                 }
             }
         }
@@ -271,10 +281,15 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     // the tile's ids, loaded first so their latency overlaps the histogram reads
     constexpr int R = kSortTile / 256;
     int idr[R];
+    if (!builder && t < ntiles) {                 // block uniform
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int e = t * kSortTile + r * 256 + tid;
-        idr[r] = (!builder && e < n) ? ((set_id(S, h, na, e) >> S.shift) & (B - 1)) : 0;
+        for (int r = 0; r < R; ++r) idr[r] = set_bucket(S, h, na, n, t * kSortTile + r * 256 + tid, B);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (t * kSortTile + r * 256 + tid >= n) idr[r] = 0;
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) idr[r] = 0;
     }
 
     // ---- the tile's base offsets (and, for the lead block, off); the part

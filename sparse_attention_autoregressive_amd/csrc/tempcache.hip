@@ -106,12 +106,21 @@ struct SlotRange {
                 key[k + 2] = ts_key(t.z); key[k + 3] = ts_key(t.w);
             }
         } else {
+            // clamped indices, no branch (n >= 1 when called)
 #pragma unroll
-            for (int k = 0; k < ITEMS; ++k) key[k] = (base + k < n) ? ts_key(ts[base + k]) : 0u;
+            for (int k = 0; k < ITEMS; ++k) key[k] = ts_key(ts[min(base + k, n - 1)]);
+#pragma unroll
+            for (int k = 0; k < ITEMS; ++k)
+                if (base + k >= n) key[k] = 0u;
         }
         const int left = n - base;
         const uint32_t valid = left >= ITEMS ? 0xFFFFFFFFu : (left > 0 ? (1u << left) - 1u : 0u);
-        cand = (valid && refr) ? (~refr[base >> 5] & valid) : valid;
+        if (refr) {                                     // uniform
+            const uint32_t rw = refr[min(base, n - 1) >> 5];           // no branch on the load
+            cand = ~rw & valid;
+        } else {
+            cand = valid;
+        }
     }
     __device__ __forceinline__ int slot(int k) const { return base + k; }
 };
@@ -135,8 +144,12 @@ struct SlotList {
         if (cached == c0) return;
         cached = c0;
         const int base = c0 + static_cast<int>(threadIdx.x) * ITEMS;
+        // clamped indices, no branch: all loads in flight at once (m >= 1)
 #pragma unroll
-        for (int k = 0; k < ITEMS; ++k) sl[k] = base + k < m ? list[base + k] : -1;
+        for (int k = 0; k < ITEMS; ++k) sl[k] = list[min(base + k, m - 1)];
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k)
+            if (base + k >= m) sl[k] = -1;
         cand = 0;
 #pragma unroll
         for (int k = 0; k < ITEMS; ++k) {
@@ -328,7 +341,9 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
     // Token data are held in registers, TOK_ITEMS consecutive tokens per
     // thread; with N <= TOK_CHUNK (one chunk) every phase reuses one load.
     // Each phase issues all its loads before its first store, so the round
-    // trips overlap (the stores could alias the loaded arrays).
+    // trips overlap (the stores could alias the loaded arrays).  Loads take
+    // clamped indices and are masked afterwards: a load under a branch gets
+    // its own wait, and the round trips would run one after another.
     int bi[TOK_ITEMS], up[TOK_ITEMS];
     float ci[TOK_ITEMS];
     int tok_c0 = -1;
@@ -337,9 +352,15 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         tok_c0 = c0;
         const int base = c0 + tid * TOK_ITEMS;
 #pragma unroll
-        for (int k = 0; k < TOK_ITEMS; ++k) bi[k] = (base + k < N) ? best[base + k] : -1;
+        for (int k = 0; k < TOK_ITEMS; ++k) bi[k] = best[min(base + k, N - 1)];
 #pragma unroll
-        for (int k = 0; k < TOK_ITEMS; ++k) ci[k] = (base + k < N) ? cosv[base + k] : 0.f;
+        for (int k = 0; k < TOK_ITEMS; ++k) ci[k] = cosv[min(base + k, N - 1)];
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k)
+            if (base + k >= N) {
+                bi[k] = -1;
+                ci[k] = 0.f;
+            }
     };
 
     const bool merge = p.grp_cnt != nullptr;                  // uniform
@@ -382,8 +403,10 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         const int base = c0 + tid * TOK_ITEMS;
         int cl[TOK_ITEMS];
 #pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k) cl[k] = claim[min(max(bi[k], 0), cap - 1)];   // no branch
+#pragma unroll
         for (int k = 0; k < TOK_ITEMS; ++k)
-            cl[k] = (base + k < N && is_matched(bi[k], ci[k], n, p.tau)) ? claim[bi[k]] : -2;
+            if (!(base + k < N && is_matched(bi[k], ci[k], n, p.tau))) cl[k] = -2;
         int local = 0, wins = 0;
 #pragma unroll
         for (int k = 0; k < TOK_ITEMS; ++k) {
@@ -452,14 +475,24 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
         for (int c0 = 0; c0 < N; c0 += TOK_CHUNK) {
             load_tok(c0);
             const int base = c0 + tid * TOK_ITEMS;
+            // the claim and offset reads take clamped indices (no branch), so
+            // each kind's reads are all in flight together
+            int wk[TOK_ITEMS], ok[TOK_ITEMS];
+#pragma unroll
+            for (int k = 0; k < TOK_ITEMS; ++k) wk[k] = claim[min(max(bi[k], 0), cap - 1)];
+#pragma unroll
+            for (int k = 0; k < TOK_ITEMS; ++k) {
+                const int w = min(max(wk[k], 0), N - 1);
+                ok[k] = LDSG ? gcnt[w] : goff_out[w];
+            }
+            if (N > TOK_CHUNK) {                        // uniform: positions from the workspace
+#pragma unroll
+                for (int k = 0; k < TOK_ITEMS; ++k) gp[k] = gpos[min(base + k, N - 1)];
+            }
 #pragma unroll
             for (int k = 0; k < TOK_ITEMS; ++k) {
                 const int i = base + k;
-                if (i < N && is_matched(bi[k], ci[k], n, p.tau)) {
-                    const int w = claim[bi[k]];
-                    const int off = LDSG ? gcnt[w] : goff_out[w];
-                    gmem[off + (N > TOK_CHUNK ? gpos[i] : gp[k])] = i;
-                }
+                if (i < N && is_matched(bi[k], ci[k], n, p.tau)) gmem[ok[k] + gp[k]] = i;
             }
         }
     }
@@ -487,10 +520,13 @@ __global__ __launch_bounds__(SEL_NT) void tc_select_kernel(const TcSelectParams 
 #pragma unroll
             for (int k = 0; k < TOK_ITEMS; ++k) up[k] = (base + k < N) ? upos[base + k] : -1;
         }
-        int dst[TOK_ITEMS];
+        int dst[TOK_ITEMS], evk[TOK_ITEMS];
+#pragma unroll
+        for (int k = 0; k < TOK_ITEMS; ++k)         // clamped: every load in flight at once
+            evk[k] = ev[min(max(up[k] - appended, 0), N - 1)];
 #pragma unroll
         for (int k = 0; k < TOK_ITEMS; ++k)
-            dst[k] = up[k] < 0 ? -2 : (up[k] < appended ? n + up[k] : ev[up[k] - appended]);
+            dst[k] = up[k] < 0 ? -2 : (up[k] < appended ? n + up[k] : evk[k]);
 #pragma unroll
         for (int k = 0; k < TOK_ITEMS; ++k)
             if (dst[k] != -2) dest[base + k] = (dst[k] >= 0 && dst[k] < cap) ? dst[k] : -1;
