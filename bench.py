@@ -167,6 +167,10 @@ def parse():
     ap.add_argument("--rollout", type=int, default=0, metavar="CHUNKS",
                     help="only run a rollout of CHUNKS chunks: per-chunk step latency and cache "
                          "size, next to a dense uncapped-cache baseline (one JSON line)")
+    ap.add_argument("--cpu-baseline-calls", action="store_true",
+                    help="only time the oracle per ABI call and per step (tiny and single-head "
+                         "configs) and per step over every head (Wan-1.3B and Wan-14B shapes), next "
+                         "to the library on the same inputs (one JSON line)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="only write the AnnSA traffic record from rocprofv3 counter CSVs "
                          "(FETCH_SIZE and WRITE_SIZE of a bench run, then of --copy-calibration 512)")
@@ -206,6 +210,9 @@ def main():
         return
     if args.size_sweep:
         size_sweep(args)
+        return
+    if args.cpu_baseline_calls:
+        cpu_baseline_calls(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -858,6 +865,156 @@ def cpu_baseline(cfg, seed, budget_s, line):
                       f"(hash + AnnSA + AnnCA + TempCache), "
                       f"{t_total:.1f} s on the host; BLAS threads {threads}, affinity cores {cores}",
             "ms_per_step_equiv": t_total / heads * cfg.H * 1e3}
+
+
+def cpu_baseline_calls(args):
+    """The cpu_baseline leg per call: the oracle (unchanged) timed per ABI call
+    and per step on the tiny and single-head configs, and per step over every
+    head on the Wan-1.3B and Wan-14B shapes, each next to the library's time
+    for the same work on the same inputs.  Library calls are eager (host
+    launch cost included; H = 1 calls are launch-bound), each averaged over
+    20 calls between two events; every commit and every step gets a cache
+    copy made before timing starts.  The library's step is the two-stream
+    ``AttentionStep`` (eagerly at the small configs, as a graph replay at the
+    Wan shapes, as the main bench line times it).  One JSON line."""
+    import math
+    import numpy as np
+    import torch
+    import sparse_attention_autoregressive_amd as fa
+    from oracle import (ann_hash as o_hash, annca as o_annca, annsa as o_annsa, attention_step,
+                        bucket_sort as o_sort, key_context, tempcache_commit, tempcache_top1)
+    from sparse_attention_autoregressive_amd.step import AttentionStep
+    from workloads import CONFIGS, f32_to_bf16_bits, make_step
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:                                        # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    reps = 20
+
+    def cpu_ms(fn, n=3):
+        fn()                                                 # untimed: first-call costs
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        return (time.perf_counter() - t0) / n * 1e3
+
+    def gpu_ms(fns):
+        """``fns``: one callable per timed call (a list, so each may use its own copy)."""
+        fns[0]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for fn in fns[1:]:
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (len(fns) - 1)
+
+    def inputs(cfg, st):
+        def to_dev(a):
+            if cfg.dtype == "bf16":
+                return torch.from_numpy(f32_to_bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+        t = {k: to_dev(getattr(st, k)) for k in ("q", "k_cur", "v_cur", "kp", "vp")}
+        t["planes"] = torch.from_numpy(st.planes).to(dev)
+        t["cache"] = fa.KVCache.from_keys(to_dev(st.cache_k), to_dev(st.cache_v),
+                                          torch.from_numpy(st.cache_ts).to(dev),
+                                          torch.from_numpy(st.n_valid).to(dev), t["planes"])
+        return t
+
+    out = {"calls": [], "steps": []}
+    for name in ("tiny_f32", "single_bf16"):
+        cfg = CONFIGS[name]
+        st = make_step(cfg, args.seed)
+        P, fl, d = cfg.P, cfg.frame_len, cfg.d
+        scale = 1.0 / math.sqrt(d)
+        n = int(st.n_valid[0])
+        q, kc, vc, kp, vp, pl = st.q[0], st.k_cur[0], st.v_cur[0], st.kp[0], st.vp[0], st.planes[0]
+        cid = o_hash(st.cache_k[0], pl)[0]
+        qi, ki, pi = (o_hash(x, pl)[0] for x in (q, kc, kp))
+        K, V, kid = key_context(st.cache_k[0], st.cache_v[0], cid, n, kc, vc, ki)
+        best, bcos = tempcache_top1(q, qi, st.cache_k[0], cid, n)[:2]
+        cache0 = {"k": st.cache_k[0], "v": st.cache_v[0], "ids": cid, "ts": st.cache_ts[0]}
+        tau32 = float(np.float32(cfg.tau))
+        oracle = {
+            "ann_hash (Q, K_cur, prompt keys)": lambda: [o_hash(x, pl) for x in (q, kc, kp)],
+            "bucket sort (query ids, key ids)": lambda: (o_sort(qi, P), o_sort(kid, P)),
+            "annsa_forward (attention)": lambda: o_annsa(q, qi, K, V, kid, scale),
+            "TempCache top-1 (fused into annsa_forward on the GPU)":
+                lambda: tempcache_top1(q, qi, st.cache_k[0], cid, n),
+            "annca_forward": lambda: o_annca(q, qi, fl, kp, vp, pi, scale),
+            "tempcache_update (commit on the given top-1)":
+                lambda: tempcache_commit({k: v.copy() for k, v in cache0.items()}, n, kc, vc, ki,
+                                         best, bcos, tau32, st.step),
+        }
+        t = inputs(cfg, st)
+        ids = {k: torch.empty(1, x.shape[1], dtype=torch.int16, device=dev)
+               for k, x in (("q", t["q"]), ("k", t["k_cur"]), ("p", t["kp"]))}
+        fa.ann_hash_batch([t["q"], t["k_cur"], t["kp"]], t["planes"], ids=[ids["q"], ids["k"], ids["p"]])
+        keyset = torch.cat([t["cache"].ids[:, :n], ids["k"]], dim=1).contiguous()
+        sa = lambda: fa.annsa_forward(t["q"], ids["q"], t["k_cur"], t["v_cur"], ids["k"], P, cache=t["cache"],
+                                      search=True)
+        _, _, gbest, gcos = sa()
+        copies = [t["cache"].clone() for _ in range(reps + 1)]
+        gpu = {
+            "ann_hash (Q, K_cur, prompt keys)": [lambda: fa.ann_hash_batch(
+                [t["q"], t["k_cur"], t["kp"]], t["planes"], ids=[ids["q"], ids["k"], ids["p"]])] * (reps + 1),
+            "bucket sort (query ids, key ids)": [lambda: (fa.bucket_sort(ids["q"], P),
+                                                          fa.bucket_sort(keyset, P))] * (reps + 1),
+            "annsa_forward (attention)": [sa] * (reps + 1),
+            "annca_forward": [lambda: fa.annca_forward(t["q"], ids["q"], fl, t["kp"], t["vp"], ids["p"], P)]
+                             * (reps + 1),
+            "tempcache_update (commit on the given top-1)": [
+                (lambda c=c: fa.tempcache_update(c, t["q"], ids["q"], t["k_cur"], t["v_cur"], ids["k"], P,
+                                                 cfg.tau, st.step, best_in=gbest, cos_in=gcos))
+                for c in copies],
+        }
+        for call, fn in oracle.items():
+            row = {"config": name, "call": call, "oracle_ms": cpu_ms(fn)}
+            if call in gpu:
+                row["gpu_ms"] = gpu_ms(gpu[call])
+                row["ratio"] = row["oracle_ms"] / row["gpu_ms"]
+            out["calls"].append(row)
+            print(json.dumps({"progress": row}), file=sys.stderr, flush=True)
+        cpu_step = cpu_ms(lambda: attention_step(st.q, st.k_cur, st.v_cur, st.cache_k, st.cache_v, cid[None],
+                                                 st.cache_ts, st.n_valid, st.planes, st.kp, st.vp, fl, cfg.tau,
+                                                 st.step))
+        s = AttentionStep(cfg.H, cfg.Nq, d, cfg.cap, P, fl, cfg.L, cfg.tau, device=dev)
+        scopies = [t["cache"].clone() for _ in range(reps + 1)]
+        g = gpu_ms([(lambda c=c: s(c, t["q"], t["k_cur"], t["v_cur"], t["kp"], t["vp"], t["planes"], st.step))
+                    for c in scopies])
+        out["steps"].append({"config": name, "heads": cfg.H, "oracle_ms": cpu_step, "gpu_ms": g,
+                             "gpu_form": "eager, two streams", "ratio": cpu_step / g})
+        print(json.dumps({"progress": out["steps"][-1]}), file=sys.stderr, flush=True)
+        del t, copies, scopies
+    for name in ("wan13_bf16", "wan14_bf16"):
+        cfg = CONFIGS[name]
+        t_cpu = 0.0
+        for h in range(cfg.H):                   # one head at a time: the oracle's memory stays small
+            st = make_step(cfg, args.seed, heads=range(h, h + 1))
+            cid = o_hash(st.cache_k[0], st.planes[0])[0]
+            t0 = time.perf_counter()
+            attention_step(st.q, st.k_cur, st.v_cur, st.cache_k, st.cache_v, cid[None], st.cache_ts,
+                           st.n_valid, st.planes, st.kp, st.vp, cfg.frame_len, cfg.tau, st.step)
+            t_cpu += time.perf_counter() - t0
+        st = make_step(cfg, args.seed)
+        t = inputs(cfg, st)
+        s = AttentionStep(cfg.H, cfg.Nq, cfg.d, cfg.cap, cfg.P, cfg.frame_len, cfg.L, cfg.tau, device=dev)
+        graphs = [s.graph(t["cache"].clone(), t["q"], t["k_cur"], t["v_cur"], t["kp"], t["vp"], t["planes"],
+                          st.step) for _ in range(reps + 1)]
+        g = gpu_ms([gr.replay for gr in graphs])
+        out["steps"].append({"config": name, "heads": cfg.H, "oracle_ms": t_cpu * 1e3, "gpu_ms": g,
+                             "gpu_form": "graph replay, two streams", "ratio": t_cpu * 1e3 / g})
+        print(json.dumps({"progress": out["steps"][-1]}), file=sys.stderr, flush=True)
+        del t, graphs
+    out.update({"kind": "oracle", "cores": min(cores, threads) if threads else cores,
+                "blas_threads": threads, "affinity_cores": cores, "seed": args.seed,
+                "oracle_reps": "3 calls averaged after one untimed call (small configs); one pass over every head (Wan shapes)"})
+    print(json.dumps({"cpu_baseline_calls": out}), flush=True)
 
 
 if __name__ == "__main__":
