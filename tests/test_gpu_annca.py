@@ -128,3 +128,23 @@ def test_annca_prompt_lengths_around_the_fused_selection(L):
     keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, cfg.P, f"annca pruned L={L}",
                          out_dtype=torch.bfloat16)
     assert 0 < keep.mean() < 0.3
+
+
+@pytest.mark.parametrize("frame_len,Fq", [(201, 3), (7, 5), (1, 4)])
+def test_annca_unaligned_frames(frame_len, Fq):
+    """Frames whose query ids start at any offset: the selection inside the
+    attention blocks reads them in 16-byte loads with a scalar run before and
+    after the aligned part (201 ids: both; 7 and 1: the whole frame scalar),
+    and every frame confines its queries to a few buckets so the keep masks
+    differ from frame to frame."""
+    require_gpu()
+    prep = prepared("single_bf16", frame_len=frame_len, Fq=Fq, Fc=2, P=5)
+    cfg = prep["cfg"]
+    assert cfg.Nq == frame_len * Fq
+    rng = np.random.default_rng(frame_len)
+    q_ids = np.empty_like(prep["q_ids"])
+    for f in range(Fq):
+        q_ids[:, f * frame_len:(f + 1) * frame_len] = rng.integers(3 * f, 3 * f + 4, size=(cfg.H, frame_len))
+    kp_ids = rng.integers(0, cfg.B, size=prep["kp_ids"].shape).astype(np.uint16)
+    keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, cfg.P, f"unaligned frames {frame_len}x{Fq}")
+    assert 0 < keep.mean() < 0.5
