@@ -14,11 +14,13 @@
 // permuted consistently on both operands -- lane group g sums dimensions
 // g*D/4 .. (g+1)*D/4-1 -- so every lane reads contiguous runs of both.
 //
-// A block of 4 waves takes 64 vectors (16 per wave, held in registers) and
-// streams the codebook through LDS 64 codewords at a time, with each
+// fp32 vectors: a block of 4 waves takes 64 vectors (16 per wave, held in
+// registers) and streams the codebook through LDS 64 codewords at a time, with each
 // codeword's |c|^2 / 2 (padding codewords past B get +inf).  LDS rows are
 // padded by 4 floats so the 16 rows one quarter-wave reads fall on distinct
 // banks.  The same pass can write |x|.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -165,9 +167,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const QzSets sets, const 
 // time as the three bf16 parts, with |c|^2 / 2 summed in fp32 from the fp32
 // values while they are split.  Lane group g supplies dimensions
 // 32k + 8g .. 32k + 8g + 7 of k-step k on both operands.
-// 16-vector groups per wave of the bf16 kernel (128 vectors per block):
-// measured 14.2-14.5 us per launch at the Wan-1.3B chunk's 4680 x 12 vectors
-// and 128 codewords, against 15.6 with four groups and 20.2-20.5 with one.
+// 16-vector groups per wave of the bf16 kernel (128 vectors per block;
+// codebooks above 128 codewords, and any codebook before the resident form
+// below): measured 14.2-14.5 us per launch at the Wan-1.3B chunk's 4680 x 12
+// vectors and 128 codewords, against 15.6 with four groups and 20.2-20.5 with
+// one.
 constexpr int QZB_GPW = 2;
 
 template <int D>
@@ -314,6 +318,219 @@ __global__ __launch_bounds__(256) void quantize_bf16_kernel(const QzSets sets, c
     }
 }
 
+// Codebooks of up to 128 codewords (bf16 vectors): the block stages its
+// head's whole codebook, split, once (3 x 128 rows in dynamic LDS) and then
+// streams 256-vector tiles of every set of that head through it, blocks of a
+// head taking every BPH-th tile.  Each wave holds two 16-vector groups, so
+// every codebook fragment read from LDS feeds two MFMAs, and takes the
+// codewords two 16-row blocks at a time (rows past B are zero with an
+// infinite |c|^2, so an odd block count pads safely): twelve independent
+// MFMA chains per step.  A tile's vectors are loaded while the previous
+// tile's products run (two register buffers named in alternate steps, so no
+// copy waits on a load in flight).
+// 8 waves of two groups (two waves per SIMD); measured at the Wan-1.3B
+// chunk's two sets: 20.8-21.1 us, against 24.6-25.2 for 4 waves of four
+// groups or of two (one wave per SIMD).
+#ifndef QZR_WAVES
+#define QZR_WAVES 8
+#endif
+#ifndef QZR_GROUPS
+#define QZR_GROUPS 2
+#endif
+constexpr int QZR_NT = 64 * QZR_WAVES;
+constexpr int QZR_GPW = QZR_GROUPS;            // 16-vector groups per wave
+constexpr int QZR_TV = QZR_NT / 64 * 16 * QZR_GPW;   // vectors per tile
+constexpr int QZR_MAXB = 128;
+
+template <int D>
+__global__ __launch_bounds__(QZR_NT)
+__attribute__((amdgpu_waves_per_eu(QZR_WAVES >= 8 ? 2 : 1, QZR_WAVES >= 8 ? 2 : 1)))
+void quantize_bf16_resident_kernel(const QzSets sets, int nsets,
+                                                                        const float* __restrict__ cb, int B,
+                                                                        int bph) {
+    constexpr int KS = D / 32;
+    constexpr int PSTR = D + 8;
+    extern __shared__ __align__(16) uint16_t qz_lds[];
+    uint16_t* cp0 = qz_lds;
+    uint16_t* cp1 = cp0 + QZR_MAXB * PSTR;
+    uint16_t* cp2 = cp1 + QZR_MAXB * PSTR;
+    float* hn = reinterpret_cast<float*>(cp2 + QZR_MAXB * PSTR);
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    const int nblk2 = ((B + 31) / 32) * 2;              // 16-row blocks, even
+
+    // the head's tiles, set after set
+    int tstart[kHashBatch + 1];
+    tstart[0] = 0;
+#pragma unroll
+    for (int s = 0; s < kHashBatch; ++s)
+        tstart[s + 1] = tstart[s] + (s < nsets ? (sets.N[s] + QZR_TV - 1) / QZR_TV : 0);
+    const int ntiles = tstart[kHashBatch];
+
+    // one tile's vector fragments: this lane's two vectors, 16-byte loads with
+    // a clamped row (masked at the write), all in flight together
+    struct Tile {
+        u32x4 x[QZR_GPW][KS];
+        int set, i0;
+    };
+    auto fetch = [&](Tile& t, int tile) __attribute__((always_inline)) {
+        int s = 0;
+#pragma unroll
+        for (int k = 1; k < kHashBatch; ++k) s += (k < nsets && tile >= tstart[k]) ? 1 : 0;
+        t.set = s;
+        const int Ns = sets.N[s];
+        t.i0 = (tile - tstart[s]) * QZR_TV + w * 16 * QZR_GPW + c16;
+        const uint16_t* xs = static_cast<const uint16_t*>(sets.x[s]);
+#pragma unroll
+        for (int q = 0; q < QZR_GPW; ++q) {
+            const uint16_t* row = xs + (static_cast<size_t>(h) * Ns + min(t.i0 + 16 * q, Ns - 1)) * D + g * 8;
+#pragma unroll
+            for (int k = 0; k < KS; ++k) t.x[q][k] = *reinterpret_cast<const u32x4*>(row + 32 * k);
+        }
+    };
+    auto finish = [&](const Tile& t) __attribute__((always_inline)) {
+        const int Ns = sets.N[t.set];
+        float best[QZR_GPW];
+        int bidx[QZR_GPW];
+#pragma unroll
+        for (int q = 0; q < QZR_GPW; ++q) {
+            best[q] = -__builtin_huge_valf();
+            bidx[q] = 0x7FFFFFFF;
+        }
+#pragma unroll 1
+        for (int blk = 0; blk < nblk2; blk += 2) {
+            bf16x8_t a[2][3][KS];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int k = 0; k < KS; ++k) {
+                    const int off = ((blk + bb) * 16 + c16) * PSTR + 32 * k + 8 * g;
+                    a[bb][0][k] = *reinterpret_cast<const bf16x8_t*>(&cp0[off]);
+                    a[bb][1][k] = *reinterpret_cast<const bf16x8_t*>(&cp1[off]);
+                    a[bb][2][k] = *reinterpret_cast<const bf16x8_t*>(&cp2[off]);
+                }
+            f32x4 acc[2][QZR_GPW][3];
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int q = 0; q < QZR_GPW; ++q)
+#pragma unroll
+                    for (int part = 0; part < 3; ++part) acc[bb][q][part] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int q = 0; q < QZR_GPW; ++q) {
+                        const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, t.x[q][k]);
+#pragma unroll
+                        for (int part = 0; part < 3; ++part)
+                            acc[bb][q][part] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[bb][part][k], bv,
+                                                                                      acc[bb][q][part], 0, 0, 0);
+                    }
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const float4 hb = *reinterpret_cast<const float4*>(&hn[(blk + bb) * 16 + 4 * g]);
+                const float hv[4] = {hb.x, hb.y, hb.z, hb.w};
+#pragma unroll
+                for (int q = 0; q < QZR_GPW; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float sc = (acc[bb][q][0][r] + (acc[bb][q][1][r] + acc[bb][q][2][r])) - hv[r];
+                        if (sc > best[q]) {
+                            best[q] = sc;
+                            bidx[q] = (blk + bb) * 16 + 4 * g + r;
+                        }
+                    }
+            }
+        }
+        float* norms = sets.norms[t.set];
+#pragma unroll
+        for (int q = 0; q < QZR_GPW; ++q) {
+            float bq = best[q];
+            int iq = bidx[q];
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ob = __shfl_xor(bq, off);
+                const int oi = __shfl_xor(iq, off);
+                if (ob > bq || (ob == bq && oi < iq)) {
+                    bq = ob;
+                    iq = oi;
+                }
+            }
+            float sq = 0.f;
+            if (norms) {
+#pragma unroll
+                for (int k = 0; k < KS; ++k)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float lo = __uint_as_float(t.x[q][k][j] << 16);
+                        const float hi = __uint_as_float(t.x[q][k][j] & 0xFFFF0000u);
+                        sq = __builtin_fmaf(lo, lo, sq);
+                        sq = __builtin_fmaf(hi, hi, sq);
+                    }
+                sq += __shfl_xor(sq, 16);
+                sq += __shfl_xor(sq, 32);
+            }
+            const int i = t.i0 + 16 * q;
+            if (i < Ns && g == 0) {
+                sets.ids[t.set][static_cast<size_t>(h) * Ns + i] = static_cast<uint16_t>(iq);
+                if (norms) norms[static_cast<size_t>(h) * Ns + i] = __builtin_sqrtf(sq);
+            }
+        }
+    };
+
+    Tile A, Bt;
+    int tile = blockIdx.x;
+    if (tile < ntiles) fetch(A, tile);                 // block uniform
+    // stage the codebook: thread (row r, quarter part) splits D/4 elements
+#pragma unroll
+    for (int rp = tid; rp < QZR_MAXB * 4; rp += QZR_NT) {
+        const float* cbh = cb + static_cast<size_t>(h) * B * D;
+        constexpr int EPT = D / 4;
+        const int r = rp >> 2, part = rp & 3;
+        const bool in = r < B;
+        const float* src = cbh + static_cast<size_t>(min(r, B - 1)) * D + part * EPT;
+        float sq = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPT; e += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; k += 4) {
+                const float4 f = *reinterpret_cast<const float4*>(src + e + k);
+                v[k] = in ? f.x : 0.f; v[k + 1] = in ? f.y : 0.f; v[k + 2] = in ? f.z : 0.f; v[k + 3] = in ? f.w : 0.f;
+            }
+            uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                sq = __builtin_fmaf(v[k], v[k], sq);
+                const uint32_t hi = __float_as_uint(v[k]) & 0xFFFF0000u;
+                const float r1 = v[k] - __uint_as_float(hi);
+                const uint32_t mid = __float_as_uint(r1) & 0xFFFF0000u;
+                const uint32_t lo = __float_as_uint(r1 - __uint_as_float(mid)) & 0xFFFF0000u;
+                if ((k & 1) == 0) { hw[k / 2] = hi >> 16; mw[k / 2] = mid >> 16; lw[k / 2] = lo >> 16; }
+                else { hw[k / 2] |= hi; mw[k / 2] |= mid; lw[k / 2] |= lo; }
+            }
+            const int off = r * PSTR + part * EPT + e;
+            *reinterpret_cast<u32x4*>(&cp0[off]) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            *reinterpret_cast<u32x4*>(&cp1[off]) = u32x4{mw[0], mw[1], mw[2], mw[3]};
+            *reinterpret_cast<u32x4*>(&cp2[off]) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        }
+        sq += __shfl_xor(sq, 1);
+        sq += __shfl_xor(sq, 2);
+        if (part == 0) hn[r] = in ? 0.5f * sq : __builtin_huge_valf();
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (; tile < ntiles; tile += 2 * bph) {            // block uniform
+        fetch(Bt, min(tile + bph, ntiles - 1));         // past the end: a repeated tile, not written
+        finish(A);
+        if (tile + bph >= ntiles) break;
+        fetch(A, min(tile + 2 * bph, ntiles - 1));
+        finish(Bt);
+    }
+}
+
 hipError_t launch_quantize_batch(int count, const void* const* x, const int* N, uint16_t* const* ids,
                                  float* const* norms, bool bf16, int H, int d, const float* codebook, int B,
                                  hipStream_t s) {
@@ -336,7 +553,21 @@ hipError_t launch_quantize_batch(int count, const void* const* x, const int* N, 
         sets.norms[i] = nullptr;
     }
     timer_begin("ann_quantize", s);
-    if (bf16) {
+    if (bf16 && B <= QZR_MAXB) {
+        int ntiles = 0;
+        for (int i = 0; i < used; ++i) ntiles += (sets.N[i] + QZR_TV - 1) / QZR_TV;
+        // one block per CU (the staged codebook takes most of its LDS): the
+        // head's blocks share its tiles
+        const int bph = std::max(1, std::min(ntiles, 256 / std::max(1, H)));
+        const int pstr = d + 8;
+        const size_t lds = static_cast<size_t>(3 * QZR_MAXB * pstr) * 2 + QZR_MAXB * 4;
+        if (d == 64)
+            hipLaunchKernelGGL((quantize_bf16_resident_kernel<64>), dim3(bph, H), dim3(QZR_NT), lds, s, sets, used,
+                               codebook, B, bph);
+        else
+            hipLaunchKernelGGL((quantize_bf16_resident_kernel<128>), dim3(bph, H), dim3(QZR_NT), lds, s, sets, used,
+                               codebook, B, bph);
+    } else if (bf16) {
         const dim3 gb((nmax + 64 * QZB_GPW - 1) / (64 * QZB_GPW), H, used);
         if (d == 64)
             hipLaunchKernelGGL((quantize_bf16_kernel<64>), gb, dim3(256), 0, s, sets, codebook, B);
