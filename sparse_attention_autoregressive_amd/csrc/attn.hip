@@ -63,6 +63,9 @@
 #ifndef CA_GROUPS
 #define CA_GROUPS 2              // 16-query groups per AnnCA wave
 #endif
+#ifndef CA_XCD
+#define CA_XCD 1                 // AnnCA blocks of one (head, frame) on one XCD
+#endif
 
 namespace fastar {
 
@@ -178,6 +181,18 @@ struct Blk {
         } else {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) q.f[ks] = row ? reinterpret_cast<const float*>(row)[ks * 4 + g] : 0.f;
+        }
+    }
+    // The same from a row that is always there: no branch, so the compiler
+    // can count these loads when a later wait needs only older ones.
+    static __device__ __forceinline__ void load_q_row(QF& q, const T* row, int g) {
+        if constexpr (BF) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                q.b[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(row + ks * 32 + 8 * g));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) q.f[ks] = reinterpret_cast<const float*>(row)[ks * 4 + g];
         }
     }
     // 1/|q| from the fragments (all lanes of the wave take part).
@@ -306,6 +321,18 @@ struct Blk {
     // scale, and leaves the probabilities in ``s``.  The running max is kept in
     // raw score units; the scale folds into the exponent:
     // p = 2^(s*c - m*c), c = scale * log2(e) > 0.
+    // The maximum of x over lanes i, i^16, i^32 and i^48 -- the four lane
+    // groups that hold one query's keys.  Each lane swap (gfx950's
+    // v_permlane32_swap / v_permlane16_swap) leaves x of the lane and of its
+    // partner in the two results, in the VALU, without an LDS round trip.
+    static __device__ __forceinline__ float max_over_groups(float x) {
+        const uint32_t u = __float_as_uint(x);
+        const auto a32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        const float y = fmaxf(__uint_as_float(a32[0]), __uint_as_float(a32[1]));
+        const uint32_t v = __float_as_uint(y);
+        const auto a16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return fmaxf(__uint_as_float(a16[0]), __uint_as_float(a16[1]));
+    }
     static __device__ __forceinline__ void softmax_update(Acc& a, f32x4 (&s)[4], bool full, int kbase, int nk,
                                                           float scale_log2, int g) {
         if (!full) {
@@ -319,8 +346,7 @@ struct Blk {
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4)
             tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb4][0], s[kb4][1]), fmaxf(s[kb4][2], s[kb4][3])));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = max_over_groups(tmax);
         const float m_new = fmaxf(a.m, tmax);
         const float c = scale_log2;
         const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
@@ -672,71 +698,111 @@ struct Blk {
 // are a few KB, read through L2); the frame's first block also writes the
 // keep mask and count.  Needs L <= KCH, so the list is a single staged chunk.
 // Returns the number of kept tokens.
+// AnnCA block coordinates (head h, frame f, query block c) from the block id.
+// The chip hands blocks to its eight XCDs in turn by linear id, and each XCD
+// has its own L2.  The id is re-mapped (a bijection on [0, blocks)) so that
+// consecutive logical blocks -- the query blocks of one (head, frame), which
+// all gather the same selected prompt rows -- run on one XCD and re-read
+// those rows from its L2.
+__device__ __forceinline__ void ca_block_coords(int& h, int& f, int& c) {
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+#if CA_XCD
+    constexpr int X = 8;
+    const int nb = gx * gy * gridDim.z;
+    const int per = nb / X, rem = nb % X, x = b % X;
+    const int l = x * per + min(x, rem) + b / X;
+#else
+    const int l = b;
+#endif
+    c = l % gx;
+    f = (l / gx) % gy;
+    h = l / (gx * gy);
+}
+
+// AnnCA prompt selection inside the attention block (prompts of up to
+// kCaFusedMaxL tokens): a prompt token is kept when some query of the frame
+// falls in its bucket (FAST-AR blog, "2. AnnCA").  In two parts, so that the
+// id loads are issued ahead of the query rows and do not queue behind them:
+// ca_select_issue loads the prompt ids (clamped indices, no branch) and the
+// frame's query ids (16-byte loads of 8 ids; the at most 7 ids before and
+// after the aligned part one per thread); ca_select_finish marks each
+// query's bucket in a byte-per-bucket LDS table, then one block scan over the
+// threads' kept counts writes the kept prompt positions, in ascending order,
+// to kidx (padded with 0 to a whole key tile).
 template <int NT>
-__device__ __forceinline__ int ca_select_block(const AttnParams& p, int h, int f, int* kidx) {
+struct CaSel {
+    static constexpr int PU = KCH / NT;          // consecutive prompt tokens per thread
+    uint32_t pid[PU];
+    uint32_t id_pre, id_tail;
+    u32x4 r[4];
+    const u32x4* qv;
+    const uint16_t* qi;
+    int n, pre, nv, tail;
+};
+
+template <int NT>
+__device__ __forceinline__ void ca_select_issue(const AttnParams& p, int h, int f, CaSel<NT>& S) {
     static_assert(kCaFusedMaxL == KCH, "the kept list fills at most one index chunk");
-    constexpr int PU = KCH / NT;                 // consecutive prompt tokens per thread
-    __shared__ uint32_t bits[kCaMaxBuckets / 32];
+    const int tid = threadIdx.x, L = p.L;
+    const uint16_t* pi = p.ca_kp_ids + static_cast<size_t>(h) * L;
+    if (L > 0) {
+#pragma unroll
+        for (int u = 0; u < CaSel<NT>::PU; ++u) S.pid[u] = pi[min(tid * CaSel<NT>::PU + u, L - 1)];
+    }
+    S.qi = p.q_ids + static_cast<size_t>(h) * p.Nq + static_cast<size_t>(f) * p.frame_len;
+    S.n = p.frame_len;
+    S.pre = min(S.n, static_cast<int>(((16u - (reinterpret_cast<uintptr_t>(S.qi) & 15u)) & 15u) >> 1));
+    S.nv = (S.n - S.pre) >> 3;
+    S.tail = S.pre + S.nv * 8;
+    S.qv = reinterpret_cast<const u32x4*>(S.qi + S.pre);
+    S.id_pre = S.qi[min(tid, S.n - 1)];
+    S.id_tail = S.qi[min(S.tail + tid, S.n - 1)];
+    if (S.nv > 0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) S.r[u] = S.qv[min(u * NT + tid, S.nv - 1)];
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ int ca_select_finish(const AttnParams& p, int h, int f, int* kidx, bool first,
+                                                CaSel<NT>& S) {
+    constexpr int PU = CaSel<NT>::PU;
+    __shared__ __align__(16) uint8_t flag[kCaMaxBuckets];
     __shared__ int sscan[NT / kWave];
     const int tid = threadIdx.x, L = p.L;
     const uint32_t mask = static_cast<uint32_t>(p.ca_buckets - 1);
     const size_t row = static_cast<size_t>(h) * p.F + f;
-    const bool first = blockIdx.x == 0;
-    // Every id load is issued before the first is used: the prompt ids
-    // (clamped indices, no branch), then the frame's query ids in 16-byte
-    // loads of 8 ids; the ends before and after the aligned part (at most 7
-    // ids each) are read one id per thread.
-    const uint16_t* pi = p.ca_kp_ids + static_cast<size_t>(h) * L;
-    uint32_t pid[PU];
-    if (L > 0) {
-#pragma unroll
-        for (int u = 0; u < PU; ++u) pid[u] = pi[min(tid * PU + u, L - 1)];
-    }
-    const uint16_t* qi = p.q_ids + static_cast<size_t>(h) * p.Nq + static_cast<size_t>(f) * p.frame_len;
-    const int n = p.frame_len;
-    const int pre = min(n, static_cast<int>(((16u - (reinterpret_cast<uintptr_t>(qi) & 15u)) & 15u) >> 1));
-    const int nv = (n - pre) >> 3, tail = pre + nv * 8;
-    const u32x4* qv = reinterpret_cast<const u32x4*>(qi + pre);
-    const uint32_t id_pre = qi[min(tid, n - 1)];
-    const uint32_t id_tail = qi[min(tail + tid, n - 1)];
-    u32x4 r[4];
-    auto load = [&](int v0) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = qv[min(v0 + u * NT + tid, nv - 1)];
-    };
-    auto mark = [&](uint32_t id) __attribute__((always_inline)) {
-        id &= mask;
-        atomicOr(&bits[id >> 5], 1u << (id & 31));
-    };
+    // Every query of a bucket stores the same 1, so the stores need no
+    // atomics (many queries share a bucket: atomics on a bitmap word would
+    // serialise them).
     auto mark_all = [&](int v0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (v0 + u * NT + tid < nv) {
+            if (v0 + u * NT + tid < S.nv) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    mark(r[u][e] & 0xffffu);
-                    mark(r[u][e] >> 16);
+                    flag[S.r[u][e] & mask] = 1;
+                    flag[(S.r[u][e] >> 16) & mask] = 1;
                 }
             }
         }
     };
-    if (nv > 0) load(0);
-    for (int i = tid; i < (p.ca_buckets + 31) / 32; i += NT) bits[i] = 0;
+    for (int i = tid; i < (p.ca_buckets + 3) / 4; i += NT) reinterpret_cast<uint32_t*>(flag)[i] = 0;
     __syncthreads();
-    if (nv > 0) mark_all(0);
-    for (int v0 = 4 * NT; v0 < nv; v0 += 4 * NT) {
-        load(v0);
+    if (S.nv > 0) mark_all(0);
+    for (int v0 = 4 * NT; v0 < S.nv; v0 += 4 * NT) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) S.r[u] = S.qv[min(v0 + u * NT + tid, S.nv - 1)];
         mark_all(v0);
     }
-    if (tid < pre) mark(id_pre);
-    if (tid < n - tail) mark(id_tail);
+    if (tid < S.pre) flag[S.id_pre & mask] = 1;
+    if (tid < S.n - S.tail) flag[S.id_tail & mask] = 1;
     __syncthreads();
-    // one block scan over the threads' counts places each kept token
     int keep[PU], cnt = 0;
 #pragma unroll
     for (int u = 0; u < PU; ++u) {
-        const uint32_t id = pid[u] & mask;
-        keep[u] = tid * PU + u < L ? static_cast<int>((bits[id >> 5] >> (id & 31)) & 1u) : 0;
+        keep[u] = tid * PU + u < L ? static_cast<int>(flag[S.pid[u] & mask]) : 0;
         cnt += keep[u];
     }
     int total;
@@ -785,12 +851,14 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
     // key list in ``kidx`` from here on
     const bool fused = MODE == MODE_CA && p.ca_fused != 0;
     if constexpr (MODE == MODE_CA) {
-        h = blockIdx.z;
-        const int f = blockIdx.y, c = blockIdx.x;
+        int f, c;
+        ca_block_coords(h, f, c);
         qbase = f * p.frame_len + c * QT;
         q_count = min(QT, p.frame_len - c * QT);
         if (fused) {
-            nk = ca_select_block<NT>(p, h, f, kidx);
+            CaSel<NT> S;
+            ca_select_issue<NT>(p, h, f, S);
+            nk = ca_select_finish<NT>(p, h, f, kidx, c == 0, S);
             klist = nullptr;
         } else {
             nk = p.ca_cnt[h * p.F + f];
@@ -927,15 +995,15 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    int h, q_count, nk, qbase = 0;
+    int h, q_count, nk, qbase = 0, ca_f = 0, ca_c = 0;
     const int32_t* qlist = nullptr;
     const int32_t* klist;
-    // as in attn_body; here the selection runs once the query rows are on
-    // their way
+    // as in attn_body; here the selection's id loads are issued first, then
+    // the query rows, and the selection runs while the rows are on their way
     const bool fused = MODE == MODE_CA && p.ca_fused != 0;
     if constexpr (MODE == MODE_CA) {
-        h = blockIdx.z;
-        const int f = blockIdx.y, c = blockIdx.x;
+        ca_block_coords(h, ca_f, ca_c);
+        const int f = ca_f, c = ca_c;
         qbase = f * p.frame_len + c * QT;
         q_count = min(QT, p.frame_len - c * QT);
         if (fused) {
@@ -968,6 +1036,8 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
             kfirst[u] = nk > 0 ? klist[r < nk ? r : nk - 1] : 0;
         }
     }
+    CaSel<NT> csel;
+    if (fused) ca_select_issue<NT>(p, h, ca_f, csel);
     const T* qh = static_cast<const T*>(p.q) + static_cast<size_t>(h) * p.Nq * D;
     typename B::QF qf[NG];
     typename B::Acc acc[NG];
@@ -977,13 +1047,19 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
     for (int qg = 0; qg < NG; ++qg) {
         const int ql = w * 16 * NG + qg * 16 + c16;
         qvalid[qg] = ql < q_count;
-        if constexpr (MODE == MODE_CA) qrow[qg] = qbase + (qvalid[qg] ? ql : 0);
-        else qrow[qg] = qvalid[qg] ? qlist[ql] : 0;
-        B::load_q(qf[qg], qvalid[qg] ? qh + static_cast<size_t>(qrow[qg]) * D : nullptr, g);
+        if constexpr (MODE == MODE_CA) {
+            // a query past the frame's end reads the frame's first row (its
+            // output is never written), so the row loads carry no branch
+            qrow[qg] = qbase + (qvalid[qg] ? ql : 0);
+            B::load_q_row(qf[qg], qh + static_cast<size_t>(qrow[qg]) * D, g);
+        } else {
+            qrow[qg] = qvalid[qg] ? qlist[ql] : 0;
+            B::load_q(qf[qg], qvalid[qg] ? qh + static_cast<size_t>(qrow[qg]) * D : nullptr, g);
+        }
         acc[qg].reset();
     }
     const bool wave_active = w * 16 * NG < q_count;
-    if (fused) nk = ca_select_block<NT>(p, h, blockIdx.y, kidx);
+    if (fused) nk = ca_select_finish<NT>(p, h, ca_f, kidx, ca_c == 0, csel);
 
     auto stage_idx = [&](int first) __attribute__((always_inline)) {
         for (int i = tid; i < KCH; i += NT) {
