@@ -7,7 +7,9 @@
   without the eviction candidates listed on the side stream;
 * a captured step, replayed several times with eager work (cache restore,
   output poisoning) and synchronisation between the replays, reproduces the
-  eager step bit for bit on every replay.
+  eager step bit for bit on every replay;
+* several steps captured into one graph (one per cache copy, or chained on
+  one cache) reproduce the eager steps bit for bit.
 """
 import numpy as np
 import pytest
@@ -122,3 +124,74 @@ def test_graph_replays_match_eager(name):
         torch.cuda.synchronize()
         g.replay()
         _assert_same(ref, _snapshot(two, cg), f"replay {r}")
+
+
+def _restore_and_poison(s, caches, bases):
+    for c, b in zip(caches, bases):
+        for k in ("k", "v", "ids", "ts", "n_valid", "knorm"):
+            getattr(c, k).copy_(getattr(b, k))
+    for buf in (s.o_sa, s.lse, s.o_ca, s.best_cos):
+        buf.fill_(float("nan"))
+    for buf in (s.best, s.keep, s.keep_count, *s.ids.values()):
+        buf.fill_(-1 if buf.dtype != torch.uint8 else 255)
+    torch.cuda.synchronize()
+
+
+def _cache_state(cache):
+    torch.cuda.synchronize()
+    return {k: getattr(cache, k).clone() for k in ("k", "v", "ids", "ts", "n_valid", "knorm")}
+
+
+@pytest.mark.parametrize("name", ["single_bf16", "wan13_bf16"])
+def test_steps_in_one_graph_match_eager(name):
+    """Several steps captured into one graph, as the bench times them and as
+    a model's layers would be captured: (a) one step per cache copy, (b) three
+    chained steps on one cache, each seeing the commit of the one before.
+    Every replay (eager restores and poisoned outputs between them)
+    reproduces the eager steps bit for bit: every cache, and the outputs of
+    the last step."""
+    require_gpu()
+    cfg = CONFIGS[name]
+    st, t, base = _inputs(cfg, 0)
+    s = _stepper(cfg, overlap=True)
+    steps = [st.step, st.step + 1, st.step + 2]
+
+    # (a) one step on each of three cache copies
+    eager = [base.clone() for _ in steps]
+    for c in eager:
+        _run(s, c, t, st.step)
+    ref_out = _snapshot(s, eager[-1])
+    ref_caches = [_cache_state(c) for c in eager]
+    del eager
+    copies = [base.clone() for _ in steps]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in copies:
+            _run(s, c, t, st.step)
+    for r in range(2):
+        _restore_and_poison(s, copies, [base] * len(copies))
+        g.replay()
+        _assert_same(ref_out, _snapshot(s, copies[-1]), f"copies, replay {r}")
+        for i, c in enumerate(copies):
+            _assert_same(ref_caches[i], _cache_state(c), f"copies, replay {r}, cache {i}")
+    del g, copies
+
+    # (b) three chained steps on one cache
+    ce = base.clone()
+    states = []
+    for sn in steps:
+        _run(s, ce, t, sn)
+        states.append(_cache_state(ce))
+    ref_out = _snapshot(s, ce)
+    assert not torch.equal(states[0]["ts"], states[-1]["ts"]), "the chained steps must change the cache"
+    del ce
+    cg = base.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for sn in steps:
+            _run(s, cg, t, sn)
+    for r in range(2):
+        _restore_and_poison(s, [cg], [base])
+        g.replay()
+        _assert_same(ref_out, _snapshot(s, cg), f"chained, replay {r}")
+        _assert_same(states[-1], _cache_state(cg), f"chained, replay {r}, cache")
