@@ -177,6 +177,9 @@ def parse():
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="only write the AnnSA traffic record from rocprofv3 counter CSVs "
                          "(FETCH_SIZE and WRITE_SIZE of a bench run, then of --copy-calibration 512)")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="only replay the K timed steps captured in one graph (after a W-step "
+                         "warm-up graph): the headline timing alone, for kernel traces (one JSON line)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (the plain copy whose "
                          "FETCH_SIZE / WRITE_SIZE counters scale the traffic figures), then exit")
@@ -216,6 +219,9 @@ def main():
         return
     if args.cpu_baseline_calls:
         cpu_baseline_calls(args)
+        return
+    if args.graph_only:
+        graph_only(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -591,6 +597,50 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds, line)
     print(json.dumps(line), flush=True)
+
+
+def graph_only(args):
+    """The headline timing alone: W warm-up steps and then the K timed steps,
+    each captured into one graph (one pristine cache copy per step), the
+    timed graph replayed once."""
+    import torch
+
+    import sparse_attention_autoregressive_amd as fa
+    from sparse_attention_autoregressive_amd.step import AttentionStep
+    from workloads import CONFIGS, make_step
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = make_step(cfg, args.seed)
+    to_dev = _device(cfg, dev)
+    t = {k: to_dev(getattr(st, k)) for k in ("q", "k_cur", "v_cur", "kp", "vp")}
+    t["planes"] = torch.from_numpy(st.planes).to(dev)
+    base = fa.KVCache.from_keys(to_dev(st.cache_k), to_dev(st.cache_v), torch.from_numpy(st.cache_ts).to(dev),
+                                torch.from_numpy(st.n_valid).to(dev), t["planes"])
+    out_dt = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    s = AttentionStep(cfg.H, cfg.Nq, cfg.d, cfg.cap, cfg.P, cfg.frame_len, cfg.L, cfg.tau, out_dtype=out_dt,
+                      device=dev)
+
+    def steps_graph(caches):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in caches:
+                s(c, t["q"], t["k_cur"], t["v_cur"], t["kp"], t["vp"], t["planes"], st.step)
+        return g
+
+    warm = [base.clone() for _ in range(max(1, args.warmup))]
+    timed = [base.clone() for _ in range(args.steps)]
+    g_warm, g_steps = steps_graph(warm), steps_graph(timed)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_steps.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"graph_only": True, "config": cfg.name, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step_graph": e0.elapsed_time(e1) / args.steps}), flush=True)
 
 
 def _device(cfg, dev):
