@@ -86,6 +86,9 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(SortArgs a) {
 // the parts meet in LDS and thread b keeps bucket b (k = 1).  With B > 256
 // thread i keeps buckets i*k .. i*k+k-1 (k = B / 256) and sums all tiles.
 constexpr int kTileLoads = 32;
+// Keys per tile of the attention kernels: an item's cost is its key tiles,
+// which order the work list (only the order, never a result, depends on it).
+constexpr int kItemKeyTile = 64;
 // Tiles per head above which the histograms are scanned in a launch of their
 // own.  Measured over 12 heads of 128 buckets: at 75 tiles the two-launch
 // form takes 21.9 us and the three-launch form 27.8; at 293 tiles 77 and
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
         if (lead && offp && tid == 0) offp[B] = total;
     }
 
-    // ---- the attention work list: items in decreasing order of key count
+    // ---- the attention work list: items in decreasing order of key tiles
     // (ties: lower bucket first), so the longest items start first.  Built by
     // the builder block from both sets' histograms (its ``start`` and
     // ``tot`` above are the query set's; after a scan, both sets' off).
@@ -372,18 +375,49 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
         // index; with B <= 256 the 256 / B threads of a bucket split the count
         int rank[4], tiles[4];
         if (k == 1) {
-            const int parts = 256 / B, part = tid / B, b = tid % B;
-            if (tid < B) racc[tid] = 0;
-            __syncthreads();
-            if (part < parts) {
-                const int per = (B + parts - 1) / parts, kn = kcnt[b];
-                int r = 0;
-                for (int c = part * per; c < min(B, (part + 1) * per); ++c) {
-                    const int kc = kcnt[c];
-                    r += (kc > kn) || (kc == kn && c < b);
-                }
-                atomicAdd(&racc[b], r);
+            // B <= 256, bucket b = thread b.  Items are ordered by their key
+            // tiles (an item's cost; 255 and more share the top class),
+            // larger first, ties by bucket: a stable counting sort of the
+            // buckets by class.  Each wave finds the lanes of its own class
+            // with one ballot per class bit; per-wave class counts in LDS
+            // carry the order across waves.
+            int* chist = racc;                       // [256] buckets per class
+            int* wcls = base;                        // [4][256] buckets per wave and class
+            const int b = tid, w = tid / kWave;
+            const bool has = b < B;
+            const int cls = has ? min((kcnt[b] + kItemKeyTile - 1) / kItemKeyTile, 255) : 0;
+            chist[tid] = 0;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) wcls[v * 256 + tid] = 0;
+            uint64_t same = __ballot(has);
+#pragma unroll
+            for (int bit = 0; bit < 8; ++bit) {
+                const bool on = (cls >> bit) & 1;
+                const uint64_t m = __ballot(on);
+                same &= on ? m : ~m;
             }
+            const int in_wave = __popcll(same & lanemask_lt());
+            __syncthreads();
+            if (has && in_wave == 0) {               // one lane per (wave, class)
+                const int c = __popcll(same);
+                wcls[w * 256 + cls] = c;
+                atomicAdd(&chist[cls], c);
+            }
+            __syncthreads();
+            // buckets in larger classes: a scan over the classes, largest first
+            const int hc = chist[255 - tid];
+            int tot_c;
+            const int above = block_exclusive_scan<256>(hc, smem, tot_c);
+            __syncthreads();
+            chist[255 - tid] = above;
+            __syncthreads();
+            int r = 0;
+            if (has) {
+                r = chist[cls] + in_wave;
+                for (int v = 0; v < w; ++v) r += wcls[v * 256 + cls];
+            }
+            __syncthreads();
+            if (has) racc[b] = r;
             __syncthreads();
         }
 #pragma unroll
@@ -395,9 +429,10 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
                 if (k == 1) {
                     rank[j] = racc[b];
                 } else {
-                    const int kn = kcnt[b];
+                    auto cls_of = [](int kc) { return min((kc + kItemKeyTile - 1) / kItemKeyTile, 255); };
+                    const int kn = cls_of(kcnt[b]);
                     for (int c = 0; c < B; ++c) {
-                        const int kc = kcnt[c];
+                        const int kc = cls_of(kcnt[c]);
                         rank[j] += (kc > kn) || (kc == kn && c < b);
                     }
                 }
