@@ -56,6 +56,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+HBM_TARGET_FRAC = 0.60         # targets: hash / sort / compaction at 60% of HBM peak,
+MFMA_TARGET_FRAC = 0.40        # bucket attention at 40% of the bf16 MFMA peak
 
 # HBM bytes per launch of the AnnSA attention kernel, from rocprofv3's
 # FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) scaled by what the same
@@ -424,6 +426,20 @@ def main():
     kernel_gbs = {k: {"bytes": step_bytes[k], "GB/s": step_bytes[k] / (step_ms[k] * 1e-3) / 1e9,
                       "frac_hbm_peak": step_bytes[k] / (step_ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS}
                   for k in step_bytes if step_ms.get(k)}
+    # the HBM target for hash, sort and compaction (60% of peak), stated
+    # beside each such kernel's fraction
+    for k in ("ann_hash", "sort", "annca_select"):
+        if k in kernel_gbs:
+            kernel_gbs[k]["target_frac_hbm_peak"] = HBM_TARGET_FRAC
+            kernel_gbs[k]["target_met"] = kernel_gbs[k]["frac_hbm_peak"] >= HBM_TARGET_FRAC
+    # bucket attention against the bf16 MFMA peak (kept-pair products,
+    # 4 d flops per pair), with its 40% target
+    kernel_mfma = {}
+    for k, pairs in (("annsa_attn", sa_pairs), ("annca_attn", ca_pairs)):
+        if step_ms.get(k):
+            tf = 4.0 * d * pairs / (step_ms[k] * 1e-3) / 1e12
+            kernel_mfma[k] = {"kept_pair_TFLOP/s": tf, "frac_bf16_mfma_peak": tf / BF16_PEAK_TFLOPS,
+                              "target_frac": MFMA_TARGET_FRAC, "target_met": tf / BF16_PEAK_TFLOPS >= MFMA_TARGET_FRAC}
 
     # ---- the same step on a mean-merged cache (Lemma 5.1 of the FAST-AR
     # summary): slots carry group sizes (uniform 1..32), AnnSA shifts their
@@ -586,7 +602,7 @@ def main():
         "roofline": roofline,
         "latency_ms": latency,
         "kernel_ms": kernel_ms, "kernel_launches_per_step": kernel_launches,
-        "kernel_gbs": kernel_gbs, "eviction_list": eviction_list,
+        "kernel_gbs": kernel_gbs, "kernel_mfma": kernel_mfma, "eviction_list": eviction_list,
         "kept_pairs": {"annsa": sa_pairs, "annca": ca_pairs,
                        "annsa_frac_of_dense": sa_pairs / (H * Nq * (cap + Nq))},
         "mean_merge": merge,
