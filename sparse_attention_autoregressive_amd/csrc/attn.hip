@@ -66,6 +66,9 @@
 #ifndef CA_XCD
 #define CA_XCD 1                 // AnnCA blocks of one (head, frame) on one XCD
 #endif
+#ifndef SA_XCD_RUN
+#define SA_XCD_RUN 4             // AnnSA work items dealt to the XCDs in runs of this many (1: in turn)
+#endif
 
 namespace fastar {
 
@@ -720,6 +723,32 @@ __device__ __forceinline__ void ca_block_coords(int& h, int& f, int& c) {
     h = l / (gx * gy);
 }
 
+// AnnSA / TOP1 block coordinates (head h, work item) from the block id of a
+// (heads, max_items) grid.  Blocks go to the eight XCDs in turn by linear id,
+// each XCD with its own L2; a bucket whose queries fill several items has
+// those items next to one another in its head's list, and they gather the
+// same key rows.  So runs of SA_XCD_RUN consecutive items of one head are
+// dealt to one XCD, where they run one after another and the later ones find
+// the rows in that L2.  Runs are dealt to the XCDs in turn, in the list's
+// order (heads fastest, longest items first); the blocks past the last full
+// round of eight runs (the end of every list: short items and padding) keep
+// the plain order.  A bijection on the grid: max_items is a multiple of 8.
+static_assert(SA_XCD_RUN >= 1 && 8 % SA_XCD_RUN == 0, "runs must divide the item count's multiple of 8");
+__device__ __forceinline__ void sa_block_coords(int& h, int& item) {
+    const int H = gridDim.x, M = gridDim.y;
+    const int b = blockIdx.x + H * blockIdx.y;
+    constexpr int G = SA_XCD_RUN, X = 8;
+    const int full = (H * M / G / X) * X * G;    // blocks in full rounds
+    int l = b;
+    if (b < full) {
+        const int s = b / X;
+        l = ((s / G) * X + b % X) * G + s % G;
+    }
+    const int run = l / G;
+    h = run % H;
+    item = (run / H) * G + l % G;
+}
+
 // AnnCA prompt selection inside the attention block (prompts of up to
 // kCaFusedMaxL tokens): a prompt token is kept when some query of the frame
 // falls in its bucket (FAST-AR blog, "2. AnnCA").  In two parts, so that the
@@ -865,8 +894,8 @@ __device__ __forceinline__ void attn_body(const AttnParams& p) {
             klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
         }
     } else {
-        h = blockIdx.x;                          // heads fastest: the longest items
-        const int item = blockIdx.y;            // of every head dispatch first
+        int item;
+        sa_block_coords(h, item);               // heads fastest: the longest items of every head first
         const int4 it = p.items[static_cast<size_t>(h) * p.max_items + item];
         if (it.y <= 0) return;
         q_count = it.y;
@@ -1014,8 +1043,9 @@ __device__ __forceinline__ void attn_wide_body(const AttnParams& p) {
             klist = p.ca_idx + (static_cast<size_t>(h) * p.F + f) * p.L;
         }
     } else {
-        h = blockIdx.x;                          // heads fastest, as in attn_body
-        const int4 it = p.items[static_cast<size_t>(h) * p.max_items + blockIdx.y];
+        int item;
+        sa_block_coords(h, item);               // as in attn_body
+        const int4 it = p.items[static_cast<size_t>(h) * p.max_items + item];
         if (it.y <= 0) return;
         q_count = it.y;
         qlist = p.qperm + static_cast<size_t>(h) * p.qperm_stride + it.x;
