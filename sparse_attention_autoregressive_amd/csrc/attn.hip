@@ -77,6 +77,13 @@ namespace {
 constexpr int KT = 64;            // keys per LDS tile
 constexpr int KCH = 1024;         // key indices staged in LDS at a time
 constexpr float kNegInf = -__builtin_huge_valf();
+// Online softmax: the exponent's reference (a running maximum) moves only when
+// a score passes it by more than this many powers of two (log2 units; 0
+// rescales whenever the maximum grows).
+#ifndef SOFTMAX_RESCALE_LOG2
+#define SOFTMAX_RESCALE_LOG2 8
+#endif
+constexpr float kRescaleLog2 = SOFTMAX_RESCALE_LOG2;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -117,6 +124,12 @@ struct Blk {
     static constexpr int E = TL::E, CPR = TL::CPR, EPC = TL::EPC;
     static constexpr int STRK = TL::STRK, STRV = TL::STRV, ROWB = TL::ROWB;
     static constexpr int NDB = TL::NDB, NKS = TL::NKS;
+    // AnnCA (no lse output) lets the softmax reference lag (kRescaleLog2) and,
+    // with bf16 products, sums the probabilities as rounded for the PV
+    // product; AnnSA keeps the exact running maximum and fp32 sums, so that
+    // its lse carries no bf16 rounding.
+    static constexpr bool LAZY = MODE == MODE_CA;
+    static constexpr bool RSUM = LAZY && BF;
 
     // B operand of S^T: lane holds Q[query l%16][k-slice of group g].
     struct QF {
@@ -138,7 +151,7 @@ struct Blk {
     // hold disjoint keys and are merged at the end).
     struct Acc {
         f32x4 o[HAS_V ? NDB : 1];
-        float m, l;                 // softmax: raw-score max, sum
+        float m, l;                 // softmax: reference maximum (raw score units), sum
         float bc;                   // search: best dot/|k|
         int bs;                     //         and its slot
         __device__ __forceinline__ void reset() {
@@ -320,10 +333,19 @@ struct Blk {
     }
 
     // Online softmax of one 16-query group over a 64-key tile (one query per
-    // lane): masks the keys past nk, updates the running max, sum and output
-    // scale, and leaves the probabilities in ``s``.  The running max is kept in
-    // raw score units; the scale folds into the exponent:
-    // p = 2^(s*c - m*c), c = scale * log2(e) > 0.
+    // lane): masks the keys past nk, updates the reference maximum, sum and
+    // output scale, and leaves the probabilities in ``s``.  The reference m is
+    // kept in raw score units; the scale folds into the exponent:
+    // p = 2^(s*c - m*c), c = scale * log2(e) > 0.  m follows the running
+    // maximum lazily: it moves (and the sum and output are rescaled) only on
+    // a query's first keys or when the tile's maximum passes it by more than
+    // kRescaleLog2 in the exponent, so p <= 2^kRescaleLog2 and most tiles skip
+    // the rescale (LAZY; otherwise m is the running maximum itself).  Output,
+    // sum and lse share the one reference, so the result is the softmax's up
+    // to rounding.  With RSUM the caller sums the probabilities as rounded for
+    // the PV product (bf16_sum8), so that the normaliser matches the
+    // numerator: with a lagging reference the largest p is not 1, and its
+    // rounding would otherwise show in the output.
     // The maximum of x over lanes i, i^16, i^32 and i^48 -- the four lane
     // groups that hold one query's keys.  Each lane swap (gfx950's
     // v_permlane32_swap / v_permlane16_swap) leaves x of the lane and of its
@@ -352,7 +374,8 @@ struct Blk {
         tmax = max_over_groups(tmax);
         const float m_new = fmaxf(a.m, tmax);
         const float c = scale_log2;
-        const float mc = (m_new == kNegInf) ? 0.f : m_new * c;
+        const float m_ref = (a.m == kNegInf || (m_new - a.m) * c > (LAZY ? kRescaleLog2 : 0.f)) ? m_new : a.m;
+        const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
         float psum = 0.f;
 #pragma unroll
         for (int kb4 = 0; kb4 < 4; ++kb4) {
@@ -360,17 +383,25 @@ struct Blk {
             for (int r = 0; r < 4; ++r) {
                 const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb4][r], c, -mc));
                 s[kb4][r] = e;
-                psum += e;
+                if constexpr (!RSUM) psum += e;
             }
         }
-        if (__ballot(m_new > a.m) != 0) {                   // some lane's max grew
+        if (__ballot(m_ref > a.m) != 0) {                   // some lane's reference moved
             const float alpha = (a.m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(a.m, c, -mc));
             a.l *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) a.o[db] *= alpha;
         }
-        a.l += psum;
-        a.m = m_new;
+        if constexpr (!RSUM) a.l += psum;
+        a.m = m_ref;
+    }
+    // acc plus the eight bf16 values of ``p`` (exact products with 1, fp32 sums).
+    static __device__ __forceinline__ float bf16_sum8(const bf16x8_t& p, float acc) {
+        const bf16x2_t ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), ones, acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), ones, acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), ones, acc, false);
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), ones, acc, false);
     }
 
     // One 64-key tile (keys kbase.. of an item with nk keys, the first na of
@@ -481,6 +512,7 @@ struct Blk {
                         pb[r] = static_cast<__bf16>(s[2 * kg][r]);
                         pb[4 + r] = static_cast<__bf16>(s[2 * kg + 1][r]);
                     }
+                    if constexpr (RSUM) a.l = bf16_sum8(pb, a.l);
                     // lane j of group g addresses V[kg*32 + 4g + j/4][db*16 + 4(j%4)]
                     const T* vb0 = &sm.Vs[(kg * 32 + 4 * g + (c16 >> 2)) * STRV + 4 * (c16 & 3)];
                     v4i16 lo[NDB], hi[NDB];
@@ -561,6 +593,9 @@ struct Blk {
                         pb[qg][r] = static_cast<__bf16>(s[qg][2 * kg][r]);
                         pb[qg][4 + r] = static_cast<__bf16>(s[qg][2 * kg + 1][r]);
                     }
+#pragma unroll
+                for (int qg = 0; qg < NG; ++qg)
+                    if constexpr (RSUM) a[qg].l = bf16_sum8(pb[qg], a[qg].l);
                 const T* vb0 = &sm.Vs[(kg * 32 + 4 * g + (c16 >> 2)) * STRV + 4 * (c16 & 3)];
                 v4i16 lo[NDB], hi[NDB];
 #pragma unroll
@@ -718,9 +753,9 @@ __device__ __forceinline__ void ca_block_coords(int& h, int& f, int& c) {
 #else
     const int l = b;
 #endif
-    c = l % gx;
-    f = (l / gx) % gy;
-    h = l / (gx * gy);
+    c = __builtin_amdgcn_readfirstlane(l % gx);             // uniform: scalar registers
+    f = __builtin_amdgcn_readfirstlane((l / gx) % gy);
+    h = __builtin_amdgcn_readfirstlane(l / (gx * gy));
 }
 
 // AnnSA / TOP1 block coordinates (head h, work item) from the block id of a
@@ -745,8 +780,10 @@ __device__ __forceinline__ void sa_block_coords(int& h, int& item) {
         l = ((s / G) * X + b % X) * G + s % G;
     }
     const int run = l / G;
-    h = run % H;
-    item = (run / H) * G + l % G;
+    // uniform values out of a vector division: back to scalar registers, so
+    // the head's row pointers stay scalar too
+    h = __builtin_amdgcn_readfirstlane(run % H);
+    item = __builtin_amdgcn_readfirstlane((run / H) * G + l % G);
 }
 
 // AnnCA prompt selection inside the attention block (prompts of up to

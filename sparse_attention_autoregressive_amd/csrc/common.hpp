@@ -7,6 +7,7 @@
 namespace fastar {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16 bytes as a native vector: copies are vector loads/stores (HIP's uint4 is
 // a struct whose copies become memcpy, which keeps register arrays of it in

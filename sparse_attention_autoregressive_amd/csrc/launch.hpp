@@ -113,7 +113,7 @@ struct AttnParams {
     const uint16_t* ida = nullptr;    // [H][a_rows] ids of source a
     const uint16_t* idb = nullptr;    // [H][b_rows] ids of source b
     float* st_o = nullptr;            // [H][Nq][D] unnormalised output
-    float* st_m = nullptr;            // [H][Nq] running max (raw score units)
+    float* st_m = nullptr;            // [H][Nq] softmax reference maximum (raw score units)
     float* st_l = nullptr;            // [H][Nq] running sum
     float* st_bc = nullptr;           // [H][Nq] search: best dot/|k|
     int32_t* st_bs = nullptr;         // [H][Nq] search: its slot
