@@ -2,14 +2,17 @@
 bit-exact, outputs within tolerance; workloads as generated (nearly every
 prompt token kept), constructed ids that prune most of the prompt, frames with
 nothing kept, an empty prompt, fp32 / bf16 at d = 64 and 128 with frames
-that end in a partial block, and prompts on either side of the longest one
-whose selection the attention blocks do themselves."""
+that end in a partial block, prompts on either side of the longest one
+whose selection the attention blocks do themselves, and logits that grow or
+shrink by hundreds of powers of two along the kept list (the softmax's
+reference then moves, or stays, across many tiles)."""
 import numpy as np
 import pytest
 import torch
 
 import sparse_attention_autoregressive_amd as fa
 from oracle import annca as o_annca
+from workloads.gen import bf16_round
 from tests.gpu_util import assert_attention_close, dev, dev_ids, prepared, require_gpu
 
 pytestmark = pytest.mark.gpu
@@ -148,3 +151,36 @@ def test_annca_unaligned_frames(frame_len, Fq):
     kp_ids = rng.integers(0, cfg.B, size=prep["kp_ids"].shape).astype(np.uint16)
     keep = run_and_check(prep, q_ids.astype(np.uint16), kp_ids, cfg.P, f"unaligned frames {frame_len}x{Fq}")
     assert 0 < keep.mean() < 0.5
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_bf16"])
+@pytest.mark.parametrize("ramp", [1.0, -1.0])
+def test_annca_logits_spanning_many_tiles(name, ramp):
+    """Every prompt token kept (P = 0), scale 1, and prompt keys that move
+    along the queries' mean direction with the token index: the logits of a
+    query grow (ramp 1, for most queries) or shrink (ramp -1) by about 300 in
+    natural units over the kept list, so the softmax's reference has to move
+    many times, or never after the first tile, while the outputs stay within
+    tolerance of the oracle."""
+    require_gpu()
+    prep = prepared(name)
+    st, cfg = prep["step"], prep["cfg"]
+    rng = np.random.default_rng(7)
+    L = st.kp.shape[1]
+    kp = np.empty_like(st.kp)
+    for h in range(cfg.H):
+        u = st.q[h].mean(0)
+        u = u / np.linalg.norm(u)
+        proj = st.q[h] @ u
+        c = ramp * 300.0 / max(float(np.abs(proj).mean()), 1e-3) * (np.arange(L) / L - 0.5)
+        kp[h] = c[:, None] * u[None, :] + 0.05 * rng.standard_normal((L, cfg.d))
+    if cfg.dtype == "bf16":
+        kp = bf16_round(kp.astype(np.float32))
+    kp = kp.astype(np.float32)
+    zq = np.zeros_like(prep["q_ids"])
+    zk = np.zeros((cfg.H, L), np.uint16)
+    out, keep, _ = fa.annca_forward(dev(st.q, cfg.dtype), dev_ids(zq), cfg.frame_len, dev(kp, cfg.dtype),
+                                    dev(st.vp, cfg.dtype), dev_ids(zk), 0, scale=1.0)
+    assert keep.cpu().numpy().all()
+    Os = [o_annca(st.q[h], zq[h], cfg.frame_len, kp[h], st.vp[h], zk[h], 1.0)[0] for h in range(cfg.H)]
+    assert_attention_close(out, np.stack(Os), cfg.dtype, f"annca ramp {ramp} {name}")
