@@ -82,7 +82,8 @@ def kernel_sources_sha256() -> str:
 
 
 def measured_traffic(config: str, out_dtype: str):
-    """(bytes per launch, note) for the AnnSA kernel of this build, or (None, why not)."""
+    """(bytes per launch, note) for the AnnSA kernel built from the current
+    sources (their SHA-256 must match the record's), or (None, why not)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -135,7 +136,7 @@ def ingest_counters(paths):
            "sources": KERNEL_SOURCES, "sources_sha256": kernel_sources_sha256(),
            "commands": [
                "cd /tmp && export TMPDIR=/tmp",
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/<run>/FETCH_SIZE -o FETCH_SIZE "
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/FETCH_SIZE -o FETCH_SIZE "
                "-- python3 <repo>/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-merge --no-multi --no-quantize",
                "rocprofv3 --pmc WRITE_SIZE (the same bench command)",
                "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python3 <repo>/bench.py --copy-calibration 512",
