@@ -10,7 +10,9 @@
 //                inside its tile (wave ballots on the P id bits give the rank
 //                among equal ids of the wave; LDS counters tagged by round
 //                carry it across waves and rounds), and perm[base + rank] =
-//                index.  For a (queries, keys) pair of sets one more block
+//                index (from kSortStagedTiles tiles per head on, the tile's
+//                indices go through LDS in bucket order first, so that the
+//                stores form runs).  For a (queries, keys) pair of sets one more block
 //                per head builds the attention work list (one item per bucket
 //                and 64- or 256-query slice, longest key lists first) beside the
 //                tiles.  The tile's ids are loaded before the histograms, so
@@ -39,6 +41,7 @@ struct SortArgs {
     int P;
     int builder_block;            // grid x index of the work-list blocks, or -1
     int scanned;                  // hist holds per-tile prefixes and off is written (scan launch)
+    int staged;                   // perm written from LDS in bucket order (coalesced runs)
 };
 
 __device__ __forceinline__ int set_count(const IdSet& s, int h, int& na) {
@@ -94,6 +97,13 @@ constexpr int kItemKeyTile = 64;
 // form takes 21.9 us and the three-launch form 27.8; at 293 tiles 77 and
 // 57.8.  (The step's 37 tiles keep the two-launch form.)
 constexpr int kSortScanTiles = 128;
+// Tiles per head from which the scatter writes perm from LDS in bucket order
+// (coalesced runs); below it the scattered 4-byte stores are not what bounds
+// the launch, and the extra scan and barriers would only add latency.
+#ifndef SORT_STAGED_TILES
+#define SORT_STAGED_TILES 64
+#endif
+constexpr int kSortStagedTiles = SORT_STAGED_TILES;
 
 struct BucketSums {
     int before[4], total[4];
@@ -482,6 +492,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
     const int lane = lane_id();
     const int w = threadIdx.x / kWave;
     int32_t* perm = O.perm + static_cast<size_t>(h) * O.perm_stride;
+    int rk[R];                                    // the elements' ranks, for the staged write-out
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int e = t * kSortTile + r * 256 + threadIdx.x;
@@ -511,11 +522,54 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
             rank = pre + rank_w;
         }
         __syncthreads();
+        rk[r] = rank;
         if (valid) {
             if (last) run[id] = rank + 1;
-            perm[base[id] + rank] = e;
+            if (!a.staged) perm[base[id] + rank] = e;
         }
     }
+    if (!a.staged) return;                        // block uniform
+
+    // Staged write-out: run[b] now counts bucket b in this tile.  Its
+    // exclusive scan places the tile's elements in bucket order in LDS (each
+    // with its global position), and consecutive threads then write
+    // consecutive positions of one bucket: runs of stores instead of 4-byte
+    // scatter.  wcnt is free again and holds the two arrays.
+    __syncthreads();
+    {
+        const int k = (B + 255) / 256, b0 = tid * k;
+        int mine = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mine += (j < k && b0 + j < B) ? run[b0 + j] : 0;
+        int tot;
+        int off = block_exclusive_scan<256>(mine, smem, tot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < k && b0 + j < B) {
+                const int c = run[b0 + j];
+                run[b0 + j] = off;                // tile-local start of bucket b0 + j
+                off += c;
+            }
+        }
+    }
+    __syncthreads();
+    int* s_pos = reinterpret_cast<int*>(wcnt[0]);
+    int* s_e = reinterpret_cast<int*>(wcnt[1]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = t * kSortTile + r * 256 + threadIdx.x;
+        if (e < n) {
+            const int id = idr[r];
+            const int lp = run[id] + rk[r];
+            if (lp >= 0 && lp < kSortTile) {      // in range whenever the counts are right
+                s_pos[lp] = base[id] + rk[r];
+                s_e[lp] = e;
+            }
+        }
+    }
+    __syncthreads();
+    const int tile_n = min(kSortTile, n - t * kSortTile);
+    for (int i = threadIdx.x; i < tile_n; i += 256) perm[s_pos[i]] = s_e[i];
 }
 
 hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const SortBufs* bufs,
@@ -541,6 +595,7 @@ hipError_t launch_bucket_sort(int H, int P, int nsets, const IdSet* sets, const 
     bool offs = true;
     for (int i = 0; i < nsets; ++i) offs = offs && bufs[i].off != nullptr;
     a.scanned = (max_tiles > kSortScanTiles && offs) ? 1 : 0;
+    a.staged = max_tiles >= kSortStagedTiles ? 1 : 0;
     if (max_tiles > 0) {
         timer_begin("sort_hist", s);
         hipLaunchKernelGGL(sort_hist_kernel, dim3(max_tiles, H, nsets), dim3(256), 0, s, a);
