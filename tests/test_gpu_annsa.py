@@ -6,7 +6,8 @@ empty buckets, bf16 outputs and run-to-run determinism.  Few buckets (at least
 checked at 2, 4 and 8 buckets, with a partly filled cache and with buckets
 that hold queries but no keys.  Calls that ask for the fused TempCache search
 also have its (slot, cosine) checked against the oracle's top-1 under the
-tie protocol (``assert_top1_matches``)."""
+tie protocol (``assert_top1_matches``).  Head counts of 3 and 5 give grids
+where only part of the blocks take the XCD-run order."""
 
 import numpy as np
 import pytest
@@ -77,6 +78,25 @@ def test_annsa_matches_oracle(name):
     err = assert_attention_close(out, O, cfg.dtype, f"annsa {name}")
     check_lse(lse, L)
     print(f"annsa {name}: max err {err:.3e}")
+
+
+@pytest.mark.parametrize("H", [3, 5])
+def test_annsa_head_counts_off_the_block_rounds(H):
+    """Head counts whose (heads x work-list entries) grid is not a whole number
+    of rounds of eight four-item runs (3 x 24 and 5 x 24 entries at the tiny
+    shape): part of the grid takes the XCD-run block order and the rest the
+    plain order.  Every item must still run exactly once: outputs, lse and
+    the fused search on every head against the oracle."""
+    require_gpu()
+    prep = prepared("tiny_f32", H=H)
+    st, cfg = prep["step"], prep["cfg"]
+    out, lse, best, bcos = fa.annsa_forward(dev(st.q, cfg.dtype), dev_ids(prep["q_ids"]), dev(st.k_cur, cfg.dtype),
+                                            dev(st.v_cur, cfg.dtype), dev_ids(prep["k_cur_ids"]), cfg.P,
+                                            cache=device_cache(prep), search=True)
+    O, L = oracle_annsa(prep, cfg.n0)
+    assert_attention_close(out, O, cfg.dtype, f"annsa H={H}")
+    check_lse(lse, L)
+    check_search(prep, best, bcos, cfg.n0, what=f"H={H}")
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "single_bf16"])
