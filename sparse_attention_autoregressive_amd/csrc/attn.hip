@@ -350,13 +350,18 @@ struct Blk {
     // groups that hold one query's keys.  Each lane swap (gfx950's
     // v_permlane32_swap / v_permlane16_swap) leaves x of the lane and of its
     // partner in the two results, in the VALU, without an LDS round trip.
+    // Larger of two scores.  gfx950's NaN-propagating maximum takes its
+    // operands as they are, where fmaxf first canonicalises each operand not
+    // known to be canonical (MFMA results, lane swaps): one more VALU op per
+    // operand.  Scores hold no NaN (masked keys are -inf), so the two agree.
+    static __device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
     static __device__ __forceinline__ float max_over_groups(float x) {
         const uint32_t u = __float_as_uint(x);
         const auto a32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        const float y = fmaxf(__uint_as_float(a32[0]), __uint_as_float(a32[1]));
+        const float y = smax(__uint_as_float(a32[0]), __uint_as_float(a32[1]));
         const uint32_t v = __float_as_uint(y);
         const auto a16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-        return fmaxf(__uint_as_float(a16[0]), __uint_as_float(a16[1]));
+        return smax(__uint_as_float(a16[0]), __uint_as_float(a16[1]));
     }
     static __device__ __forceinline__ void softmax_update(Acc& a, f32x4 (&s)[4], bool full, int kbase, int nk,
                                                           float scale_log2, int g) {
@@ -367,12 +372,11 @@ struct Blk {
                 for (int r = 0; r < 4; ++r)
                     if (kbase + kb4 * 16 + 4 * g + r >= nk) s[kb4][r] = kNegInf;
         }
-        float tmax = kNegInf;
+        float t[4];
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4)
-            tmax = fmaxf(tmax, fmaxf(fmaxf(s[kb4][0], s[kb4][1]), fmaxf(s[kb4][2], s[kb4][3])));
-        tmax = max_over_groups(tmax);
-        const float m_new = fmaxf(a.m, tmax);
+        for (int kb4 = 0; kb4 < 4; ++kb4) t[kb4] = smax(smax(s[kb4][0], s[kb4][1]), smax(s[kb4][2], s[kb4][3]));
+        const float tmax = max_over_groups(smax(smax(t[0], t[1]), smax(t[2], t[3])));
+        const float m_new = smax(a.m, tmax);
         const float c = scale_log2;
         const float m_ref = (a.m == kNegInf || (m_new - a.m) * c > (LAZY ? kRescaleLog2 : 0.f)) ? m_new : a.m;
         const float mc = (m_ref == kNegInf) ? 0.f : m_ref * c;
